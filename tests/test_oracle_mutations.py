@@ -1,0 +1,122 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and require the pins to
+catch every one of them.
+
+Each mutant is the oracle's C source with one edit: a dropped term, a wrong
+sign or index, a transposed operand, a reordered step, or an alternative
+reading of the pages that the design rejects.  The mutant is compiled to a
+temporary library and every pin of ``oracle_pins`` is run against it; at
+least one must fail.  This checks the pins, not the oracle.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kdn_oracle.c")
+
+
+def _block(src, start, end):
+    a = src.index(start)
+    b = src.index(end, a)
+    return a, b
+
+
+def _swap(src, m1, m2, m3):
+    """Swap the text [m1, m2) with [m2, m3)."""
+    a, b = _block(src, m1, m2)
+    _, c = _block(src, m2, m3)
+    return src[:a] + src[b:c] + src[a:b] + src[c:]
+
+
+def _sub(old, new):
+    def f(src):
+        assert old in src, old
+        return src.replace(old, new, 1)
+    return f
+
+
+MUTANTS = {
+    "error_sign": _sub("e[j] = vt[j] - e[j];", "e[j] = vt[j] + e[j];"),
+    "predict_alpha_not_squared": _sub(
+        "pm[i] = a[i] * a[i] * p[i] + xi[tok * dk + i];",
+        "pm[i] = a[i] * p[i] + xi[tok * dk + i];"),
+    "predict_drops_process_noise": _sub(
+        "pm[i] = a[i] * a[i] * p[i] + xi[tok * dk + i];",
+        "pm[i] = a[i] * a[i] * p[i];"),
+    "innovation_k_not_squared": _sub("s += pm[i] * kt[i] * kt[i];",
+                                     "s += pm[i] * kt[i];"),
+    "innovation_drops_obs_noise": _sub("double s = rt;", "double s = 0.0 * rt;"),
+    "mu_in_current_gain": _sub("s += pm[i] * kt[i] * kt[i];",
+                               "s += mu * pm[i] * kt[i] * kt[i];"),
+    "mu_dropped": _sub("const double den = rt + mu * pm[i] * kt[i] * kt[i];",
+                       "const double den = rt + pm[i] * kt[i] * kt[i];"),
+    "moment_matching_projection": _sub(
+        "p[i] = (den != 0.0) ? pm[i] * rt / den : pm[i];",
+        "p[i] = pm[i] - pm[i] * pm[i] * kt[i] * kt[i] / s;"),
+    "gain_uses_prior_not_predicted": _sub(
+        "w[i] = (s != 0.0) ? pm[i] * kt[i] / s : 0.0;",
+        "w[i] = (s != 0.0) ? p[i] * kt[i] / s : 0.0;"),
+    "gain_without_variance": _sub(
+        "w[i] = (s != 0.0) ? pm[i] * kt[i] / s : 0.0;",
+        "w[i] = (s != 0.0) ? kt[i] / s : 0.0;"),
+    "decay_after_read": lambda s: _swap(s, "        /* 3. Decay", "        /* 4. Read",
+                                        "        /* 5. Correct"),
+    "output_before_write": lambda s: _swap(s, "        /* 5. Correct",
+                                           "        /* 6. Read the output",
+                                           "    }\n}\n"),
+    "output_reads_key": _sub("ot[j] += S[i * dv + j] * qt[i];",
+                             "ot[j] += S[i * dv + j] * kt[i];"),
+    "write_wrong_value_index": _sub("S[i * dv + j] += w[i] * e[j];",
+                                    "S[i * dv + j] += w[i] * e[dv - 1 - j];"),
+    "read_transposed": _sub("e[j] += S[i * dv + j] * kt[i];",
+                            "e[j] += S[i * dv + j] * kt[dk - 1 - i];"),
+    "channel_decay_reversed": _sub("a[i] = alpha[tok * dk + i];",
+                                   "a[i] = alpha[tok * dk + (dk - 1 - i)];"),
+    "beta_from_head_zero": _sub("const double bt = beta[tok];",
+                                "const double bt = beta[(b * T + t) * H];"),
+    "decay_on_value_axis": _sub("S[i * dv + j] *= a[i];",
+                                "S[i * dv + j] *= a[j % dk];"),
+    "initial_state_ignored": _sub("        if (S0) {", "        if (0) {"),
+    "no_decay_scalar_gate": _sub("a[i] = alpha[tok];", "a[i] = 1.0;"),
+    "variance_not_carried": _sub("p[i] = (den != 0.0) ? pm[i] * rt / den : pm[i];",
+                                 "p[i] = (den != 0.0) ? p[i] : pm[i];"),
+}
+
+
+@pytest.fixture(scope="module")
+def tmpdir_mut():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmpdir_mut):
+    with open(SRC) as f:
+        src = f.read()
+    mutated = MUTANTS[name](src)
+    assert mutated != src
+    c = os.path.join(tmpdir_mut, f"{name}.c")
+    so = os.path.join(tmpdir_mut, f"lib{name}.so")
+    with open(c, "w") as f:
+        f.write(mutated)
+    oracle.build(src=c, out=so)
+    lib = oracle.OracleLib(so)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib.recurrence)
+        except (AssertionError, FloatingPointError, ValueError,
+                ZeroDivisionError, RuntimeError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name!r}"
+
+
+def test_unmutated_source_passes_every_pin(tmpdir_mut):
+    so = os.path.join(tmpdir_mut, "libclean.so")
+    oracle.build(src=SRC, out=so)
+    lib = oracle.OracleLib(so)
+    for pin in oracle_pins.ALL_PINS:
+        pin(lib.recurrence)
