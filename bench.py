@@ -1,0 +1,276 @@
+"""Benchmark of the delta-rule / diagonal-KDN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workloads all|headline]
+
+One step is one chunkwise prefill call over the Gated DeltaNet workload
+(B=4, H=16, T=4096, d_k=d_v=128, bf16 inputs, fp32 state, C=64) with inputs
+resident in HBM.  Rank 0 prints ONE JSON line with the headline value
+(prefill tokens/s), the roofline of the prefill kernel (HBM-bound by its
+algorithmic bytes; the MFMA fraction of its algorithmic flops is reported
+next to it), the fp64 oracle timed on the host cores, and the other
+workloads (KDA and diagonal-KDN prefill, diagonal-KDN decode) each with its
+own roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + decode steps/s per head-state; % MFMA / % HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_decode.hip", "kdn_device.h", "kdn_launch.h"]
+
+
+def kernel_hash(names=KERNEL_SOURCES):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_attention_recurrent_delta_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_bytes(variant, B, T, H, dk, dv, es, has_S0):
+    tok = B * T * H
+    n = tok * (2 * dk + 2 * dv) * es               # q, k, v, o
+    if variant == "gated_deltanet":
+        n += tok * es
+    elif variant in ("kda", "diag_kdn"):
+        n += tok * dk * es
+    if variant == "diag_kdn":
+        n += tok * dk * es + tok * es               # xi, r
+        n += 2 * B * H * dk * 4                     # p0, p_out
+    else:
+        n += tok * es                               # beta
+    n += B * H * dk * dv * 4 * (2 if has_S0 else 1)
+    return n
+
+
+def prefill_flops_per_head_token(C, dk, dv):
+    # A_kk, A_qk (2 C dk), T solve (C^2/3), products with T ((C-1)(dk+dv)),
+    # A_qk E ((C+1) dv), K~S, Q~S, W~^T E (6 dk dv); triangles counted as half.
+    return 2 * C * dk + C * C / 3 + (C - 1) * (dk + dv) + (C + 1) * dv + 6 * dk * dv
+
+
+def decode_bytes(N, H, dk, dv, es):
+    """Diagonal-KDN decode step: S and p read and written once; q, k, alpha,
+    xi [dk], v [dv], r read; o [dv] written."""
+    nh = N * H
+    return (nh * dk * dv * 4 * 2 + nh * dk * 4 * 2 + nh * 4 * dk * es
+            + nh * dv * es + nh * es + nh * dv * es)
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / 1e3
+
+
+def bench_prefill(name, steps, warmup, torch, kdn, synth):
+    c = synth.CONFIGS[name]
+    inp = synth.gen_config(name, device="cuda")
+    B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
+    o = torch.empty((B, T, H, dv), dtype=inp["q"].dtype, device="cuda")
+    S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+    p = torch.empty_like(inp["p0"]) if c["variant"] == "diag_kdn" else None
+
+    def step():
+        kdn.prefill(c["variant"], inp["q"], inp["k"], inp["v"], alpha=inp.get("alpha"),
+                    beta=inp.get("beta"), proc_noise=inp.get("xi"),
+                    obs_noise=inp.get("r"), S0=inp.get("S0"), p0=inp.get("p0"),
+                    out=(o, S, p))
+
+    wall, gpu = time_launches(step, steps, warmup, torch)
+    es = 2 if c["dtype"] == "bf16" else 4
+    C = kdn.kdn_chunk_prefill_chunk_size(1 if c["dtype"] == "bf16" else 0, dk, dv, 0)
+    nbytes = prefill_bytes(c["variant"], B, T, H, dk, dv, es, inp.get("S0") is not None)
+    flops = prefill_flops_per_head_token(C, dk, dv) * B * H * T
+    launch_s = gpu / steps
+    traffic = load_traffic(f"prefill_{name}")
+    res = {
+        "value": B * T * steps / wall, "unit": "tokens/s",
+        "head_tokens_per_s": B * H * T * steps / wall,
+        "ms_per_step": wall / steps * 1e3,
+        "config": {"workload": f"{name}_prefill", "variant": c["variant"], "B": B,
+                   "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": C,
+                   "dtype": c["dtype"]},
+        "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "kernel_ms": launch_s * 1e3},
+        "mfma": {"achieved": flops / launch_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": flops / launch_s / 1e12 / BF16_PEAK_TFLOPS,
+                 "algorithmic_flops": flops},
+    }
+    del inp, o, S, p
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(name, reps, torch, kdn, synth):
+    c = synth.CONFIGS[name]
+    N, H, steps, dk, dv = c["N"], c["H"], c["steps"], c["dk"], c["dv"]
+    d = synth.gen_decode(N, H, steps, dk, dv, c["dtype"], seed=synth.seed_of(name),
+                         device="cuda")
+    S = d["S0"].clone()
+    p = d["p0"].clone()
+    o = torch.empty((N, H, dv), dtype=d["q"].dtype, device="cuda")
+    args = [(d["q"][t], d["k"][t], d["v"][t], d["alpha"][t], d["xi"][t], d["r"][t])
+            for t in range(steps)]
+
+    def run_all():
+        for (q, k, v, a, x, r) in args:
+            kdn.decode("diag_kdn", q, k, v, S, p, alpha=a, proc_noise=x, obs_noise=r,
+                       o=o)
+
+    wall, gpu = time_launches(run_all, reps, 1, torch)
+    nsteps = steps * reps
+    es = 2 if c["dtype"] == "bf16" else 4
+    nbytes = decode_bytes(N, H, dk, dv, es)
+    launch_s = gpu / nsteps
+    res = {
+        "value": nsteps / wall, "unit": "steps/s",
+        "head_state_steps_per_s": nsteps * N * H / wall,
+        "ms_per_step": wall / nsteps * 1e3,
+        "config": {"workload": f"{name}", "variant": "diag_kdn", "N": N, "H": H,
+                   "steps": steps, "d_k": dk, "d_v": dv, "dtype": c["dtype"]},
+        "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": load_traffic(name), "algorithmic_bytes": nbytes,
+                     "kernel_ms": launch_s * 1e3},
+    }
+    del d, S, p, o, args
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name, synth, budget_s=20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    whole-length (batch, head) streams, as many as fit the time budget."""
+    import numpy as np
+    import torch
+    import oracle
+    c = synth.CONFIGS[name]
+    inp = synth.gen_config(name, device="cpu")
+    B, T, H = c["B"], c["T"], c["H"]
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    f64 = synth.to_f64
+
+    def sample(nheads):
+        heads = [(i // H, i % H) for i in range(nheads)]
+        sl = {}
+        for k in ("q", "k", "v", "alpha", "beta", "xi", "r"):
+            x = inp.get(k)
+            if x is None:
+                sl[k] = None
+                continue
+            parts = [f64(x[b:b + 1, :, h:h + 1]) for (b, h) in heads]
+            sl[k] = np.concatenate(parts, axis=2)
+        p0 = None if c["variant"] != "diag_kdn" else np.ones((1, nheads, c["dk"]))
+        return sl, p0
+
+    sl, p0 = sample(1)
+    t0 = time.perf_counter()
+    oracle.recurrence(c["variant"], sl["q"], sl["k"], sl["v"], alpha=sl["alpha"],
+                      beta=sl["beta"], xi=sl["xi"], r=sl["r"], p0=p0, nthreads=1)
+    one = time.perf_counter() - t0
+    nheads = int(max(1, min(B * H, budget_s * threads / max(one, 1e-6))))
+    nheads = max(1, (nheads // threads) * threads) if nheads >= threads else nheads
+    sl, p0 = sample(nheads)
+    used = min(threads, nheads)
+    reps, el = 0, 0.0
+    # whole sample, repeated until about a quarter of the budget has elapsed
+    while reps == 0 or el < budget_s / 4:
+        t0 = time.perf_counter()
+        oracle.recurrence(c["variant"], sl["q"], sl["k"], sl["v"], alpha=sl["alpha"],
+                          beta=sl["beta"], xi=sl["xi"], r=sl["r"], p0=p0,
+                          nthreads=threads)
+        el += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * nheads * T / H / el, "unit": "tokens/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{nheads} of {B * H} (batch, head) streams at full length "
+                      f"T={T} ({nheads * T} head-tokens) x {reps} passes, fp64, "
+                      f"{el:.1f} s on {used} threads; tokens/s counts all {H} heads "
+                      f"of a token"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", choices=["all", "headline"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the recurrence shards "
+              "over (batch, head) with no communication, so N GPUs = N "
+              "independent copies of this run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_recurrent_delta_amd import kdn, synth
+    kdn.ensure_built()
+    torch.cuda.set_device(0)
+
+    head = bench_prefill("gated_deltanet", args.steps, args.warmup, torch, kdn, synth)
+    out = {
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workloads)",
+        "config": dict(head["config"], parallelism="single GPU"),
+        "roofline": head["roofline"], "mfma": head["mfma"],
+    }
+    if args.workloads == "all":
+        w = {}
+        for name in ("kda", "diag_kdn"):
+            w[f"{name}_prefill"] = bench_prefill(name, max(3, args.steps // 2),
+                                                 args.warmup, torch, kdn, synth)
+        w["decode_diag_kdn"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
+        out["workloads"] = w
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline("gated_deltanet", synth)
+    out["kernel_hash"] = kernel_hash()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * kdn.h -- C ABI of the MI355X (gfx950) delta-rule / diagonal-KDN library.
+ *
+ * Per head the library keeps an associative memory S (d_k x d_v, float32)
+ * and, for diagonal KDN, a per-channel variance p (d_k, float32).  For each
+ * token, in this order:
+ *   1. decay vector a: 1 (DeltaNet), alpha_t * 1 (Gated DeltaNet), or the
+ *      per-key-channel vector alpha_t (KDA, diagonal KDN);
+ *   2. write vector w: beta_t k_t, or for diagonal KDN the Kalman gain
+ *        p- = a*a*p + xi_t,  s = r_t + sum_i p-_i k_i^2,  w = p- (.) k / s
+ *      (w = 0 if s == 0) followed by the mean-field variance update
+ *        p_i = p-_i r_t / (r_t + mu p-_i k_i^2)   (p-_i if that is 0/0);
+ *   3. S <- diag(a) S;   4. e = v_t - S^T k_t;   5. S <- S + w e^T;
+ *   6. o_t = S^T q_t.
+ * Sources (page title, section):
+ *   - "Внимание в LLM · часть 11 -- Память с поправкой", sections "Сначала
+ *     решить, сколько прошлого оставить" (gated state) and "Записать не новое
+ *     значение, а ошибку памяти" (read / compare / correct);
+ *   - "معماری KDA: حذف تداخل حافظه با قانون دلتا در توالی‌های بلند", sections
+ *     "تکامل قانون دلتا", "از فراموشی کلی به فراموشی جزئی" (decay before the
+ *     delta write; per-channel retention) and "پیاده‌سازی فنی و گذارهای DPLR"
+ *     (fused-recurrent decode vs chunkwise prefill);
+ *   - "给记忆装一个信任度探测器：Kalman Delta Networks 如何让AI知道自己"记得准不准"",
+ *     sections "把记忆问题重新想成一个滤波问题" and "对角近似：把矩阵压扁成一个向量"
+ *     (Kalman predict/update, diagonal covariance with exact mean, information
+ *     scaling mu).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major data
+ *     owned by the caller.  The library never allocates, frees or keeps them.
+ *   - Per-token inputs (q, k, v, alpha, beta, proc_noise, obs_noise) and the
+ *     output o use the call's dtype; S and p are always float32.
+ *   - Every pointer must be 16-byte aligned (else KDN_ERR_ALIGN).
+ *   - A pointer the variant does not use must be NULL.  An empty tensor may
+ *     be passed as NULL: the per-token tensors when there are no tokens, the
+ *     state tensors when there are no heads.
+ *   - All validation runs on the host before any HIP call; on an error nothing
+ *     is launched and no output is touched.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising.  Faults surface at the caller's
+ *     next synchronisation.  Non-finite inputs are not checked; they propagate.
+ *   - Argument contracts that are not checked on the device: alpha in [0, 1],
+ *     proc_noise >= 0, obs_noise >= 0.
+ *   - Thread-safe: no global mutable state.
+ */
+#ifndef KDN_H
+#define KDN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kdn_variant {
+    KDN_DELTANET = 0,        /* no decay, write strength beta            */
+    KDN_GATED_DELTANET = 1,  /* scalar decay alpha_t per token/head      */
+    KDN_KDA = 2,             /* per-key-channel decay alpha_t[d_k]       */
+    KDN_DIAG_KDN = 3         /* per-channel decay + diagonal Kalman gain */
+} kdn_variant;
+
+typedef enum kdn_dtype {
+    KDN_F32 = 0,
+    KDN_BF16 = 1
+} kdn_dtype;
+
+typedef enum kdn_status {
+    KDN_OK = 0,
+    KDN_ERR_NULL = 1,         /* a required pointer is NULL, or a pointer the
+                                 variant does not use is non-NULL          */
+    KDN_ERR_SHAPE = 2,        /* negative or overflowing sizes             */
+    KDN_ERR_UNSUPPORTED = 3,  /* variant/dtype/d_k/d_v/chunk not built      */
+    KDN_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned          */
+    KDN_ERR_ALIAS = 5,        /* an output overlaps an input it may not    */
+    KDN_ERR_HIP = 6           /* the HIP runtime refused the launch        */
+} kdn_status;
+
+/*
+ * Chunkwise prefill of T tokens for B sequences x H heads (the chunked form
+ * equals the serial recurrence exactly in exact arithmetic: provisional errors
+ * resolved by a causal triangular solve -- "معماری KDA ...", section "حل مشکل
+ * وابستگی علی").
+ *
+ *   q, k        [B, T, H, d_k]  dtype
+ *   v           [B, T, H, d_v]  dtype
+ *   alpha       NULL (DeltaNet) | [B, T, H] (Gated DeltaNet) |
+ *               [B, T, H, d_k] (KDA, diagonal KDN)            dtype
+ *   beta        [B, T, H] dtype for DeltaNet / GDN / KDA; NULL for diag KDN
+ *   proc_noise  [B, T, H, d_k] dtype, diagonal KDN only (else NULL)
+ *   obs_noise   [B, T, H]      dtype, diagonal KDN only (else NULL)
+ *   S0          [B, H, d_k, d_v] float32, or NULL for a zero memory
+ *   p0          [B, H, d_k] float32, required for diagonal KDN (else NULL)
+ *   o           [B, T, H, d_v] dtype (output, o_t = S_t^T q_t)
+ *   S_out       [B, H, d_k, d_v] float32 (output); may be exactly S0, must not
+ *               overlap it otherwise
+ *   p_out       [B, H, d_k] float32 (output, diagonal KDN only, else NULL);
+ *               must not overlap p0
+ *   mu          information scaling of the variance update (diagonal KDN
+ *               only; 1 = unscaled)
+ *   chunk       chunk length C; 0 picks the library default (64 for bf16,
+ *               32 for float32 with d_k = 128, else 64)
+ * Supported: d_k, d_v in {64, 128}; dtype KDN_F32 or KDN_BF16; chunk in
+ * {0, 32, 64} subject to the per-dtype limits above; T >= 0 (T = 0 copies
+ * S0 / p0 to S_out / p_out); B * H * d_k * d_v < 2^31.
+ * o must not overlap any input.
+ */
+kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype,
+                             int B, int T, int H, int d_k, int d_v, int chunk,
+                             float mu,
+                             const void *q, const void *k, const void *v,
+                             const void *alpha, const void *beta,
+                             const void *proc_noise, const void *obs_noise,
+                             const float *S0, const float *p0,
+                             void *o, float *S_out, float *p_out,
+                             void *stream);
+
+/*
+ * One decode step: one token for each of N sequences x H heads, from the
+ * resident state (the fused-recurrent regime: "معماری KDA ...", section
+ * "پیاده‌سازی فنی و گذارهای DPLR").
+ *
+ *   q, k        [N, H, d_k] dtype;   v [N, H, d_v] dtype
+ *   alpha       NULL | [N, H] | [N, H, d_k] dtype (as for prefill)
+ *   beta        [N, H] dtype, NULL for diagonal KDN
+ *   proc_noise  [N, H, d_k] dtype, obs_noise [N, H] dtype (diagonal KDN only)
+ *   S           [N, H, d_k, d_v] float32, read and updated IN PLACE
+ *   p           [N, H, d_k] float32, read and updated in place (diag KDN only,
+ *               else NULL)
+ *   o           [N, H, d_v] dtype (output)
+ * Supported: d_k, d_v in {64, 128}; dtype KDN_F32 or KDN_BF16; N, H >= 0.
+ * o must not overlap any input or S / p.
+ */
+kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype,
+                                int N, int H, int d_k, int d_v, float mu,
+                                const void *q, const void *k, const void *v,
+                                const void *alpha, const void *beta,
+                                const void *proc_noise, const void *obs_noise,
+                                float *S, float *p, void *o, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kdn_status_string(kdn_status status);
+
+/* The chunk length kdn_chunk_prefill uses for `chunk` = 0 (or the validated
+ * explicit value), or -1 if the combination is not supported. */
+int kdn_chunk_prefill_chunk_size(kdn_dtype dtype, int d_k, int d_v, int chunk);
+
+/* ABI version of this header (incremented on any incompatible change). */
+int kdn_abi_version(void);
+
+#define KDN_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDN_H */

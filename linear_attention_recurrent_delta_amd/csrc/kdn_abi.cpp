@@ -1,0 +1,204 @@
+// kdn_abi.cpp -- the C ABI declared in include/kdn.h: host-side validation of
+// every argument (before any HIP call), then one kernel launch on the
+// caller's stream.
+#include "kdn.h"
+#include "kdn_launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges, empty ranges never overlap)
+bool overlap(const void *a, long long na, const void *b, long long nb) {
+    if (!a || !b || na <= 0 || nb <= 0)
+        return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+bool valid_variant(int v) { return v >= KDN_DELTANET && v <= KDN_DIAG_KDN; }
+bool valid_dtype(int d) { return d == KDN_F32 || d == KDN_BF16; }
+bool valid_dim(int d) { return d == 64 || d == 128; }
+
+// Gate pointers the variant does not use must be NULL; the ones it uses must
+// be non-NULL unless the per-token tensors are empty.
+kdn_status check_gates(int variant, const void *alpha, const void *beta,
+                       const void *xi, const void *r, bool empty) {
+    const bool need_alpha = variant != KDN_DELTANET;
+    const bool kdn = variant == KDN_DIAG_KDN;
+    if (!need_alpha && alpha) return KDN_ERR_NULL;
+    if (kdn && beta) return KDN_ERR_NULL;
+    if (!kdn && (xi || r)) return KDN_ERR_NULL;
+    if (empty) return KDN_OK;
+    if (need_alpha && !alpha) return KDN_ERR_NULL;
+    if (!kdn && !beta) return KDN_ERR_NULL;
+    if (kdn && (!xi || !r)) return KDN_ERR_NULL;
+    return KDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kdn_abi_version(void) { return KDN_ABI_VERSION; }
+
+const char *kdn_status_string(kdn_status s) {
+    switch (s) {
+    case KDN_OK: return "ok";
+    case KDN_ERR_NULL: return "a required pointer is NULL, or a pointer the variant does not use is set";
+    case KDN_ERR_SHAPE: return "negative or overflowing sizes";
+    case KDN_ERR_UNSUPPORTED: return "unsupported variant, dtype, head dimension or chunk length";
+    case KDN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDN_ERR_ALIAS: return "an output overlaps an input it may not overlap";
+    case KDN_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    }
+    return "unknown status";
+}
+
+int kdn_chunk_prefill_chunk_size(kdn_dtype dtype, int d_k, int d_v, int chunk) {
+    if (!valid_dtype(dtype) || !valid_dim(d_k) || !valid_dim(d_v))
+        return -1;
+    if (chunk == 0)
+        chunk = (dtype == KDN_F32 && d_k == 128) ? 32 : 64;
+    if (chunk != 32 && chunk != 64)
+        return -1;
+    if (dtype == KDN_F32 && d_k == 128 && chunk == 64)
+        return -1;   // float32 operands of a 64 x 128 chunk exceed the LDS
+    return chunk;
+}
+
+kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
+                             int H, int d_k, int d_v, int chunk, float mu,
+                             const void *q, const void *k, const void *v,
+                             const void *alpha, const void *beta,
+                             const void *proc_noise, const void *obs_noise,
+                             const float *S0, const float *p0, void *o,
+                             float *S_out, float *p_out, void *stream) {
+    if (!valid_variant(variant) || !valid_dtype(dtype))
+        return KDN_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || H < 0 || d_k <= 0 || d_v <= 0)
+        return KDN_ERR_SHAPE;
+    const long long bh = (long long)B * H;
+    const long long tok = bh * T;
+    if (bh * d_k * d_v >= (1LL << 31) || tok * (d_k > d_v ? d_k : d_v) >= (1LL << 40))
+        return KDN_ERR_SHAPE;
+    if (!valid_dim(d_k) || !valid_dim(d_v))
+        return KDN_ERR_UNSUPPORTED;
+    const int C = kdn_chunk_prefill_chunk_size(dtype, d_k, d_v, chunk);
+    if (C < 0)
+        return KDN_ERR_UNSUPPORTED;
+    const bool kdn = variant == KDN_DIAG_KDN;
+    // Empty tensors may be passed as NULL (a zero-size torch tensor has no
+    // storage): per-token tensors when B*H*T = 0, state tensors when B*H = 0.
+    if (tok > 0 && (!q || !k || !v || !o))
+        return KDN_ERR_NULL;
+    if (kdn_status st = check_gates(variant, alpha, beta, proc_noise, obs_noise, tok == 0))
+        return st;
+    if (bh > 0 && !S_out)
+        return KDN_ERR_NULL;
+    if (kdn && bh > 0 && (!p0 || !p_out))
+        return KDN_ERR_NULL;
+    if (!kdn && (p0 || p_out))
+        return KDN_ERR_NULL;
+    const void *ptrs[] = {q, k, v, alpha, beta, proc_noise, obs_noise, S0, p0,
+                          o, S_out, p_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return KDN_ERR_ALIGN;
+
+    const long long es = dtype == KDN_BF16 ? 2 : 4;
+    const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
+    const long long n_a = variant == KDN_GATED_DELTANET ? tok * es
+                        : (variant == KDN_DELTANET ? 0 : tok * d_k * es);
+    const long long n_b = kdn ? 0 : tok * es;
+    const long long n_x = kdn ? tok * d_k * es : 0, n_r = kdn ? tok * es : 0;
+    const long long n_S = bh * d_k * d_v * 4, n_p = kdn ? bh * d_k * 4 : 0;
+    // o overlaps no input; S_out may be S0 exactly; p_out must not touch p0.
+    struct R { const void *p; long long n; } ins[] = {
+        {q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, n_b},
+        {proc_noise, n_x}, {obs_noise, n_r}, {S0, n_S}, {p0, n_p}};
+    for (const R &x : ins) {
+        if (overlap(o, tok * d_v * es, x.p, x.n)) return KDN_ERR_ALIAS;
+        if (x.p != S0 && overlap(S_out, n_S, x.p, x.n)) return KDN_ERR_ALIAS;
+        if (kdn && overlap(p_out, n_p, x.p, x.n)) return KDN_ERR_ALIAS;
+    }
+    if (S0 && S0 != S_out && overlap(S_out, n_S, S0, n_S)) return KDN_ERR_ALIAS;
+    if (overlap(o, tok * d_v * es, S_out, n_S)) return KDN_ERR_ALIAS;
+    if (kdn && (overlap(o, tok * d_v * es, p_out, n_p) || overlap(S_out, n_S, p_out, n_p)))
+        return KDN_ERR_ALIAS;
+
+    kdn::PrefillParams P;
+    P.variant = variant;
+    P.bf16 = dtype == KDN_BF16;
+    P.B = B; P.T = T; P.H = H; P.dk = d_k; P.dv = d_v; P.chunk = C;
+    P.mu = mu;
+    P.q = q; P.k = k; P.v = v; P.alpha = alpha; P.beta = beta;
+    P.xi = proc_noise; P.r = obs_noise;
+    P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
+    const hipError_t e = kdn::launch_prefill(P, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;
+}
+
+kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype, int N, int H,
+                                int d_k, int d_v, float mu, const void *q,
+                                const void *k, const void *v, const void *alpha,
+                                const void *beta, const void *proc_noise,
+                                const void *obs_noise, float *S, float *p, void *o,
+                                void *stream) {
+    if (!valid_variant(variant) || !valid_dtype(dtype))
+        return KDN_ERR_UNSUPPORTED;
+    if (N < 0 || H < 0 || d_k <= 0 || d_v <= 0)
+        return KDN_ERR_SHAPE;
+    const long long nh = (long long)N * H;
+    if (nh * d_k * d_v >= (1LL << 31))
+        return KDN_ERR_SHAPE;
+    if (!valid_dim(d_k) || !valid_dim(d_v))
+        return KDN_ERR_UNSUPPORTED;
+    const bool kdn = variant == KDN_DIAG_KDN;
+    if (nh > 0 && (!q || !k || !v || !o || !S))
+        return KDN_ERR_NULL;
+    if (kdn_status st = check_gates(variant, alpha, beta, proc_noise, obs_noise, nh == 0))
+        return st;
+    if (!kdn && p)
+        return KDN_ERR_NULL;
+    if (kdn && nh > 0 && !p)
+        return KDN_ERR_NULL;
+    const void *ptrs[] = {q, k, v, alpha, beta, proc_noise, obs_noise, S, p, o};
+    for (const void *x : ptrs)
+        if (x && !aligned16(x))
+            return KDN_ERR_ALIGN;
+
+    const long long es = dtype == KDN_BF16 ? 2 : 4;
+    const long long n_qk = nh * d_k * es, n_v = nh * d_v * es;
+    const long long n_a = variant == KDN_GATED_DELTANET ? nh * es
+                        : (variant == KDN_DELTANET ? 0 : nh * d_k * es);
+    const long long n_b = kdn ? 0 : nh * es;
+    const long long n_x = kdn ? nh * d_k * es : 0, n_r = kdn ? nh * es : 0;
+    const long long n_S = nh * d_k * d_v * 4, n_p = kdn ? nh * d_k * 4 : 0;
+    const long long n_o = nh * d_v * es;
+    struct R { const void *p; long long n; } ins[] = {
+        {q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, n_b},
+        {proc_noise, n_x}, {obs_noise, n_r}};
+    for (const R &x : ins) {
+        if (overlap(o, n_o, x.p, x.n)) return KDN_ERR_ALIAS;
+        if (overlap(S, n_S, x.p, x.n)) return KDN_ERR_ALIAS;
+        if (kdn && overlap(p, n_p, x.p, x.n)) return KDN_ERR_ALIAS;
+    }
+    if (overlap(o, n_o, S, n_S) || (kdn && (overlap(o, n_o, p, n_p) ||
+                                            overlap(S, n_S, p, n_p))))
+        return KDN_ERR_ALIAS;
+
+    kdn::DecodeParams P;
+    P.variant = variant;
+    P.bf16 = dtype == KDN_BF16;
+    P.N = N; P.H = H; P.dk = d_k; P.dv = d_v; P.mu = mu;
+    P.q = q; P.k = k; P.v = v; P.alpha = alpha; P.beta = beta;
+    P.xi = proc_noise; P.r = obs_noise;
+    P.S = S; P.p = p; P.o = o;
+    const hipError_t e = kdn::launch_decode(P, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;
+}
+
+}  // extern "C"

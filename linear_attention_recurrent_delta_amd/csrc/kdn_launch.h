@@ -1,0 +1,46 @@
+// kdn_launch.h -- host-side launch parameters and launchers of the gfx950
+// kernels.  The C ABI (kdn_abi.cpp) validates arguments and fills these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kdn {
+
+struct DecodeParams {
+    int variant;       // kdn_variant
+    int bf16;          // 1: per-token tensors are bfloat16, 0: float32
+    int N, H, dk, dv;
+    float mu;
+    const void *q, *k, *v, *alpha, *beta, *xi, *r;
+    float *S;          // [N, H, dk, dv], in place
+    float *p;          // [N, H, dk], in place (diagonal KDN)
+    void *o;           // [N, H, dv]
+};
+
+struct PrefillParams {
+    int variant;
+    int bf16;
+    int B, T, H, dk, dv;
+    int chunk;         // C
+    float mu;
+    const void *q, *k, *v, *alpha, *beta, *xi, *r;
+    const float *S0;   // may be null
+    const float *p0;   // diagonal KDN
+    void *o;
+    float *S_out;
+    float *p_out;      // diagonal KDN
+};
+
+hipError_t launch_decode(const DecodeParams &P, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &P, hipStream_t stream);
+
+// Per-variant prefill launchers (one compilation unit each).
+hipError_t launch_prefill_v0(const PrefillParams &P, hipStream_t stream, int nv);
+hipError_t launch_prefill_v1(const PrefillParams &P, hipStream_t stream, int nv);
+hipError_t launch_prefill_v2(const PrefillParams &P, hipStream_t stream, int nv);
+hipError_t launch_prefill_v3(const PrefillParams &P, hipStream_t stream, int nv);
+
+// d_v block width one prefill workgroup owns for this problem.
+int prefill_value_block(const PrefillParams &P);
+
+}  // namespace kdn

@@ -1,0 +1,166 @@
+"""ctypes binding of libkdn.so (the C ABI declared in include/kdn.h).
+
+Argument marshalling only: tensors become device pointers, the current HIP
+stream is passed through, and a non-OK status raises.  Every step of the
+recurrence runs in the library's gfx950 kernels; PyTorch provides device
+memory and streams.  If the library is not built this module raises -- there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkdn.so")
+
+# kdn_variant / kdn_dtype / kdn_status values of include/kdn.h
+VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "diag_kdn": 3}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+STATUS = {0: "KDN_OK", 1: "KDN_ERR_NULL", 2: "KDN_ERR_SHAPE",
+          3: "KDN_ERR_UNSUPPORTED", 4: "KDN_ERR_ALIGN", 5: "KDN_ERR_ALIAS",
+          6: "KDN_ERR_HIP"}
+
+_lib = None
+
+
+class KdnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libkdn.so and declare its signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -m linear_attention_recurrent_delta_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.kdn_chunk_prefill.restype = i
+    lib.kdn_chunk_prefill.argtypes = [i, i, i, i, i, i, i, i, f] + [vp] * 13
+    lib.kdn_recurrent_decode.restype = i
+    lib.kdn_recurrent_decode.argtypes = [i, i, i, i, i, i, f] + [vp] * 11
+    lib.kdn_status_string.restype = ctypes.c_char_p
+    lib.kdn_status_string.argtypes = [i]
+    lib.kdn_chunk_prefill_chunk_size.restype = i
+    lib.kdn_chunk_prefill_chunk_size.argtypes = [i, i, i, i]
+    lib.kdn_abi_version.restype = i
+    lib.kdn_abi_version.argtypes = []
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def ensure_built():
+    """Build the library if no build is present, then load it."""
+    if not os.path.exists(LIB_PATH):
+        from . import build
+        build.build()
+    return load()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("kdn: tensor arguments must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(lib, st):
+    if st != 0:
+        raise KdnError(st, lib.kdn_status_string(st).decode())
+
+
+def kdn_status_string(status: int) -> str:
+    return load().kdn_status_string(int(status)).decode()
+
+
+def kdn_abi_version() -> int:
+    return int(load().kdn_abi_version())
+
+
+def kdn_chunk_prefill_chunk_size(dtype: int, d_k: int, d_v: int, chunk: int) -> int:
+    return int(load().kdn_chunk_prefill_chunk_size(int(dtype), d_k, d_v, chunk))
+
+
+def kdn_chunk_prefill(variant, dtype, B, T, H, d_k, d_v, chunk, mu, q, k, v,
+                      alpha, beta, proc_noise, obs_noise, S0, p0, o, S_out,
+                      p_out, stream=None):
+    """Raw entry point: same arguments as the C function (tensors or ints
+    for pointers, None for NULL)."""
+    lib = load()
+    st = lib.kdn_chunk_prefill(
+        int(variant), int(dtype), int(B), int(T), int(H), int(d_k), int(d_v),
+        int(chunk), float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _ptr(proc_noise), _ptr(obs_noise), _ptr(S0), _ptr(p0),
+        _ptr(o), _ptr(S_out), _ptr(p_out), _stream(stream))
+    _check(lib, st)
+
+
+def kdn_recurrent_decode(variant, dtype, N, H, d_k, d_v, mu, q, k, v, alpha,
+                         beta, proc_noise, obs_noise, S, p, o, stream=None):
+    """Raw entry point: same arguments as the C function."""
+    lib = load()
+    st = lib.kdn_recurrent_decode(
+        int(variant), int(dtype), int(N), int(H), int(d_k), int(d_v),
+        float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(proc_noise), _ptr(obs_noise), _ptr(S), _ptr(p), _ptr(o),
+        _stream(stream))
+    _check(lib, st)
+
+
+# ---------------------------------------------------------------------------
+# Tensor-shaped conveniences (allocate outputs, infer sizes, then call the
+# entry points above).
+# ---------------------------------------------------------------------------
+def prefill(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
+            obs_noise=None, S0=None, p0=None, mu=1.0, chunk=0, out=None,
+            stream=None):
+    """Chunkwise prefill.  q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bf16).
+    Returns (o, S, p); p is None unless variant is diag_kdn.  ``out`` may pass
+    preallocated (o, S_out, p_out)."""
+    vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = DTYPES[q.dtype]
+    if out is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+        S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+        p = (torch.empty((B, H, dk), dtype=torch.float32, device=q.device)
+             if vid == 3 else None)
+    else:
+        o, S, p = out
+    kdn_chunk_prefill(vid, dt, B, T, H, dk, dv, chunk, mu, q, k, v, alpha, beta,
+                      proc_noise, obs_noise, S0, p0, o, S, p, stream)
+    return o, S, p
+
+
+def decode(variant, q, k, v, S, p=None, alpha=None, beta=None, proc_noise=None,
+           obs_noise=None, mu=1.0, o=None, stream=None):
+    """One decode step; S [N,H,dk,dv] (and p [N,H,dk]) are updated in place.
+    Returns o [N,H,dv]."""
+    vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    kdn_recurrent_decode(vid, DTYPES[q.dtype], N, H, dk, dv, mu, q, k, v, alpha,
+                         beta, proc_noise, obs_noise, S, p, o, stream)
+    return o

@@ -1,0 +1,167 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load and export every symbol include/kdn.h declares, and
+argument validation must reject bad calls with the documented status codes
+before any HIP call.  Pointers here are fake addresses: every call below fails
+validation, so nothing touches a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrent_delta_amd import kdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdn.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EHIP = range(7)
+A = 1 << 32          # fake, 16-byte aligned device addresses spaced far apart
+MB = 1 << 26
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kdn.ensure_built()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kdn_chunk_prefill", "kdn_recurrent_decode", "kdn_status_string",
+              "kdn_chunk_prefill_chunk_size", "kdn_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version(lib):
+    assert lib.kdn_abi_version() == 1
+
+
+def test_status_strings(lib):
+    seen = set()
+    for s in range(7):
+        msg = lib.kdn_status_string(s).decode()
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert lib.kdn_status_string(99).decode() == "unknown status"
+
+
+def test_chunk_size_query(lib):
+    f = lib.kdn_chunk_prefill_chunk_size
+    assert f(1, 128, 128, 0) == 64
+    assert f(0, 64, 64, 0) == 64
+    assert f(0, 128, 128, 0) == 32
+    assert f(0, 128, 128, 64) == -1
+    assert f(1, 128, 64, 32) == 32
+    assert f(1, 96, 128, 0) == -1
+    assert f(1, 128, 128, 48) == -1
+    assert f(2, 128, 128, 0) == -1
+
+
+def _prefill_args(variant=1, dtype=1, B=2, T=100, H=4, dk=128, dv=128, chunk=0,
+                  **over):
+    kdn_ = variant == 3
+    a = dict(q=A, k=A + MB, v=A + 2 * MB,
+             alpha=None if variant == 0 else A + 3 * MB,
+             beta=None if kdn_ else A + 4 * MB,
+             xi=A + 5 * MB if kdn_ else None, r=A + 6 * MB if kdn_ else None,
+             S0=A + 7 * MB, p0=A + 8 * MB if kdn_ else None, o=A + 9 * MB,
+             S_out=A + 10 * MB, p_out=A + 11 * MB if kdn_ else None)
+    a.update(over)
+    return (variant, dtype, B, T, H, dk, dv, chunk, 1.0, a["q"], a["k"], a["v"],
+            a["alpha"], a["beta"], a["xi"], a["r"], a["S0"], a["p0"], a["o"],
+            a["S_out"], a["p_out"], None)
+
+
+def _decode_args(variant=3, dtype=1, N=8, H=4, dk=128, dv=128, **over):
+    kdn_ = variant == 3
+    a = dict(q=A, k=A + MB, v=A + 2 * MB,
+             alpha=None if variant == 0 else A + 3 * MB,
+             beta=None if kdn_ else A + 4 * MB,
+             xi=A + 5 * MB if kdn_ else None, r=A + 6 * MB if kdn_ else None,
+             S=A + 7 * MB, p=A + 8 * MB if kdn_ else None, o=A + 9 * MB)
+    a.update(over)
+    return (variant, dtype, N, H, dk, dv, 1.0, a["q"], a["k"], a["v"], a["alpha"],
+            a["beta"], a["xi"], a["r"], a["S"], a["p"], a["o"], None)
+
+
+PREFILL_CASES = [
+    ("bad variant", dict(variant=7), EUNSUP),
+    ("bad dtype", dict(dtype=5), EUNSUP),
+    ("negative B", dict(B=-1), ESHAPE),
+    ("negative T", dict(T=-3), ESHAPE),
+    ("negative H", dict(H=-2), ESHAPE),
+    ("zero d_k", dict(dk=0), ESHAPE),
+    ("d_k 96", dict(dk=96), EUNSUP),
+    ("d_v 256", dict(dv=256), EUNSUP),
+    ("chunk 48", dict(chunk=48), EUNSUP),
+    ("f32 d128 chunk 64", dict(dtype=0, chunk=64), EUNSUP),
+    ("state too large", dict(B=1 << 14, H=1 << 4), ESHAPE),
+    ("q NULL", dict(q=None), ENULL),
+    ("o NULL", dict(o=None), ENULL),
+    ("S_out NULL", dict(S_out=None), ENULL),
+    ("GDN without alpha", dict(alpha=None), ENULL),
+    ("GDN without beta", dict(beta=None), ENULL),
+    ("DeltaNet with alpha", dict(variant=0, alpha=A + 3 * MB), ENULL),
+    ("GDN with proc noise", dict(xi=A + 5 * MB), ENULL),
+    ("GDN with p0", dict(p0=A + 8 * MB), ENULL),
+    ("KDN with beta", dict(variant=3, beta=A + 4 * MB), ENULL),
+    ("KDN without obs noise", dict(variant=3, r=None), ENULL),
+    ("KDN without p0", dict(variant=3, p0=None), ENULL),
+    ("KDN without p_out", dict(variant=3, p_out=None), ENULL),
+    ("misaligned q", dict(q=A + 8), EALIGN),
+    ("misaligned S0", dict(S0=A + 7 * MB + 4), EALIGN),
+    ("o overlaps v", dict(o=A + 2 * MB + 4096), EALIAS),
+    ("S_out overlaps q", dict(S_out=A + 64), EALIAS),
+    ("S_out partially overlaps S0", dict(S_out=A + 7 * MB + 1024), EALIAS),
+    ("o overlaps S_out", dict(o=A + 10 * MB + 16), EALIAS),
+    ("KDN p_out equals p0", dict(variant=3, p_out=A + 8 * MB), EALIAS),
+]
+
+
+@pytest.mark.parametrize("name,over,status", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_validation(lib, name, over, status):
+    assert lib.kdn_chunk_prefill(*_prefill_args(**over)) == status
+
+
+DECODE_CASES = [
+    ("bad variant", dict(variant=-1), EUNSUP),
+    ("negative N", dict(N=-1), ESHAPE),
+    ("d_k 32", dict(dk=32), EUNSUP),
+    ("S NULL", dict(S=None), ENULL),
+    ("KDN without p", dict(p=None), ENULL),
+    ("GDN with p", dict(variant=1, p=A + 8 * MB), ENULL),
+    ("KDN with beta", dict(beta=A + 4 * MB), ENULL),
+    ("misaligned o", dict(o=A + 9 * MB + 2), EALIGN),
+    ("o overlaps S", dict(o=A + 7 * MB + 512), EALIAS),
+    ("S overlaps k", dict(S=A + MB), EALIAS),
+    ("p overlaps S", dict(p=A + 7 * MB + 256), EALIAS),
+]
+
+
+@pytest.mark.parametrize("name,over,status", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_validation(lib, name, over, status):
+    assert lib.kdn_recurrent_decode(*_decode_args(**over)) == status
+
+
+def test_binding_raises_with_status(lib):
+    with pytest.raises(kdn.KdnError) as e:
+        kdn.kdn_chunk_prefill(*_prefill_args(q=None)[:-1], stream=0)
+    assert e.value.status == ENULL
+
+
+def test_binding_missing_library_raises(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        kdn.load(str(tmp_path / "libkdn.so"))
