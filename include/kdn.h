@@ -30,7 +30,10 @@
  *     owned by the caller.  The library never allocates, frees or keeps them.
  *   - Per-token inputs (q, k, v, alpha, beta, proc_noise, obs_noise) and the
  *     output o use the call's dtype; S and p are always float32.
- *   - Every pointer must be 16-byte aligned (else KDN_ERR_ALIGN).
+ *   - Alignment (else KDN_ERR_ALIGN): tensors whose last axis is d_k or d_v
+ *     (q, k, v, per-channel alpha, proc_noise, o, S*, p*) start on a 16-byte
+ *     boundary; per-head scalars (beta, obs_noise, the Gated DeltaNet alpha)
+ *     on their element size.
  *   - A pointer the variant does not use must be NULL.  An empty tensor may
  *     be passed as NULL: the per-token tensors when there are no tokens, the
  *     state tensors when there are no heads.

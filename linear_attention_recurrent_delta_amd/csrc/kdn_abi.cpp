@@ -8,7 +8,7 @@
 
 namespace {
 
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // [a, a+na) and [b, b+nb) overlap (byte ranges, empty ranges never overlap)
 bool overlap(const void *a, long long na, const void *b, long long nb) {
@@ -102,13 +102,18 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
         return KDN_ERR_NULL;
     if (!kdn && (p0 || p_out))
         return KDN_ERR_NULL;
-    const void *ptrs[] = {q, k, v, alpha, beta, proc_noise, obs_noise, S0, p0,
-                          o, S_out, p_out};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p))
+    const long long es = dtype == KDN_BF16 ? 2 : 4;
+    // vectors of d_k / d_v elements: 16 bytes; per-head scalars: one element
+    const void *vec[] = {q, k, v, variant == KDN_GATED_DELTANET ? nullptr : alpha,
+                         proc_noise, S0, p0, o, S_out, p_out};
+    const void *sca[] = {beta, obs_noise, variant == KDN_GATED_DELTANET ? alpha : nullptr};
+    for (const void *x : vec)
+        if (x && !aligned(x, 16))
+            return KDN_ERR_ALIGN;
+    for (const void *x : sca)
+        if (x && !aligned(x, (uintptr_t)es))
             return KDN_ERR_ALIGN;
 
-    const long long es = dtype == KDN_BF16 ? 2 : 4;
     const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
     const long long n_a = variant == KDN_GATED_DELTANET ? tok * es
                         : (variant == KDN_DELTANET ? 0 : tok * d_k * es);
@@ -165,12 +170,17 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype, int N, int
         return KDN_ERR_NULL;
     if (kdn && nh > 0 && !p)
         return KDN_ERR_NULL;
-    const void *ptrs[] = {q, k, v, alpha, beta, proc_noise, obs_noise, S, p, o};
-    for (const void *x : ptrs)
-        if (x && !aligned16(x))
+    const long long es = dtype == KDN_BF16 ? 2 : 4;
+    const void *vec[] = {q, k, v, variant == KDN_GATED_DELTANET ? nullptr : alpha,
+                         proc_noise, S, p, o};
+    const void *sca[] = {beta, obs_noise, variant == KDN_GATED_DELTANET ? alpha : nullptr};
+    for (const void *x : vec)
+        if (x && !aligned(x, 16))
+            return KDN_ERR_ALIGN;
+    for (const void *x : sca)
+        if (x && !aligned(x, (uintptr_t)es))
             return KDN_ERR_ALIGN;
 
-    const long long es = dtype == KDN_BF16 ? 2 : 4;
     const long long n_qk = nh * d_k * es, n_v = nh * d_v * es;
     const long long n_a = variant == KDN_GATED_DELTANET ? nh * es
                         : (variant == KDN_DELTANET ? 0 : nh * d_k * es);

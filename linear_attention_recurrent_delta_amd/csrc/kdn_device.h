@@ -89,6 +89,126 @@ template <> struct Mma<float> {       // v_mfma_f32_16x16x4_f32
     }
 };
 
+// K = 16 step for small products (the triangular-inverse blocks).
+template <typename E> struct Mma16;
+
+template <> struct Mma16<bf16> {      // v_mfma_f32_16x16x16_bf16
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    // A: [row][k] pitch lda, rows (lane & 15), k = (lane >> 4) * 4 .. + 3
+    __device__ __forceinline__ static void tile(f32x4 &acc, const bf16 *A, int lda,
+                                                const bf16 *B, int ldb, int lane) {
+        const int r = lane & 15, ko = (lane >> 4) * 4;
+        const s16x4 av = *reinterpret_cast<const s16x4 *>(A + r * lda + ko);
+        const s16x4 bv = *reinterpret_cast<const s16x4 *>(B + r * ldb + ko);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+    }
+};
+
+template <> struct Mma16<float> {     // 4 x v_mfma_f32_16x16x4_f32
+    __device__ __forceinline__ static void tile(f32x4 &acc, const float *A, int lda,
+                                                const float *B, int ldb, int lane) {
+        const int r = lane & 15, ko = lane >> 4;
+        float a[4], b[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            a[s] = A[r * lda + ko + 4 * s];
+            b[s] = B[r * ldb + ko + 4 * s];
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    }
+};
+
+// As mma_tile with a compile-time K: every operand load is issued before the
+// first MFMA so the LDS latency is paid once per tile.
+template <typename E, int K>
+__device__ __forceinline__ void mma_tile_k(f32x4 &acc, const E *A, int lda,
+                                           const E *B, int ldb, int lane) {
+    constexpr int NS = K / Mma<E>::KSTEP;
+    static_assert(NS * Mma<E>::KSTEP == K, "K multiple of the MFMA step");
+    const int r = lane & 15;
+    const int ko = (lane >> 4) * Mma<E>::KPL;
+    const E *pa = A + r * lda + ko;
+    const E *pb = B + r * ldb + ko;
+    if constexpr (sizeof(E) == 2) {
+        bf16x8 av[NS], bv[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            av[s] = *reinterpret_cast<const bf16x8 *>(pa + s * Mma<E>::KSTEP);
+            bv[s] = *reinterpret_cast<const bf16x8 *>(pb + s * Mma<E>::KSTEP);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], bv[s], acc, 0, 0, 0);
+    } else {
+        float av[NS], bv[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            av[s] = pa[s * Mma<E>::KSTEP];
+            bv[s] = pb[s * Mma<E>::KSTEP];
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
+    }
+}
+
+// Eight consecutive elements of E in LDS (16-byte aligned) as floats.
+__device__ __forceinline__ void lds_ld8(const bf16 *p, float (&f)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void lds_ld8(const float *p, float (&f)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void lds_st8(bf16 *p, const float (&f)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = static_cast<bf16>(f[i]);
+    *reinterpret_cast<bf16x8 *>(p) = v;
+}
+__device__ __forceinline__ void lds_st8(float *p, const float (&f)[8]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+// N (1, 2 or 4) consecutive elements of E in LDS, aligned to N elements.
+template <int N>
+__device__ __forceinline__ void lds_stn(bf16 *p, const float *f) {
+    if constexpr (N == 4) {
+        bf16x4 v;
+        v[0] = static_cast<bf16>(f[0]); v[1] = static_cast<bf16>(f[1]);
+        v[2] = static_cast<bf16>(f[2]); v[3] = static_cast<bf16>(f[3]);
+        *reinterpret_cast<bf16x4 *>(p) = v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            p[i] = static_cast<bf16>(f[i]);
+    }
+}
+template <int N>
+__device__ __forceinline__ void lds_stn(float *p, const float *f) {
+    if constexpr (N == 4) {
+        *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            p[i] = f[i];
+    }
+}
+
+// Fast reciprocal (v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // acc += A[m0:m0+16, 0:K] * B[0:K, n0:n0+16], A given as [row][k] with
 // pitch lda, B as [col][k] with pitch ldb (both in elements).  K must be a
 // multiple of Mma<E>::KSTEP.

@@ -123,6 +123,8 @@ PREFILL_CASES = [
     ("KDN without p_out", dict(variant=3, p_out=None), ENULL),
     ("misaligned q", dict(q=A + 8), EALIGN),
     ("misaligned S0", dict(S0=A + 7 * MB + 4), EALIGN),
+    ("misaligned KDA alpha", dict(variant=2, alpha=A + 3 * MB + 2), EALIGN),
+    ("odd scalar beta", dict(beta=A + 4 * MB + 1), EALIGN),
     ("o overlaps v", dict(o=A + 2 * MB + 4096), EALIAS),
     ("S_out overlaps q", dict(S_out=A + 64), EALIAS),
     ("S_out partially overlaps S0", dict(S_out=A + 7 * MB + 1024), EALIAS),
@@ -145,6 +147,8 @@ DECODE_CASES = [
     ("GDN with p", dict(variant=1, p=A + 8 * MB), ENULL),
     ("KDN with beta", dict(beta=A + 4 * MB), ENULL),
     ("misaligned o", dict(o=A + 9 * MB + 2), EALIGN),
+    ("misaligned S", dict(S=A + 7 * MB + 8), EALIGN),
+    ("odd scalar r", dict(r=A + 6 * MB + 1), EALIGN),
     ("o overlaps S", dict(o=A + 7 * MB + 512), EALIAS),
     ("S overlaps k", dict(S=A + MB), EALIAS),
     ("p overlaps S", dict(p=A + 7 * MB + 256), EALIAS),
