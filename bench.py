@@ -237,6 +237,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain streaming kernel (out = 1.0 * in, "
+                         "float32) over this many MiB, as a reference for "
+                         "hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the recurrence shards "
@@ -248,6 +252,14 @@ def main():
     from linear_attention_recurrent_delta_amd import kdn, synth
     kdn.ensure_built()
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     head = bench_prefill("gated_deltanet", args.steps, args.warmup, torch, kdn, synth)
     out = {
