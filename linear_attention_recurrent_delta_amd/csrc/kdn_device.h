@@ -184,7 +184,12 @@ __device__ __forceinline__ void lds_st8(float *p, const float (&f)[8]) {
 // N (1, 2 or 4) consecutive elements of E in LDS, aligned to N elements.
 template <int N>
 __device__ __forceinline__ void lds_stn(bf16 *p, const float *f) {
-    if constexpr (N == 4) {
+    if constexpr (N == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        bf16x2 v;
+        v[0] = static_cast<bf16>(f[0]); v[1] = static_cast<bf16>(f[1]);
+        *reinterpret_cast<bf16x2 *>(p) = v;
+    } else if constexpr (N == 4) {
         bf16x4 v;
         v[0] = static_cast<bf16>(f[0]); v[1] = static_cast<bf16>(f[1]);
         v[2] = static_cast<bf16>(f[2]); v[3] = static_cast<bf16>(f[3]);
@@ -197,7 +202,9 @@ __device__ __forceinline__ void lds_stn(bf16 *p, const float *f) {
 }
 template <int N>
 __device__ __forceinline__ void lds_stn(float *p, const float *f) {
-    if constexpr (N == 4) {
+    if constexpr (N == 2) {
+        *reinterpret_cast<float2 *>(p) = make_float2(f[0], f[1]);
+    } else if constexpr (N == 4) {
         *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
     } else {
 #pragma unroll

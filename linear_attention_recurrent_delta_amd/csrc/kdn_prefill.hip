@@ -28,7 +28,7 @@
 //      ahead into registers with 16 B loads) to LDS;
 //   2  decay and write vectors: KDN variance chain (one thread per key
 //      channel, sequential in t), then a two-level product scan of the decays
-//      over token groups with all 256 threads, then the scaled operands K~,
+//      over token groups (256 threads), then the scaled operands K~,
 //      Q~, W' = w / gamma and W~^T with 16 B LDS accesses;
 //   3  A_kk, A_qk on MFMA from K~ W'^T and Q~ W'^T (exact elementwise
 //      fallback when a channel decays below 2^-90 inside the chunk);
@@ -49,9 +49,9 @@ namespace kdn {
 // used (it would leave the float range); the chunk takes the exact path.
 #define KDN_DECAY_FLOOR 8.077935669463161e-28f   /* 2^-90 */
 
-template <typename E, int VAR, int DK, int NV, int C>
+template <typename E, int VAR, int DK, int NV, int C, int NW>
 struct PrefillLayout {
-    static constexpr int NT = 256;
+    static constexpr int NT = 64 * NW;       // threads per workgroup
     static constexpr int ES = (int)sizeof(E);
     static constexpr int PADE = 16 / ES;
     static constexpr int PK = DK + PADE;     // pitch of [*][DK] operands
@@ -65,7 +65,8 @@ struct PrefillLayout {
     static constexpr bool KDN = VAR == DIAG_KDN;
     // row layout of the decay scan: 8 channels x TPG tokens per thread
     static constexpr int NO = DK / 8;        // channel octets
-    static constexpr int NG = NT / NO;       // token groups
+    static constexpr int NG = 256 / NO < C ? 256 / NO : C; // token groups
+    static constexpr int NTS = NO * NG;      // threads of the scan layout
     static constexpr int TPG = C / NG;       // tokens per group
 
     static constexpr int SZ_CK = C * PK * ES;
@@ -89,17 +90,18 @@ struct PrefillLayout {
     static constexpr int OFF_GS = OFF_GP + NG * DK * 4;
     static constexpr int END_SCAN = OFF_GS + (DECAY ? NG * DK * 4 : 0);
     static constexpr int END_A = END_ET > END_SCAN ? END_ET : END_SCAN;
-    // fp32 scratch of the triangular inverse: T[0:32,0:32]^T (pitch 36),
-    // T[32:48,32:48]^T (pitch 20) and the transposed block products; in W'
-    // (and the raw alpha tile after it, both dead after phase 3) when it
-    // fits, else a region of its own
-    static constexpr int SZ_T = NB == 4 ? (32 * 36 + 16 * 20 + 32 * 36) * 4
-                                        : (16 * 36 + 16 * 20) * 4;
+    // T in the operand type for E = T U
+    static constexpr int OFF_TM = END_A;
+    static constexpr int END_TM = OFF_TM + C * PC * ES;
+    // fp32 scratch of the triangular inverse (16 x 20 blocks): T[I,I] for
+    // all I, T[I,I]^T for I < NB-1, then per column-chain wave J the
+    // products P^T and T[K,J]^T (K = J+1 .. NB-2); in W' (and the alpha tile after it,
+    // both dead after phase 3) when it fits, else a region of its own
+    static constexpr int NSLOT = NB + (NB - 1) + (NB - 1) * NB / 2;
+    static constexpr int SZ_T = NSLOT * 16 * 20 * 4;
     static constexpr bool T_IN_WP = SZ_T <= SZ_CK * (VDECAY ? 2 : 1);
-    static constexpr int OFF_TTA = T_IN_WP ? OFF_WP : END_A;
-    static constexpr int OFF_TTB = OFF_TTA + (NB == 4 ? 32 : 16) * 36 * 4;
-    static constexpr int OFF_TS = OFF_TTB + (NB == 4 ? 16 * 20 * 4 : 0);
-    static constexpr int OFF_SM = T_IN_WP ? END_A : END_A + SZ_T;
+    static constexpr int OFF_TD = T_IN_WP ? OFF_WP : END_TM;
+    static constexpr int OFF_SM = T_IN_WP ? END_TM : END_TM + SZ_T;
     static constexpr int SM_BETA = 0, SM_R = C, SM_ALPH = 2 * C, SM_INVS = 3 * C,
                          SM_GC = 4 * C, SM_FLAG = 4 * C + DK;
     static constexpr int SZ_SM = (4 * C + DK + 4) * 4;
@@ -111,6 +113,8 @@ struct PrefillLayout {
     static_assert(C % 16 == 0 && NV % 16 == 0 && DK % 16 == 0, "tiles");
     static_assert(NB == 2 || NB == 4, "chunk of 32 or 64");
     static_assert(NT % C == 0, "row reduction layout");
+    // KDN innovation sums: TPR threads per token row, 8k channels each
+    static constexpr int TPR = (NT / C) < (DK / 8) ? (NT / C) : (DK / 8);
 };
 
 // A ROWS x D tile held in registers between its global load and its LDS
@@ -118,12 +122,12 @@ struct PrefillLayout {
 // compute.  The loaded registers are not touched until commit() (any use
 // would make the wave wait for the load).  Rows t >= L load row L-1 (always
 // in bounds, L >= 1) and are replaced by `pad` at commit.
-template <typename T, int D, int ROWS>
+template <typename T, int D, int ROWS, int NT>
 struct TileRegs {
     static constexpr int VN = 16 / (int)sizeof(T);
     static constexpr int VPR = D / VN;
     static constexpr int NV16 = ROWS * VPR;
-    static constexpr int N = (NV16 + 255) / 256;
+    static constexpr int N = (NV16 + NT - 1) / NT;
     static_assert(VPR * VN == D, "row width");
     uint4 r[N];
     int L;
@@ -133,8 +137,8 @@ struct TileRegs {
         L = L_;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const int x = tid + 256 * n;
-            if (NV16 % 256 == 0 || x < NV16) {
+            const int x = tid + NT * n;
+            if (NV16 % NT == 0 || x < NV16) {
                 const int t = x / VPR, c = x % VPR;
                 const int tl = t < L_ ? t : L_ - 1;
                 r[n] = *reinterpret_cast<const uint4 *>(src + (long)tl * stride + c * VN);
@@ -151,8 +155,8 @@ struct TileRegs {
         const uint4 padv = *reinterpret_cast<const uint4 *>(tmp);
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const int x = tid + 256 * n;
-            if (NV16 % 256 == 0 || x < NV16) {
+            const int x = tid + NT * n;
+            if (NV16 % NT == 0 || x < NV16) {
                 const int t = x / VPR, c = x % VPR;
                 const bool in = t < L;
                 uint4 v;
@@ -168,10 +172,10 @@ struct TileRegs {
 
 // Copy ROWS x D elements straight from global memory into LDS (the exact
 // decay path only; rows t >= L get `pad`).
-template <typename T, int D, int ROWS>
+template <typename T, int D, int ROWS, int NT>
 __device__ __forceinline__ void stage_rows(T *dst, int pitch, const T *src,
                                            long stride, int L, float pad, int tid) {
-    TileRegs<T, D, ROWS> t;
+    TileRegs<T, D, ROWS, NT> t;
     t.fetch(src, stride, L, tid);
     t.commit(dst, pitch, pad, tid);
 }
@@ -179,43 +183,52 @@ __device__ __forceinline__ void stage_rows(T *dst, int pitch, const T *src,
 template <typename E>
 __device__ __forceinline__ float ld(const E *p) { return to_f32(*p); }
 
-// acc += A[0:16, 0:K] * B[0:K, 0:16] with A read from fp32 LDS rows ([row][k],
-// pitch lda) and rounded to the operand type E, B given as [col][k] in E.
+// acc += A[0:16, 0:16] * B[0:16, 0:16] in (near) fp32: A from fp32 LDS rows
+// ([row][k], pitch lda), B from fp32 LDS as [col][k] (pitch ldb).  For bf16
+// kernels each operand is split into hi + lo bf16 parts and the three
+// significant partial products run on bf16 MFMA; float kernels use the fp32
+// MFMA.
 template <typename E>
-__device__ __forceinline__ void mma_tile_f32a(f32x4 &acc, const float *A, int lda,
-                                              const E *B, int ldb, int K, int lane) {
-    const int r = lane & 15;
-    const int ko = (lane >> 4) * Mma<E>::KPL;
-    const float *pa = A + r * lda + ko;
-    const E *pb = B + r * ldb + ko;
-    for (int k = 0; k < K; k += Mma<E>::KSTEP) {
-        if constexpr (sizeof(E) == 2) {
-            const float4 a0 = *reinterpret_cast<const float4 *>(pa + k);
-            const float4 a1 = *reinterpret_cast<const float4 *>(pa + k + 4);
-            bf16x8 av;
-            av[0] = static_cast<bf16>(a0.x); av[1] = static_cast<bf16>(a0.y);
-            av[2] = static_cast<bf16>(a0.z); av[3] = static_cast<bf16>(a0.w);
-            av[4] = static_cast<bf16>(a1.x); av[5] = static_cast<bf16>(a1.y);
-            av[6] = static_cast<bf16>(a1.z); av[7] = static_cast<bf16>(a1.w);
-            const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(pb + k);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-        } else {
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k], pb[k], acc, 0, 0, 0);
+__device__ __forceinline__ void mma16_f32(f32x4 &acc, const float *A, int lda,
+                                          const float *B, int ldb, int lane) {
+    if constexpr (sizeof(E) == 2) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const int r = lane & 15, ko = (lane >> 4) * 4;
+        const float4 a = *reinterpret_cast<const float4 *>(A + r * lda + ko);
+        const float4 b = *reinterpret_cast<const float4 *>(B + r * ldb + ko);
+        const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+        bf16x4 ah, al, bh, bl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ah[e] = static_cast<bf16>(av[e]);
+            al[e] = static_cast<bf16>(av[e] - static_cast<float>(ah[e]));
+            bh[e] = static_cast<bf16>(bv[e]);
+            bl[e] = static_cast<bf16>(bv[e] - static_cast<float>(bh[e]));
         }
+        const s16x4 ahs = *reinterpret_cast<const s16x4 *>(&ah);
+        const s16x4 als = *reinterpret_cast<const s16x4 *>(&al);
+        const s16x4 bhs = *reinterpret_cast<const s16x4 *>(&bh);
+        const s16x4 bls = *reinterpret_cast<const s16x4 *>(&bl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(als, bhs, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahs, bls, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahs, bhs, acc, 0, 0, 0);
+    } else {
+        Mma16<float>::tile(acc, A, lda, B, ldb, lane);
     }
 }
 
-template <typename E, int VAR, int DK, int NV, int C>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
-    using LY = PrefillLayout<E, VAR, DK, NV, C>;
+template <typename E, int VAR, int DK, int NV, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
+    using LY = PrefillLayout<E, VAR, DK, NV, C, NW>;
+    constexpr int NT = LY::NT;
     constexpr int PK = LY::PK, PC = LY::PC, PV = LY::PV, PA = LY::PA,
                   PP = LY::PP, NB = LY::NB;
     constexpr int NO = LY::NO, NG = LY::NG, TPG = LY::TPG;
     constexpr bool DECAY = LY::DECAY, VDECAY = LY::VDECAY, KDN = LY::KDN;
     constexpr int NTJ = NV / 16;                // value tiles
     constexpr int NTI = DK / 16;                // key tiles
-    constexpr int NS = NTI * NTJ / 4;           // S tiles per wave
-    static_assert(NS * 4 == NTI * NTJ, "S tiles per wave");
+    constexpr int NST = NTI * NTJ;              // S tiles
+    constexpr int NS = (NST + NW - 1) / NW;     // S tiles per wave (max)
     constexpr int KS = Mma<E>::KSTEP;
 
     __shared__ __attribute__((aligned(16))) char smem[LY::TOTAL];
@@ -234,9 +247,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
     E *AQ = reinterpret_cast<E *>(smem + LY::OFF_AQ);
     E *UT = reinterpret_cast<E *>(smem + LY::OFF_UT);
     E *ET = reinterpret_cast<E *>(smem + LY::OFF_ET);
-    float *TTA = reinterpret_cast<float *>(smem + LY::OFF_TTA);   // T^T blocks
-    float *TTB = reinterpret_cast<float *>(smem + LY::OFF_TTB);
-    float *TS = reinterpret_cast<float *>(smem + LY::OFF_TS);     // products
+    E *Tm = reinterpret_cast<E *>(smem + LY::OFF_TM);             // T
+    float *TD = reinterpret_cast<float *>(smem + LY::OFF_TD);     // T scratch
     float *sm = reinterpret_cast<float *>(smem + LY::OFF_SM);
     float *s_beta = sm + LY::SM_BETA, *s_r = sm + LY::SM_R,
           *s_alph = sm + LY::SM_ALPH, *s_invs = sm + LY::SM_INVS,
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
 
     // Workgroup -> (batch*head, value block).  Dispatch is round-robin over
     // the 8 XCDs; place the value blocks of one head on one XCD.
@@ -268,12 +280,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
     const E *gr = static_cast<const E *>(P.r);
 
     // ---- S slice in accumulator layout: tile u of this wave is
-    //      (ti, tj) = divmod(wv + 4u, NTJ); acc[r] = S[ti*16 + (lane>>4)*4 + r]
+    //      (ti, tj) = divmod(wv + NW u, NTJ); acc[r] = S[ti*16 + (lane>>4)*4 + r]
     //                                                 [tj*16 + (lane&15)].
     f32x4 sacc[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        const int tau = wv + 4 * u, ti = tau / NTJ, tj = tau % NTJ;
+        const int tau = wv + NW * u, ti = tau / NTJ, tj = tau % NTJ;
+        if (NST % NW != 0 && tau >= NST) continue;
         const int j = tj * 16 + (lane & 15);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -290,8 +303,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
     const long sv_ = (long)H * DV;     // token stride of v/o
 
     // Raw tiles of the next chunk, in flight while the current one computes.
-    TileRegs<E, DK, C> rk, rq, ra, rx;
-    TileRegs<E, NV, C> rv;
+    TileRegs<E, DK, C, NT> rk, rq, ra, rx;
+    TileRegs<E, NV, C, NT> rv;
     E sc_b = from_f32<E>(0.f), sc_r = from_f32<E>(1.f), sc_a = from_f32<E>(1.f);
     auto fetch = [&](int cs) {
         const int Ls = min(C, T - cs);
@@ -310,9 +323,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
     if (T > 0)
         fetch(0);
 
-    // scan-layout coordinates: channels i0..i0+7, tokens t0..t0+TPG-1
-    const int oc = tid % NO, grp = tid / NO;
+    // Scan layout (threads < NTS): channels i0..i0+7, tokens t0..t0+TPG-1,
+    // token groups vary fastest across lanes.  The operand pass uses every
+    // thread: H2 threads per group, TPG2 tokens each.
+    constexpr int H2 = (NT / LY::NTS) < TPG ? (NT / LY::NTS) : TPG;
+    constexpr int TPG2 = TPG / H2, NG2 = NG * H2, NTO = LY::NTS * H2;
+    static_assert(TPG2 * H2 == TPG && NTO <= NT, "operand layout");
+    const int grp = tid % NG, oc = (tid / NG) % NO;
     const int i0 = oc * 8, t0 = grp * TPG;
+    const int gh = tid % NG2, oc2 = tid / NG2;
+    const int j0 = oc2 * 8, u0 = gh * TPG2;        // operand pass: channels, tokens
+    const int ug0 = (gh / H2) * TPG;               // first token of its group
 
     for (int c0 = 0; c0 < T; c0 += C) {
         const int L = min(C, T - c0);
@@ -340,28 +361,54 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
         if constexpr (KDN) {
             // Variance chain, one thread per key channel (sequential in t):
             //   p- = a^2 p + xi,  u = p- k,  p = p- r / (r + mu p- k^2).
+            // Inputs are read a few tokens ahead into registers so the LDS
+            // latency stays off the dependent chain.  Tokens past the end of
+            // the sequence were staged as a = 1, xi = 0, k = 0, r = 1, which
+            // leaves p unchanged bit for bit.
             if (tid < DK) {
                 const int i = tid;
-#pragma unroll 8
-                for (int t = 0; t < C; ++t) {
-                    const float kk = ld(Kt + t * PK + i);
-                    const float a = ld(ALP + t * PK + i);
-                    const float x = ld(XR + t * PK + i);
-                    const float r = s_r[t];
-                    const float pm = a * a * p_reg + x;
-                    const float u = pm * kk;
-                    U32[t * PP + i] = u;
-                    const float den = r + P.mu * pm * kk * kk;
-                    if (t < L)
-                        p_reg = (den != 0.f) ? pm * r * fast_rcp(den) : pm;
+                const float mu = P.mu;
+                float pc = p_reg;
+                constexpr int PF = 4;              // tokens read ahead
+                float kk[PF], aa[PF], xx[PF], rr[PF];
+                auto loadpf = [&](int tb) {
+#pragma unroll
+                    for (int j = 0; j < PF; ++j) {
+                        kk[j] = ld(Kt + (tb + j) * PK + i);
+                        aa[j] = ld(ALP + (tb + j) * PK + i);
+                        xx[j] = ld(XR + (tb + j) * PK + i);
+                        rr[j] = s_r[tb + j];
+                    }
+                };
+                loadpf(0);
+#pragma unroll
+                for (int tb = 0; tb < C; tb += PF) {
+                    float a2[PF], x8[PF], m8[PF], k8[PF], r8[PF];
+#pragma unroll
+                    for (int j = 0; j < PF; ++j) {
+                        a2[j] = aa[j] * aa[j];
+                        m8[j] = mu * kk[j] * kk[j];
+                        x8[j] = xx[j]; k8[j] = kk[j]; r8[j] = rr[j];
+                    }
+                    if (tb + PF < C)
+                        loadpf(tb + PF);
+#pragma unroll
+                    for (int j = 0; j < PF; ++j) {
+                        const float pm = fmaf(a2[j], pc, x8[j]);
+                        U32[(tb + j) * PP + i] = pm * k8[j];
+                        const float den = fmaf(m8[j], pm, r8[j]);
+                        pc = (den != 0.f) ? pm * r8[j] * fast_rcp(den) : pm;
+                    }
                 }
+                p_reg = pc;
             }
             __syncthreads();
             // innovation variances s_t = r_t + sum_i u_ti k_ti
-            constexpr int TPR = 256 / C;          // threads per token row
+            constexpr int TPR = LY::TPR;           // threads per token row
             constexpr int CPT = DK / TPR;          // channels per thread
             const int t = tid / TPR, part = tid % TPR;
             float acc = 0.f;
+            if (tid < TPR * C) {
 #pragma unroll
             for (int c = 0; c < CPT; c += 8) {
                 float uu[8], kk[8];
@@ -371,33 +418,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
                 for (int e = 0; e < 8; ++e)
                     acc += uu[e] * kk[e];
             }
+            }
 #pragma unroll
             for (int off = TPR / 2; off >= 1; off >>= 1)
                 acc += __shfl_xor(acc, off, WAVE);
-            if (part == 0) {
+            if (tid < TPR * C && part == 0) {
                 const float s = s_r[t] + acc;
                 s_invs[t] = (s != 0.f) ? 1.f / s : 0.f;
             }
         }
-        // 2a. in-group products of the decays
-        float av[TPG][8], lp[TPG][8];
+        // 2a. group products of the decays (scan threads)
         if constexpr (DECAY) {
+            if (tid < LY::NTS) {
+                float gprod[8];
 #pragma unroll
-            for (int tt = 0; tt < TPG; ++tt) {
-                const int t = t0 + tt;
-                if constexpr (VDECAY) {
-                    lds_ld8(ALP + t * PK + i0, av[tt]);
-                } else {
-                    const float a = s_alph[t];
+                for (int tt = 0; tt < TPG; ++tt) {
+                    float a8[8];
+                    if constexpr (VDECAY) {
+                        lds_ld8(ALP + (t0 + tt) * PK + i0, a8);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c)
+                            a8[c] = s_alph[t0 + tt];
+                    }
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
-                        av[tt][c] = a;
+                        gprod[c] = tt ? gprod[c] * a8[c] : a8[c];
                 }
-#pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    lp[tt][c] = tt ? lp[tt - 1][c] * av[tt][c] : av[tt][c];
+                lds_st8(GP + grp * DK + i0, gprod);   // group totals
             }
-            lds_st8(GP + grp * DK + i0, lp[TPG - 1]);   // group totals
             __syncthreads();
             // 2b. exclusive prefix / suffix over groups, one thread per channel
             if (tid < DK) {
@@ -423,23 +472,44 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
             }
         }
         __syncthreads();
-        // 2c. scaled operands (row layout, 16 B LDS accesses)
+        // 2c. scaled operands, every thread: channels j0..j0+7, tokens
+        //     u0..u0+TPG2-1 (tokens vary fastest across lanes: 16 B row
+        //     accesses and the transposed W~ stores stay conflict-free)
         const bool fb = DECAY && (*s_flag != 0);
-        {
-            float pre[8], suf[8];
+        if (tid < NTO) {
+            const int g = gh / H2;
+            float pre[8], suf[8], a8[TPG][8];
             if constexpr (DECAY) {
-                lds_ld8(GP + grp * DK + i0, pre);
-                lds_ld8(GS + grp * DK + i0, suf);
-            }
-            float w[TPG][8];
+                lds_ld8(GP + g * DK + j0, pre);
+                lds_ld8(GS + g * DK + j0, suf);
 #pragma unroll
-            for (int tt = 0; tt < TPG; ++tt) {
-                const int t = t0 + tt;
+                for (int tt = 0; tt < TPG; ++tt) {
+                    if constexpr (VDECAY) {
+                        lds_ld8(ALP + (ug0 + tt) * PK + j0, a8[tt]);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c)
+                            a8[tt][c] = s_alph[ug0 + tt];
+                    }
+                }
+                // in-group tokens before / after this thread's tokens
+#pragma unroll
+                for (int tt = 0; tt < TPG; ++tt)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        if (ug0 + tt < u0) pre[c] *= a8[tt][c];
+                        if (ug0 + tt >= u0 + TPG2) suf[c] *= a8[tt][c];
+                    }
+            }
+            float w[TPG2][8], ap[TPG2][8];
+#pragma unroll
+            for (int tt = 0; tt < TPG2; ++tt) {
+                const int t = u0 + tt;
                 float kk[8];
-                lds_ld8(Kt + t * PK + i0, kk);
+                lds_ld8(Kt + t * PK + j0, kk);
                 if constexpr (KDN) {
                     float uu[8];
-                    lds_ld8(U32 + t * PP + i0, uu);
+                    lds_ld8(U32 + t * PP + j0, uu);
                     const float inv = s_invs[t];
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
@@ -451,50 +521,56 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
                         w[tt][c] = bt * kk[c];
                 }
                 if constexpr (DECAY) {
-                    float qq[8], g[8], o[8];
-                    lds_ld8(Qt + t * PK + i0, qq);
+                    float qq[8], o[8];
+                    lds_ld8(Qt + t * PK + j0, qq);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        // this token's decay (in registers from the group load)
+                        float at = 1.f;
+#pragma unroll
+                        for (int t2 = 0; t2 < TPG; ++t2)
+                            if (ug0 + t2 == t) at = a8[t2][c];
+                        ap[tt][c] = at;
+                        pre[c] *= at;                   // gamma_t
+                    }
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
-                        g[c] = pre[c] * lp[tt][c];
+                        o[c] = pre[c] * kk[c];
+                    lds_st8(Kt + t * PK + j0, o);
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
-                        o[c] = g[c] * kk[c];
-                    lds_st8(Kt + t * PK + i0, o);
+                        o[c] = pre[c] * qq[c];
+                    lds_st8(Qt + t * PK + j0, o);
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
-                        o[c] = g[c] * qq[c];
-                    lds_st8(Qt + t * PK + i0, o);
-#pragma unroll
-                    for (int c = 0; c < 8; ++c)
-                        o[c] = fb ? w[tt][c] : w[tt][c] * fast_rcp(g[c]);
-                    lds_st8(Wp + t * PK + i0, o);
+                        o[c] = fb ? w[tt][c] : w[tt][c] * fast_rcp(pre[c]);
+                    lds_st8(Wp + t * PK + j0, o);
                 } else {
-                    lds_st8(Wp + t * PK + i0, w[tt]);
+                    lds_st8(Wp + t * PK + j0, w[tt]);
                 }
             }
-            // W~^T[i][t] = (gamma_C / gamma_t) w_t: suffix products of the
-            // group's own tokens times the groups after it
-            float wt[8][TPG];
+            // W~^T[i][t] = (gamma_C / gamma_t) w_t
+            float wt[8][TPG2];
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 float sg = DECAY ? suf[c] : 1.f;
 #pragma unroll
-                for (int tt = TPG - 1; tt >= 0; --tt) {
+                for (int tt = TPG2 - 1; tt >= 0; --tt) {
                     wt[c][tt] = sg * w[tt][c];
                     if (DECAY)
-                        sg *= av[tt][c];
+                        sg *= ap[tt][c];
                 }
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                lds_stn<TPG>(WtT + (i0 + c) * PC + t0, wt[c]);
+                lds_stn<TPG2>(WtT + (j0 + c) * PC + u0, wt[c]);
         }
         __syncthreads();
 
         // ---------------- 3. interaction matrices ----------------
         constexpr int NL = NB * (NB + 1) / 2;
         if (!fb) {
-            for (int x = wv; x < 2 * NL; x += 4) {
+            for (int x = wv; x < 2 * NL; x += NW) {
                 const int which = x >= NL;
                 int idx = x - which * NL, mi = 0;
                 while (idx > mi) { idx -= mi + 1; ++mi; }
@@ -514,10 +590,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
             }
         } else if constexpr (DECAY) {
             // Exact path: reload raw k, q; products of the decays directly.
-            stage_rows<E, DK, C>(Kt, PK, gk + tok0 * DK, sk_, L, 0.f, tid);
-            stage_rows<E, DK, C>(Qt, PK, gq + tok0 * DK, sk_, L, 0.f, tid);
+            stage_rows<E, DK, C, NT>(Kt, PK, gk + tok0 * DK, sk_, L, 0.f, tid);
+            stage_rows<E, DK, C, NT>(Qt, PK, gq + tok0 * DK, sk_, L, 0.f, tid);
             __syncthreads();
-            for (int pidx = tid; pidx < C * C; pidx += 256) {
+            for (int pidx = tid; pidx < C * C; pidx += NT) {
                 const int t = pidx / C, s = pidx % C;
                 float akk = 0.f, aqk = 0.f;
                 if (s <= t) {
@@ -547,53 +623,63 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
                 }
             }
         }
-        // zero the blocks above the diagonal of A_qk and A_kk (T is built in
-        // place in A_kk; MFMA K ranges may cover these blocks)
-        for (int x = tid; x < C * C; x += 256) {
+        // zero the blocks above the diagonal of A_qk and T (MFMA K ranges
+        // may cover them)
+        for (int x = tid; x < C * C; x += NT) {
             const int t = x / C, s = x % C;
             if ((s >> 4) > (t >> 4)) {
                 AQ[t * PC + s] = from_f32<E>(0.f);
-                Akk[t * PA + s] = 0.f;
+                Tm[t * PC + s] = from_f32<E>(0.f);
             }
         }
         __syncthreads();
 
-        // ---------------- 5. U = V - K~ S  (overlaps 4a) ----------------
+        // ---------------- 5. U = V - K~ S  ||  4a. T[I,I] ----------------
         constexpr int NTU = NB * NTJ;
-        for (int x = wv; x < NTU; x += 4) {
-            const int mi = x / NTJ, nj = x % NTJ;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma_tile_k<E, DK>(acc, Kt + mi * 16 * PK, PK, ST + nj * 16 * PK, PK, lane);
-            const int j = nj * 16 + (lane & 15);
-            float uo[4];
+        static_assert(NW >= 4 + NB, "waves 0-3 take U, waves 4.. the T blocks");
+        if (wv < 4) {
+            for (int x = wv; x < NTU; x += 4) {
+                const int mi = x / NTJ, nj = x % NTJ;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                mma_tile_k<E, DK>(acc, Kt + mi * 16 * PK, PK, ST + nj * 16 * PK, PK, lane);
+                const int j = nj * 16 + (lane & 15);
+                float uo[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = mi * 16 + (lane >> 4) * 4 + r;
-                uo[r] = ld(VR + t * PV + j) - acc[r];
+                for (int r = 0; r < 4; ++r) {
+                    const int t = mi * 16 + (lane >> 4) * 4 + r;
+                    uo[r] = ld(VR + t * PV + j) - acc[r];
+                }
+                lds_stn<4>(UT + j * PC + mi * 16 + (lane >> 4) * 4, uo);
             }
-            lds_stn<4>(UT + j * PC + mi * 16 + (lane >> 4) * 4, uo);
-        }
-        // ---------------- 4a. diagonal blocks of T ----------------
-        // T[I,I] = (I + A[I,I])^-1 by forward substitution, in place in A_kk
-        // (fp32); wave I, lane j computes column j.  Row r of the block is
-        // read before it is overwritten (LDS operations of a wave are in
-        // order).  Transposed copies of the blocks that later products take
-        // as B operands go to TTA (blocks 0, 1) and TTB (block 2).
-        if (wv < NB && lane < 16) {
-            const int o0 = wv * 16, j = lane;
+        } else if (wv - 4 < NB && lane < 16) {
+            // T[I,I] = (I + A[I,I])^-1 by forward substitution; lane j
+            // computes column j.  A_kk is only read here (no aliasing store),
+            // so the row loads can run ahead of the arithmetic.
+            const int I = wv - 4, o0 = I * 16, j = lane;
             float xv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float acc = 0.f;
+                float arow[16];
 #pragma unroll
-                for (int m = 0; m < r; ++m)
-                    acc += Akk[(o0 + r) * PA + o0 + m] * xv[m];
-                xv[r] = (r == j) ? 1.f : ((r < j) ? 0.f : -acc);
-                Akk[(o0 + r) * PA + o0 + j] = xv[r];
+                for (int m = 0; m < 16; m += 4) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(Akk + (o0 + r) * PA + o0 + m);
+                    arow[m] = a4.x; arow[m + 1] = a4.y; arow[m + 2] = a4.z; arow[m + 3] = a4.w;
+                }
+                float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) {
+                    if (m & 1) acc1 += arow[m] * xv[m];
+                    else acc0 += arow[m] * xv[m];
+                }
+                xv[r] = (r == j) ? 1.f : ((r < j) ? 0.f : -(acc0 + acc1));
             }
-            float *dst = wv < 2 ? TTA + (o0 + j) * 36 + o0
-                                : (wv == 2 ? TTB + j * 20 : nullptr);
-            if (dst) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                TD[I * 320 + r * 20 + j] = xv[r];                 // T[I,I]
+                Tm[(o0 + r) * PC + o0 + j] = from_f32<E>(xv[r]);
+            }
+            if (I < NB - 1) {                  // T[I,I]^T: B operand of chain I
+                float *dst = TD + (NB + I) * 320 + j * 20;
 #pragma unroll
                 for (int r = 0; r < 16; r += 4)
                     *reinterpret_cast<float4 *>(dst + r) =
@@ -602,73 +688,41 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
         }
         __syncthreads();
         // ---------------- 4b. off-diagonal blocks of T ----------------
-        // 16-row pairs: T[2p+1,2p] = -T[2p+1,2p+1] (A[2p+1,2p] T[2p,2p]).
-        {
-            constexpr int NPAIR = NB / 2;
-            if (wv < NPAIR) {
-                const int ra = (2 * wv + 1) * 16, ca = 2 * wv * 16;
-                const float *Bt = wv == 0 ? TTA : TTB;          // T[ca,ca]^T
-                const int ldb = wv == 0 ? 36 : 20;
+        // Column chain J on wave J (no barriers between its steps):
+        //   T[I,J] = -T[I,I] sum_{K=J}^{I-1} A[I,K] T[K,J],  I = J+1 .. NB-1.
+        // Products in (near) fp32: bf16 data is split into hi + lo parts.
+        if (wv < NB - 1) {
+            const int J = wv;
+            // private slots of wave J: P^T, then T[K,J]^T for K = J+1 .. NB-2
+            float *ps = TD + (NB + (NB - 1) + J * (2 * NB - 1 - J) / 2) * 320;
+            for (int I = J + 1; I < NB; ++I) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                Mma16<float>::tile(acc, Akk + ra * PA + ca, PA, Bt, ldb, lane);
-                // P^T[n][k] for the next product's B operand
-                *reinterpret_cast<float4 *>(TS + wv * 16 * 20 + (lane & 15) * 20 +
-                                            (lane >> 4) * 4) =
+                for (int K = J; K < I; ++K) {
+                    const float *bk = (K == J) ? TD + (NB + J) * 320 : ps + (K - J) * 320;
+                    mma16_f32<E>(acc, Akk + I * 16 * PA + K * 16, PA, bk, 20, lane);
+                }
+                *reinterpret_cast<float4 *>(ps + (lane & 15) * 20 + (lane >> 4) * 4) =
                     make_float4(acc[0], acc[1], acc[2], acc[3]);
-            }
-            __syncthreads();
-            if (wv < NPAIR) {
-                const int ra = (2 * wv + 1) * 16, ca = 2 * wv * 16;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                Mma16<float>::tile(acc, Akk + ra * PA + ra, PA, TS + wv * 16 * 20, 20, lane);
-                const int col = ca + (lane & 15), row0 = ra + (lane >> 4) * 4;
+                f32x4 tij = {0.f, 0.f, 0.f, 0.f};
+                mma16_f32<E>(tij, TD + I * 320, 20, ps, 20, lane);
+                const int col = J * 16 + (lane & 15), row0 = I * 16 + (lane >> 4) * 4;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Akk[(row0 + r) * PA + col] = -acc[r];
-                if (wv == 0)            // T[1,0]^T joins T[0:32,0:32]^T
-                    *reinterpret_cast<float4 *>(TTA + col * 36 + row0) =
-                        make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
+                    Tm[(row0 + r) * PC + col] = from_f32<E>(-tij[r]);
+                if (I < NB - 1)                    // T[I,J]^T for later steps
+                    *reinterpret_cast<float4 *>(ps + (I - J) * 320 + (lane & 15) * 20 +
+                                                (lane >> 4) * 4) =
+                        make_float4(-tij[0], -tij[1], -tij[2], -tij[3]);
             }
-            __syncthreads();
         }
-        if constexpr (NB == 4) {
-            // 32-row halves: T[b,a] = -T[b,b] (A[b,a] T[a,a]), b = rows 32..63,
-            // a = rows 0..31; one 16x16 tile (mi, ni) per wave.
-            const int mi = wv >> 1, ni = wv & 1;
-            {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    if (kb >= ni)            // T[a] is lower block-triangular
-                        Mma16<float>::tile(acc, Akk + (32 + mi * 16) * PA + kb * 16, PA,
-                                           TTA + ni * 16 * 36 + kb * 16, 36, lane);
-                // Q^T[ni*16 + j][mi*16 + row]
-                *reinterpret_cast<float4 *>(TS + (ni * 16 + (lane & 15)) * 36 + mi * 16 +
-                                            (lane >> 4) * 4) =
-                    make_float4(acc[0], acc[1], acc[2], acc[3]);
-            }
-            __syncthreads();
-            {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    if (kb <= mi)
-                        Mma16<float>::tile(acc, Akk + (32 + mi * 16) * PA + 32 + kb * 16, PA,
-                                           TS + ni * 16 * 36 + kb * 16, 36, lane);
-                const int col = ni * 16 + (lane & 15), row0 = 32 + mi * 16 + (lane >> 4) * 4;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Akk[(row0 + r) * PA + col] = -acc[r];
-            }
-            __syncthreads();
-        }
+        __syncthreads();
 
         // ---------------- 6. E = T U ----------------
-        for (int x = wv; x < NTU; x += 4) {
+        for (int x = wv; x < NTU; x += NW) {
             const int mi = x / NTJ, nj = x % NTJ;
             const int kc = min(C, ((mi + 1) * 16 + KS - 1) / KS * KS);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma_tile_f32a<E>(acc, Akk + mi * 16 * PA, PA, UT + nj * 16 * PC, PC, kc, lane);
+            mma_tile<E>(acc, Tm + mi * 16 * PC, PC, UT + nj * 16 * PC, PC, kc, lane);
             const int j = nj * 16 + (lane & 15);
             float eo[4] = {acc[0], acc[1], acc[2], acc[3]};
             lds_stn<4>(ET + j * PC + mi * 16 + (lane >> 4) * 4, eo);
@@ -677,7 +731,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
 
         // ---------------- 7. outputs and state ----------------
         E *go = static_cast<E *>(P.o);
-        for (int x = wv; x < NTU; x += 4) {
+        for (int x = wv; x < NTU; x += NW) {
             const int mi = x / NTJ, nj = x % NTJ;
             const int kc = min(C, ((mi + 1) * 16 + KS - 1) / KS * KS);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -693,7 +747,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
         }
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
-            const int tau = wv + 4 * u, ti = tau / NTJ, tj = tau % NTJ;
+            const int tau = wv + NW * u, ti = tau / NTJ, tj = tau % NTJ;
+        if (NST % NW != 0 && tau >= NST) continue;
             if (DECAY) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -706,7 +761,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
         // ---------------- 8. S for the next chunk's products ----------------
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
-            const int tau = wv + 4 * u, ti = tau / NTJ, tj = tau % NTJ;
+            const int tau = wv + NW * u, ti = tau / NTJ, tj = tau % NTJ;
+        if (NST % NW != 0 && tau >= NST) continue;
             const int j = tj * 16 + (lane & 15);
             float so[4] = {sacc[u][0], sacc[u][1], sacc[u][2], sacc[u][3]};
             lds_stn<4>(ST + j * PK + ti * 16 + (lane >> 4) * 4, so);
@@ -716,7 +772,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
     // ---- final state
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        const int tau = wv + 4 * u, ti = tau / NTJ, tj = tau % NTJ;
+        const int tau = wv + NW * u, ti = tau / NTJ, tj = tau % NTJ;
+        if (NST % NW != 0 && tau >= NST) continue;
         const int j = tj * 16 + (lane & 15);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -735,11 +792,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams P) {
 // and once with KDN_PREFILL_DISPATCH for the entry point below.
 // ---------------------------------------------------------------------------
 #ifdef KDN_PREFILL_VARIANT
+#ifndef KDN_PREFILL_WAVES
+#define KDN_PREFILL_WAVES 8
+#endif
 template <typename E, int VAR, int DK, int NV, int C>
 static hipError_t launch_one(const PrefillParams &P, hipStream_t st) {
+    constexpr int NW = KDN_PREFILL_WAVES;
     const long heads = (long)P.B * P.H;
-    const dim3 grid((unsigned)(heads * (P.dv / NV))), block(256);
-    hipLaunchKernelGGL((prefill_kernel<E, VAR, DK, NV, C>), grid, block, 0, st, P);
+    const dim3 grid((unsigned)(heads * (P.dv / NV))), block(64 * NW);
+    hipLaunchKernelGGL((prefill_kernel<E, VAR, DK, NV, C, NW>), grid, block, 0, st, P);
     return hipGetLastError();
 }
 
