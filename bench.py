@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s + decode steps/s per head-state; % MFMA / % HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_decode.hip", "kdn_device.h", "kdn_launch.h"]
+KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_variance.hip",
+                  "kdn_decode.hip", "kdn_device.h", "kdn_launch.h", "kdn_workspace.h"]
 
 
 def kernel_hash(names=KERNEL_SOURCES):
@@ -99,19 +100,21 @@ def time_launches(fn, steps, warmup, torch):
     return wall, e0.elapsed_time(e1) / 1e3
 
 
-def bench_prefill(name, steps, warmup, torch, kdn, synth):
+def bench_prefill(name, steps, warmup, torch, kdn, synth, schedule="two_pass"):
     c = synth.CONFIGS[name]
     inp = synth.gen_config(name, device="cuda")
     B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
     o = torch.empty((B, T, H, dv), dtype=inp["q"].dtype, device="cuda")
     S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
     p = torch.empty_like(inp["p0"]) if c["variant"] == "diag_kdn" else None
+    # caller-owned workspace of the two-pass schedule, allocated once
+    ws = kdn.workspace(c["variant"], inp["q"], inp["v"]) if schedule == "two_pass" else None
 
     def step():
         kdn.prefill(c["variant"], inp["q"], inp["k"], inp["v"], alpha=inp.get("alpha"),
                     beta=inp.get("beta"), proc_noise=inp.get("xi"),
                     obs_noise=inp.get("r"), S0=inp.get("S0"), p0=inp.get("p0"),
-                    out=(o, S, p))
+                    out=(o, S, p), workspace=ws)
 
     wall, gpu = time_launches(step, steps, warmup, torch)
     es = 2 if c["dtype"] == "bf16" else 4
@@ -126,7 +129,8 @@ def bench_prefill(name, steps, warmup, torch, kdn, synth):
         "ms_per_step": wall / steps * 1e3,
         "config": {"workload": f"{name}_prefill", "variant": c["variant"], "B": B,
                    "T": T, "H": H, "d_k": dk, "d_v": dv, "chunk": C,
-                   "dtype": c["dtype"]},
+                   "dtype": c["dtype"], "schedule": schedule,
+                   "workspace_bytes": 0 if ws is None else ws.numel()},
         "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
@@ -136,7 +140,7 @@ def bench_prefill(name, steps, warmup, torch, kdn, synth):
                  "unit": "TFLOP/s", "frac": flops / launch_s / 1e12 / BF16_PEAK_TFLOPS,
                  "algorithmic_flops": flops},
     }
-    del inp, o, S, p
+    del inp, o, S, p, ws
     torch.cuda.empty_cache()
     return res
 
@@ -237,6 +241,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=["two_pass", "single_pass"], default="two_pass",
+                    help="prefill schedule: with a workspace (two-pass) or without")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain streaming kernel (out = 1.0 * in, "
                          "float32) over this many MiB, as a reference for "
@@ -261,7 +267,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head = bench_prefill("gated_deltanet", args.steps, args.warmup, torch, kdn, synth)
+    head = bench_prefill("gated_deltanet", args.steps, args.warmup, torch, kdn, synth,
+                         args.schedule)
     out = {
         "metric": METRIC, "value": head["value"], "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -275,7 +282,8 @@ def main():
         w = {}
         for name in ("kda", "diag_kdn"):
             w[f"{name}_prefill"] = bench_prefill(name, max(3, args.steps // 2),
-                                                 args.warmup, torch, kdn, synth)
+                                                 args.warmup, torch, kdn, synth,
+                                                 args.schedule)
         w["decode_diag_kdn"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
         out["workloads"] = w
     if not args.no_cpu_baseline:

@@ -73,7 +73,8 @@ typedef enum kdn_status {
     KDN_ERR_UNSUPPORTED = 3,  /* variant/dtype/d_k/d_v/chunk not built      */
     KDN_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned          */
     KDN_ERR_ALIAS = 5,        /* an output overlaps an input it may not    */
-    KDN_ERR_HIP = 6           /* the HIP runtime refused the launch        */
+    KDN_ERR_HIP = 6,          /* the HIP runtime refused the launch        */
+    KDN_ERR_WORKSPACE = 7     /* workspace smaller than the size query     */
 } kdn_status;
 
 /*
@@ -81,6 +82,16 @@ typedef enum kdn_status {
  * equals the serial recurrence exactly in exact arithmetic: provisional errors
  * resolved by a causal triangular solve -- "معماری KDA ...", section "حل مشکل
  * وابستگی علی").
+ *
+ * Two schedules compute the same result (up to floating-point rounding):
+ *   - workspace == NULL: a single kernel walks the chunks of each sequence in
+ *     order (no scratch memory);
+ *   - workspace != NULL: the two-pass schedule.  Chunk-parallel kernels write
+ *     each chunk's S-independent products (decay-scaled operands, A_qk, the
+ *     triangular inverse; for diagonal KDN also the variance at each chunk
+ *     start, from a scan over per-chunk variance maps) to the workspace, then
+ *     a sequential pass carries S through the chunks.  This is the fast path
+ *     for long sequences.
  *
  *   q, k        [B, T, H, d_k]  dtype
  *   v           [B, T, H, d_v]  dtype
@@ -100,6 +111,13 @@ typedef enum kdn_status {
  *               only; 1 = unscaled)
  *   chunk       chunk length C; 0 picks the library default (64 for bf16,
  *               32 for float32 with d_k = 128, else 64)
+ *   workspace   NULL, or device memory of at least workspace_bytes >=
+ *               kdn_chunk_prefill_workspace_size(...) bytes (else
+ *               KDN_ERR_WORKSPACE), 256-byte aligned (else KDN_ERR_ALIGN),
+ *               overlapping no other argument (else KDN_ERR_ALIAS).  Owned by
+ *               the caller; its contents are scratch (ignored on entry,
+ *               undefined after).  Calls sharing a workspace must not overlap
+ *               in time.
  * Supported: d_k, d_v in {64, 128}; dtype KDN_F32 or KDN_BF16; chunk in
  * {0, 32, 64} subject to the per-dtype limits above; T >= 0 (T = 0 copies
  * S0 / p0 to S_out / p_out); B * H * d_k * d_v < 2^31.
@@ -113,7 +131,20 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype,
                              const void *proc_noise, const void *obs_noise,
                              const float *S0, const float *p0,
                              void *o, float *S_out, float *p_out,
+                             void *workspace, unsigned long long workspace_bytes,
                              void *stream);
+
+/*
+ * Bytes of workspace kdn_chunk_prefill's two-pass schedule needs for these
+ * sizes (0 when there are no tokens or heads), or 0 with *status set when the
+ * combination is invalid or unsupported (status may be NULL).  For bf16,
+ * d_k = d_v = 128, C = 64 this is 66,048 bytes per (sequence, head, chunk),
+ * plus 2,560 for diagonal KDN.
+ */
+unsigned long long kdn_chunk_prefill_workspace_size(kdn_variant variant, kdn_dtype dtype,
+                                                    int B, int T, int H, int d_k,
+                                                    int d_v, int chunk,
+                                                    kdn_status *status);
 
 /*
  * One decode step: one token for each of N sequences x H heads, from the
@@ -148,7 +179,7 @@ int kdn_chunk_prefill_chunk_size(kdn_dtype dtype, int d_k, int d_v, int chunk);
 /* ABI version of this header (incremented on any incompatible change). */
 int kdn_abi_version(void);
 
-#define KDN_ABI_VERSION 1
+#define KDN_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -3,6 +3,7 @@
 // caller's stream.
 #include "kdn.h"
 #include "kdn_launch.h"
+#include "kdn_workspace.h"
 
 #include <stdint.h>
 
@@ -53,6 +54,7 @@ const char *kdn_status_string(kdn_status s) {
     case KDN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDN_ERR_ALIAS: return "an output overlaps an input it may not overlap";
     case KDN_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case KDN_ERR_WORKSPACE: return "the workspace is smaller than kdn_chunk_prefill_workspace_size";
     }
     return "unknown status";
 }
@@ -69,13 +71,10 @@ int kdn_chunk_prefill_chunk_size(kdn_dtype dtype, int d_k, int d_v, int chunk) {
     return chunk;
 }
 
-kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
-                             int H, int d_k, int d_v, int chunk, float mu,
-                             const void *q, const void *k, const void *v,
-                             const void *alpha, const void *beta,
-                             const void *proc_noise, const void *obs_noise,
-                             const float *S0, const float *p0, void *o,
-                             float *S_out, float *p_out, void *stream) {
+// Shape checks shared by kdn_chunk_prefill and its workspace query; the
+// chunk length in use goes to *C.
+static kdn_status prefill_shape(int variant, int dtype, int B, int T, int H, int d_k,
+                                int d_v, int chunk, int *C) {
     if (!valid_variant(variant) || !valid_dtype(dtype))
         return KDN_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || d_k <= 0 || d_v <= 0)
@@ -86,9 +85,39 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
         return KDN_ERR_SHAPE;
     if (!valid_dim(d_k) || !valid_dim(d_v))
         return KDN_ERR_UNSUPPORTED;
-    const int C = kdn_chunk_prefill_chunk_size(dtype, d_k, d_v, chunk);
-    if (C < 0)
+    *C = kdn_chunk_prefill_chunk_size((kdn_dtype)dtype, d_k, d_v, chunk);
+    if (*C < 0)
         return KDN_ERR_UNSUPPORTED;
+    return KDN_OK;
+}
+
+unsigned long long kdn_chunk_prefill_workspace_size(kdn_variant variant, kdn_dtype dtype,
+                                                    int B, int T, int H, int d_k,
+                                                    int d_v, int chunk,
+                                                    kdn_status *status) {
+    int C = 0;
+    const kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C);
+    if (status)
+        *status = st;
+    if (st != KDN_OK || (long long)B * H * T == 0)
+        return 0;
+    return (unsigned long long)kdn::prefill_workspace_bytes(variant, dtype == KDN_BF16, B, T,
+                                                            H, d_k, C);
+}
+
+kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
+                             int H, int d_k, int d_v, int chunk, float mu,
+                             const void *q, const void *k, const void *v,
+                             const void *alpha, const void *beta,
+                             const void *proc_noise, const void *obs_noise,
+                             const float *S0, const float *p0, void *o,
+                             float *S_out, float *p_out, void *workspace,
+                             unsigned long long workspace_bytes, void *stream) {
+    int C = 0;
+    if (kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C))
+        return st;
+    const long long bh = (long long)B * H;
+    const long long tok = bh * T;
     const bool kdn = variant == KDN_DIAG_KDN;
     // Empty tensors may be passed as NULL (a zero-size torch tensor has no
     // storage): per-token tensors when B*H*T = 0, state tensors when B*H = 0.
@@ -133,6 +162,20 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     if (overlap(o, tok * d_v * es, S_out, n_S)) return KDN_ERR_ALIAS;
     if (kdn && (overlap(o, tok * d_v * es, p_out, n_p) || overlap(S_out, n_S, p_out, n_p)))
         return KDN_ERR_ALIAS;
+    // Workspace of the two-pass schedule: none when there is nothing to do.
+    long long n_ws = 0;
+    if (workspace && tok > 0) {
+        n_ws = kdn::prefill_workspace_bytes(variant, dtype == KDN_BF16, B, T, H, d_k, C);
+        if ((long long)workspace_bytes < n_ws)
+            return KDN_ERR_WORKSPACE;
+        if (!aligned(workspace, 256))
+            return KDN_ERR_ALIGN;
+        const R outs[] = {{o, tok * d_v * es}, {S_out, n_S}, {p_out, n_p}};
+        for (const R &x : ins)
+            if (overlap(workspace, n_ws, x.p, x.n)) return KDN_ERR_ALIAS;
+        for (const R &x : outs)
+            if (overlap(workspace, n_ws, x.p, x.n)) return KDN_ERR_ALIAS;
+    }
 
     kdn::PrefillParams P;
     P.variant = variant;
@@ -142,6 +185,17 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.q = q; P.k = k; P.v = v; P.alpha = alpha; P.beta = beta;
     P.xi = proc_noise; P.r = obs_noise;
     P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
+    P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr;
+    if (n_ws > 0) {
+        P.ws = workspace;
+        if (kdn) {
+            const long long nc = kdn::num_chunks(T, C);
+            char *base = static_cast<char *>(workspace) +
+                         kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
+            P.ws_mob = reinterpret_cast<float *>(base);
+            P.ws_p0 = reinterpret_cast<float *>(base + kdn::WsLayout::mobius_bytes(bh, nc, d_k));
+        }
+    }
     const hipError_t e = kdn::launch_prefill(P, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;
 }

@@ -29,6 +29,11 @@ struct PrefillParams {
     void *o;
     float *S_out;
     float *p_out;      // diagonal KDN
+    // Two-pass schedule (null: single pass).  ws holds the per-chunk records
+    // (kdn_workspace.h); ws_mob / ws_p0 the diagonal-KDN variance scan.
+    void *ws;
+    float *ws_mob;
+    float *ws_p0;
 };
 
 hipError_t launch_decode(const DecodeParams &P, hipStream_t stream);
@@ -42,5 +47,18 @@ hipError_t launch_prefill_v3(const PrefillParams &P, hipStream_t stream, int nv)
 
 // d_v block width one prefill workgroup owns for this problem.
 int prefill_value_block(const PrefillParams &P);
+
+// Two-pass prefill: chunk-parallel prep kernels (one unit per variant), the
+// diagonal-KDN variance scan, and the sequential state pass.
+hipError_t launch_prefill_prep_v0(const PrefillParams &P, hipStream_t stream);
+hipError_t launch_prefill_prep_v1(const PrefillParams &P, hipStream_t stream);
+hipError_t launch_prefill_prep_v2(const PrefillParams &P, hipStream_t stream);
+hipError_t launch_prefill_prep_v3(const PrefillParams &P, hipStream_t stream);
+hipError_t launch_variance_scan(const PrefillParams &P, hipStream_t stream);
+hipError_t launch_prefill_state(const PrefillParams &P, hipStream_t stream);
+
+// Bytes of workspace the two-pass schedule needs (0 when there is no chunk).
+long long prefill_workspace_bytes(int variant, int bf16, long long B, long long T,
+                                  long long H, int dk, int C);
 
 }  // namespace kdn

@@ -41,6 +41,7 @@
 //   8  S rounded to the operand type for the next chunk's products.
 #include "kdn_device.h"
 #include "kdn_launch.h"
+#include "kdn_workspace.h"
 
 namespace kdn {
 
@@ -217,7 +218,39 @@ __device__ __forceinline__ void mma16_f32(f32x4 &acc, const float *A, int lda,
     }
 }
 
-template <typename E, int VAR, int DK, int NV, int C, int NW>
+// A-operand fragment order of the workspace (kdn_workspace.h): copy the
+// R x K matrix at src (LDS, pitch in elements) to dst, 16 bytes per unit.
+template <typename E, int R, int K, int NT>
+__device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, int tid) {
+    constexpr int EPU = 16 / (int)sizeof(E);
+    constexpr int KG = sizeof(E) == 2 ? 32 : 16;
+    constexpr int NU = R * K / EPU;
+    static_assert(K % KG == 0 && R % 16 == 0, "fragment tiling");
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int u0 = 0; u0 < NU; u0 += NT) {
+        const int u = u0 + tid;
+        if (NU % NT == 0 || u < NU) {
+            const int l = u & 63, grp = u >> 6;
+            const int m = grp / (K / KG), g = grp % (K / KG);
+            const int row = m * 16 + (l & 15);
+            uint4 val;
+            if constexpr (sizeof(E) == 2) {
+                val = *reinterpret_cast<const uint4 *>(src + row * pitch + g * 32 + (l >> 4) * 8);
+            } else {
+                const float *sp = reinterpret_cast<const float *>(src) + row * pitch + g * 16 + (l >> 4);
+                val = __builtin_bit_cast(uint4, make_float4(sp[0], sp[4], sp[8], sp[12]));
+            }
+            d[u] = val;
+        }
+    }
+}
+
+// PREP = false: the single-pass kernel, one workgroup per (batch*head, value
+// block) walking all chunks.  PREP = true: the prep kernel of the two-pass
+// schedule, one workgroup per (batch*head, chunk): steps 1-4 only, results to
+// the workspace record of the chunk.
+template <typename E, int VAR, int DK, int NV, int C, int NW, bool PREP>
 __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     using LY = PrefillLayout<E, VAR, DK, NV, C, NW>;
     constexpr int NT = LY::NT;
@@ -261,15 +294,26 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
 
     // Workgroup -> (batch*head, value block).  Dispatch is round-robin over
     // the 8 XCDs; place the value blocks of one head on one XCD.
-    const int nvb = P.dv / NV;
-    const int G = gridDim.x;
-    int lid = blockIdx.x;
-    if ((G & 7) == 0 && ((G >> 3) % nvb) == 0)
-        lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    const int bh = lid / nvb, vb = lid % nvb;
+    const int T = P.T, H = P.H, DV = P.dv;
+    const int NC = (T + C - 1) / C;
+    int bh, vb, cbeg;
+    if constexpr (PREP) {
+        bh = blockIdx.x / NC;
+        cbeg = (blockIdx.x % NC) * C;
+        vb = 0;
+    } else {
+        const int nvb = P.dv / NV;
+        const int G = gridDim.x;
+        int lid = blockIdx.x;
+        if ((G & 7) == 0 && ((G >> 3) % nvb) == 0)
+            lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+        bh = lid / nvb;
+        vb = lid % nvb;
+        cbeg = 0;
+    }
+    const int cend = PREP ? cbeg + C : T;
     const int b = bh / P.H, h = bh % P.H;
     const int v0 = vb * NV;
-    const int T = P.T, H = P.H, DV = P.dv;
 
     const E *gq = static_cast<const E *>(P.q);
     const E *gk = static_cast<const E *>(P.k);
@@ -286,7 +330,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
         const int tau = wv + NW * u, ti = tau / NTJ, tj = tau % NTJ;
-        if (NST % NW != 0 && tau >= NST) continue;
+        if (PREP || (NST % NW != 0 && tau >= NST)) continue;
         const int j = tj * 16 + (lane & 15);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -297,7 +341,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     }
     float p_reg = 0.f;                 // KDN variance of channel tid
     if (KDN && tid < DK)
-        p_reg = P.p0[(long)bh * DK + tid];
+        p_reg = PREP ? P.ws_p0[((long)bh * NC + cbeg / C) * DK + tid]
+                     : P.p0[(long)bh * DK + tid];
 
     const long sk_ = (long)H * DK;     // token stride of q/k/alpha/xi
     const long sv_ = (long)H * DV;     // token stride of v/o
@@ -313,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         rq.fetch(gq + tk * DK, sk_, Ls, tid);
         if (VDECAY) ra.fetch(ga + tk * DK, sk_, Ls, tid);
         if (KDN) rx.fetch(gx + tk * DK, sk_, Ls, tid);
-        rv.fetch(gv + tk * DV + v0, sv_, Ls, tid);
+        if (!PREP) rv.fetch(gv + tk * DV + v0, sv_, Ls, tid);
         if (tid < C) {
             const long ti = tk + (long)min(tid, Ls - 1) * H;
             if (!KDN) sc_b = gb[ti]; else sc_r = gr[ti];
@@ -321,7 +366,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         }
     };
     if (T > 0)
-        fetch(0);
+        fetch(cbeg);
 
     // Scan layout (threads < NTS): channels i0..i0+7, tokens t0..t0+TPG-1,
     // token groups vary fastest across lanes.  The operand pass uses every
@@ -335,7 +380,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     const int j0 = oc2 * 8, u0 = gh * TPG2;        // operand pass: channels, tokens
     const int ug0 = (gh / H2) * TPG;               // first token of its group
 
-    for (int c0 = 0; c0 < T; c0 += C) {
+    for (int c0 = cbeg; c0 < cend; c0 += C) {
         const int L = min(C, T - c0);
         const long tok0 = ((long)b * T + c0) * H + h;   // (b, c0, h)
 
@@ -344,7 +389,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         rq.commit(Qt, PK, 0.f, tid);
         if (VDECAY) ra.commit(ALP, PK, 1.f, tid);
         if (KDN) rx.commit(XR, PK, 0.f, tid);
-        rv.commit(VR, PV, 0.f, tid);
+        if (!PREP) rv.commit(VR, PV, 0.f, tid);
         if (tid < C) {
             const bool in = tid < L;
             if (!KDN) s_beta[tid] = in ? to_f32(sc_b) : 0.f;
@@ -354,7 +399,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         if (tid == 0)
             *s_flag = 0;
         __syncthreads();
-        if (c0 + C < T)
+        if (!PREP && c0 + C < T)
             fetch(c0 + C);
 
         // ---------------- 2. decays and write vectors ----------------
@@ -637,7 +682,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         // ---------------- 5. U = V - K~ S  ||  4a. T[I,I] ----------------
         constexpr int NTU = NB * NTJ;
         static_assert(NW >= 4 + NB, "waves 0-3 take U, waves 4.. the T blocks");
-        if (wv < 4) {
+        if (!PREP && wv < 4) {
             for (int x = wv; x < NTU; x += 4) {
                 const int mi = x / NTJ, nj = x % NTJ;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -651,7 +696,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                 }
                 lds_stn<4>(UT + j * PC + mi * 16 + (lane >> 4) * 4, uo);
             }
-        } else if (wv - 4 < NB && lane < 16) {
+        } else if (wv >= 4 && wv - 4 < NB && lane < 16) {
             // T[I,I] = (I + A[I,I])^-1 by forward substitution; lane j
             // computes column j.  A_kk is only read here (no aliasing store),
             // so the row loads can run ahead of the arithmetic.
@@ -716,6 +761,19 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             }
         }
         __syncthreads();
+        if constexpr (PREP) {
+            // ---------------- record of this chunk ----------------
+            const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
+            char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
+            store_frag<E, C, DK, NT>(rec + LW.off_kd, Kt, PK, tid);
+            store_frag<E, C, DK, NT>(rec + LW.off_qd, Qt, PK, tid);
+            store_frag<E, DK, C, NT>(rec + LW.off_wdt, WtT, PC, tid);
+            store_frag<E, C, C, NT>(rec + LW.off_aqk, AQ, PC, tid);
+            store_frag<E, C, C, NT>(rec + LW.off_tm, Tm, PC, tid);
+            if (DECAY && tid < DK)
+                reinterpret_cast<float *>(rec + LW.off_gc)[tid] = s_gc[tid];
+            continue;
+        }
 
         // ---------------- 6. E = T U ----------------
         for (int x = wv; x < NTU; x += NW) {
@@ -770,6 +828,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     }
 
     // ---- final state
+    if constexpr (PREP)
+        return;
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
         const int tau = wv + NW * u, ti = tau / NTJ, tj = tau % NTJ;
@@ -800,8 +860,30 @@ static hipError_t launch_one(const PrefillParams &P, hipStream_t st) {
     constexpr int NW = KDN_PREFILL_WAVES;
     const long heads = (long)P.B * P.H;
     const dim3 grid((unsigned)(heads * (P.dv / NV))), block(64 * NW);
-    hipLaunchKernelGGL((prefill_kernel<E, VAR, DK, NV, C, NW>), grid, block, 0, st, P);
+    hipLaunchKernelGGL((prefill_kernel<E, VAR, DK, NV, C, NW, false>), grid, block, 0, st, P);
     return hipGetLastError();
+}
+
+template <typename E, int VAR, int DK, int C>
+static hipError_t launch_prep_one(const PrefillParams &P, hipStream_t st) {
+    constexpr int NW = KDN_PREFILL_WAVES;
+    const long nc = (P.T + C - 1) / C;
+    const dim3 grid((unsigned)((long)P.B * P.H * nc)), block(64 * NW);
+    hipLaunchKernelGGL((prefill_kernel<E, VAR, DK, 16, C, NW, true>), grid, block, 0, st, P);
+    return hipGetLastError();
+}
+
+template <typename E, int VAR>
+static hipError_t launch_prep_var(const PrefillParams &P, hipStream_t st) {
+    if (P.dk == 128 && P.chunk == 64) {
+        if constexpr (sizeof(E) == 2)
+            return launch_prep_one<E, VAR, 128, 64>(P, st);
+        return hipErrorInvalidValue;
+    }
+    if (P.dk == 128 && P.chunk == 32) return launch_prep_one<E, VAR, 128, 32>(P, st);
+    if (P.dk == 64 && P.chunk == 64) return launch_prep_one<E, VAR, 64, 64>(P, st);
+    if (P.dk == 64 && P.chunk == 32) return launch_prep_one<E, VAR, 64, 32>(P, st);
+    return hipErrorInvalidValue;
 }
 
 template <typename E, int VAR, int DK, int C>
@@ -835,6 +917,11 @@ hipError_t KDN_CAT(launch_prefill_v, KDN_PREFILL_VARIANT)(const PrefillParams &P
     return P.bf16 ? launch_var<bf16, KDN_PREFILL_VARIANT>(P, st, nv)
                   : launch_var<float, KDN_PREFILL_VARIANT>(P, st, nv);
 }
+hipError_t KDN_CAT(launch_prefill_prep_v, KDN_PREFILL_VARIANT)(const PrefillParams &P,
+                                                               hipStream_t st) {
+    return P.bf16 ? launch_prep_var<bf16, KDN_PREFILL_VARIANT>(P, st)
+                  : launch_prep_var<float, KDN_PREFILL_VARIANT>(P, st);
+}
 #endif  // KDN_PREFILL_VARIANT
 
 #ifdef KDN_PREFILL_DISPATCH
@@ -850,9 +937,38 @@ int prefill_value_block(const PrefillParams &P) {
     return nv;
 }
 
+long long prefill_workspace_bytes(int variant, int bf16, long long B, long long T,
+                                  long long H, int dk, int C) {
+    const long long bh = B * H, nc = num_chunks(T, C);
+    long long n = WsLayout::make(bf16, C, dk).records(bh, nc);
+    if (variant == DIAG_KDN)
+        n += WsLayout::mobius_bytes(bh, nc, dk) + WsLayout::p0_bytes(bh, nc, dk);
+    return n;
+}
+
+static hipError_t launch_two_pass(const PrefillParams &P, hipStream_t st) {
+    hipError_t e = hipSuccess;
+    if (P.variant == DIAG_KDN && (e = launch_variance_scan(P, st)) != hipSuccess)
+        return e;
+    if (P.T > 0) {
+        switch (P.variant) {
+        case DELTANET: e = launch_prefill_prep_v0(P, st); break;
+        case GATED_DELTANET: e = launch_prefill_prep_v1(P, st); break;
+        case KDA: e = launch_prefill_prep_v2(P, st); break;
+        case DIAG_KDN: e = launch_prefill_prep_v3(P, st); break;
+        default: e = hipErrorInvalidValue;
+        }
+        if (e != hipSuccess)
+            return e;
+    }
+    return launch_prefill_state(P, st);
+}
+
 hipError_t launch_prefill(const PrefillParams &P, hipStream_t st) {
     if ((long)P.B * P.H == 0)
         return hipSuccess;
+    if (P.ws)
+        return launch_two_pass(P, st);
     const int nv = prefill_value_block(P);
     switch (P.variant) {
     case DELTANET: return launch_prefill_v0(P, st, nv);

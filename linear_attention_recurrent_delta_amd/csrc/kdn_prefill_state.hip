@@ -1,0 +1,290 @@
+// kdn_prefill_state.hip -- sequential state pass of the two-pass chunkwise
+// prefill on gfx950.
+//
+// The prep kernel has already written, per chunk, the S-independent
+// quantities K~, Q~, W~^T, A_qk, T and gamma_C (kdn_workspace.h).  What is
+// left is the inter-chunk recurrence ("معماری KDA ...", section "حل مشکل
+// وابستگی علی": provisional errors resolved by the causal triangular solve):
+//   U = V - K~ S,   E = T U,   O = Q~ S + A_qk E,   S <- diag(gamma_C) S + W~^T E.
+//
+// One workgroup of four waves owns one (batch*head, NV-column block of S).
+// S stays in registers in MFMA accumulator layout for the whole sequence and
+// is mirrored in LDS (operand type, [col][row]) for the products that read
+// it.  Wave w owns token block w of the chunk (rows 16w..16w+15 of U, E, O)
+// and key blocks w, w+4 of S.  Every A operand (the prep kernel's matrices)
+// is loaded straight from global memory into registers in fragment order,
+// one chunk ahead, so the only LDS traffic is the S / U / E exchange between
+// the MFMA output and operand layouts.  Three barriers per chunk.
+#include "kdn_device.h"
+#include "kdn_launch.h"
+#include "kdn_workspace.h"
+
+namespace kdn {
+
+typedef uint4 Frag;   // 16 bytes of an A-operand fragment
+
+template <typename E> struct FragMma;
+
+// acc += A(16 x 32) * B(32 x 16): A from a bf16 fragment, B from LDS as
+// [col][k] (pitch ldb, k offset k0).
+template <> struct FragMma<bf16> {
+    static constexpr int KG = 32;
+    __device__ __forceinline__ static void mma(f32x4 &acc, const Frag &a, const bf16 *B,
+                                               int ldb, int k0, int lane) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(
+            B + (lane & 15) * ldb + k0 + (lane >> 4) * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+    }
+};
+
+// acc += A(16 x 16) * B(16 x 16) as four fp32 MFMA steps of k = 4.
+template <> struct FragMma<float> {
+    static constexpr int KG = 16;
+    __device__ __forceinline__ static void mma(f32x4 &acc, const Frag &a, const float *B,
+                                               int ldb, int k0, int lane) {
+        const float4 af = __builtin_bit_cast(float4, a);
+        const float *pb = B + (lane & 15) * ldb + k0 + (lane >> 4);
+        const float b0 = pb[0], b1 = pb[4], b2 = pb[8], b3 = pb[12];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af.x, b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af.y, b1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af.z, b2, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af.w, b3, acc, 0, 0, 0);
+    }
+};
+
+template <typename E, bool DECAY, int DK, int NV, int C>
+__global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
+    constexpr int KG = FragMma<E>::KG;
+    constexpr int NB = C / 16;          // token blocks of a chunk
+    constexpr int NTJ = NV / 16;        // column tiles of the S block
+    constexpr int NIB = DK / 64;        // key blocks per wave (DK/16 over 4 waves)
+    constexpr int GK = DK / KG;         // fragment groups over DK
+    constexpr int GC = C / KG;          // fragment groups over C
+    constexpr int PADE = 16 / (int)sizeof(E);
+    constexpr int PK = DK + PADE, PC = C + PADE;
+    static_assert(GK * KG == DK && GC * KG == C && NB <= 4, "tiling");
+
+    __shared__ __attribute__((aligned(16))) E ST[NV * PK];   // S^T block
+    __shared__ __attribute__((aligned(16))) E UT[NV * PC];   // U^T
+    __shared__ __attribute__((aligned(16))) E ET[NV * PC];   // E^T
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool tok_wave = wv < NB;      // owns token block wv
+
+    // Workgroup -> (batch*head, value block); the value blocks of one head
+    // land on one XCD (dispatch is round-robin over the 8 XCDs), so they
+    // share the head's workspace records through that XCD's L2.
+    const int nvb = P.dv / NV;
+    const int G = gridDim.x;
+    int lid = blockIdx.x;
+    if ((G & 7) == 0 && ((G >> 3) % nvb) == 0)
+        lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int bh = lid / nvb, vb = lid % nvb;
+    const int b = bh / P.H, h = bh % P.H;
+    const int v0 = vb * NV;
+    const int T = P.T, H = P.H, DV = P.dv;
+    const int NC = (T + C - 1) / C;
+    const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
+    const char *ws = static_cast<const char *>(P.ws) + (long)bh * NC * LW.rec;
+    const E *gv = static_cast<const E *>(P.v);
+    E *go = static_cast<E *>(P.o);
+
+    // S block in accumulator layout: sacc[n][nj][r] =
+    //   S[(wv + 4n)*16 + (lane>>4)*4 + r][v0 + nj*16 + (lane&15)]
+    f32x4 sacc[NIB][NTJ];
+#pragma unroll
+    for (int n = 0; n < NIB; ++n)
+#pragma unroll
+        for (int nj = 0; nj < NTJ; ++nj) {
+            const int i0 = (wv + 4 * n) * 16 + (lane >> 4) * 4;
+            const int j = nj * 16 + (lane & 15);
+            float s4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sacc[n][nj][r] = P.S0 ? P.S0[((long)bh * DK + i0 + r) * DV + v0 + j] : 0.f;
+                s4[r] = sacc[n][nj][r];
+            }
+            lds_stn<4>(ST + j * PK + i0, s4);
+        }
+
+    struct Chunk {
+        Frag kd[GK], qd[GK], tm[GC], aq[GC], wt[NIB][GC];
+        float4 gc[NIB];
+        E v[NTJ][4];
+    };
+    auto load = [&](Chunk &X, int c) {
+        const char *rec = ws + (long)c * LW.rec;
+        const Frag *kd = reinterpret_cast<const Frag *>(rec + LW.off_kd);
+        const Frag *qd = reinterpret_cast<const Frag *>(rec + LW.off_qd);
+        const Frag *wt = reinterpret_cast<const Frag *>(rec + LW.off_wdt);
+        const Frag *aq = reinterpret_cast<const Frag *>(rec + LW.off_aqk);
+        const Frag *tm = reinterpret_cast<const Frag *>(rec + LW.off_tm);
+        const float *gc = reinterpret_cast<const float *>(rec + LW.off_gc);
+        if (tok_wave) {
+#pragma unroll
+            for (int g = 0; g < GK; ++g) {
+                X.kd[g] = kd[(wv * GK + g) * 64 + lane];
+                X.qd[g] = qd[(wv * GK + g) * 64 + lane];
+            }
+#pragma unroll
+            for (int g = 0; g < GC; ++g)
+                if (g * KG < (wv + 1) * 16) {       // T, A_qk: lower blocks only
+                    X.tm[g] = tm[(wv * GC + g) * 64 + lane];
+                    X.aq[g] = aq[(wv * GC + g) * 64 + lane];
+                }
+            const int L = min(C, T - c * C);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = wv * 16 + (lane >> 4) * 4 + r;
+                const long row = ((long)b * T + c * C + min(t, L - 1)) * H + h;
+#pragma unroll
+                for (int nj = 0; nj < NTJ; ++nj)
+                    X.v[nj][r] = gv[row * DV + v0 + nj * 16 + (lane & 15)];
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NIB; ++n) {
+            const int ib = wv + 4 * n;
+#pragma unroll
+            for (int g = 0; g < GC; ++g)
+                X.wt[n][g] = wt[(ib * GC + g) * 64 + lane];
+            if (DECAY)
+                X.gc[n] = *reinterpret_cast<const float4 *>(gc + ib * 16 + (lane >> 4) * 4);
+        }
+    };
+
+    auto compute = [&](const Chunk &X, int c) {
+        const int c0 = c * C, L = min(C, T - c0);
+        f32x4 accq[NTJ];
+        // U = V - K~ S and the first half of O = Q~ S
+        if (tok_wave) {
+#pragma unroll
+            for (int nj = 0; nj < NTJ; ++nj) {
+                f32x4 accu = {0.f, 0.f, 0.f, 0.f};
+                accq[nj] = accu;
+#pragma unroll
+                for (int g = 0; g < GK; ++g) {
+                    FragMma<E>::mma(accu, X.kd[g], ST + nj * 16 * PK, PK, g * KG, lane);
+                    FragMma<E>::mma(accq[nj], X.qd[g], ST + nj * 16 * PK, PK, g * KG, lane);
+                }
+                float u[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tt = wv * 16 + (lane >> 4) * 4 + r;
+                    u[r] = (tt < L ? to_f32(X.v[nj][r]) : 0.f) - accu[r];
+                }
+                lds_stn<4>(UT + (nj * 16 + (lane & 15)) * PC + wv * 16 + (lane >> 4) * 4, u);
+            }
+        }
+        __syncthreads();
+        // E = T U
+        if (tok_wave) {
+#pragma unroll
+            for (int nj = 0; nj < NTJ; ++nj) {
+                f32x4 acce = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int g = 0; g < GC; ++g)
+                    if (g * KG < (wv + 1) * 16)
+                        FragMma<E>::mma(acce, X.tm[g], UT + nj * 16 * PC, PC, g * KG, lane);
+                float e[4] = {acce[0], acce[1], acce[2], acce[3]};
+                lds_stn<4>(ET + (nj * 16 + (lane & 15)) * PC + wv * 16 + (lane >> 4) * 4, e);
+            }
+        }
+        __syncthreads();
+        // O = Q~ S + A_qk E;  S <- diag(gamma_C) S + W~^T E
+        if (tok_wave) {
+#pragma unroll
+            for (int nj = 0; nj < NTJ; ++nj) {
+#pragma unroll
+                for (int g = 0; g < GC; ++g)
+                    if (g * KG < (wv + 1) * 16)
+                        FragMma<E>::mma(accq[nj], X.aq[g], ET + nj * 16 * PC, PC, g * KG, lane);
+                const int j = v0 + nj * 16 + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = wv * 16 + (lane >> 4) * 4 + r;
+                    if (t < L)
+                        go[(((long)b * T + c0 + t) * H + h) * DV + j] = from_f32<E>(accq[nj][r]);
+                }
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NIB; ++n) {
+            const int i0 = (wv + 4 * n) * 16 + (lane >> 4) * 4;
+#pragma unroll
+            for (int nj = 0; nj < NTJ; ++nj) {
+                if (DECAY) {
+                    sacc[n][nj][0] *= X.gc[n].x;
+                    sacc[n][nj][1] *= X.gc[n].y;
+                    sacc[n][nj][2] *= X.gc[n].z;
+                    sacc[n][nj][3] *= X.gc[n].w;
+                }
+#pragma unroll
+                for (int g = 0; g < GC; ++g)
+                    FragMma<E>::mma(sacc[n][nj], X.wt[n][g], ET + nj * 16 * PC, PC, g * KG, lane);
+                float s4[4] = {sacc[n][nj][0], sacc[n][nj][1], sacc[n][nj][2], sacc[n][nj][3]};
+                lds_stn<4>(ST + (nj * 16 + (lane & 15)) * PK + i0, s4);
+            }
+        }
+        __syncthreads();
+    };
+
+    __syncthreads();
+    Chunk A, B;
+    if (NC > 0)
+        load(A, 0);
+    for (int c = 0; c < NC; c += 2) {
+        if (c + 1 < NC)
+            load(B, c + 1);
+        compute(A, c);
+        if (c + 1 < NC) {
+            if (c + 2 < NC)
+                load(A, c + 2);
+            compute(B, c + 1);
+        }
+    }
+
+#pragma unroll
+    for (int n = 0; n < NIB; ++n)
+#pragma unroll
+        for (int nj = 0; nj < NTJ; ++nj) {
+            const int i0 = (wv + 4 * n) * 16 + (lane >> 4) * 4;
+            const int j = nj * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                P.S_out[((long)bh * DK + i0 + r) * DV + v0 + j] = sacc[n][nj][r];
+        }
+}
+
+template <typename E, bool DECAY, int DK, int NV, int C>
+static hipError_t launch_state_one(const PrefillParams &P, hipStream_t st) {
+    const long heads = (long)P.B * P.H;
+    const dim3 grid((unsigned)(heads * (P.dv / NV))), block(256);
+    hipLaunchKernelGGL((prefill_state_kernel<E, DECAY, DK, NV, C>), grid, block, 0, st, P);
+    return hipGetLastError();
+}
+
+template <typename E, bool DECAY, int DK>
+static hipError_t launch_state_c(const PrefillParams &P, hipStream_t st) {
+    if (P.chunk == 64) return launch_state_one<E, DECAY, DK, 16, 64>(P, st);
+    if (P.chunk == 32) return launch_state_one<E, DECAY, DK, 16, 32>(P, st);
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+static hipError_t launch_state_e(const PrefillParams &P, hipStream_t st) {
+    const bool decay = P.variant != DELTANET;
+    if (P.dk == 128)
+        return decay ? launch_state_c<E, true, 128>(P, st) : launch_state_c<E, false, 128>(P, st);
+    if (P.dk == 64)
+        return decay ? launch_state_c<E, true, 64>(P, st) : launch_state_c<E, false, 64>(P, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_state(const PrefillParams &P, hipStream_t st) {
+    return P.bf16 ? launch_state_e<bf16>(P, st) : launch_state_e<float>(P, st);
+}
+
+}  // namespace kdn

@@ -1,0 +1,65 @@
+// kdn_workspace.h -- layout of the prefill workspace that carries one chunk's
+// S-independent quantities from the chunk-parallel prep kernel to the
+// sequential state kernel.
+//
+// One record per (batch*head, chunk), records ordered [bh][chunk]:
+//   Kd   C  x DK   decay-scaled keys     K~ = gamma (.) K
+//   Qd   C  x DK   decay-scaled queries  Q~ = gamma (.) Q
+//   WdT  DK x C    W~^T, W~_s = (gamma_C / gamma_s) (.) w_s
+//   Aqk  C  x C    A_qk (lower triangle, diagonal included)
+//   Tm   C  x C    T = (I + A_kk)^-1 (unit lower triangular)
+//   gC   DK        gamma_C (float32)
+// (chunk algebra: "معماری KDA ...", section "حل مشکل وابستگی علی").
+//
+// The five matrices are in the operand type E and stored in MFMA A-operand
+// fragment order, so that a wave loads the 16-row block it multiplies with
+// one coalesced 16-byte load per lane per group:
+//   a matrix X[R][K] is cut into 16-row blocks m and k groups g of
+//   KG = 16 / sizeof(E) * KSTEP / KPL elements (32 for bf16, 16 for float);
+//   lane l of group (m, g) holds 16 bytes at ((m * (K / KG) + g) * 64 + l),
+//     bf16 : X[m*16 + (l & 15)][g*32 + (l >> 4)*8 + e],      e = 0..7
+//     float: X[m*16 + (l & 15)][g*16 + s*4 + (l >> 4)],       s = 0..3
+//   i.e. exactly the A operand of v_mfma_f32_16x16x32_bf16 (one step) or of
+//   four v_mfma_f32_16x16x4_f32 steps.
+//
+// For diagonal KDN the workspace also holds, after the records:
+//   Mob  [bh][chunk][DK][4] float32  per-chunk composition of the variance
+//                                    maps (Mobius form, kdn_variance.hip)
+//   P0   [bh][chunk][DK]    float32  variance at each chunk start
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kdn {
+
+struct WsLayout {
+    long es;          // bytes per operand element
+    int C, DK;
+    long off_kd, off_qd, off_wdt, off_aqk, off_tm, off_gc, rec;
+
+    __host__ __device__ static WsLayout make(int bf16, int C, int DK) {
+        WsLayout w;
+        w.es = bf16 ? 2 : 4;
+        w.C = C;
+        w.DK = DK;
+        const long ck = (long)C * DK * w.es, cc = (long)C * C * w.es;
+        w.off_kd = 0;
+        w.off_qd = w.off_kd + ck;
+        w.off_wdt = w.off_qd + ck;
+        w.off_aqk = w.off_wdt + ck;
+        w.off_tm = w.off_aqk + cc;
+        w.off_gc = w.off_tm + cc;
+        w.rec = (w.off_gc + (long)DK * 4 + 255) / 256 * 256;
+        return w;
+    }
+    // bytes of the records, and of the whole workspace
+    __host__ __device__ long records(long bh, long nc) const { return bh * nc * rec; }
+    __host__ __device__ static long mobius_bytes(long bh, long nc, int DK) { return bh * nc * DK * 4 * 4; }
+    __host__ __device__ static long p0_bytes(long bh, long nc, int DK) { return bh * nc * DK * 4; }
+};
+
+// Number of chunks of a sequence of T tokens.
+__host__ __device__ inline long num_chunks(long T, int C) { return (T + C - 1) / C; }
+
+}  // namespace kdn

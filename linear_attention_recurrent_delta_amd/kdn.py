@@ -21,7 +21,7 @@ VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "diag_kdn": 3}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "KDN_OK", 1: "KDN_ERR_NULL", 2: "KDN_ERR_SHAPE",
           3: "KDN_ERR_UNSUPPORTED", 4: "KDN_ERR_ALIGN", 5: "KDN_ERR_ALIAS",
-          6: "KDN_ERR_HIP"}
+          6: "KDN_ERR_HIP", 7: "KDN_ERR_WORKSPACE"}
 
 _lib = None
 
@@ -43,7 +43,10 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.kdn_chunk_prefill.restype = i
-    lib.kdn_chunk_prefill.argtypes = [i, i, i, i, i, i, i, i, f] + [vp] * 13
+    u64 = ctypes.c_ulonglong
+    lib.kdn_chunk_prefill.argtypes = [i, i, i, i, i, i, i, i, f] + [vp] * 12 + [vp, u64, vp]
+    lib.kdn_chunk_prefill_workspace_size.restype = u64
+    lib.kdn_chunk_prefill_workspace_size.argtypes = [i] * 8 + [ctypes.POINTER(i)]
     lib.kdn_recurrent_decode.restype = i
     lib.kdn_recurrent_decode.argtypes = [i, i, i, i, i, i, f] + [vp] * 11
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -102,16 +105,31 @@ def kdn_chunk_prefill_chunk_size(dtype: int, d_k: int, d_v: int, chunk: int) -> 
 
 def kdn_chunk_prefill(variant, dtype, B, T, H, d_k, d_v, chunk, mu, q, k, v,
                       alpha, beta, proc_noise, obs_noise, S0, p0, o, S_out,
-                      p_out, stream=None):
+                      p_out, workspace=None, workspace_bytes=0, stream=None):
     """Raw entry point: same arguments as the C function (tensors or ints
-    for pointers, None for NULL)."""
+    for pointers, None for NULL).  A tensor workspace passes its byte size
+    when ``workspace_bytes`` is 0."""
     lib = load()
+    if workspace is not None and not isinstance(workspace, int) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib.kdn_chunk_prefill(
         int(variant), int(dtype), int(B), int(T), int(H), int(d_k), int(d_v),
         int(chunk), float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _ptr(proc_noise), _ptr(obs_noise), _ptr(S0), _ptr(p0),
-        _ptr(o), _ptr(S_out), _ptr(p_out), _stream(stream))
+        _ptr(o), _ptr(S_out), _ptr(p_out), _ptr(workspace), int(workspace_bytes),
+        _stream(stream))
     _check(lib, st)
+
+
+def kdn_chunk_prefill_workspace_size(variant, dtype, B, T, H, d_k, d_v, chunk):
+    """Bytes of workspace for the two-pass schedule; raises on invalid sizes."""
+    lib = load()
+    st = ctypes.c_int(0)
+    n = lib.kdn_chunk_prefill_workspace_size(int(variant), int(dtype), int(B), int(T),
+                                             int(H), int(d_k), int(d_v), int(chunk),
+                                             ctypes.byref(st))
+    _check(lib, st.value)
+    return int(n)
 
 
 def kdn_recurrent_decode(variant, dtype, N, H, d_k, d_v, mu, q, k, v, alpha,
@@ -130,12 +148,26 @@ def kdn_recurrent_decode(variant, dtype, N, H, d_k, d_v, mu, q, k, v, alpha,
 # Tensor-shaped conveniences (allocate outputs, infer sizes, then call the
 # entry points above).
 # ---------------------------------------------------------------------------
+def workspace(variant, q, v, chunk=0):
+    """A workspace tensor (uint8, on q's device) for the two-pass prefill of
+    inputs shaped like q [B,T,H,dk] and v [B,T,H,dv]; None if none is needed."""
+    vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    B, T, H, dk = q.shape
+    n = kdn_chunk_prefill_workspace_size(vid, DTYPES[q.dtype], B, T, H, dk,
+                                         v.shape[-1], chunk)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def prefill(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
             obs_noise=None, S0=None, p0=None, mu=1.0, chunk=0, out=None,
-            stream=None):
+            workspace="auto", stream=None):
     """Chunkwise prefill.  q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bf16).
     Returns (o, S, p); p is None unless variant is diag_kdn.  ``out`` may pass
-    preallocated (o, S_out, p_out)."""
+    preallocated (o, S_out, p_out).  ``workspace``: "auto" allocates one for
+    the two-pass schedule, None selects the single-pass kernel, a uint8
+    tensor from :func:`workspace` is used as given."""
     vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -147,8 +179,12 @@ def prefill(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
              if vid == 3 else None)
     else:
         o, S, p = out
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"kdn: workspace must be 'auto', None or a tensor, not {workspace!r}")
+        workspace = globals()["workspace"](vid, q, v, chunk)
     kdn_chunk_prefill(vid, dt, B, T, H, dk, dv, chunk, mu, q, k, v, alpha, beta,
-                      proc_noise, obs_noise, S0, p0, o, S, p, stream)
+                      proc_noise, obs_noise, S0, p0, o, S, p, workspace, 0, stream)
     return o, S, p
 
 

@@ -45,12 +45,17 @@ def to_device(inp, device="cuda"):
             for k, v in inp.items()}
 
 
+# Prefill schedule the GPU tests run: "auto" (two-pass, with a workspace) or
+# None (single pass).  test_gpu_parity runs every case under both.
+SCHEDULE = {"workspace": "auto"}
+
+
 def gpu_prefill(variant, inp, mu=1.0, chunk=0, out=None):
     o, S, p = kdn.prefill(variant, inp["q"], inp["k"], inp["v"],
                           alpha=inp.get("alpha"), beta=inp.get("beta"),
                           proc_noise=inp.get("xi"), obs_noise=inp.get("r"),
                           S0=inp.get("S0"), p0=inp.get("p0"), mu=mu, chunk=chunk,
-                          out=out)
+                          out=out, workspace=SCHEDULE["workspace"])
     torch.cuda.synchronize()
     return o, S, p
 

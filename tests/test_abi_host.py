@@ -16,7 +16,7 @@ from linear_attention_recurrent_delta_amd import kdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kdn.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EHIP = range(7)
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EHIP, EWS = range(8)
 A = 1 << 32          # fake, 16-byte aligned device addresses spaced far apart
 MB = 1 << 26
 
@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kdn_chunk_prefill", "kdn_recurrent_decode", "kdn_status_string",
-              "kdn_chunk_prefill_chunk_size", "kdn_abi_version"):
+              "kdn_chunk_prefill_chunk_size", "kdn_abi_version",
+              "kdn_chunk_prefill_workspace_size"):
         assert n in names
 
 
@@ -46,12 +47,12 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.kdn_abi_version() == 1
+    assert lib.kdn_abi_version() == 2
 
 
 def test_status_strings(lib):
     seen = set()
-    for s in range(7):
+    for s in range(8):
         msg = lib.kdn_status_string(s).decode()
         assert msg and msg not in seen
         seen.add(msg)
@@ -78,11 +79,60 @@ def _prefill_args(variant=1, dtype=1, B=2, T=100, H=4, dk=128, dv=128, chunk=0,
              beta=None if kdn_ else A + 4 * MB,
              xi=A + 5 * MB if kdn_ else None, r=A + 6 * MB if kdn_ else None,
              S0=A + 7 * MB, p0=A + 8 * MB if kdn_ else None, o=A + 9 * MB,
-             S_out=A + 10 * MB, p_out=A + 11 * MB if kdn_ else None)
+             S_out=A + 10 * MB, p_out=A + 11 * MB if kdn_ else None,
+             ws=None, ws_bytes=0)
     a.update(over)
     return (variant, dtype, B, T, H, dk, dv, chunk, 1.0, a["q"], a["k"], a["v"],
             a["alpha"], a["beta"], a["xi"], a["r"], a["S0"], a["p0"], a["o"],
-            a["S_out"], a["p_out"], None)
+            a["S_out"], a["p_out"], a["ws"], a["ws_bytes"], None)
+
+
+def _ws_size(lib, variant=1, dtype=1, B=2, T=100, H=4, dk=128, dv=128, chunk=0):
+    st = ctypes.c_int(-1)
+    n = lib.kdn_chunk_prefill_workspace_size(variant, dtype, B, T, H, dk, dv, chunk,
+                                             ctypes.byref(st))
+    return n, st.value
+
+
+def test_workspace_size_query(lib):
+    # bf16, d_k = 128, C = 64: K~, Q~, W~^T (3 x 16 KiB), A_qk and T (2 x 8 KiB)
+    # and gamma_C (512 B) per (sequence, head, chunk) record
+    rec = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4
+    assert rec == 66048
+    assert _ws_size(lib) == (2 * 4 * 2 * rec, OK)                # T = 100: 2 chunks
+    kdn_extra = 128 * 4 * 4 + 128 * 4                            # variance maps, p0
+    assert _ws_size(lib, variant=3) == (2 * 4 * 2 * (rec + kdn_extra), OK)
+    # float32, d_k = 128: default chunk 32, record rounded up to 256 bytes
+    rec32 = 3 * 32 * 128 * 4 + 2 * 32 * 32 * 4 + 128 * 4
+    assert _ws_size(lib, dtype=0) == (2 * 4 * 4 * ((rec32 + 255) // 256 * 256), OK)
+    assert _ws_size(lib, T=0) == (0, OK)
+    assert _ws_size(lib, B=0) == (0, OK)
+    assert _ws_size(lib, dk=96) == (0, EUNSUP)
+    assert _ws_size(lib, T=-1) == (0, ESHAPE)
+    assert _ws_size(lib, chunk=48) == (0, EUNSUP)
+    assert lib.kdn_chunk_prefill_workspace_size(1, 1, 1, 64, 1, 64, 64, 0, None) > 0
+
+
+def _ws_ok(lib, **kw):
+    n, st = _ws_size(lib, **kw)
+    assert st == OK and n > 0
+    return n
+
+
+def test_workspace_validation(lib):
+    n = _ws_ok(lib)
+    W = A + 12 * MB
+    call = lambda **o: lib.kdn_chunk_prefill(*_prefill_args(**o))
+    assert call(ws=W, ws_bytes=n - 1) == EWS
+    assert call(ws=W, ws_bytes=0) == EWS
+    assert call(ws=W + 16, ws_bytes=n) == EALIGN
+    assert call(ws=A + 9 * MB, ws_bytes=n) == EALIAS           # overlaps o
+    assert call(ws=A + 10 * MB - 256, ws_bytes=n) == EALIAS    # runs into S_out
+    assert call(ws=A + 2 * MB, ws_bytes=n) == EALIAS           # overlaps v
+    nk = _ws_ok(lib, variant=3)
+    assert lib.kdn_chunk_prefill(*_prefill_args(variant=3, ws=W, ws_bytes=nk - 1)) == EWS
+    # validation of the other arguments still comes first
+    assert call(q=None, ws=W, ws_bytes=0) == ENULL
 
 
 def _decode_args(variant=3, dtype=1, N=8, H=4, dk=128, dv=128, **over):
@@ -164,6 +214,9 @@ def test_binding_raises_with_status(lib):
     with pytest.raises(kdn.KdnError) as e:
         kdn.kdn_chunk_prefill(*_prefill_args(q=None)[:-1], stream=0)
     assert e.value.status == ENULL
+    with pytest.raises(kdn.KdnError) as e:
+        kdn.kdn_chunk_prefill_workspace_size(1, 1, 2, 100, 4, 96, 128, 0)
+    assert e.value.status == EUNSUP
 
 
 def test_binding_missing_library_raises(tmp_path):

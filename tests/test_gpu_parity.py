@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_util
+
 from gpu_util import (TOL, check, compare_prefill, decode_inputs_as_prefill,
                       gpu_decode_run, gpu_prefill, log, np64, oracle_prefill,
                       to_device)
@@ -26,6 +28,15 @@ def _lib():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     kdn.ensure_built()
     yield
+
+
+@pytest.fixture(params=["two_pass", "single_pass"], autouse=True)
+def schedule(request):
+    """Every prefill case runs under both schedules of kdn_chunk_prefill."""
+    gpu_util.SCHEDULE["workspace"] = "auto" if request.param == "two_pass" else None
+    log(f"schedule {request.param}")
+    yield request.param
+    gpu_util.SCHEDULE["workspace"] = "auto"
 
 
 def _inputs(variant, B, T, H, dk, dv, dtype, seed, random_state=True, device="cuda"):
