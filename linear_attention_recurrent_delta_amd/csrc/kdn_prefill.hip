@@ -294,8 +294,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
 
     // Workgroup -> (batch*head, value block).  Dispatch is round-robin over
     // the 8 XCDs; place the value blocks of one head on one XCD.
+    // PREP: persistent workgroups; unit u = (batch*head, chunk) = divmod(u, NC)
+    // for u = blockIdx.x, blockIdx.x + gridDim.x, ...
     const int T = P.T, H = P.H, DV = P.dv;
     const int NC = (T + C - 1) / C;
+    const int NU = P.B * H * NC;
     int bh, vb, cbeg;
     if constexpr (PREP) {
         bh = blockIdx.x / NC;
@@ -311,8 +314,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         vb = lid % nvb;
         cbeg = 0;
     }
-    const int cend = PREP ? cbeg + C : T;
-    const int b = bh / P.H, h = bh % P.H;
+    int b = bh / P.H, h = bh % P.H;
     const int v0 = vb * NV;
 
     const E *gq = static_cast<const E *>(P.q);
@@ -340,9 +342,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         }
     }
     float p_reg = 0.f;                 // KDN variance of channel tid
-    if (KDN && tid < DK)
-        p_reg = PREP ? P.ws_p0[((long)bh * NC + cbeg / C) * DK + tid]
-                     : P.p0[(long)bh * DK + tid];
+    float p_nxt = 0.f;                 // PREP: variance at the next unit's start
+    if (KDN && tid < DK && !PREP)
+        p_reg = P.p0[(long)bh * DK + tid];
 
     const long sk_ = (long)H * DK;     // token stride of q/k/alpha/xi
     const long sv_ = (long)H * DV;     // token stride of v/o
@@ -351,9 +353,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     TileRegs<E, DK, C, NT> rk, rq, ra, rx;
     TileRegs<E, NV, C, NT> rv;
     E sc_b = from_f32<E>(0.f), sc_r = from_f32<E>(1.f), sc_a = from_f32<E>(1.f);
-    auto fetch = [&](int cs) {
+    auto fetch = [&](int bs, int cs) {
         const int Ls = min(C, T - cs);
-        const long tk = ((long)b * T + cs) * H + h;
+        const long tk = ((long)(bs / H) * T + cs) * H + bs % H;
+        if (PREP && KDN && tid < DK)
+            p_nxt = P.ws_p0[((long)bs * NC + cs / C) * DK + tid];
         rk.fetch(gk + tk * DK, sk_, Ls, tid);
         rq.fetch(gq + tk * DK, sk_, Ls, tid);
         if (VDECAY) ra.fetch(ga + tk * DK, sk_, Ls, tid);
@@ -365,8 +369,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             if (VAR == GATED_DELTANET) sc_a = ga[ti];
         }
     };
-    if (T > 0)
-        fetch(cbeg);
+    if (T > 0 && (!PREP || (int)blockIdx.x < NU))
+        fetch(bh, cbeg);
 
     // Scan layout (threads < NTS): channels i0..i0+7, tokens t0..t0+TPG-1,
     // token groups vary fastest across lanes.  The operand pass uses every
@@ -380,7 +384,16 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     const int j0 = oc2 * 8, u0 = gh * TPG2;        // operand pass: channels, tokens
     const int ug0 = (gh / H2) * TPG;               // first token of its group
 
-    for (int c0 = cbeg; c0 < cend; c0 += C) {
+    for (int it = PREP ? (int)blockIdx.x : 0; it < (PREP ? NU : T);
+         it += PREP ? (int)gridDim.x : C) {
+        int c0 = it;
+        if constexpr (PREP) {
+            bh = it / NC;
+            c0 = (it % NC) * C;
+            b = bh / H;
+            h = bh % H;
+            p_reg = p_nxt;
+        }
         const int L = min(C, T - c0);
         const long tok0 = ((long)b * T + c0) * H + h;   // (b, c0, h)
 
@@ -399,8 +412,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         if (tid == 0)
             *s_flag = 0;
         __syncthreads();
-        if (!PREP && c0 + C < T)
-            fetch(c0 + C);
+        if (PREP) {
+            const int nu = it + (int)gridDim.x;
+            if (nu < NU)
+                fetch(nu / NC, (nu % NC) * C);
+        } else if (c0 + C < T) {
+            fetch(bh, c0 + C);
+        }
 
         // ---------------- 2. decays and write vectors ----------------
         if constexpr (KDN) {
@@ -772,6 +790,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             store_frag<E, C, C, NT>(rec + LW.off_tm, Tm, PC, tid);
             if (DECAY && tid < DK)
                 reinterpret_cast<float *>(rec + LW.off_gc)[tid] = s_gc[tid];
+            __syncthreads();            // LDS reads done before the next commit
             continue;
         }
 
@@ -867,8 +886,15 @@ static hipError_t launch_one(const PrefillParams &P, hipStream_t st) {
 template <typename E, int VAR, int DK, int C>
 static hipError_t launch_prep_one(const PrefillParams &P, hipStream_t st) {
     constexpr int NW = KDN_PREFILL_WAVES;
-    const long nc = (P.T + C - 1) / C;
-    const dim3 grid((unsigned)((long)P.B * P.H * nc)), block(64 * NW);
+    const long units = (long)P.B * P.H * ((P.T + C - 1) / C);
+    // persistent: one workgroup per CU (the LDS footprint allows one), each
+    // walking every gridDim-th (batch*head, chunk) unit
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const long g = units < cus ? units : cus;
+    const dim3 grid((unsigned)g), block(64 * NW);
     hipLaunchKernelGGL((prefill_kernel<E, VAR, DK, 16, C, NW, true>), grid, block, 0, st, P);
     return hipGetLastError();
 }

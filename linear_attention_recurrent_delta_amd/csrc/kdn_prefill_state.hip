@@ -19,6 +19,7 @@
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
 
+
 namespace kdn {
 
 typedef uint4 Frag;   // 16 bytes of an A-operand fragment
@@ -53,6 +54,32 @@ template <> struct FragMma<float> {
     }
 };
 
+// Raw buffer access (offsets in bytes).  Word 3 of the descriptor selects
+// 32-bit data format so the range check applies; offsets at or beyond
+// `bytes` read as 0 and drop stores.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ Frag buf_frag(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+    return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
+}
+template <typename E> __device__ __forceinline__ E buf_elem(__amdgpu_buffer_rsrc_t r, unsigned voff);
+template <> __device__ __forceinline__ bf16 buf_elem<bf16>(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0));
+}
+template <> __device__ __forceinline__ float buf_elem<float>(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+}
+template <typename E> __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, unsigned voff, E x);
+template <> __device__ __forceinline__ void buf_store<bf16>(__amdgpu_buffer_rsrc_t r, unsigned voff, bf16 x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, (int)voff, 0, 0);
+}
+template <> __device__ __forceinline__ void buf_store<float>(__amdgpu_buffer_rsrc_t r, unsigned voff, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, (int)voff, 0, 0);
+}
+
 template <typename E, bool DECAY, int DK, int NV, int C>
 __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
     constexpr int KG = FragMma<E>::KG;
@@ -71,7 +98,7 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool tok_wave = wv < NB;      // owns token block wv
+    const bool tok_wave = NB >= 4 || wv < NB;   // owns token block wv
 
     // Workgroup -> (batch*head, value block); the value blocks of one head
     // land on one XCD (dispatch is round-robin over the 8 XCDs), so they
@@ -85,7 +112,7 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
     const int b = bh / P.H, h = bh % P.H;
     const int v0 = vb * NV;
     const int T = P.T, H = P.H, DV = P.dv;
-    const int NC = (T + C - 1) / C;
+    const int NC = (T + C - 1) / C;     // chunks
     const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
     const char *ws = static_cast<const char *>(P.ws) + (long)bh * NC * LW.rec;
     const E *gv = static_cast<const E *>(P.v);
@@ -109,54 +136,86 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
             lds_stn<4>(ST + j * PK + i0, s4);
         }
 
+    // Operands of the first two phases are loaded one chunk ahead; those of
+    // the last phase (A_qk, W~^T, gamma_C) at the start of their own chunk,
+    // which keeps the register footprint at two workgroups per CU.
     struct Chunk {
-        Frag kd[GK], qd[GK], tm[GC], aq[GC], wt[NIB][GC];
-        float4 gc[NIB];
+        Frag kd[GK], qd[GK], tm[GC];
         E v[NTJ][4];
     };
+    struct Late {
+        Frag aq[GC], wt[NIB][GC];
+        Frag gc[NIB];
+    };
+    // Memory access: buffer instructions with a wave-uniform descriptor per
+    // chunk (scalar registers) and per-lane byte offsets fixed for the whole
+    // sequence, so no vector address arithmetic runs per chunk.  Rows of v
+    // and o past the end of the sequence fall outside the descriptor's range:
+    // those loads return 0 and those stores are dropped by the hardware.
+    const unsigned lane16 = (unsigned)lane * 16u;          // fragment slot
+    const long hdv = (long)H * DV;                         // token stride of v, o
+    const long seq0 = ((long)b * T * H + h) * DV + v0;     // (b, t=0, h, v0)
+    unsigned vofs[NTJ][4];                                 // byte offsets in a chunk
+#pragma unroll
+    for (int nj = 0; nj < NTJ; ++nj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            vofs[nj][r] = (unsigned)(((wv * 16 + (lane >> 4) * 4 + r) * hdv +
+                                      (lane & 15) + nj * 16) * (long)sizeof(E));
+    const unsigned gc_lane = (unsigned)(lane >> 4) * 16u;
+    auto rec_rsrc = [&](int c) { return buf_rsrc(ws + (long)c * LW.rec, (unsigned)LW.rec); };
+    // v / o rows of chunk c: [c*C, c*C + L) in range
+    auto row_rsrc = [&](const E *base, int c) {
+        const int L = min(C, T - c * C);
+        return buf_rsrc(base + seq0 + (long)c * C * hdv,
+                        (unsigned)(((L - 1) * hdv + NV) * (long)sizeof(E)));
+    };
+
     auto load = [&](Chunk &X, int c) {
-        const char *rec = ws + (long)c * LW.rec;
-        const Frag *kd = reinterpret_cast<const Frag *>(rec + LW.off_kd);
-        const Frag *qd = reinterpret_cast<const Frag *>(rec + LW.off_qd);
-        const Frag *wt = reinterpret_cast<const Frag *>(rec + LW.off_wdt);
-        const Frag *aq = reinterpret_cast<const Frag *>(rec + LW.off_aqk);
-        const Frag *tm = reinterpret_cast<const Frag *>(rec + LW.off_tm);
-        const float *gc = reinterpret_cast<const float *>(rec + LW.off_gc);
         if (tok_wave) {
+            const auto rr = rec_rsrc(c);
+            const int okd = (int)LW.off_kd + wv * GK * 1024;
+            const int oqd = (int)LW.off_qd + wv * GK * 1024;
+            const int otm = (int)LW.off_tm + wv * GC * 1024;
 #pragma unroll
             for (int g = 0; g < GK; ++g) {
-                X.kd[g] = kd[(wv * GK + g) * 64 + lane];
-                X.qd[g] = qd[(wv * GK + g) * 64 + lane];
+                X.kd[g] = buf_frag(rr, lane16, okd + g * 1024);
+                X.qd[g] = buf_frag(rr, lane16, oqd + g * 1024);
             }
 #pragma unroll
             for (int g = 0; g < GC; ++g)
-                if (g * KG < (wv + 1) * 16) {       // T, A_qk: lower blocks only
-                    X.tm[g] = tm[(wv * GC + g) * 64 + lane];
-                    X.aq[g] = aq[(wv * GC + g) * 64 + lane];
-                }
-            const int L = min(C, T - c * C);
+                X.tm[g] = buf_frag(rr, lane16, otm + g * 1024);
+            const auto vr = row_rsrc(gv, c);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = wv * 16 + (lane >> 4) * 4 + r;
-                const long row = ((long)b * T + c * C + min(t, L - 1)) * H + h;
+            for (int nj = 0; nj < NTJ; ++nj)
 #pragma unroll
-                for (int nj = 0; nj < NTJ; ++nj)
-                    X.v[nj][r] = gv[row * DV + v0 + nj * 16 + (lane & 15)];
-            }
+                for (int r = 0; r < 4; ++r)
+                    X.v[nj][r] = buf_elem<E>(vr, vofs[nj][r]);
+        }
+    };
+    auto load_late = [&](Late &Y, int c) {
+        const auto rr = rec_rsrc(c);
+        if (tok_wave) {
+            const int oaq = (int)LW.off_aqk + wv * GC * 1024;
+#pragma unroll
+            for (int g = 0; g < GC; ++g)
+                Y.aq[g] = buf_frag(rr, lane16, oaq + g * 1024);
         }
 #pragma unroll
         for (int n = 0; n < NIB; ++n) {
             const int ib = wv + 4 * n;
+            const int owt = (int)LW.off_wdt + ib * GC * 1024;
 #pragma unroll
             for (int g = 0; g < GC; ++g)
-                X.wt[n][g] = wt[(ib * GC + g) * 64 + lane];
+                Y.wt[n][g] = buf_frag(rr, lane16, owt + g * 1024);
             if (DECAY)
-                X.gc[n] = *reinterpret_cast<const float4 *>(gc + ib * 16 + (lane >> 4) * 4);
+                Y.gc[n] = buf_frag(rr, gc_lane, (int)LW.off_gc + ib * 64);
         }
     };
 
     auto compute = [&](const Chunk &X, int c) {
-        const int c0 = c * C, L = min(C, T - c0);
+        Late Y;
+        load_late(Y, c);
         f32x4 accq[NTJ];
         // U = V - K~ S and the first half of O = Q~ S
         if (tok_wave) {
@@ -171,10 +230,8 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
                 }
                 float u[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tt = wv * 16 + (lane >> 4) * 4 + r;
-                    u[r] = (tt < L ? to_f32(X.v[nj][r]) : 0.f) - accu[r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    u[r] = to_f32(X.v[nj][r]) - accu[r];
                 lds_stn<4>(UT + (nj * 16 + (lane & 15)) * PC + wv * 16 + (lane >> 4) * 4, u);
             }
         }
@@ -195,35 +252,33 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
         __syncthreads();
         // O = Q~ S + A_qk E;  S <- diag(gamma_C) S + W~^T E
         if (tok_wave) {
+            const auto orr = row_rsrc(go, c);
 #pragma unroll
             for (int nj = 0; nj < NTJ; ++nj) {
 #pragma unroll
                 for (int g = 0; g < GC; ++g)
                     if (g * KG < (wv + 1) * 16)
-                        FragMma<E>::mma(accq[nj], X.aq[g], ET + nj * 16 * PC, PC, g * KG, lane);
-                const int j = v0 + nj * 16 + (lane & 15);
+                        FragMma<E>::mma(accq[nj], Y.aq[g], ET + nj * 16 * PC, PC, g * KG, lane);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = wv * 16 + (lane >> 4) * 4 + r;
-                    if (t < L)
-                        go[(((long)b * T + c0 + t) * H + h) * DV + j] = from_f32<E>(accq[nj][r]);
-                }
+                for (int r = 0; r < 4; ++r)
+                    buf_store<E>(orr, vofs[nj][r], from_f32<E>(accq[nj][r]));
             }
         }
 #pragma unroll
         for (int n = 0; n < NIB; ++n) {
             const int i0 = (wv + 4 * n) * 16 + (lane >> 4) * 4;
+            const float4 g4 = __builtin_bit_cast(float4, Y.gc[n]);
 #pragma unroll
             for (int nj = 0; nj < NTJ; ++nj) {
                 if (DECAY) {
-                    sacc[n][nj][0] *= X.gc[n].x;
-                    sacc[n][nj][1] *= X.gc[n].y;
-                    sacc[n][nj][2] *= X.gc[n].z;
-                    sacc[n][nj][3] *= X.gc[n].w;
+                    sacc[n][nj][0] *= g4.x;
+                    sacc[n][nj][1] *= g4.y;
+                    sacc[n][nj][2] *= g4.z;
+                    sacc[n][nj][3] *= g4.w;
                 }
 #pragma unroll
                 for (int g = 0; g < GC; ++g)
-                    FragMma<E>::mma(sacc[n][nj], X.wt[n][g], ET + nj * 16 * PC, PC, g * KG, lane);
+                    FragMma<E>::mma(sacc[n][nj], Y.wt[n][g], ET + nj * 16 * PC, PC, g * KG, lane);
                 float s4[4] = {sacc[n][nj][0], sacc[n][nj][1], sacc[n][nj][2], sacc[n][nj][3]};
                 lds_stn<4>(ST + (nj * 16 + (lane & 15)) * PK + i0, s4);
             }
@@ -231,19 +286,19 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
         __syncthreads();
     };
 
+    // Software pipeline: chunk c+1's operands load while chunk c computes
+    // (the last chunk re-loads itself rather than branching around a load).
     __syncthreads();
     Chunk A, B;
     if (NC > 0)
         load(A, 0);
     for (int c = 0; c < NC; c += 2) {
-        if (c + 1 < NC)
-            load(B, c + 1);
+        load(B, min(c + 1, NC - 1));
         compute(A, c);
-        if (c + 1 < NC) {
-            if (c + 2 < NC)
-                load(A, c + 2);
-            compute(B, c + 1);
-        }
+        if (c + 1 >= NC)
+            break;
+        load(A, min(c + 2, NC - 1));
+        compute(B, c + 1);
     }
 
 #pragma unroll
@@ -266,10 +321,34 @@ static hipError_t launch_state_one(const PrefillParams &P, hipStream_t st) {
     return hipGetLastError();
 }
 
+#ifndef KDN_STATE_NV
+#define KDN_STATE_NV 0
+#endif
+
+// Columns of S per workgroup.  Every value block of a head reads the same
+// per-chunk operands, so wider blocks cut that traffic; narrower ones give
+// more workgroups to fill the CUs.
+static int state_value_block(const PrefillParams &P) {
+    if (KDN_STATE_NV)
+        return KDN_STATE_NV;
+    return 16;
+}
+
+template <typename E, bool DECAY, int DK, int C>
+static hipError_t launch_state_nv(const PrefillParams &P, hipStream_t st) {
+    const int nv = state_value_block(P);
+    if (nv == 16) return launch_state_one<E, DECAY, DK, 16, C>(P, st);
+    if constexpr (sizeof(E) == 2) {
+        if (nv == 32 && P.dv % 32 == 0) return launch_state_one<E, DECAY, DK, 32, C>(P, st);
+        if (nv == 64 && P.dv % 64 == 0) return launch_state_one<E, DECAY, DK, 64, C>(P, st);
+    }
+    return launch_state_one<E, DECAY, DK, 16, C>(P, st);
+}
+
 template <typename E, bool DECAY, int DK>
 static hipError_t launch_state_c(const PrefillParams &P, hipStream_t st) {
-    if (P.chunk == 64) return launch_state_one<E, DECAY, DK, 16, 64>(P, st);
-    if (P.chunk == 32) return launch_state_one<E, DECAY, DK, 16, 32>(P, st);
+    if (P.chunk == 64) return launch_state_nv<E, DECAY, DK, 64>(P, st);
+    if (P.chunk == 32) return launch_state_nv<E, DECAY, DK, 32>(P, st);
     return hipErrorInvalidValue;
 }
 
