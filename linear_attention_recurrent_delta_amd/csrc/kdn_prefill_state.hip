@@ -81,24 +81,34 @@ template <> __device__ __forceinline__ void buf_store<float>(__amdgpu_buffer_rsr
 }
 
 template <typename E, bool DECAY, int DK, int NV, int C>
-__global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
+__global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
     constexpr int KG = FragMma<E>::KG;
     constexpr int NB = C / 16;          // token blocks of a chunk
     constexpr int NTJ = NV / 16;        // column tiles of the S block
-    constexpr int NIB = DK / 64;        // key blocks per wave (DK/16 over 4 waves)
+    constexpr int NIBT = DK / 16;       // key blocks of S
+    constexpr int NSTT = NIBT * NTJ;    // S tiles
+    constexpr int NSW = (NSTT + 7) / 8; // S tiles per wave (max)
     constexpr int GK = DK / KG;         // fragment groups over DK
     constexpr int GC = C / KG;          // fragment groups over C
     constexpr int PADE = 16 / (int)sizeof(E);
     constexpr int PK = DK + PADE, PC = C + PADE;
     static_assert(GK * KG == DK && GC * KG == C && NB <= 4, "tiling");
+    static_assert(8 % NIBT == 0 || NIBT % 8 == 0, "S tiles of a wave share one key block");
 
     __shared__ __attribute__((aligned(16))) E ST[NV * PK];   // S^T block
     __shared__ __attribute__((aligned(16))) E UT[NV * PC];   // U^T
-    __shared__ __attribute__((aligned(16))) E ET[NV * PC];   // E^T
+    __shared__ __attribute__((aligned(16))) E ETB[2][NV * PC]; // E^T, by chunk parity
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool tok_wave = NB >= 4 || wv < NB;   // owns token block wv
+    // waves 0-3: the serial chain U -> E for token block wv;
+    // waves 4-7: the output path of token block wv - 4;
+    // all waves: S tiles tau = wv + 8k, (key block, column tile) =
+    //            (tau % NIBT, tau / NIBT).
+    const bool chain = wv < NB;
+    const bool outw = wv >= 4 && wv - 4 < NB;
+    const int m = chain ? wv : wv - 4;          // token block
+    const int ib = wv % NIBT;                   // key block of this wave's S tiles
 
     // Workgroup -> (batch*head, value block); the value blocks of one head
     // land on one XCD (dispatch is round-robin over the 8 XCDs), so they
@@ -118,34 +128,30 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
     const E *gv = static_cast<const E *>(P.v);
     E *go = static_cast<E *>(P.o);
 
-    // S block in accumulator layout: sacc[n][nj][r] =
-    //   S[(wv + 4n)*16 + (lane>>4)*4 + r][v0 + nj*16 + (lane&15)]
-    f32x4 sacc[NIB][NTJ];
+    // S tiles in accumulator layout: sacc[k][r] =
+    //   S[ib*16 + (lane>>4)*4 + r][v0 + nj_k*16 + (lane&15)],  nj_k = (wv + 8k) / NIBT
+    f32x4 sacc[NSW];
+    const int i0 = ib * 16 + (lane >> 4) * 4;
 #pragma unroll
-    for (int n = 0; n < NIB; ++n)
+    for (int k = 0; k < NSW; ++k) {
+        const int tau = wv + 8 * k;
+        if (tau >= NSTT) continue;
+        const int j = (tau / NIBT) * 16 + (lane & 15);
+        float s4[4];
 #pragma unroll
-        for (int nj = 0; nj < NTJ; ++nj) {
-            const int i0 = (wv + 4 * n) * 16 + (lane >> 4) * 4;
-            const int j = nj * 16 + (lane & 15);
-            float s4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sacc[n][nj][r] = P.S0 ? P.S0[((long)bh * DK + i0 + r) * DV + v0 + j] : 0.f;
-                s4[r] = sacc[n][nj][r];
-            }
-            lds_stn<4>(ST + j * PK + i0, s4);
+        for (int r = 0; r < 4; ++r) {
+            sacc[k][r] = P.S0 ? P.S0[((long)bh * DK + i0 + r) * DV + v0 + j] : 0.f;
+            s4[r] = sacc[k][r];
         }
+        lds_stn<4>(ST + j * PK + i0, s4);
+    }
 
-    // Operands of the first two phases are loaded one chunk ahead; those of
-    // the last phase (A_qk, W~^T, gamma_C) at the start of their own chunk,
-    // which keeps the register footprint at two workgroups per CU.
+    // One chunk's operands for this wave: the token-block fragments (K~ and T
+    // for a chain wave, Q~ and A_qk for an output wave), the W~^T key block
+    // and gamma_C of its S tiles, and (chain waves) the v tile.
     struct Chunk {
-        Frag kd[GK], qd[GK], tm[GC];
+        Frag kq[GK], ta[GC], wt[GC], gc;
         E v[NTJ][4];
-    };
-    struct Late {
-        Frag aq[GC], wt[NIB][GC];
-        Frag gc[NIB];
     };
     // Memory access: buffer instructions with a wave-uniform descriptor per
     // chunk (scalar registers) and per-lane byte offsets fixed for the whole
@@ -160,9 +166,13 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
     for (int nj = 0; nj < NTJ; ++nj)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            vofs[nj][r] = (unsigned)(((wv * 16 + (lane >> 4) * 4 + r) * hdv +
+            vofs[nj][r] = (unsigned)(((m * 16 + (lane >> 4) * 4 + r) * hdv +
                                       (lane & 15) + nj * 16) * (long)sizeof(E));
     const unsigned gc_lane = (unsigned)(lane >> 4) * 16u;
+    const int okq = (int)(chain ? LW.off_kd : LW.off_qd) + m * GK * 1024;
+    const int ota = (int)(chain ? LW.off_tm : LW.off_aqk) + m * GC * 1024;
+    const int owt = (int)LW.off_wdt + ib * GC * 1024;
+    const int ogc = (int)LW.off_gc + ib * 64;
     auto rec_rsrc = [&](int c) { return buf_rsrc(ws + (long)c * LW.rec, (unsigned)LW.rec); };
     // v / o rows of chunk c: [c*C, c*C + L) in range
     auto row_rsrc = [&](const E *base, int c) {
@@ -172,19 +182,23 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
     };
 
     auto load = [&](Chunk &X, int c) {
-        if (tok_wave) {
-            const auto rr = rec_rsrc(c);
-            const int okd = (int)LW.off_kd + wv * GK * 1024;
-            const int oqd = (int)LW.off_qd + wv * GK * 1024;
-            const int otm = (int)LW.off_tm + wv * GC * 1024;
+        const auto rr = rec_rsrc(c);
+        if (chain || outw) {
 #pragma unroll
-            for (int g = 0; g < GK; ++g) {
-                X.kd[g] = buf_frag(rr, lane16, okd + g * 1024);
-                X.qd[g] = buf_frag(rr, lane16, oqd + g * 1024);
-            }
+            for (int g = 0; g < GK; ++g)
+                X.kq[g] = buf_frag(rr, lane16, okq + g * 1024);
 #pragma unroll
             for (int g = 0; g < GC; ++g)
-                X.tm[g] = buf_frag(rr, lane16, otm + g * 1024);
+                X.ta[g] = buf_frag(rr, lane16, ota + g * 1024);
+        }
+        if (wv < NSTT) {
+#pragma unroll
+            for (int g = 0; g < GC; ++g)
+                X.wt[g] = buf_frag(rr, lane16, owt + g * 1024);
+            if (DECAY)
+                X.gc = buf_frag(rr, gc_lane, ogc);
+        }
+        if (chain) {
             const auto vr = row_rsrc(gv, c);
 #pragma unroll
             for (int nj = 0; nj < NTJ; ++nj)
@@ -193,95 +207,103 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
                     X.v[nj][r] = buf_elem<E>(vr, vofs[nj][r]);
         }
     };
-    auto load_late = [&](Late &Y, int c) {
-        const auto rr = rec_rsrc(c);
-        if (tok_wave) {
-            const int oaq = (int)LW.off_aqk + wv * GC * 1024;
+
+    // Output waves: Q~ S of chunk c in phase 1, finished in phase 2 of chunk
+    // c+1 with A_qk E (E^T of chunk c is kept in the other E^T buffer).
+    f32x4 accq[NTJ], accn[NTJ];
+    Frag aq_prev[GC];
+#pragma unroll
+    for (int nj = 0; nj < NTJ; ++nj)
+        accq[nj] = accn[nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < GC; ++g)
+        aq_prev[g] = Frag{0u, 0u, 0u, 0u};
+    // c = -1 (before the first chunk) stores through an empty descriptor:
+    // every store is dropped, and no branch guards it.
+    auto finish_output = [&](int c) {
+        const auto orr = c >= 0 ? row_rsrc(go, c) : buf_rsrc(go, 0u);
+        const E *ET = ETB[c & 1];
+#pragma unroll
+        for (int nj = 0; nj < NTJ; ++nj) {
 #pragma unroll
             for (int g = 0; g < GC; ++g)
-                Y.aq[g] = buf_frag(rr, lane16, oaq + g * 1024);
-        }
+                if (g * KG < (m + 1) * 16)
+                    FragMma<E>::mma(accq[nj], aq_prev[g], ET + nj * 16 * PC, PC, g * KG, lane);
 #pragma unroll
-        for (int n = 0; n < NIB; ++n) {
-            const int ib = wv + 4 * n;
-            const int owt = (int)LW.off_wdt + ib * GC * 1024;
-#pragma unroll
-            for (int g = 0; g < GC; ++g)
-                Y.wt[n][g] = buf_frag(rr, lane16, owt + g * 1024);
-            if (DECAY)
-                Y.gc[n] = buf_frag(rr, gc_lane, (int)LW.off_gc + ib * 64);
+            for (int r = 0; r < 4; ++r)
+                buf_store<E>(orr, vofs[nj][r], from_f32<E>(accq[nj][r]));
         }
     };
 
     auto compute = [&](const Chunk &X, int c) {
-        Late Y;
-        load_late(Y, c);
-        f32x4 accq[NTJ];
-        // U = V - K~ S and the first half of O = Q~ S
-        if (tok_wave) {
+        // phase 1: chain waves U = V - K~ S; output waves finish chunk c-1
+        // and start Q~ S of chunk c
+        if (chain) {
 #pragma unroll
             for (int nj = 0; nj < NTJ; ++nj) {
                 f32x4 accu = {0.f, 0.f, 0.f, 0.f};
-                accq[nj] = accu;
 #pragma unroll
-                for (int g = 0; g < GK; ++g) {
-                    FragMma<E>::mma(accu, X.kd[g], ST + nj * 16 * PK, PK, g * KG, lane);
-                    FragMma<E>::mma(accq[nj], X.qd[g], ST + nj * 16 * PK, PK, g * KG, lane);
-                }
+                for (int g = 0; g < GK; ++g)
+                    FragMma<E>::mma(accu, X.kq[g], ST + nj * 16 * PK, PK, g * KG, lane);
                 float u[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     u[r] = to_f32(X.v[nj][r]) - accu[r];
-                lds_stn<4>(UT + (nj * 16 + (lane & 15)) * PC + wv * 16 + (lane >> 4) * 4, u);
+                lds_stn<4>(UT + (nj * 16 + (lane & 15)) * PC + m * 16 + (lane >> 4) * 4, u);
+            }
+        } else if (outw) {
+#pragma unroll
+            for (int nj = 0; nj < NTJ; ++nj) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int g = 0; g < GK; ++g)
+                    FragMma<E>::mma(a, X.kq[g], ST + nj * 16 * PK, PK, g * KG, lane);
+                accn[nj] = a;
             }
         }
         __syncthreads();
-        // E = T U
-        if (tok_wave) {
+        E *ET = ETB[c & 1];
+        // phase 2: E = T U (chain waves); output waves finish chunk c-1
+        if (outw) {
+            finish_output(c - 1);
+#pragma unroll
+            for (int nj = 0; nj < NTJ; ++nj)
+                accq[nj] = accn[nj];
+#pragma unroll
+            for (int g = 0; g < GC; ++g)
+                aq_prev[g] = X.ta[g];
+        }
+        if (chain) {
 #pragma unroll
             for (int nj = 0; nj < NTJ; ++nj) {
                 f32x4 acce = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int g = 0; g < GC; ++g)
-                    if (g * KG < (wv + 1) * 16)
-                        FragMma<E>::mma(acce, X.tm[g], UT + nj * 16 * PC, PC, g * KG, lane);
+                    if (g * KG < (m + 1) * 16)
+                        FragMma<E>::mma(acce, X.ta[g], UT + nj * 16 * PC, PC, g * KG, lane);
                 float e[4] = {acce[0], acce[1], acce[2], acce[3]};
-                lds_stn<4>(ET + (nj * 16 + (lane & 15)) * PC + wv * 16 + (lane >> 4) * 4, e);
+                lds_stn<4>(ET + (nj * 16 + (lane & 15)) * PC + m * 16 + (lane >> 4) * 4, e);
             }
         }
         __syncthreads();
-        // O = Q~ S + A_qk E;  S <- diag(gamma_C) S + W~^T E
-        if (tok_wave) {
-            const auto orr = row_rsrc(go, c);
+        // phase 3: S <- diag(gamma_C) S + W~^T E (all waves)
+        const float4 g4 = __builtin_bit_cast(float4, X.gc);
 #pragma unroll
-            for (int nj = 0; nj < NTJ; ++nj) {
-#pragma unroll
-                for (int g = 0; g < GC; ++g)
-                    if (g * KG < (wv + 1) * 16)
-                        FragMma<E>::mma(accq[nj], Y.aq[g], ET + nj * 16 * PC, PC, g * KG, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    buf_store<E>(orr, vofs[nj][r], from_f32<E>(accq[nj][r]));
+        for (int k = 0; k < NSW; ++k) {
+            const int tau = wv + 8 * k;
+            if (NSTT % 8 != 0 && tau >= NSTT) continue;
+            const int nj = tau / NIBT;
+            if (DECAY) {
+                sacc[k][0] *= g4.x;
+                sacc[k][1] *= g4.y;
+                sacc[k][2] *= g4.z;
+                sacc[k][3] *= g4.w;
             }
-        }
 #pragma unroll
-        for (int n = 0; n < NIB; ++n) {
-            const int i0 = (wv + 4 * n) * 16 + (lane >> 4) * 4;
-            const float4 g4 = __builtin_bit_cast(float4, Y.gc[n]);
-#pragma unroll
-            for (int nj = 0; nj < NTJ; ++nj) {
-                if (DECAY) {
-                    sacc[n][nj][0] *= g4.x;
-                    sacc[n][nj][1] *= g4.y;
-                    sacc[n][nj][2] *= g4.z;
-                    sacc[n][nj][3] *= g4.w;
-                }
-#pragma unroll
-                for (int g = 0; g < GC; ++g)
-                    FragMma<E>::mma(sacc[n][nj], Y.wt[n][g], ET + nj * 16 * PC, PC, g * KG, lane);
-                float s4[4] = {sacc[n][nj][0], sacc[n][nj][1], sacc[n][nj][2], sacc[n][nj][3]};
-                lds_stn<4>(ST + (nj * 16 + (lane & 15)) * PK + i0, s4);
-            }
+            for (int g = 0; g < GC; ++g)
+                FragMma<E>::mma(sacc[k], X.wt[g], ET + nj * 16 * PC, PC, g * KG, lane);
+            float s4[4] = {sacc[k][0], sacc[k][1], sacc[k][2], sacc[k][3]};
+            lds_stn<4>(ST + (nj * 16 + (lane & 15)) * PK + i0, s4);
         }
         __syncthreads();
     };
@@ -300,23 +322,24 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillParams P) {
         load(A, min(c + 2, NC - 1));
         compute(B, c + 1);
     }
+    if (outw && NC > 0)
+        finish_output(NC - 1);
 
 #pragma unroll
-    for (int n = 0; n < NIB; ++n)
+    for (int k = 0; k < NSW; ++k) {
+        const int tau = wv + 8 * k;
+        if (tau >= NSTT) continue;
+        const int j = (tau / NIBT) * 16 + (lane & 15);
 #pragma unroll
-        for (int nj = 0; nj < NTJ; ++nj) {
-            const int i0 = (wv + 4 * n) * 16 + (lane >> 4) * 4;
-            const int j = nj * 16 + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                P.S_out[((long)bh * DK + i0 + r) * DV + v0 + j] = sacc[n][nj][r];
-        }
+        for (int r = 0; r < 4; ++r)
+            P.S_out[((long)bh * DK + i0 + r) * DV + v0 + j] = sacc[k][r];
+    }
 }
 
 template <typename E, bool DECAY, int DK, int NV, int C>
 static hipError_t launch_state_one(const PrefillParams &P, hipStream_t st) {
     const long heads = (long)P.B * P.H;
-    const dim3 grid((unsigned)(heads * (P.dv / NV))), block(256);
+    const dim3 grid((unsigned)(heads * (P.dv / NV))), block(512);
     hipLaunchKernelGGL((prefill_state_kernel<E, DECAY, DK, NV, C>), grid, block, 0, st, P);
     return hipGetLastError();
 }
@@ -331,7 +354,12 @@ static hipError_t launch_state_one(const PrefillParams &P, hipStream_t st) {
 static int state_value_block(const PrefillParams &P) {
     if (KDN_STATE_NV)
         return KDN_STATE_NV;
-    return 16;
+    const long heads = (long)P.B * P.H;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    return (P.bf16 && P.dv % 32 == 0 && heads * (P.dv / 32) >= cus) ? 32 : 16;
 }
 
 template <typename E, bool DECAY, int DK, int C>
@@ -340,7 +368,6 @@ static hipError_t launch_state_nv(const PrefillParams &P, hipStream_t st) {
     if (nv == 16) return launch_state_one<E, DECAY, DK, 16, C>(P, st);
     if constexpr (sizeof(E) == 2) {
         if (nv == 32 && P.dv % 32 == 0) return launch_state_one<E, DECAY, DK, 32, C>(P, st);
-        if (nv == 64 && P.dv % 64 == 0) return launch_state_one<E, DECAY, DK, 64, C>(P, st);
     }
     return launch_state_one<E, DECAY, DK, 16, C>(P, st);
 }

@@ -24,13 +24,18 @@
 
 namespace kdn {
 
+// Channels per thread: one 16-byte load of k, alpha and xi per token.
+template <typename E> struct VarVec { static constexpr int N = 16 / (int)sizeof(E); };
+
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void variance_chunk_kernel(PrefillParams P) {
-    constexpr int UPW = 256 / DK;                      // chunks per workgroup
+    constexpr int N = VarVec<E>::N;                    // channels per thread
+    constexpr int TPU = DK / N;                        // threads per (head, chunk)
+    constexpr int UPW = 256 / TPU;                     // units per workgroup
     const int C = P.chunk, T = P.T, H = P.H;
     const int NC = (T + C - 1) / C;
-    const long unit = (long)blockIdx.x * UPW + threadIdx.x / DK;
-    const int i = threadIdx.x % DK;
+    const long unit = (long)blockIdx.x * UPW + threadIdx.x / TPU;
+    const int i0 = (threadIdx.x % TPU) * N;
     if (unit >= (long)P.B * H * NC)
         return;
     const int bh = (int)(unit / NC), c = (int)(unit % NC);
@@ -42,33 +47,46 @@ __global__ __launch_bounds__(256) void variance_chunk_kernel(PrefillParams P) {
     const E *gr = static_cast<const E *>(P.r);
     const float mu = P.mu;
 
-    float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;   // maps p(chunk start) -> p
-#pragma unroll 4
+    float m00[N], m01[N], m10[N], m11[N];              // maps p(chunk start) -> p
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        m00[e] = 1.f; m01[e] = 0.f; m10[e] = 0.f; m11[e] = 1.f;
+    }
+    const long row0 = ((long)b * T + c0) * H + h;
+#pragma unroll 2
     for (int t = 0; t < L; ++t) {
-        const long row = ((long)b * T + c0 + t) * H + h;
-        const float k = to_f32(gk[row * DK + i]);
-        const float a = to_f32(ga[row * DK + i]);
-        const float x = to_f32(gx[row * DK + i]);
+        const long row = row0 + (long)t * H;
+        float k[N], a[N], x[N];
+        load16(gk + row * DK + i0, k);
+        load16(ga + row * DK + i0, a);
+        load16(gx + row * DK + i0, x);
         const float r = to_f32(gr[row]);
-        const float a2 = a * a, mk2 = mu * k * k;
-        float n00 = a2, n01 = x, n10 = 0.f, n11 = 1.f;
-        if (r > 0.f) {
-            const float cc = mk2 / r;
-            n10 = cc * a2;
-            n11 = fmaf(cc, x, 1.f);
-        } else if (mk2 != 0.f) {
-            n00 = 0.f;
-            n01 = 0.f;
-        }
-        const float p00 = n00 * m00 + n01 * m10, p01 = n00 * m01 + n01 * m11;
-        const float p10 = n10 * m00 + n11 * m10, p11 = n10 * m01 + n11 * m11;
-        m00 = p00; m01 = p01; m10 = p10; m11 = p11;
-        if ((t & 3) == 3) {
-            const float s = fast_rcp(fmaxf(fmaxf(m00, m01), fmaxf(m10, m11)));
-            m00 *= s; m01 *= s; m10 *= s; m11 *= s;
+        const float rinv = r > 0.f ? 1.f / r : 0.f;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            const float a2 = a[e] * a[e], mk2 = mu * k[e] * k[e];
+            float n00 = a2, n01 = x[e], n10 = 0.f, n11 = 1.f;
+            if (r > 0.f) {
+                const float cc = mk2 * rinv;
+                n10 = cc * a2;
+                n11 = fmaf(cc, x[e], 1.f);
+            } else if (mk2 != 0.f) {
+                n00 = 0.f;
+                n01 = 0.f;
+            }
+            const float p00 = n00 * m00[e] + n01 * m10[e], p01 = n00 * m01[e] + n01 * m11[e];
+            const float p10 = n10 * m00[e] + n11 * m10[e], p11 = n10 * m01[e] + n11 * m11[e];
+            m00[e] = p00; m01[e] = p01; m10[e] = p10; m11[e] = p11;
+            if ((t & 3) == 3) {
+                const float sc = fast_rcp(fmaxf(fmaxf(m00[e], m01[e]), fmaxf(m10[e], m11[e])));
+                m00[e] *= sc; m01[e] *= sc; m10[e] *= sc; m11[e] *= sc;
+            }
         }
     }
-    reinterpret_cast<float4 *>(P.ws_mob)[unit * DK + i] = make_float4(m00, m01, m10, m11);
+    float4 *dst = reinterpret_cast<float4 *>(P.ws_mob) + unit * DK + i0;
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        dst[e] = make_float4(m00[e], m01[e], m10[e], m11[e]);
 }
 
 template <int DK>
@@ -107,7 +125,7 @@ static hipError_t launch_variance_dk(const PrefillParams &P, hipStream_t st) {
     const long bh = (long)P.B * P.H;
     const long nc = (P.T + P.chunk - 1) / P.chunk;
     if (nc > 0) {
-        constexpr int UPW = 256 / DK;
+        constexpr int UPW = 256 / (DK / VarVec<E>::N);
         const dim3 grid((unsigned)((bh * nc + UPW - 1) / UPW)), block(256);
         hipLaunchKernelGGL((variance_chunk_kernel<E, DK>), grid, block, 0, st, P);
         if (hipError_t e = hipGetLastError())
