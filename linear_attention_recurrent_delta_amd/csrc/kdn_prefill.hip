@@ -104,8 +104,9 @@ struct PrefillLayout {
     static constexpr int OFF_TD = T_IN_WP ? OFF_WP : END_TM;
     static constexpr int OFF_SM = T_IN_WP ? END_TM : END_TM + SZ_T;
     static constexpr int SM_BETA = 0, SM_R = C, SM_ALPH = 2 * C, SM_INVS = 3 * C,
-                         SM_GC = 4 * C, SM_FLAG = 4 * C + DK;
-    static constexpr int SZ_SM = (4 * C + DK + 4) * 4;
+                         SM_GC = 4 * C, SM_FLAG = 4 * C + DK, SM_WSC = 4 * C + DK + 4,
+                         SM_ZR = 5 * C + DK + 4;
+    static constexpr int SZ_SM = (6 * C + DK + 4) * 4;
     static constexpr int TOTAL = OFF_SM + SZ_SM;
 
     static_assert(TOTAL <= 163840, "prefill LDS budget");
@@ -246,6 +247,31 @@ __device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, i
     }
 }
 
+// As store_frag, each element computed by f(row, k) (a float).
+template <typename E, int R, int K, int NT, typename F>
+__device__ __forceinline__ void store_frag_fn(char *dst, int tid, F f) {
+    constexpr int EPU = 16 / (int)sizeof(E);
+    constexpr int KG = sizeof(E) == 2 ? 32 : 16;
+    constexpr int NU = R * K / EPU;
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int u0 = 0; u0 < NU; u0 += NT) {
+        const int u = u0 + tid;
+        if (NU % NT == 0 || u < NU) {
+            const int l = u & 63, grp = u >> 6;
+            const int m = grp / (K / KG), g = grp % (K / KG);
+            const int row = m * 16 + (l & 15);
+            E v[EPU];
+#pragma unroll
+            for (int e = 0; e < EPU; ++e) {
+                const int k = sizeof(E) == 2 ? g * 32 + (l >> 4) * 8 + e : g * 16 + e * 4 + (l >> 4);
+                v[e] = from_f32<E>(f(row, k));
+            }
+            d[u] = *reinterpret_cast<const uint4 *>(v);
+        }
+    }
+}
+
 // PREP = false: the single-pass kernel, one workgroup per (batch*head, value
 // block) walking all chunks.  PREP = true: the prep kernel of the two-pass
 // schedule, one workgroup per (batch*head, chunk): steps 1-4 only, results to
@@ -258,6 +284,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                   PP = LY::PP, NB = LY::NB;
     constexpr int NO = LY::NO, NG = LY::NG, TPG = LY::TPG;
     constexpr bool DECAY = LY::DECAY, VDECAY = LY::VDECAY, KDN = LY::KDN;
+    // Prep kernel, scalar decay: no per-channel scan; the decay enters as
+    // ratios gamma_t / gamma_s in log2 form (section 2s below).
+    constexpr bool SPREP = PREP && VAR == GATED_DELTANET;
     constexpr int NTJ = NV / 16;                // value tiles
     constexpr int NTI = DK / 16;                // key tiles
     constexpr int NST = NTI * NTJ;              // S tiles
@@ -287,6 +316,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
           *s_alph = sm + LY::SM_ALPH, *s_invs = sm + LY::SM_INVS,
           *s_gc = sm + LY::SM_GC;
     int *s_flag = reinterpret_cast<int *>(sm + LY::SM_FLAG);
+    float *s_gl = s_r;                 // SPREP: log2 gamma over nonzero decays
+    float *s_gt = s_invs;              // SPREP: gamma_t
+    float *s_wsc = sm + LY::SM_WSC;    // SPREP: beta_s gamma_C / gamma_s
+    int *s_zr = reinterpret_cast<int *>(sm + LY::SM_ZR);   // SPREP: last zero decay <= t
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -490,6 +523,39 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                 s_invs[t] = (s != 0.f) ? 1.f / s : 0.f;
             }
         }
+        bool fb = false;
+        if constexpr (SPREP) {
+            // 2s. scalar decay: one wave scans log2(alpha_t) over the chunk
+            // (zeros tracked separately: the ratio gamma_t / gamma_s is 0 when a
+            // zero decay lies in (s, t], else 2^(G_t - G_s)).
+            if (wv == 0) {
+                const int t = lane;
+                const float a = t < C ? s_alph[t] : 1.f;
+                float gl = a > 0.f ? __builtin_amdgcn_logf(a) : 0.f;
+                int zr = a > 0.f ? -1 : t;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float g2 = __shfl_up(gl, off, WAVE);
+                    const int z2 = __shfl_up(zr, off, WAVE);
+                    if (lane >= off) {
+                        gl += g2;
+                        zr = max(zr, z2);
+                    }
+                }
+                const float glc = __shfl(gl, C - 1, WAVE);
+                const int zrc = __shfl(zr, C - 1, WAVE);
+                if (t < C) {
+                    s_gl[t] = gl;
+                    s_zr[t] = zr;
+                    s_gt[t] = zr >= 0 ? 0.f : __builtin_amdgcn_exp2f(gl);
+                    s_wsc[t] = zrc > t ? 0.f : s_beta[t] * __builtin_amdgcn_exp2f(glc - gl);
+                }
+                const float gc = zrc >= 0 ? 0.f : __builtin_amdgcn_exp2f(glc);
+                for (int i = lane; i < DK; i += WAVE)
+                    s_gc[i] = gc;
+            }
+            __syncthreads();
+        } else {
         // 2a. group products of the decays (scan threads)
         if constexpr (DECAY) {
             if (tid < LY::NTS) {
@@ -538,7 +604,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         // 2c. scaled operands, every thread: channels j0..j0+7, tokens
         //     u0..u0+TPG2-1 (tokens vary fastest across lanes: 16 B row
         //     accesses and the transposed W~ stores stay conflict-free)
-        const bool fb = DECAY && (*s_flag != 0);
+        fb = DECAY && (*s_flag != 0);
         if (tid < NTO) {
             const int g = gh / H2;
             float pre[8], suf[8], a8[TPG][8];
@@ -630,9 +696,43 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         }
         __syncthreads();
 
+        }
         // ---------------- 3. interaction matrices ----------------
         constexpr int NL = NB * (NB + 1) / 2;
-        if (!fb) {
+        if constexpr (SPREP) {
+            // A_kk = (K K^T) . gamma_t / gamma_s . beta_s (s < t), A_qk likewise
+            // with Q (s <= t): raw operands on MFMA, decay in the epilogue
+            for (int x = wv; x < 2 * NL; x += NW) {
+                const int which = x >= NL;
+                int idx = x - which * NL, mi = 0;
+                while (idx > mi) { idx -= mi + 1; ++mi; }
+                const int ni = idx;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                mma_tile_k<E, DK>(acc, (which ? Qt : Kt) + mi * 16 * PK, PK,
+                                  Kt + ni * 16 * PK, PK, lane);
+                const int s = ni * 16 + (lane & 15);
+                const float gls = s_gl[s], bs = s_beta[s];
+                const int t0r = mi * 16 + (lane >> 4) * 4;
+                float val[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {         // branch-free epilogue
+                    const int t = t0r + r;
+                    const int zt = s_zr[t];
+                    const float ex = __builtin_amdgcn_exp2f(fminf(s_gl[t] - gls, 0.f));
+                    const bool keep = (which ? s <= t : s < t) & (zt <= s);
+                    val[r] = keep ? acc[r] * ex * bs : 0.f;
+                }
+                if (which) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        AQ[(t0r + r) * PC + s] = from_f32<E>(val[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Akk[(t0r + r) * PA + s] = val[r];
+                }
+            }
+        } else if (!fb) {
             for (int x = wv; x < 2 * NL; x += NW) {
                 const int which = x >= NL;
                 int idx = x - which * NL, mi = 0;
@@ -783,9 +883,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             // ---------------- record of this chunk ----------------
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
-            store_frag<E, C, DK, NT>(rec + LW.off_kd, Kt, PK, tid);
-            store_frag<E, C, DK, NT>(rec + LW.off_qd, Qt, PK, tid);
-            store_frag<E, DK, C, NT>(rec + LW.off_wdt, WtT, PC, tid);
+            if constexpr (SPREP) {
+                store_frag_fn<E, C, DK, NT>(rec + LW.off_kd, tid, [&](int t, int i) {
+                    return ld(Kt + t * PK + i) * s_gt[t]; });
+                store_frag_fn<E, C, DK, NT>(rec + LW.off_qd, tid, [&](int t, int i) {
+                    return ld(Qt + t * PK + i) * s_gt[t]; });
+                store_frag_fn<E, DK, C, NT>(rec + LW.off_wdt, tid, [&](int i, int t) {
+                    return ld(Kt + t * PK + i) * s_wsc[t]; });
+            } else {
+                store_frag<E, C, DK, NT>(rec + LW.off_kd, Kt, PK, tid);
+                store_frag<E, C, DK, NT>(rec + LW.off_qd, Qt, PK, tid);
+                store_frag<E, DK, C, NT>(rec + LW.off_wdt, WtT, PC, tid);
+            }
             store_frag<E, C, C, NT>(rec + LW.off_aqk, AQ, PC, tid);
             store_frag<E, C, C, NT>(rec + LW.off_tm, Tm, PC, tid);
             if (DECAY && tid < DK)
