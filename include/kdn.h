@@ -44,7 +44,8 @@
  *     next synchronisation.  Non-finite inputs are not checked; they propagate.
  *   - Argument contracts that are not checked on the device: alpha in [0, 1],
  *     proc_noise >= 0, obs_noise >= 0.
- *   - Thread-safe: no global mutable state.
+ *   - Thread-safe.  The only global state is a per-device cache of the
+ *     device's compute-unit count, filled on first use.
  */
 #ifndef KDN_H
 #define KDN_H

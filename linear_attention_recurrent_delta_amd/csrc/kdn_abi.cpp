@@ -5,9 +5,28 @@
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
 
+#include <atomic>
 #include <stdint.h>
 
 namespace {
+
+// Compute units of the current device, queried once per device (the value
+// never changes; concurrent first calls store the same number).
+int device_cus() {
+    constexpr int MAXDEV = 64;
+    static std::atomic<int> cache[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV)
+        return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -186,6 +205,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.xi = proc_noise; P.r = obs_noise;
     P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
     P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr;
+    P.cus = device_cus();
     if (n_ws > 0) {
         P.ws = workspace;
         if (kdn) {

@@ -34,6 +34,7 @@ struct PrefillParams {
     void *ws;
     float *ws_mob;
     float *ws_p0;
+    int cus;           // compute units of the current device
 };
 
 hipError_t launch_decode(const DecodeParams &P, hipStream_t stream);

@@ -998,11 +998,7 @@ static hipError_t launch_prep_one(const PrefillParams &P, hipStream_t st) {
     const long units = (long)P.B * P.H * ((P.T + C - 1) / C);
     // persistent: one workgroup per CU (the LDS footprint allows one), each
     // walking every gridDim-th (batch*head, chunk) unit
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const long g = units < cus ? units : cus;
+    const long g = units < P.cus ? units : P.cus;
     const dim3 grid((unsigned)g), block(64 * NW);
     hipLaunchKernelGGL((prefill_kernel<E, VAR, DK, 16, C, NW, true>), grid, block, 0, st, P);
     return hipGetLastError();

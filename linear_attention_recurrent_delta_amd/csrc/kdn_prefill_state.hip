@@ -355,11 +355,7 @@ static int state_value_block(const PrefillParams &P) {
     if (KDN_STATE_NV)
         return KDN_STATE_NV;
     const long heads = (long)P.B * P.H;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    return (P.bf16 && P.dv % 32 == 0 && heads * (P.dv / 32) >= cus) ? 32 : 16;
+    return (P.bf16 && P.dv % 32 == 0 && heads * (P.dv / 32) >= P.cus) ? 32 : 16;
 }
 
 template <typename E, bool DECAY, int DK, int C>
