@@ -524,10 +524,29 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             }
         }
         bool fb = false;
+        // SPREP: raw A-matrix tiles of waves 1.. (tile x = wv-1 + k(NW-1)),
+        // computed while wave 0 scans the decays
+        constexpr int NL = NB * (NB + 1) / 2;
+        constexpr int SPT = SPREP ? (2 * NL + NW - 2) / (NW - 1) : 1;
+        f32x4 spacc[SPT];
         if constexpr (SPREP) {
             // 2s. scalar decay: one wave scans log2(alpha_t) over the chunk
             // (zeros tracked separately: the ratio gamma_t / gamma_s is 0 when a
-            // zero decay lies in (s, t], else 2^(G_t - G_s)).
+            // zero decay lies in (s, t], else 2^(G_t - G_s)).  The other waves
+            // meanwhile form K K^T and Q K^T on MFMA.
+            if (wv != 0) {
+#pragma unroll
+                for (int k = 0; k < SPT; ++k) {
+                    const int x = wv - 1 + k * (NW - 1);
+                    if (x >= 2 * NL) continue;
+                    const int which = x >= NL;
+                    int idx = x - which * NL, mi = 0;
+                    while (idx > mi) { idx -= mi + 1; ++mi; }
+                    spacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    mma_tile_k<E, DK>(spacc[k], (which ? Qt : Kt) + mi * 16 * PK, PK,
+                                      Kt + idx * 16 * PK, PK, lane);
+                }
+            }
             if (wv == 0) {
                 const int t = lane;
                 const float a = t < C ? s_alph[t] : 1.f;
@@ -698,18 +717,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
 
         }
         // ---------------- 3. interaction matrices ----------------
-        constexpr int NL = NB * (NB + 1) / 2;
         if constexpr (SPREP) {
             // A_kk = (K K^T) . gamma_t / gamma_s . beta_s (s < t), A_qk likewise
-            // with Q (s <= t): raw operands on MFMA, decay in the epilogue
-            for (int x = wv; x < 2 * NL; x += NW) {
+            // with Q (s <= t): raw products from phase 2s, decay applied here
+#pragma unroll
+            for (int k = 0; k < SPT; ++k) {
+                const int x = wv - 1 + k * (NW - 1);
+                if (wv == 0 || x >= 2 * NL) continue;
                 const int which = x >= NL;
                 int idx = x - which * NL, mi = 0;
                 while (idx > mi) { idx -= mi + 1; ++mi; }
                 const int ni = idx;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                mma_tile_k<E, DK>(acc, (which ? Qt : Kt) + mi * 16 * PK, PK,
-                                  Kt + ni * 16 * PK, PK, lane);
+                const f32x4 acc = spacc[k];
                 const int s = ni * 16 + (lane & 15);
                 const float gls = s_gl[s], bs = s_beta[s];
                 const int t0r = mi * 16 + (lane >> 4) * 4;
@@ -800,7 +819,25 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         // ---------------- 5. U = V - K~ S  ||  4a. T[I,I] ----------------
         constexpr int NTU = NB * NTJ;
         static_assert(NW >= 4 + NB, "waves 0-3 take U, waves 4.. the T blocks");
-        if (!PREP && wv < 4) {
+        if (PREP && wv < 4) {
+            // record parts that do not need T, written by waves 0-3 while
+            // waves 4.. invert the diagonal blocks
+            const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
+            char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
+            if constexpr (SPREP) {
+                store_frag_fn<E, C, DK, 256>(rec + LW.off_kd, tid, [&](int t, int i) {
+                    return ld(Kt + t * PK + i) * s_gt[t]; });
+                store_frag_fn<E, C, DK, 256>(rec + LW.off_qd, tid, [&](int t, int i) {
+                    return ld(Qt + t * PK + i) * s_gt[t]; });
+                store_frag_fn<E, DK, C, 256>(rec + LW.off_wdt, tid, [&](int i, int t) {
+                    return ld(Kt + t * PK + i) * s_wsc[t]; });
+            } else {
+                store_frag<E, C, DK, 256>(rec + LW.off_kd, Kt, PK, tid);
+                store_frag<E, C, DK, 256>(rec + LW.off_qd, Qt, PK, tid);
+                store_frag<E, DK, C, 256>(rec + LW.off_wdt, WtT, PC, tid);
+            }
+            store_frag<E, C, C, 256>(rec + LW.off_aqk, AQ, PC, tid);
+        } else if (!PREP && wv < 4) {
             for (int x = wv; x < NTU; x += 4) {
                 const int mi = x / NTJ, nj = x % NTJ;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -883,19 +920,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             // ---------------- record of this chunk ----------------
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
-            if constexpr (SPREP) {
-                store_frag_fn<E, C, DK, NT>(rec + LW.off_kd, tid, [&](int t, int i) {
-                    return ld(Kt + t * PK + i) * s_gt[t]; });
-                store_frag_fn<E, C, DK, NT>(rec + LW.off_qd, tid, [&](int t, int i) {
-                    return ld(Qt + t * PK + i) * s_gt[t]; });
-                store_frag_fn<E, DK, C, NT>(rec + LW.off_wdt, tid, [&](int i, int t) {
-                    return ld(Kt + t * PK + i) * s_wsc[t]; });
-            } else {
-                store_frag<E, C, DK, NT>(rec + LW.off_kd, Kt, PK, tid);
-                store_frag<E, C, DK, NT>(rec + LW.off_qd, Qt, PK, tid);
-                store_frag<E, DK, C, NT>(rec + LW.off_wdt, WtT, PC, tid);
-            }
-            store_frag<E, C, C, NT>(rec + LW.off_aqk, AQ, PC, tid);
             store_frag<E, C, C, NT>(rec + LW.off_tm, Tm, PC, tid);
             if (DECAY && tid < DK)
                 reinterpret_cast<float *>(rec + LW.off_gc)[tid] = s_gc[tid];
