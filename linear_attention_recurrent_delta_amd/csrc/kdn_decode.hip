@@ -25,9 +25,12 @@
 
 namespace kdn {
 
-template <typename TIn, int VAR, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
-    constexpr int NT = 256;
+#ifndef KDN_DECODE_NT
+#define KDN_DECODE_NT 256
+#endif
+
+template <typename TIn, int VAR, int DK, int DV, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
     constexpr int CG = DV / 4;        // float4 column groups
     constexpr int RG = NT / CG;       // row groups
     constexpr int RPT = DK / RG;      // rows per thread
@@ -41,14 +44,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     float *S = P.S + bh * (long)DK * DV;
     const int row0 = rg * RPT;
 
-    // Issue the state loads first; the per-head vector work below overlaps
-    // with them.
-    f32x4 s[RPT];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m)
-        s[m] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4 *>(S + (long)(row0 + m) * DV) + cg);
-
     __shared__ float sk[DK], sq[DK], sa[DK], sg[DK];
     __shared__ f32x4 red[RG][CG];
     __shared__ float part[NT / WAVE];
@@ -56,25 +51,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
     const TIn *q = static_cast<const TIn *>(P.q) + bh * DK;
     const TIn *k = static_cast<const TIn *>(P.k) + bh * DK;
 
-    float kk = 0.f, pm = 0.f, u = 0.f, pk2 = 0.f;
+    // The per-head vectors are requested first and the state after them:
+    // loads return in order, so the gain below is formed while the state is
+    // still streaming in.
+    float kk = 0.f, qq = 0.f, aa = 1.f, xi = 0.f, p0 = 0.f, bt = 0.f;
     if (tid < DK) {
         kk = to_f32(k[tid]);
-        const float qq = to_f32(q[tid]);
-        float aa = 1.f;
+        qq = to_f32(q[tid]);
         if (VAR == GATED_DELTANET)
             aa = to_f32(static_cast<const TIn *>(P.alpha)[bh]);
         else if (VAR == KDA || VAR == DIAG_KDN)
             aa = to_f32(static_cast<const TIn *>(P.alpha)[bh * DK + tid]);
+        if (VAR == DIAG_KDN) {
+            xi = to_f32(static_cast<const TIn *>(P.xi)[bh * DK + tid]);
+            p0 = P.p[bh * DK + tid];
+        } else {
+            bt = to_f32(static_cast<const TIn *>(P.beta)[bh]);
+        }
+    }
+    const float rr = VAR == DIAG_KDN ? to_f32(static_cast<const TIn *>(P.r)[bh]) : 0.f;
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4 *>(S + (long)(row0 + m) * DV) + cg);
+
+    float pm = 0.f, u = 0.f, pk2 = 0.f;
+    if (tid < DK) {
         sk[tid] = kk;
         sq[tid] = qq;
         sa[tid] = aa;
         if (VAR == DIAG_KDN) {
-            const float xi = to_f32(static_cast<const TIn *>(P.xi)[bh * DK + tid]);
-            pm = aa * aa * P.p[bh * DK + tid] + xi;     // predict
+            pm = aa * aa * p0 + xi;                     // predict
             u = pm * kk;
             pk2 = u * kk;
         } else {
-            sg[tid] = to_f32(static_cast<const TIn *>(P.beta)[bh]) * kk;
+            sg[tid] = bt * kk;
         }
     }
     if (VAR == DIAG_KDN) {
@@ -84,7 +96,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
             part[tid / WAVE] = ws;
         __syncthreads();
         if (tid < DK) {
-            const float r = to_f32(static_cast<const TIn *>(P.r)[bh]);
+            const float r = rr;
             float sum = r;
 #pragma unroll
             for (int w = 0; w < (DK + WAVE - 1) / WAVE; ++w)
@@ -156,11 +168,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams P) {
 
 template <typename TIn, int VAR>
 static hipError_t launch_decode_v(const DecodeParams &P, hipStream_t st) {
-    const dim3 grid((unsigned)((long)P.N * P.H)), block(256);
+    constexpr int NT = KDN_DECODE_NT;
+    const dim3 grid((unsigned)((long)P.N * P.H)), block(NT);
 #define KDN_DEC(DK_, DV_)                                                      \
     if (P.dk == DK_ && P.dv == DV_) {                                          \
-        hipLaunchKernelGGL((decode_kernel<TIn, VAR, DK_, DV_>), grid, block,   \
-                           0, st, P);                                          \
+        hipLaunchKernelGGL((decode_kernel<TIn, VAR, DK_, DV_, NT>), grid,      \
+                           block, 0, st, P);                                   \
         return hipGetLastError();                                              \
     }
     KDN_DEC(64, 64)
