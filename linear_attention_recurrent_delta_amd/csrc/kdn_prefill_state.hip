@@ -7,20 +7,29 @@
 // وابستگی علی": provisional errors resolved by the causal triangular solve):
 //   U = V - K~ S,   E = T U,   O = Q~ S + A_qk E,   S <- diag(gamma_C) S + W~^T E.
 //
-// One workgroup of four waves owns one (batch*head, NV-column block of S).
+// One workgroup of eight waves owns one (batch*head, NV-column block of S).
 // S stays in registers in MFMA accumulator layout for the whole sequence and
 // is mirrored in LDS (operand type, [col][row]) for the products that read
-// it.  Wave w owns token block w of the chunk (rows 16w..16w+15 of U, E, O)
-// and key blocks w, w+4 of S.  Every A operand (the prep kernel's matrices)
-// is loaded straight from global memory into registers in fragment order,
-// one chunk ahead, so the only LDS traffic is the S / U / E exchange between
-// the MFMA output and operand layouts.  Three barriers per chunk.
+// it.  Waves 0-3 carry the serial chain of token block w (U = V - K~ S, then
+// E = T U); waves 4-7 the output of token block w-4 (Q~ S while the chain
+// runs, A_qk E one chunk later from a second E^T buffer); every wave updates
+// its S tiles.  Every A operand (the prep kernel's matrices) is loaded
+// straight from global memory into registers in fragment order, one chunk
+// ahead, and the record two chunks ahead is prefetched into L2, so the only
+// LDS traffic is the S / U / E exchange between the MFMA output and operand
+// layouts.  Three barriers per chunk.
 #include "kdn_device.h"
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
 
 
 namespace kdn {
+
+// Distance in chunks from the chunk whose operands a wave loads to the chunk
+// it prefetches into L2 at the same time (0: no prefetch).
+#ifndef KDN_STATE_PFD
+#define KDN_STATE_PFD 2
+#endif
 
 typedef uint4 Frag;   // 16 bytes of an A-operand fragment
 
@@ -65,12 +74,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uns
 __device__ __forceinline__ Frag buf_frag(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
     return __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
 }
-template <typename E> __device__ __forceinline__ E buf_elem(__amdgpu_buffer_rsrc_t r, unsigned voff);
-template <> __device__ __forceinline__ bf16 buf_elem<bf16>(__amdgpu_buffer_rsrc_t r, unsigned voff) {
-    return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0));
+// One element as raw bits in a 32-bit register (bf16: the low half), and its
+// value.  Kept as 32-bit words, separate loads are never packed into one
+// register, which would make the wave wait for them at once.
+template <typename E> __device__ __forceinline__ unsigned buf_raw(__amdgpu_buffer_rsrc_t r, unsigned voff);
+template <> __device__ __forceinline__ unsigned buf_raw<bf16>(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
 }
-template <> __device__ __forceinline__ float buf_elem<float>(__amdgpu_buffer_rsrc_t r, unsigned voff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+template <> __device__ __forceinline__ unsigned buf_raw<float>(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+}
+template <typename E> __device__ __forceinline__ float raw_f32(unsigned x) {
+    return __builtin_bit_cast(float, sizeof(E) == 2 ? x << 16 : x);
 }
 template <typename E> __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, unsigned voff, E x);
 template <> __device__ __forceinline__ void buf_store<bf16>(__amdgpu_buffer_rsrc_t r, unsigned voff, bf16 x) {
@@ -115,8 +130,9 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
     // share the head's workspace records through that XCD's L2.
     const int nvb = P.dv / NV;
     const int G = gridDim.x;
+    const bool remap = (G & 7) == 0 && ((G >> 3) % nvb) == 0;
     int lid = blockIdx.x;
-    if ((G & 7) == 0 && ((G >> 3) % nvb) == 0)
+    if (remap)
         lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const int bh = lid / nvb, vb = lid % nvb;
     const int b = bh / P.H, h = bh % P.H;
@@ -149,9 +165,12 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
     // One chunk's operands for this wave: the token-block fragments (K~ and T
     // for a chain wave, Q~ and A_qk for an output wave), the W~^T key block
     // and gamma_C of its S tiles, and (chain waves) the v tile.
+    constexpr int REC = (int)WsLayout::make(sizeof(E) == 2, C, DK).rec;
+    constexpr int NPF = (REC + 512 * 128 - 1) / (512 * 128);
     struct Chunk {
         Frag kq[GK], ta[GC], wt[GC], gc;
-        E v[NTJ][4];
+        unsigned v[NTJ][4];             // raw bits of the v tile
+        unsigned pf[NPF + 1];           // L2 prefetch probes (see touch)
     };
     // Memory access: buffer instructions with a wave-uniform descriptor per
     // chunk (scalar registers) and per-lane byte offsets fixed for the whole
@@ -181,6 +200,25 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
                         (unsigned)(((L - 1) * hdv + NV) * (long)sizeof(E)));
     };
 
+    // L2 prefetch of chunk cn into X.pf: one dword of every 128-byte line of
+    // its record (read by one value block of the head when the head's blocks
+    // share an XCD, by every block otherwise) and, wave 0, of this block's v
+    // rows.  Each dword has a register of its own that nothing reads until
+    // the end of the chunk computed from X (an empty asm statement uses it
+    // there), so the wave waits for these loads no earlier than for the next
+    // chunk's operands, issued after them.  Chunks past the end, and the v
+    // rows in waves other than 0, read through an empty descriptor, which
+    // touches no memory.
+    auto touch = [&](Chunk &X, int cn) {
+        const bool mine = !remap || vb == cn % nvb;
+        const auto rr = (cn < NC && mine) ? rec_rsrc(cn) : buf_rsrc(ws, 0u);
+#pragma unroll
+        for (int i = 0; i < NPF; ++i)
+            X.pf[i] = __builtin_amdgcn_raw_buffer_load_b32(rr, (tid + i * 512) * 128, 0, 0);
+        const auto vr = (cn < NC && wv == 0) ? row_rsrc(gv, cn) : buf_rsrc(gv, 0u);
+        X.pf[NPF] = __builtin_amdgcn_raw_buffer_load_b32(vr, (unsigned)(lane * hdv * (long)sizeof(E)), 0, 0);
+        asm volatile("" ::: "memory");   // keeps the loads here, ahead of the compute
+    };
     auto load = [&](Chunk &X, int c) {
         const auto rr = rec_rsrc(c);
         if (chain || outw) {
@@ -204,8 +242,11 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
             for (int nj = 0; nj < NTJ; ++nj)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    X.v[nj][r] = buf_elem<E>(vr, vofs[nj][r]);
+                    X.v[nj][r] = buf_raw<E>(vr, vofs[nj][r]);
         }
+        // issued after the operands, so waiting for those does not wait for it
+        if (KDN_STATE_PFD > 0)
+            touch(X, c + KDN_STATE_PFD);
     };
 
     // Output waves: Q~ S of chunk c in phase 1, finished in phase 2 of chunk
@@ -248,7 +289,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
                 float u[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    u[r] = to_f32(X.v[nj][r]) - accu[r];
+                    u[r] = raw_f32<E>(X.v[nj][r]) - accu[r];
                 lds_stn<4>(UT + (nj * 16 + (lane & 15)) * PC + m * 16 + (lane >> 4) * 4, u);
             }
         } else if (outw) {
@@ -306,6 +347,11 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
             lds_stn<4>(ST + (nj * 16 + (lane & 15)) * PK + i0, s4);
         }
         __syncthreads();
+        if (KDN_STATE_PFD > 0) {
+#pragma unroll
+            for (int i = 0; i <= NPF; ++i)
+                asm volatile("" ::"v"(X.pf[i]));
+        }
     };
 
     // Software pipeline: chunk c+1's operands load while chunk c computes

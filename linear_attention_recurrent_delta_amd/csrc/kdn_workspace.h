@@ -38,8 +38,8 @@ struct WsLayout {
     int C, DK;
     long off_kd, off_qd, off_wdt, off_aqk, off_tm, off_gc, rec;
 
-    __host__ __device__ static WsLayout make(int bf16, int C, int DK) {
-        WsLayout w;
+    __host__ __device__ static constexpr WsLayout make(int bf16, int C, int DK) {
+        WsLayout w{};
         w.es = bf16 ? 2 : 4;
         w.C = C;
         w.DK = DK;
