@@ -888,34 +888,131 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         }
         __syncthreads();
         // ---------------- 4b. off-diagonal blocks of T ----------------
-        // Column chain J on wave J (no barriers between its steps):
-        //   T[I,J] = -T[I,I] sum_{K=J}^{I-1} A[I,K] T[K,J],  I = J+1 .. NB-1.
-        // Products in (near) fp32: bf16 data is split into hi + lo parts.
-        if (wv < NB - 1) {
-            const int J = wv;
-            // private slots of wave J: P^T, then T[K,J]^T for K = J+1 .. NB-2
-            float *ps = TD + (NB + (NB - 1) + J * (2 * NB - 1 - J) / 2) * 320;
-            for (int I = J + 1; I < NB; ++I) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int K = J; K < I; ++K) {
-                    const float *bk = (K == J) ? TD + (NB + J) * 320 : ps + (K - J) * 320;
-                    mma16_f32<E>(acc, Akk + I * 16 * PA + K * 16, PA, bk, 20, lane);
-                }
-                *reinterpret_cast<float4 *>(ps + (lane & 15) * 20 + (lane >> 4) * 4) =
-                    make_float4(acc[0], acc[1], acc[2], acc[3]);
-                f32x4 tij = {0.f, 0.f, 0.f, 0.f};
-                mma16_f32<E>(tij, TD + I * 320, 20, ps, 20, lane);
-                const int col = J * 16 + (lane & 15), row0 = I * 16 + (lane >> 4) * 4;
+        if constexpr (PREP) {
+            // With D = diag(T[I,I]) and N the blocks of A below the diagonal,
+            // I + A = (I + N D) D^-1, so T = D X with X = (I + M)^-1, M = N D:
+            //   M[I,K] = A[I,K] T[K,K];  X[I,I-1] = -M[I,I-1],
+            //   X[2,0] = -M[2,0] + M[2,1] M[1,0],  X[3,1] = -M[3,1] + M[3,2] M[2,1],
+            //   X[3,0] = -M[3,0] + M[3,1] M[1,0] - M[3,2] X[2,0];  T[I,K] = T[I,I] X[I,K].
+            // Three levels of independent 16 x 16 products on waves 0-5 (four
+            // products deep) instead of one chain per column.  Scratch: 16 x 20
+            // slots over K~ / Q~, free once their records are written.  "t"
+            // slots hold the transpose (the B operand of mma16_f32), row slots
+            // the matrix (its A operand).
+            static_assert(LY::OFF_QT == LY::OFF_KT + LY::SZ_CK &&
+                              (NB == 2 ? 1 : 12) * 320 * 4 <= 2 * LY::SZ_CK,
+                          "scratch slots fit over K~ and Q~");
+            float *SL = reinterpret_cast<float *>(smem + LY::OFF_KT);
+            auto slot = [&](int n) { return SL + n * 320; };
+            auto tdiag = [&](int I) { return TD + I * 320; };            // T[I,I]
+            auto tdiag_t = [&](int I) { return TD + (NB + I) * 320; };   // T[I,I]^T
+            auto akk = [&](int I, int K) { return Akk + I * 16 * PA + K * 16; };
+            const int col = lane & 15, row0 = (lane >> 4) * 4;
+            auto put_t = [&](float *d, const f32x4 &v) {
+                *reinterpret_cast<float4 *>(d + col * 20 + row0) = make_float4(v[0], v[1], v[2], v[3]);
+            };
+            auto put_row = [&](float *d, const f32x4 &v) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Tm[(row0 + r) * PC + col] = from_f32<E>(-tij[r]);
-                if (I < NB - 1)                    // T[I,J]^T for later steps
-                    *reinterpret_cast<float4 *>(ps + (I - J) * 320 + (lane & 15) * 20 +
-                                                (lane >> 4) * 4) =
-                        make_float4(-tij[0], -tij[1], -tij[2], -tij[3]);
+                    d[(row0 + r) * 20 + col] = v[r];
+            };
+            auto get_t = [&](const float *d) {
+                const float4 x = *reinterpret_cast<const float4 *>(d + col * 20 + row0);
+                return f32x4{x.x, x.y, x.z, x.w};
+            };
+            // T[I,K] = sgn T[I,I] X (X^T in xt) into Tm
+            auto put_tm = [&](int I, int K, const float *xt, float sgn) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                mma16_f32<E>(acc, tdiag(I), 20, xt, 20, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Tm[(I * 16 + row0 + r) * PC + K * 16 + col] = from_f32<E>(sgn * acc[r]);
+            };
+            if constexpr (NB == 2) {
+                if (wv == 0) {                 // T[1,0] = -T[1,1] A[1,0] T[0,0]
+                    f32x4 m = {0.f, 0.f, 0.f, 0.f};
+                    mma16_f32<E>(m, akk(1, 0), PA, tdiag_t(0), 20, lane);
+                    put_t(slot(0), m);
+                    put_tm(1, 0, slot(0), -1.f);
+                }
+            } else {
+                static_assert(NB == 4, "chunk of 32 or 64");
+                // slots: M10t 0, M21 1 (row) 2 (t), M32 3 (row) 4 (t), M20t 5,
+                //        M31 6 (row) 7 (t), M30t 8, X20t 9, X31t 10, Y30t 11, X30t 5
+                constexpr int LI[6] = {1, 2, 3, 2, 3, 3}, LK[6] = {0, 1, 2, 0, 1, 0};
+                if (wv < 6) {                  // level 1: M = A[I,K] T[K,K]
+                    const int I = LI[wv], K = LK[wv];
+                    f32x4 m = {0.f, 0.f, 0.f, 0.f};
+                    mma16_f32<E>(m, akk(I, K), PA, tdiag_t(K), 20, lane);
+                    if (wv == 0) put_t(slot(0), m);
+                    if (wv == 1) { put_row(slot(1), m); put_t(slot(2), m); }
+                    if (wv == 2) { put_row(slot(3), m); put_t(slot(4), m); }
+                    if (wv == 3) put_t(slot(5), m);
+                    if (wv == 4) { put_row(slot(6), m); put_t(slot(7), m); }
+                    if (wv == 5) put_t(slot(8), m);
+                }
+                __syncthreads();
+                if (wv < 3) {                  // level 2: T[I,I-1] = -T[I,I] M[I,I-1]
+                    const int I = wv + 1;
+                    put_tm(I, I - 1, slot(wv == 0 ? 0 : (wv == 1 ? 2 : 4)), -1.f);
+                } else if (wv < 6) {           // X[2,0], X[3,1], Y = -M[3,0] + M[3,1] M[1,0]
+                    const int ia = wv == 3 ? 1 : (wv == 4 ? 3 : 6);   // A operand (row)
+                    const int ib = wv == 3 ? 0 : (wv == 4 ? 2 : 0);   // B operand (t)
+                    const int ic = wv == 3 ? 5 : (wv == 4 ? 7 : 8);   // -initial (t)
+                    f32x4 acc = get_t(slot(ic));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[r] = -acc[r];
+                    mma16_f32<E>(acc, slot(ia), 20, slot(ib), 20, lane);
+                    put_t(slot(6 + wv), acc);                         // X20t 9, X31t 10, Y30t 11
+                }
+                __syncthreads();
+                if (wv == 0) {
+                    put_tm(2, 0, slot(9), 1.f);                       // T[2,0] = T[2,2] X[2,0]
+                } else if (wv == 1) {
+                    put_tm(3, 1, slot(10), 1.f);                      // T[3,1] = T[3,3] X[3,1]
+                } else if (wv == 2) {                                 // X[3,0] = Y - M[3,2] X[2,0]
+                    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+                    mma16_f32<E>(p, slot(3), 20, slot(9), 20, lane);
+                    f32x4 x = get_t(slot(11));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        x[r] -= p[r];
+                    put_t(slot(5), x);          // read back by this wave only
+                    put_tm(3, 0, slot(5), 1.f);
+                }
             }
+            __syncthreads();
+        } else {
+            // Column chain J on wave J (no barriers between its steps):
+            //   T[I,J] = -T[I,I] sum_{K=J}^{I-1} A[I,K] T[K,J],  I = J+1 .. NB-1.
+            // Products in (near) fp32: bf16 data is split into hi + lo parts.
+            if (wv < NB - 1) {
+                const int J = wv;
+                // private slots of wave J: P^T, then T[K,J]^T for K = J+1 .. NB-2
+                float *ps = TD + (NB + (NB - 1) + J * (2 * NB - 1 - J) / 2) * 320;
+                for (int I = J + 1; I < NB; ++I) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int K = J; K < I; ++K) {
+                        const float *bk = (K == J) ? TD + (NB + J) * 320 : ps + (K - J) * 320;
+                        mma16_f32<E>(acc, Akk + I * 16 * PA + K * 16, PA, bk, 20, lane);
+                    }
+                    *reinterpret_cast<float4 *>(ps + (lane & 15) * 20 + (lane >> 4) * 4) =
+                        make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    f32x4 tij = {0.f, 0.f, 0.f, 0.f};
+                    mma16_f32<E>(tij, TD + I * 320, 20, ps, 20, lane);
+                    const int col = J * 16 + (lane & 15), row0 = I * 16 + (lane >> 4) * 4;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Tm[(row0 + r) * PC + col] = from_f32<E>(-tij[r]);
+                    if (I < NB - 1)                    // T[I,J]^T for later steps
+                        *reinterpret_cast<float4 *>(ps + (I - J) * 320 + (lane & 15) * 20 +
+                                                    (lane >> 4) * 4) =
+                            make_float4(-tij[0], -tij[1], -tij[2], -tij[3]);
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
         if constexpr (PREP) {
             // ---------------- record of this chunk ----------------
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
