@@ -851,39 +851,80 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                 }
                 lds_stn<4>(UT + j * PC + mi * 16 + (lane >> 4) * 4, uo);
             }
-        } else if (wv >= 4 && wv - 4 < NB && lane < 16) {
-            // T[I,I] = (I + A[I,I])^-1 by forward substitution; lane j
-            // computes column j.  A_kk is only read here (no aliasing store),
-            // so the row loads can run ahead of the arithmetic.
-            const int I = wv - 4, o0 = I * 16, j = lane;
-            float xv[16];
+        } else if (wv >= 4 && wv - 4 < NB) {
+            // T[I,I] = (I + A[I,I])^-1, one wave per block, as 2 x 2 blocks of
+            // 8 x 8:  T1 = (I + A11)^-1 and T2 = (I + A22)^-1 by forward
+            // substitution (lane j < 8: column j of T1, lane 8 + j: column j
+            // of T2), then T21 = -T2 A21 T1 on all 64 lanes, one element
+            // each.  The block goes to its TD slot (row-major, pitch 20);
+            // LDS accesses of one wave complete in order, so the wave reads
+            // back what it wrote without a barrier.
+            const int I = wv - 4, o0 = I * 16;
+            float *td = TD + I * 320;
+            if (lane < 16) {
+                const int h = lane >> 3, j = lane & 7, off = h * 8;
+                const float *arow0 = Akk + (o0 + off) * PA + o0 + off;
+                float xv[8];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float arow[16];
+                for (int r = 0; r < 8; ++r) {
+                    const float4 a0 = *reinterpret_cast<const float4 *>(arow0 + r * PA);
+                    const float4 a1 = *reinterpret_cast<const float4 *>(arow0 + r * PA + 4);
+                    const float ar[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-                for (int m = 0; m < 16; m += 4) {
-                    const float4 a4 = *reinterpret_cast<const float4 *>(Akk + (o0 + r) * PA + o0 + m);
-                    arow[m] = a4.x; arow[m + 1] = a4.y; arow[m + 2] = a4.z; arow[m + 3] = a4.w;
+                    for (int m = 0; m < r; ++m) {
+                        if (m & 1) acc1 += ar[m] * xv[m];
+                        else acc0 += ar[m] * xv[m];
+                    }
+                    xv[r] = (r == j) ? 1.f : ((r < j) ? 0.f : -(acc0 + acc1));
                 }
-                float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) {
-                    if (m & 1) acc1 += arow[m] * xv[m];
-                    else acc0 += arow[m] * xv[m];
+                for (int r = 0; r < 8; ++r) {
+                    td[(off + r) * 20 + off + j] = xv[r];
+                    if (h == 0)
+                        td[r * 20 + 8 + j] = 0.f;          // upper-right block
                 }
-                xv[r] = (r == j) ? 1.f : ((r < j) ? 0.f : -(acc0 + acc1));
             }
+            __builtin_amdgcn_wave_barrier();
+            {
+                const int i = lane >> 3, j = lane & 7;      // element (i, j) of the 8 x 8
+                const float *a21 = Akk + (o0 + 8 + i) * PA + o0;
+                const float4 a0 = *reinterpret_cast<const float4 *>(a21);
+                const float4 a1 = *reinterpret_cast<const float4 *>(a21 + 4);
+                const float ar[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                float y = 0.f;                              // (A21 T1)[i][j]
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                TD[I * 320 + r * 20 + j] = xv[r];                 // T[I,I]
-                Tm[(o0 + r) * PC + o0 + j] = from_f32<E>(xv[r]);
+                for (int k = 0; k < 8; ++k)
+                    y += ar[k] * td[k * 20 + j];
+                td[i * 20 + 8 + j] = y;                     // parked in the upper right
+                __builtin_amdgcn_wave_barrier();
+                const float4 t0 = *reinterpret_cast<const float4 *>(td + (8 + i) * 20 + 8);
+                const float4 t1 = *reinterpret_cast<const float4 *>(td + (8 + i) * 20 + 12);
+                const float t2r[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+                float z = 0.f;                              // (T2 A21 T1)[i][j]
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    z += t2r[k] * td[k * 20 + 8 + j];
+                __builtin_amdgcn_wave_barrier();
+                td[(8 + i) * 20 + j] = -z;
+                td[i * 20 + 8 + j] = 0.f;
             }
-            if (I < NB - 1) {                  // T[I,I]^T: B operand of chain I
-                float *dst = TD + (NB + I) * 320 + j * 20;
+            __builtin_amdgcn_wave_barrier();
+            {
+                // T[I,I] in the operand type, and its transpose (the B operand
+                // of the block products); lane: row r, columns c0 .. c0 + 3
+                const int r = lane >> 2, c0 = (lane & 3) * 4;
+                const float4 t = *reinterpret_cast<const float4 *>(td + r * 20 + c0);
+                const float tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-                for (int r = 0; r < 16; r += 4)
-                    *reinterpret_cast<float4 *>(dst + r) =
-                        make_float4(xv[r], xv[r + 1], xv[r + 2], xv[r + 3]);
+                for (int e = 0; e < 4; ++e)
+                    Tm[(o0 + r) * PC + o0 + c0 + e] = from_f32<E>(tv[e]);
+                if (I < NB - 1) {
+                    float *dst = TD + (NB + I) * 320;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dst[(c0 + e) * 20 + r] = tv[e];
+                }
             }
         }
         __syncthreads();
