@@ -411,11 +411,36 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     constexpr int H2 = (NT / LY::NTS) < TPG ? (NT / LY::NTS) : TPG;
     constexpr int TPG2 = TPG / H2, NG2 = NG * H2, NTO = LY::NTS * H2;
     static_assert(TPG2 * H2 == TPG && NTO <= NT, "operand layout");
-    const int grp = tid % NG, oc = (tid / NG) % NO;
+    // Diagonal KDN runs the scan layout on the last NTS threads, alongside
+    // the variance chain on the first DK (phase 2).
+    static_assert(!KDN || LY::NTS <= NT - DK, "scan threads clear of the variance chain");
+    const int ts = KDN ? tid - (NT - LY::NTS) : tid;   // scan-layout thread, if >= 0
+    const int grp = ts % NG, oc = (ts / NG) % NO;
     const int i0 = oc * 8, t0 = grp * TPG;
     const int gh = tid % NG2, oc2 = tid / NG2;
     const int j0 = oc2 * 8, u0 = gh * TPG2;        // operand pass: channels, tokens
     const int ug0 = (gh / H2) * TPG;               // first token of its group
+
+    // 2a. group products of the decays (scan-layout threads): the product of
+    // each thread's TPG tokens, per channel
+    auto group_products = [&]() {
+        float gprod[8];
+#pragma unroll
+        for (int tt = 0; tt < TPG; ++tt) {
+            float a8[8];
+            if constexpr (VDECAY) {
+                lds_ld8(ALP + (t0 + tt) * PK + i0, a8);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    a8[c] = s_alph[t0 + tt];
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                gprod[c] = tt ? gprod[c] * a8[c] : a8[c];
+        }
+        lds_st8(GP + grp * DK + i0, gprod);   // group totals
+    };
 
     for (int it = PREP ? (int)blockIdx.x : 0; it < (PREP ? NU : T);
          it += PREP ? (int)gridDim.x : C) {
@@ -461,6 +486,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             // latency stays off the dependent chain.  Tokens past the end of
             // the sequence were staged as a = 1, xi = 0, k = 0, r = 1, which
             // leaves p unchanged bit for bit.
+            if (ts >= 0)
+                group_products();          // decays, independent of the variance
             if (tid < DK) {
                 const int i = tid;
                 const float mu = P.mu;
@@ -575,27 +602,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             }
             __syncthreads();
         } else {
-        // 2a. group products of the decays (scan threads)
+        // 2a. group products of the decays (diagonal KDN: done in phase 2)
         if constexpr (DECAY) {
-            if (tid < LY::NTS) {
-                float gprod[8];
-#pragma unroll
-                for (int tt = 0; tt < TPG; ++tt) {
-                    float a8[8];
-                    if constexpr (VDECAY) {
-                        lds_ld8(ALP + (t0 + tt) * PK + i0, a8);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 8; ++c)
-                            a8[c] = s_alph[t0 + tt];
-                    }
-#pragma unroll
-                    for (int c = 0; c < 8; ++c)
-                        gprod[c] = tt ? gprod[c] * a8[c] : a8[c];
-                }
-                lds_st8(GP + grp * DK + i0, gprod);   // group totals
+            if constexpr (!KDN) {
+                if (ts < LY::NTS)
+                    group_products();
+                __syncthreads();
             }
-            __syncthreads();
             // 2b. exclusive prefix / suffix over groups, one thread per channel
             if (tid < DK) {
                 float gt[NG];
