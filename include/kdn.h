@@ -170,6 +170,42 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype,
                                 const void *proc_noise, const void *obs_noise,
                                 float *S, float *p, void *o, void *stream);
 
+/*
+ * Several decode steps in one pass over the state: T consecutive tokens for
+ * each of N sequences x H heads (multi-token decode, e.g. verifying T draft
+ * tokens of speculative decoding).  S and p are read once, stepped through
+ * the T tokens in registers with exactly the arithmetic of
+ * kdn_recurrent_decode, and written once, so the call costs about one decode
+ * step of state traffic instead of T.  The token-by-token regime of
+ * "معماری KDA ...", section "پیاده‌سازی فنی و گذارهای DPLR", applied to a
+ * short run of tokens from a resident state.
+ *
+ *   q, k        [N, T, H, d_k] dtype;   v [N, T, H, d_v] dtype
+ *   alpha       NULL | [N, T, H] | [N, T, H, d_k] dtype (as for prefill)
+ *   beta        [N, T, H] dtype, NULL for diagonal KDN
+ *   proc_noise  [N, T, H, d_k] dtype, obs_noise [N, T, H] dtype (diag KDN only)
+ *   S0          [N, H, d_k, d_v] float32 state before the tokens (NULL: zeros)
+ *   p0          [N, H, d_k] float32 (diagonal KDN only, else NULL)
+ *   o           [N, T, H, d_v] dtype (output, one row per token)
+ *   S_out       [N, H, d_k, d_v] float32, the state after the T tokens
+ *   p_out       [N, H, d_k] float32 (diagonal KDN only, else NULL)
+ * S_out may be S0 exactly and p_out may be p0 exactly (update in place);
+ * any other overlap between outputs and inputs is KDN_ERR_ALIAS.  With S_out
+ * and p_out elsewhere the resident state is left as it was, which is the
+ * rollback of a rejected draft.  T = 0 copies the state.  Token t of
+ * sequence n gives the same bits as the t-th of T kdn_recurrent_decode calls
+ * on row (n, t) of the same inputs.
+ * Supported: d_k, d_v in {64, 128}; dtype KDN_F32 or KDN_BF16; N, T, H >= 0.
+ * Errors and asynchrony as for kdn_chunk_prefill.
+ */
+kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype,
+                                      int N, int T, int H, int d_k, int d_v, float mu,
+                                      const void *q, const void *k, const void *v,
+                                      const void *alpha, const void *beta,
+                                      const void *proc_noise, const void *obs_noise,
+                                      const float *S0, const float *p0, void *o,
+                                      float *S_out, float *p_out, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kdn_status_string(kdn_status status);
 
@@ -180,7 +216,7 @@ int kdn_chunk_prefill_chunk_size(kdn_dtype dtype, int d_k, int d_v, int chunk);
 /* ABI version of this header (incremented on any incompatible change). */
 int kdn_abi_version(void);
 
-#define KDN_ABI_VERSION 2
+#define KDN_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

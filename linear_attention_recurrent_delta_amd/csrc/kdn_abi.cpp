@@ -280,8 +280,82 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype, int N, int
     P.N = N; P.H = H; P.dk = d_k; P.dv = d_v; P.mu = mu;
     P.q = q; P.k = k; P.v = v; P.alpha = alpha; P.beta = beta;
     P.xi = proc_noise; P.r = obs_noise;
-    P.S = S; P.p = p; P.o = o;
+    P.T = 1;
+    P.S0 = S; P.p0 = p; P.S = S; P.p = p; P.o = o;
     const hipError_t e = kdn::launch_decode(P, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;
+}
+
+kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype, int N, int T,
+                                      int H, int d_k, int d_v, float mu, const void *q,
+                                      const void *k, const void *v, const void *alpha,
+                                      const void *beta, const void *proc_noise,
+                                      const void *obs_noise, const float *S0,
+                                      const float *p0, void *o, float *S_out,
+                                      float *p_out, void *stream) {
+    if (!valid_variant(variant) || !valid_dtype(dtype))
+        return KDN_ERR_UNSUPPORTED;
+    if (N < 0 || T < 0 || H < 0 || d_k <= 0 || d_v <= 0)
+        return KDN_ERR_SHAPE;
+    const long long nh = (long long)N * H;
+    const long long tok = nh * T;
+    if (nh * d_k * d_v >= (1LL << 31) || tok * (d_k > d_v ? d_k : d_v) >= (1LL << 40))
+        return KDN_ERR_SHAPE;
+    if (!valid_dim(d_k) || !valid_dim(d_v))
+        return KDN_ERR_UNSUPPORTED;
+    const bool kdn = variant == KDN_DIAG_KDN;
+    if (tok > 0 && (!q || !k || !v || !o))
+        return KDN_ERR_NULL;
+    if (kdn_status st = check_gates(variant, alpha, beta, proc_noise, obs_noise, tok == 0))
+        return st;
+    if (nh > 0 && !S_out)
+        return KDN_ERR_NULL;
+    if (kdn && nh > 0 && (!p0 || !p_out))
+        return KDN_ERR_NULL;
+    if (!kdn && (p0 || p_out))
+        return KDN_ERR_NULL;
+    const long long es = dtype == KDN_BF16 ? 2 : 4;
+    const void *vec[] = {q, k, v, variant == KDN_GATED_DELTANET ? nullptr : alpha,
+                         proc_noise, S0, p0, o, S_out, p_out};
+    const void *sca[] = {beta, obs_noise, variant == KDN_GATED_DELTANET ? alpha : nullptr};
+    for (const void *x : vec)
+        if (x && !aligned(x, 16))
+            return KDN_ERR_ALIGN;
+    for (const void *x : sca)
+        if (x && !aligned(x, (uintptr_t)es))
+            return KDN_ERR_ALIGN;
+
+    const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
+    const long long n_a = variant == KDN_GATED_DELTANET ? tok * es
+                        : (variant == KDN_DELTANET ? 0 : tok * d_k * es);
+    const long long n_b = kdn ? 0 : tok * es;
+    const long long n_x = kdn ? tok * d_k * es : 0, n_r = kdn ? tok * es : 0;
+    const long long n_S = nh * d_k * d_v * 4, n_p = kdn ? nh * d_k * 4 : 0;
+    const long long n_o = tok * d_v * es;
+    // o overlaps nothing; S_out may be S0 exactly and p_out may be p0 exactly
+    // (each workgroup reads its slice before writing it); no other overlap.
+    struct R { const void *p; long long n; } ins[] = {
+        {q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, n_b},
+        {proc_noise, n_x}, {obs_noise, n_r}, {S0, n_S}, {p0, n_p}};
+    for (const R &x : ins) {
+        if (overlap(o, n_o, x.p, x.n)) return KDN_ERR_ALIAS;
+        if (x.p != S0 && overlap(S_out, n_S, x.p, x.n)) return KDN_ERR_ALIAS;
+        if (kdn && x.p != p0 && overlap(p_out, n_p, x.p, x.n)) return KDN_ERR_ALIAS;
+    }
+    if (S0 && S0 != S_out && overlap(S_out, n_S, S0, n_S)) return KDN_ERR_ALIAS;
+    if (kdn && p0 != p_out && overlap(p_out, n_p, p0, n_p)) return KDN_ERR_ALIAS;
+    if (overlap(o, n_o, S_out, n_S)) return KDN_ERR_ALIAS;
+    if (kdn && (overlap(o, n_o, p_out, n_p) || overlap(S_out, n_S, p_out, n_p)))
+        return KDN_ERR_ALIAS;
+
+    kdn::DecodeParams P;
+    P.variant = variant;
+    P.bf16 = dtype == KDN_BF16;
+    P.N = N; P.H = H; P.dk = d_k; P.dv = d_v; P.T = T; P.mu = mu;
+    P.q = q; P.k = k; P.v = v; P.alpha = alpha; P.beta = beta;
+    P.xi = proc_noise; P.r = obs_noise;
+    P.S0 = S0; P.p0 = p0; P.S = S_out; P.p = p_out; P.o = o;
+    const hipError_t e = kdn::launch_decode_multi(P, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;
 }
 

@@ -29,7 +29,41 @@ namespace kdn {
 #define KDN_DECODE_NT 256
 #endif
 
-template <typename TIn, int VAR, int DK, int DV, int NT>
+// Per-token inputs of one head: the d_k vectors (k, q, decay, process noise)
+// in threads < d_k, the per-head scalars, and this thread's 4 values of v.
+template <typename TIn, int VAR, int DK>
+struct TokenIn {
+    float k = 0.f, q = 0.f, a = 1.f, xi = 0.f, beta = 0.f, r = 0.f;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+
+    __device__ __forceinline__ void load(const DecodeParams &P, long row, int tid, int cg) {
+        if (tid < DK) {
+            k = to_f32(static_cast<const TIn *>(P.k)[row * DK + tid]);
+            q = to_f32(static_cast<const TIn *>(P.q)[row * DK + tid]);
+            if (VAR == GATED_DELTANET)
+                a = to_f32(static_cast<const TIn *>(P.alpha)[row]);
+            else if (VAR == KDA || VAR == DIAG_KDN)
+                a = to_f32(static_cast<const TIn *>(P.alpha)[row * DK + tid]);
+            if (VAR == DIAG_KDN)
+                xi = to_f32(static_cast<const TIn *>(P.xi)[row * DK + tid]);
+            else
+                beta = to_f32(static_cast<const TIn *>(P.beta)[row]);
+        }
+        if (VAR == DIAG_KDN)
+            r = to_f32(static_cast<const TIn *>(P.r)[row]);
+        const TIn *vp = static_cast<const TIn *>(P.v) + row * P.dv + 4 * cg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = to_f32(vp[e]);
+    }
+};
+
+// MULTI = false: one token per (sequence, head), S and p updated in place
+// (P.S0 == P.S, P.p0 == P.p).  MULTI = true: P.T tokens per (sequence, head)
+// with per-token tensors [N, T, H, .]; S and p are read from S0 / p0 once,
+// stepped through the T tokens in registers, and written to S / p once.  The
+// arithmetic of a token is the same in both.
+template <typename TIn, int VAR, int DK, int DV, int NT, bool MULTI>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
     constexpr int CG = DV / 4;        // float4 column groups
     constexpr int RG = NT / CG;       // row groups
@@ -40,7 +74,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
     const int cg = tid % CG;
     const int rg = tid / CG;
     const long bh = blockIdx.x;
+    const int T = MULTI ? P.T : 1;
+    // row of token t in the per-token tensors: (n, t, h) for [N, T, H, .]
+    const long n = MULTI ? bh / P.H : 0, h = MULTI ? bh % P.H : bh;
+    auto row_of = [&](int t) { return MULTI ? (n * T + t) * P.H + h : bh; };
 
+    const float *Sin = P.S0 ? P.S0 + bh * (long)DK * DV : nullptr;
     float *S = P.S + bh * (long)DK * DV;
     const int row0 = rg * RPT;
 
@@ -48,131 +87,136 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
     __shared__ f32x4 red[RG][CG];
     __shared__ float part[NT / WAVE];
 
-    const TIn *q = static_cast<const TIn *>(P.q) + bh * DK;
-    const TIn *k = static_cast<const TIn *>(P.k) + bh * DK;
-
-    // The per-head vectors are requested first and the state after them:
-    // loads return in order, so the gain below is formed while the state is
-    // still streaming in.
-    float kk = 0.f, qq = 0.f, aa = 1.f, xi = 0.f, p0 = 0.f, bt = 0.f;
-    if (tid < DK) {
-        kk = to_f32(k[tid]);
-        qq = to_f32(q[tid]);
-        if (VAR == GATED_DELTANET)
-            aa = to_f32(static_cast<const TIn *>(P.alpha)[bh]);
-        else if (VAR == KDA || VAR == DIAG_KDN)
-            aa = to_f32(static_cast<const TIn *>(P.alpha)[bh * DK + tid]);
-        if (VAR == DIAG_KDN) {
-            xi = to_f32(static_cast<const TIn *>(P.xi)[bh * DK + tid]);
-            p0 = P.p[bh * DK + tid];
-        } else {
-            bt = to_f32(static_cast<const TIn *>(P.beta)[bh]);
-        }
-    }
-    const float rr = VAR == DIAG_KDN ? to_f32(static_cast<const TIn *>(P.r)[bh]) : 0.f;
+    // The first token's vectors are requested first and the state after
+    // them: loads return in order, so the gain below is formed while the
+    // state is still streaming in.
+    TokenIn<TIn, VAR, DK> in;
+    if (T > 0)
+        in.load(P, row_of(0), tid, cg);
+    float pc = 0.f;                   // variance of channel tid (diagonal KDN)
+    if (VAR == DIAG_KDN && tid < DK)
+        pc = P.p0[bh * DK + tid];
     f32x4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        s[m] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4 *>(S + (long)(row0 + m) * DV) + cg);
+        s[m] = Sin ? __builtin_nontemporal_load(
+                         reinterpret_cast<const f32x4 *>(Sin + (long)(row0 + m) * DV) + cg)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float pm = 0.f, u = 0.f, pk2 = 0.f;
-    if (tid < DK) {
-        sk[tid] = kk;
-        sq[tid] = qq;
-        sa[tid] = aa;
-        if (VAR == DIAG_KDN) {
-            pm = aa * aa * p0 + xi;                     // predict
-            u = pm * kk;
-            pk2 = u * kk;
-        } else {
-            sg[tid] = bt * kk;
-        }
-    }
-    if (VAR == DIAG_KDN) {
-        // innovation variance s = r + sum_i p-_i k_i^2 (block reduction)
-        const float ws = wave_sum(pk2);
-        if ((tid & (WAVE - 1)) == 0)
-            part[tid / WAVE] = ws;
-        __syncthreads();
+    for (int t = 0; t < T; ++t) {
+        TokenIn<TIn, VAR, DK> nxt;    // next token's inputs, in flight meanwhile
+        if (MULTI && t + 1 < T)
+            nxt.load(P, row_of(t + 1), tid, cg);
+
+        float pm = 0.f, u = 0.f, pk2 = 0.f;
         if (tid < DK) {
-            const float r = rr;
-            float sum = r;
-#pragma unroll
-            for (int w = 0; w < (DK + WAVE - 1) / WAVE; ++w)
-                sum += part[w];
-            sg[tid] = (sum != 0.f) ? u / sum : 0.f;    // gain
-            const float den = r + P.mu * pm * kk * kk;
-            P.p[bh * DK + tid] = (den != 0.f) ? pm * r / den : pm;
+            sk[tid] = in.k;
+            sq[tid] = in.q;
+            sa[tid] = in.a;
+            if (VAR == DIAG_KDN) {
+                pm = in.a * in.a * pc + in.xi;          // predict
+                u = pm * in.k;
+                pk2 = u * in.k;
+            } else {
+                sg[tid] = in.beta * in.k;
+            }
         }
-    }
-    __syncthreads();
+        if (VAR == DIAG_KDN) {
+            // innovation variance s = r + sum_i p-_i k_i^2 (block reduction)
+            const float ws = wave_sum(pk2);
+            if ((tid & (WAVE - 1)) == 0)
+                part[tid / WAVE] = ws;
+            __syncthreads();
+            if (tid < DK) {
+                const float r = in.r;
+                float sum = r;
+#pragma unroll
+                for (int w = 0; w < (DK + WAVE - 1) / WAVE; ++w)
+                    sum += part[w];
+                sg[tid] = (sum != 0.f) ? u / sum : 0.f;    // gain
+                const float den = r + P.mu * pm * in.k * in.k;
+                pc = (den != 0.f) ? pm * r / den : pm;
+            }
+        }
+        __syncthreads();
 
-    // S- = diag(a) S and the partial read over this thread's rows.
-    f32x4 vh = {0.f, 0.f, 0.f, 0.f};
+        // S- = diag(a) S and the partial read over this thread's rows.
+        f32x4 vh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const float a = sa[row0 + m];
-        const float ki = sk[row0 + m];
-        s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
-        vh.x += s[m].x * ki; vh.y += s[m].y * ki;
-        vh.z += s[m].z * ki; vh.w += s[m].w * ki;
-    }
-    red[rg][cg] = vh;
-    __syncthreads();
-    float ev[4];
-    {
-        f32x4 t = red[0][cg];
-#pragma unroll
-        for (int g = 1; g < RG; ++g) {
-            const f32x4 x = red[g][cg];
-            t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
+        for (int m = 0; m < RPT; ++m) {
+            const float a = sa[row0 + m];
+            const float ki = sk[row0 + m];
+            s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
+            vh.x += s[m].x * ki; vh.y += s[m].y * ki;
+            vh.z += s[m].z * ki; vh.w += s[m].w * ki;
         }
-        const TIn *v = static_cast<const TIn *>(P.v) + bh * DV + 4 * cg;
-        ev[0] = to_f32(v[0]) - t.x;
-        ev[1] = to_f32(v[1]) - t.y;
-        ev[2] = to_f32(v[2]) - t.z;
-        ev[3] = to_f32(v[3]) - t.w;
-    }
-    __syncthreads();   // red is reused below
+        red[rg][cg] = vh;
+        __syncthreads();
+        float ev[4];
+        {
+            f32x4 x0 = red[0][cg];
+#pragma unroll
+            for (int g = 1; g < RG; ++g) {
+                const f32x4 x = red[g][cg];
+                x0.x += x.x; x0.y += x.y; x0.z += x.z; x0.w += x.w;
+            }
+            ev[0] = in.v[0] - x0.x;
+            ev[1] = in.v[1] - x0.y;
+            ev[2] = in.v[2] - x0.z;
+            ev[3] = in.v[3] - x0.w;
+        }
+        __syncthreads();   // red is reused below
 
-    // Write S = S- + w e^T, partial output over this thread's rows.
-    f32x4 op = {0.f, 0.f, 0.f, 0.f};
+        // Write S = S- + w e^T, partial output over this thread's rows.
+        const bool last = t + 1 == T;
+        f32x4 op = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const float g = sg[row0 + m];
-        const float qi = sq[row0 + m];
-        s[m].x += g * ev[0]; s[m].y += g * ev[1];
-        s[m].z += g * ev[2]; s[m].w += g * ev[3];
-        op.x += s[m].x * qi; op.y += s[m].y * qi;
-        op.z += s[m].z * qi; op.w += s[m].w * qi;
-        __builtin_nontemporal_store(
-            s[m], reinterpret_cast<f32x4 *>(S + (long)(row0 + m) * DV) + cg);
-    }
-    red[rg][cg] = op;
-    __syncthreads();
-    if (tid < CG) {
-        f32x4 t = red[0][tid];
-#pragma unroll
-        for (int g = 1; g < RG; ++g) {
-            const f32x4 x = red[g][tid];
-            t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
+        for (int m = 0; m < RPT; ++m) {
+            const float g = sg[row0 + m];
+            const float qi = sq[row0 + m];
+            s[m].x += g * ev[0]; s[m].y += g * ev[1];
+            s[m].z += g * ev[2]; s[m].w += g * ev[3];
+            op.x += s[m].x * qi; op.y += s[m].y * qi;
+            op.z += s[m].z * qi; op.w += s[m].w * qi;
+            if (last)
+                __builtin_nontemporal_store(
+                    s[m], reinterpret_cast<f32x4 *>(S + (long)(row0 + m) * DV) + cg);
         }
-        TIn *o = static_cast<TIn *>(P.o) + bh * DV + 4 * tid;
-        o[0] = from_f32<TIn>(t.x);
-        o[1] = from_f32<TIn>(t.y);
-        o[2] = from_f32<TIn>(t.z);
-        o[3] = from_f32<TIn>(t.w);
+        red[rg][cg] = op;
+        __syncthreads();
+        if (tid < CG) {
+            f32x4 x0 = red[0][tid];
+#pragma unroll
+            for (int g = 1; g < RG; ++g) {
+                const f32x4 x = red[g][tid];
+                x0.x += x.x; x0.y += x.y; x0.z += x.z; x0.w += x.w;
+            }
+            TIn *o = static_cast<TIn *>(P.o) + row_of(t) * DV + 4 * tid;
+            o[0] = from_f32<TIn>(x0.x);
+            o[1] = from_f32<TIn>(x0.y);
+            o[2] = from_f32<TIn>(x0.z);
+            o[3] = from_f32<TIn>(x0.w);
+        }
+        if (MULTI)
+            in = nxt;
     }
+    if (MULTI && T == 0) {             // no token: the state passes through
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            __builtin_nontemporal_store(
+                s[m], reinterpret_cast<f32x4 *>(S + (long)(row0 + m) * DV) + cg);
+    }
+    if (VAR == DIAG_KDN && tid < DK)
+        P.p[bh * DK + tid] = pc;
 }
 
-template <typename TIn, int VAR>
+template <typename TIn, int VAR, bool MULTI>
 static hipError_t launch_decode_v(const DecodeParams &P, hipStream_t st) {
     constexpr int NT = KDN_DECODE_NT;
     const dim3 grid((unsigned)((long)P.N * P.H)), block(NT);
 #define KDN_DEC(DK_, DV_)                                                      \
     if (P.dk == DK_ && P.dv == DV_) {                                          \
-        hipLaunchKernelGGL((decode_kernel<TIn, VAR, DK_, DV_, NT>), grid,      \
+        hipLaunchKernelGGL((decode_kernel<TIn, VAR, DK_, DV_, NT, MULTI>), grid, \
                            block, 0, st, P);                                   \
         return hipGetLastError();                                              \
     }
@@ -184,13 +228,13 @@ static hipError_t launch_decode_v(const DecodeParams &P, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-template <typename TIn>
+template <typename TIn, bool MULTI>
 static hipError_t launch_decode_t(const DecodeParams &P, hipStream_t st) {
     switch (P.variant) {
-    case DELTANET: return launch_decode_v<TIn, DELTANET>(P, st);
-    case GATED_DELTANET: return launch_decode_v<TIn, GATED_DELTANET>(P, st);
-    case KDA: return launch_decode_v<TIn, KDA>(P, st);
-    case DIAG_KDN: return launch_decode_v<TIn, DIAG_KDN>(P, st);
+    case DELTANET: return launch_decode_v<TIn, DELTANET, MULTI>(P, st);
+    case GATED_DELTANET: return launch_decode_v<TIn, GATED_DELTANET, MULTI>(P, st);
+    case KDA: return launch_decode_v<TIn, KDA, MULTI>(P, st);
+    case DIAG_KDN: return launch_decode_v<TIn, DIAG_KDN, MULTI>(P, st);
     }
     return hipErrorInvalidValue;
 }
@@ -198,7 +242,13 @@ static hipError_t launch_decode_t(const DecodeParams &P, hipStream_t st) {
 hipError_t launch_decode(const DecodeParams &P, hipStream_t st) {
     if ((long)P.N * P.H == 0)
         return hipSuccess;
-    return P.bf16 ? launch_decode_t<bf16>(P, st) : launch_decode_t<float>(P, st);
+    return P.bf16 ? launch_decode_t<bf16, false>(P, st) : launch_decode_t<float, false>(P, st);
+}
+
+hipError_t launch_decode_multi(const DecodeParams &P, hipStream_t st) {
+    if ((long)P.N * P.H == 0)
+        return hipSuccess;
+    return P.bf16 ? launch_decode_t<bf16, true>(P, st) : launch_decode_t<float, true>(P, st);
 }
 
 }  // namespace kdn

@@ -10,11 +10,14 @@ struct DecodeParams {
     int variant;       // kdn_variant
     int bf16;          // 1: per-token tensors are bfloat16, 0: float32
     int N, H, dk, dv;
+    int T;             // tokens per (sequence, head): 1 for a decode step
     float mu;
-    const void *q, *k, *v, *alpha, *beta, *xi, *r;
-    float *S;          // [N, H, dk, dv], in place
-    float *p;          // [N, H, dk], in place (diagonal KDN)
-    void *o;           // [N, H, dv]
+    const void *q, *k, *v, *alpha, *beta, *xi, *r;   // [N, T, H, .]
+    const float *S0;   // [N, H, dk, dv] state read (NULL: zeros); may equal S
+    const float *p0;   // [N, H, dk] variance read (diagonal KDN); may equal p
+    float *S;          // [N, H, dk, dv] state written
+    float *p;          // [N, H, dk] variance written (diagonal KDN)
+    void *o;           // [N, T, H, dv]
 };
 
 struct PrefillParams {
@@ -38,6 +41,7 @@ struct PrefillParams {
 };
 
 hipError_t launch_decode(const DecodeParams &P, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeParams &P, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &P, hipStream_t stream);
 
 // Per-variant prefill launchers (one compilation unit each).

@@ -49,6 +49,8 @@ def load(path: str = LIB_PATH):
     lib.kdn_chunk_prefill_workspace_size.argtypes = [i] * 8 + [ctypes.POINTER(i)]
     lib.kdn_recurrent_decode.restype = i
     lib.kdn_recurrent_decode.argtypes = [i, i, i, i, i, i, f] + [vp] * 11
+    lib.kdn_recurrent_decode_multi.restype = i
+    lib.kdn_recurrent_decode_multi.argtypes = [i, i, i, i, i, i, i, f] + [vp] * 13
     lib.kdn_status_string.restype = ctypes.c_char_p
     lib.kdn_status_string.argtypes = [i]
     lib.kdn_chunk_prefill_chunk_size.restype = i
@@ -144,6 +146,19 @@ def kdn_recurrent_decode(variant, dtype, N, H, d_k, d_v, mu, q, k, v, alpha,
     _check(lib, st)
 
 
+def kdn_recurrent_decode_multi(variant, dtype, N, T, H, d_k, d_v, mu, q, k, v,
+                               alpha, beta, proc_noise, obs_noise, S0, p0, o,
+                               S_out, p_out, stream=None):
+    """Raw entry point: same arguments as the C function."""
+    lib = load()
+    st = lib.kdn_recurrent_decode_multi(
+        int(variant), int(dtype), int(N), int(T), int(H), int(d_k), int(d_v),
+        float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(proc_noise), _ptr(obs_noise), _ptr(S0), _ptr(p0), _ptr(o),
+        _ptr(S_out), _ptr(p_out), _stream(stream))
+    _check(lib, st)
+
+
 # ---------------------------------------------------------------------------
 # Tensor-shaped conveniences (allocate outputs, infer sizes, then call the
 # entry points above).
@@ -200,3 +215,26 @@ def decode(variant, q, k, v, S, p=None, alpha=None, beta=None, proc_noise=None,
     kdn_recurrent_decode(vid, DTYPES[q.dtype], N, H, dk, dv, mu, q, k, v, alpha,
                          beta, proc_noise, obs_noise, S, p, o, stream)
     return o
+
+
+def decode_multi(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
+                 obs_noise=None, S0=None, p0=None, mu=1.0, out=None, stream=None):
+    """T decode steps in one pass over the state (speculative verify).
+    q, k [N,T,H,dk], v [N,T,H,dv]; S0 [N,H,dk,dv] (None: zeros) and p0
+    [N,H,dk] are read, not modified, unless ``out`` passes them as S_out /
+    p_out (in place).  Returns (o [N,T,H,dv], S_out, p_out); p_out is None
+    unless variant is diag_kdn."""
+    vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        o = torch.empty((N, T, H, dv), dtype=q.dtype, device=q.device)
+        S = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+        p = (torch.empty((N, H, dk), dtype=torch.float32, device=q.device)
+             if vid == 3 else None)
+    else:
+        o, S, p = out
+    kdn_recurrent_decode_multi(vid, DTYPES[q.dtype], N, T, H, dk, dv, mu, q, k, v,
+                               alpha, beta, proc_noise, obs_noise, S0, p0, o, S, p,
+                               stream)
+    return o, S, p

@@ -35,6 +35,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kdn_chunk_prefill", "kdn_recurrent_decode", "kdn_status_string",
+              "kdn_recurrent_decode_multi",
               "kdn_chunk_prefill_chunk_size", "kdn_abi_version",
               "kdn_chunk_prefill_workspace_size"):
         assert n in names
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.kdn_abi_version() == 2
+    assert lib.kdn_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -208,6 +209,60 @@ DECODE_CASES = [
 @pytest.mark.parametrize("name,over,status", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
 def test_decode_validation(lib, name, over, status):
     assert lib.kdn_recurrent_decode(*_decode_args(**over)) == status
+
+
+def _multi_args(variant=3, dtype=1, N=8, T=4, H=4, dk=128, dv=128, **over):
+    kdn_ = variant == 3
+    a = dict(q=A, k=A + MB, v=A + 2 * MB,
+             alpha=None if variant == 0 else A + 3 * MB,
+             beta=None if kdn_ else A + 4 * MB,
+             xi=A + 5 * MB if kdn_ else None, r=A + 6 * MB if kdn_ else None,
+             S0=A + 7 * MB, p0=A + 8 * MB if kdn_ else None, o=A + 9 * MB,
+             S_out=A + 10 * MB, p_out=A + 11 * MB if kdn_ else None)
+    a.update(over)
+    return (variant, dtype, N, T, H, dk, dv, 1.0, a["q"], a["k"], a["v"], a["alpha"],
+            a["beta"], a["xi"], a["r"], a["S0"], a["p0"], a["o"], a["S_out"],
+            a["p_out"], None)
+
+
+MULTI_CASES = [
+    ("bad variant", dict(variant=9), EUNSUP),
+    ("bad dtype", dict(dtype=3), EUNSUP),
+    ("negative T", dict(T=-1), ESHAPE),
+    ("negative N", dict(N=-2), ESHAPE),
+    ("d_v 96", dict(dv=96), EUNSUP),
+    ("state too large", dict(N=1 << 14, H=1 << 4), ESHAPE),
+    ("q NULL", dict(q=None), ENULL),
+    ("S_out NULL", dict(S_out=None), ENULL),
+    ("KDN without p0", dict(p0=None), ENULL),
+    ("KDN without p_out", dict(p_out=None), ENULL),
+    ("GDN with p0", dict(variant=1, p0=A + 8 * MB, p_out=None), ENULL),
+    ("KDN with beta", dict(beta=A + 4 * MB), ENULL),
+    ("misaligned k", dict(k=A + MB + 4), EALIGN),
+    ("misaligned S_out", dict(S_out=A + 10 * MB + 8), EALIGN),
+    ("odd scalar r", dict(r=A + 6 * MB + 1), EALIGN),
+    ("o overlaps q", dict(o=A + 32), EALIAS),
+    ("S_out partially overlaps S0", dict(S_out=A + 7 * MB + 1024), EALIAS),
+    ("S_out overlaps v", dict(S_out=A + 2 * MB), EALIAS),
+    ("p_out partially overlaps p0", dict(p_out=A + 8 * MB + 16), EALIAS),
+    ("p_out overlaps S0", dict(p_out=A + 7 * MB + 64), EALIAS),
+    ("o overlaps p_out", dict(o=A + 11 * MB), EALIAS),
+]
+
+
+@pytest.mark.parametrize("name,over,status", MULTI_CASES, ids=[c[0] for c in MULTI_CASES])
+def test_decode_multi_validation(lib, name, over, status):
+    assert lib.kdn_recurrent_decode_multi(*_multi_args(**over)) == status
+
+
+def test_decode_multi_accepts_in_place_and_empty(lib):
+    # in place (S_out == S0, p_out == p0) and empty sizes pass validation; with
+    # N = 0 or H = 0 nothing is launched, so the fake pointers are never used
+    assert lib.kdn_recurrent_decode_multi(
+        *_multi_args(N=0, S_out=A + 7 * MB, p_out=A + 8 * MB)) == OK
+    assert lib.kdn_recurrent_decode_multi(*_multi_args(H=0, T=0)) == OK
+    assert lib.kdn_recurrent_decode_multi(
+        *_multi_args(N=0, q=None, k=None, v=None, o=None, S0=None)) == OK
 
 
 def test_binding_raises_with_status(lib):
