@@ -9,8 +9,8 @@ resident in HBM.  Rank 0 prints ONE JSON line with the headline value
 (prefill tokens/s), the roofline of the prefill kernel (HBM-bound by its
 algorithmic bytes; the MFMA fraction of its algorithmic flops is reported
 next to it), the fp64 oracle timed on the host cores, and the other
-workloads (KDA and diagonal-KDN prefill, diagonal-KDN decode) each with its
-own roofline.
+workloads (KDA and diagonal-KDN prefill, diagonal-KDN decode, 16-token
+multi-token decode) each with its own roofline.
 """
 from __future__ import annotations
 
@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s + decode steps/s per head-state; % MFMA / % HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_variance.hip",
                   "kdn_decode.hip", "kdn_device.h", "kdn_launch.h", "kdn_workspace.h"]
 
@@ -67,6 +68,20 @@ def decode_bytes(N, H, dk, dv, es):
     nh = N * H
     return (nh * dk * dv * 4 * 2 + nh * dk * 4 * 2 + nh * 4 * dk * es
             + nh * dv * es + nh * es + nh * dv * es)
+
+
+def verify_bytes(N, T, H, dk, dv, es):
+    """Multi-token decode of T tokens (diagonal KDN): S and p read and written
+    once; per token q, k, alpha, xi [dk], v [dv], r read and o [dv] written."""
+    nh = N * H
+    return (nh * dk * dv * 4 * 2 + nh * dk * 4 * 2
+            + T * (nh * 4 * dk * es + nh * dv * es + nh * es + nh * dv * es))
+
+
+def decode_flops_per_head_token(dk, dv):
+    # decay (dk dv), read S^T k (2 dk dv), write w e^T (2 dk dv), output S^T q
+    # (2 dk dv); the gain's O(dk) terms are left out
+    return 7 * dk * dv
 
 
 def load_traffic(kernel):
@@ -183,6 +198,49 @@ def bench_decode(name, reps, torch, kdn, synth):
     return res
 
 
+def bench_verify(T, reps, torch, kdn, synth):
+    """T draft tokens per sequence checked against the resident state in one
+    multi-token decode call, at the decode workload's size."""
+    name = "decode_diag_kdn"
+    c = synth.CONFIGS[name]
+    N, H, dk, dv = c["N"], c["H"], c["dk"], c["dv"]
+    inp = synth.gen_prefill("diag_kdn", N, T, H, dk, dv, c["dtype"],
+                            seed=synth.seed_of(name) + 100, device="cuda",
+                            random_state=True)
+    o = torch.empty((N, T, H, dv), dtype=inp["q"].dtype, device="cuda")
+    S = torch.empty_like(inp["S0"])
+    p = torch.empty_like(inp["p0"])
+
+    def step():
+        kdn.decode_multi("diag_kdn", inp["q"], inp["k"], inp["v"], alpha=inp["alpha"],
+                         proc_noise=inp["xi"], obs_noise=inp["r"], S0=inp["S0"],
+                         p0=inp["p0"], out=(o, S, p))
+
+    wall, gpu = time_launches(step, reps, 3, torch)
+    es = 2 if c["dtype"] == "bf16" else 4
+    nbytes = verify_bytes(N, T, H, dk, dv, es)
+    flops = decode_flops_per_head_token(dk, dv) * N * H * T
+    launch_s = gpu / reps
+    res = {
+        "value": N * T * reps / wall, "unit": "tokens/s",
+        "head_tokens_per_s": N * H * T * reps / wall,
+        "ms_per_step": wall / reps * 1e3,
+        "config": {"workload": f"verify{T}_diag_kdn", "variant": "diag_kdn", "N": N,
+                   "T": T, "H": H, "d_k": dk, "d_v": dv, "dtype": c["dtype"]},
+        "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": load_traffic(f"verify{T}_diag_kdn"),
+                     "algorithmic_bytes": nbytes, "kernel_ms": launch_s * 1e3},
+        "alu": {"achieved": flops / launch_s / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": flops / launch_s / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                "algorithmic_flops": flops},
+    }
+    del inp, o, S, p
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, synth, budget_s=20.0):
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
     whole-length (batch, head) streams, as many as fit the time budget."""
@@ -285,6 +343,7 @@ def main():
                                                  args.warmup, torch, kdn, synth,
                                                  args.schedule)
         w["decode_diag_kdn"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
+        w["verify16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth)
         out["workloads"] = w
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline("gated_deltanet", synth)
