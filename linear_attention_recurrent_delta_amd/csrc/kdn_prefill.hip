@@ -838,11 +838,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
             if constexpr (SPREP) {
-                // W~^T (strided reads of K) follows on waves 4-7, below
                 store_frag_fn<E, C, DK, 256>(rec + LW.off_kd, tid, [&](int t, int i) {
                     return ld(Kt + t * PK + i) * s_gt[t]; });
                 store_frag_fn<E, C, DK, 256>(rec + LW.off_qd, tid, [&](int t, int i) {
                     return ld(Qt + t * PK + i) * s_gt[t]; });
+                // W~^T (strided reads of K): half here, half on waves 4-7 below
+                store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, [&](int i, int t) {
+                    return ld(Kt + t * PK + i) * s_wsc[t]; });
             } else {
                 store_frag<E, C, DK, 256>(rec + LW.off_kd, Kt, PK, tid);
                 store_frag<E, C, DK, 256>(rec + LW.off_qd, Qt, PK, tid);
@@ -940,11 +942,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             }
         }
         if (SPREP && wv >= 4) {
-            // scalar-decay record W~^T[i][t] = beta_t gamma_C / gamma_t k_ti,
-            // after this wave's diagonal block
+            // scalar-decay record W~^T[i][t] = beta_t gamma_C / gamma_t k_ti:
+            // the other half of its units, after this wave's diagonal block
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
-            store_frag_fn<E, DK, C, 256>(rec + LW.off_wdt, tid - 256, [&](int i, int t) {
+            store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, [&](int i, int t) {
                 return ld(Kt + t * PK + i) * s_wsc[t]; });
         }
         __syncthreads();
