@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the gated delta-rule / diagonal-Kalman recurrence.
+"""fp64 CPU oracle of the gated delta-rule / Kalman (diagonal and isotropic) recurrence.
 
 TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` are the only callers.  The HIP library and its
@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kdn_oracle.c")
 _LIB = os.path.join(_HERE, "libkdn_oracle.so")
 
-VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "diag_kdn": 3}
+VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "diag_kdn": 3, "iso_kdn": 4}
 
 _default = None
 
@@ -96,7 +96,7 @@ def recurrence(variant, q, k, v, alpha=None, beta=None, xi=None, r=None,
     """Run the recurrence over [B, T, H, d] inputs.
 
     Returns ``(o, S, p)``: o [B,T,H,dv], final S [B,H,dk,dv], final p [B,H,dk]
-    (p is None unless the variant is diagonal KDN).  Every input is converted
+    for diagonal KDN, [B,H] for isotropic KDN, else None.  Every input is converted
     to float64 first; values that were rounded to a device dtype upstream keep
     exactly that rounding.
     """
@@ -114,22 +114,24 @@ def _run(lib, variant, q, k, v, alpha, beta, xi, r, S0, p0, mu, nthreads):
     v = _f64(v, (B, T, H, dv), "v")
     if vid == 1:
         alpha = _f64(alpha, (B, T, H), "alpha")
-    elif vid in (2, 3):
+    elif vid in (2, 3, 4):
         alpha = _f64(alpha, (B, T, H, dk), "alpha")
     else:
         alpha = None
-    beta = _f64(beta, (B, T, H), "beta") if vid != 3 else None
-    if vid == 3:
+    kdn = vid in (3, 4)
+    pshape = (B, H, dk) if vid == 3 else (B, H)
+    beta = _f64(beta, (B, T, H), "beta") if not kdn else None
+    if kdn:
         xi = _f64(xi, (B, T, H, dk), "xi")
         r = _f64(r, (B, T, H), "r")
-        p0 = _f64(p0, (B, H, dk), "p0")
+        p0 = _f64(p0, pshape, "p0")
     else:
         xi = r = p0 = None
     S0 = _f64(S0, (B, H, dk, dv), "S0") if S0 is not None else None
 
     o = np.zeros((B, T, H, dv), dtype=np.float64)
     S = np.zeros((B, H, dk, dv), dtype=np.float64)
-    p = np.zeros((B, H, dk), dtype=np.float64) if vid == 3 else None
+    p = np.zeros(pshape, dtype=np.float64) if kdn else None
     rc = lib.kdn_oracle_recurrence(
         vid, B, T, H, dk, dv, float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
         _ptr(beta), _ptr(xi), _ptr(r), _ptr(S0), _ptr(p0), _ptr(o), _ptr(S),

@@ -28,9 +28,15 @@
  *         section "对角近似：把矩阵压扁成一个向量" (diagonal covariance,
  *         per-channel update, mean-field projection whose mean is exact,
  *         information scaling mu of the precision increment).
+ *         Isotropic KDN: section "各向同性近似：把整个头压缩成一个数" (one
+ *         uncertainty scalar per head; the delta-rule form is kept and its
+ *         scalar write strength is derived from the accumulated uncertainty
+ *         and the observation reliability; otherwise shaped like KDA; the
+ *         variance recursion is a Mobius map).
  *   [AFS] "Kalman Delta Networks: Uncertainty-aware Associative Memory"
  *         (explainer): section "Approximation 1: Diagonal KDN (Mean-Field
- *         Variational Inference)".
+ *         Variational Inference)" and section "Approximation 2: Isotropic
+ *         KDN (Single Scalar Uncertainty)".
  *
  * Readings of points the pages leave open (each is argued in the design
  * notes of the repository):
@@ -45,15 +51,25 @@
  *     update, never the current write.
  *   - Degenerate values: s == 0 gives w = 0; r + mu p-_i k_i^2 == 0 leaves
  *     p_i = p-_i.
+ *   - Isotropic KDN (covariance p I): the predict p I -> diag(a^2) p +
+ *     diag(xi) is brought back to a multiple of I by the mean of its
+ *     diagonal, p- = mean(a^2) p + mean(xi); the gain is exact under p- I,
+ *     w = p- k / s with s = r + p- |k|^2 (write strength p- / s times k);
+ *     the posterior precision I / p- + k k^T / r is brought back to a
+ *     multiple of I by the mean of its diagonal, scaled by mu like the
+ *     diagonal variant: 1/p = 1/p- + mu |k|^2 / (d_k r), i.e.
+ *     p <- p- r / (r + (mu / d_k) p- |k|^2).  Degenerate values as above.
  *
  * Layouts (row-major, contiguous):
  *   q, k            [B, T, H, dk]       v, o        [B, T, H, dv]
  *   alpha           GDN: [B, T, H]      KDA/KDN:    [B, T, H, dk]
  *   beta            [B, T, H]           (not KDN)
  *   xi (proc noise) [B, T, H, dk]       r (obs noise) [B, T, H]   (KDN only)
- *   S0, S           [B, H, dk, dv]      p0, p       [B, H, dk]
+ *   S0, S           [B, H, dk, dv]      p0, p       [B, H, dk] (isotropic: [B, H])
+ *   xi and r as for diagonal KDN for the isotropic variant too.
  *
- * Variant codes: 0 DeltaNet, 1 Gated DeltaNet, 2 KDA, 3 diagonal KDN.
+ * Variant codes: 0 DeltaNet, 1 Gated DeltaNet, 2 KDA, 3 diagonal KDN,
+ * 4 isotropic KDN.
  */
 #include <stdlib.h>
 #include <string.h>
@@ -62,10 +78,11 @@
 #include <omp.h>
 #endif
 
-enum { ORC_DELTANET = 0, ORC_GATED_DELTANET = 1, ORC_KDA = 2, ORC_DIAG_KDN = 3 };
+enum { ORC_DELTANET = 0, ORC_GATED_DELTANET = 1, ORC_KDA = 2, ORC_DIAG_KDN = 3,
+       ORC_ISO_KDN = 4 };
 
-/* One (batch, head) stream, tokens 0..T-1.  S (dk x dv) and p (dk) are the
- * running state and are updated in place. */
+/* One (batch, head) stream, tokens 0..T-1.  S (dk x dv) and p (dk; one value
+ * for isotropic KDN) are the running state and are updated in place. */
 static void run_stream(int variant, long T, long H, long dk, long dv, double mu,
                        const double *q, const double *k, const double *v,
                        const double *alpha, const double *beta,
@@ -112,6 +129,27 @@ static void run_stream(int variant, long T, long H, long dk, long dv, double mu,
                 const double den = rt + mu * pm[i] * kt[i] * kt[i];
                 p[i] = (den != 0.0) ? pm[i] * rt / den : pm[i];
             }
+        } else if (variant == ORC_ISO_KDN) {
+            /* One variance for the whole head ([KDN] isotropic section):
+             * predict, brought back to a multiple of the identity by the mean
+             * of the diagonal. */
+            double a2 = 0.0, xm = 0.0, kk = 0.0;
+            for (long i = 0; i < dk; ++i) {
+                a2 += a[i] * a[i];
+                xm += xi[tok * dk + i];
+                kk += kt[i] * kt[i];
+            }
+            const double pmi = (a2 / (double)dk) * p[0] + xm / (double)dk;
+            /* Exact gain under the isotropic prior: the delta rule with the
+             * write strength pmi / s derived from the uncertainty and the
+             * observation reliability. */
+            const double rt = r[tok];
+            const double s = rt + pmi * kk;
+            for (long i = 0; i < dk; ++i)
+                w[i] = (s != 0.0) ? pmi * kt[i] / s : 0.0;
+            /* Precision gain averaged over the key channels, scaled by mu. */
+            const double den = rt + (mu / (double)dk) * pmi * kk;
+            p[0] = (den != 0.0) ? pmi * rt / den : pmi;
         } else {
             /* Delta rule write strength beta ([TAB] correct step). */
             const double bt = beta[tok];
@@ -160,7 +198,7 @@ int kdn_oracle_recurrence(int variant, long B, long T, long H, long dk, long dv,
                           const double *S0, const double *p0,
                           double *o, double *S, double *p, int nthreads)
 {
-    if (variant < ORC_DELTANET || variant > ORC_DIAG_KDN)
+    if (variant < ORC_DELTANET || variant > ORC_ISO_KDN)
         return -1;
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
         return -2;
@@ -168,9 +206,11 @@ int kdn_oracle_recurrence(int variant, long B, long T, long H, long dk, long dv,
         return -3;
     if (variant != ORC_DELTANET && !alpha)
         return -4;
-    if (variant != ORC_DIAG_KDN && !beta)
+    const int kdn = variant == ORC_DIAG_KDN || variant == ORC_ISO_KDN;
+    const long np = variant == ORC_DIAG_KDN ? dk : 1;   /* variances per stream */
+    if (!kdn && !beta)
         return -5;
-    if (variant == ORC_DIAG_KDN && (!xi || !r || !p0 || !p))
+    if (kdn && (!xi || !r || !p0 || !p))
         return -6;
 
     const long BH = B * H;
@@ -183,15 +223,15 @@ int kdn_oracle_recurrence(int variant, long B, long T, long H, long dk, long dv,
     for (long bh = 0; bh < BH; ++bh) {
         const long b = bh / H, h = bh % H;
         double *Sb = S + bh * dk * dv;
-        double *pb = (variant == ORC_DIAG_KDN) ? p + bh * dk : NULL;
+        double *pb = kdn ? p + bh * np : NULL;
         if (S0) {
             if (S0 + bh * dk * dv != Sb)
                 memcpy(Sb, S0 + bh * dk * dv, sizeof(double) * dk * dv);
         } else {
             memset(Sb, 0, sizeof(double) * dk * dv);
         }
-        if (pb && p0 + bh * dk != pb)
-            memcpy(pb, p0 + bh * dk, sizeof(double) * dk);
+        if (pb && p0 + bh * np != pb)
+            memcpy(pb, p0 + bh * np, sizeof(double) * np);
 
         double *scratch = (double *)malloc(sizeof(double) * (3 * dk + dv));
         if (!scratch) {

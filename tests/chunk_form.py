@@ -14,7 +14,8 @@ recurrence exactly).  Derivation, per chunk starting from state S0:
 
 with D_tsi = prod_{s<r<=t} a_ri, gamma_t = prod_{r<=t} a_r, K~ = gamma (.) K,
 Q~ = gamma (.) Q, W~_s = D_{C,s} (.) w_s.  The diagonal-KDN write vectors come
-from the per-channel variance recursion, which does not depend on S.
+from the per-channel variance recursion, the isotropic-KDN ones from the
+per-head scalar recursion; neither depends on S.
 """
 from __future__ import annotations
 
@@ -30,11 +31,13 @@ def chunk_form(variant, q, k, v, alpha=None, beta=None, xi=None, r=None,
     dv = v.shape[-1]
     o = np.zeros((B, T, H, dv))
     Sout = np.zeros((B, H, dk, dv))
-    pout = np.zeros((B, H, dk)) if variant == "diag_kdn" else None
+    pout = (np.zeros((B, H, dk)) if variant == "diag_kdn" else
+            np.zeros((B, H)) if variant == "iso_kdn" else None)
     for b in range(B):
         for h in range(H):
             S = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], np.float64)
-            p = np.array(p0[b, h], np.float64) if variant == "diag_kdn" else None
+            p = (np.array(p0[b, h], np.float64) if variant in ("diag_kdn", "iso_kdn")
+                 else None)
             for c0 in range(0, T, C):
                 L = min(C, T - c0)
                 sl = slice(c0, c0 + L)
@@ -55,6 +58,15 @@ def chunk_form(variant, q, k, v, alpha=None, beta=None, xi=None, r=None,
                         W[t] = pm * K[t] / s if s != 0 else 0.0
                         den = rt + mu * pm * K[t] ** 2
                         p = np.where(den != 0, pm * rt / np.where(den != 0, den, 1), pm)
+                elif variant == "iso_kdn":
+                    for t in range(L):
+                        pm = np.mean(a[t] ** 2) * p + np.mean(xi[b, c0 + t, h])
+                        rt = float(r[b, c0 + t, h])
+                        kk = float(K[t] @ K[t])
+                        s = rt + pm * kk
+                        W[t] = pm * K[t] / s if s != 0 else 0.0
+                        den = rt + mu / dk * pm * kk
+                        p = pm * rt / den if den != 0 else pm
                 else:
                     W = np.asarray(beta[b, sl, h], np.float64)[:, None] * K
                 # pairwise decay D[t, s] = prod_{s < r <= t} a_r  (s <= t)

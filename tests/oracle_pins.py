@@ -46,15 +46,16 @@ def _random_inputs(variant, B, T, H, dk, dv, seed, s0=True, kdn_p0=None):
                v=g.standard_normal((B, T, H, dv)))
     if variant == "gated_deltanet":
         inp["alpha"] = g.uniform(0.3, 1.0, (B, T, H))
-    elif variant in ("kda", "diag_kdn"):
+    elif variant in ("kda", "diag_kdn", "iso_kdn"):
         inp["alpha"] = g.uniform(0.3, 1.0, (B, T, H, dk))
-    if variant != "diag_kdn":
+    if variant not in ("diag_kdn", "iso_kdn"):
         inp["beta"] = g.uniform(0.05, 1.0, (B, T, H))
     else:
+        pshape = (B, H, dk) if variant == "diag_kdn" else (B, H)
         inp["xi"] = g.uniform(0.0, 0.2, (B, T, H, dk))
         inp["r"] = g.uniform(0.2, 2.0, (B, T, H))
-        inp["p0"] = (g.uniform(0.3, 2.0, (B, H, dk)) if kdn_p0 is None
-                     else np.full((B, H, dk), kdn_p0))
+        inp["p0"] = (g.uniform(0.3, 2.0, pshape) if kdn_p0 is None
+                     else np.full(pshape, kdn_p0))
     if s0:
         inp["S0"] = 0.5 * g.standard_normal((B, H, dk, dv))
     return inp
@@ -164,15 +165,15 @@ def pin_alpha_zero_erases(rec):
 # Chunked == serial ([KDA] "حل مشکل وابستگی علی").
 # ---------------------------------------------------------------------------
 def pin_chunk_form(rec):
-    for variant in ("deltanet", "gated_deltanet", "kda", "diag_kdn"):
+    for variant in ("deltanet", "gated_deltanet", "kda", "diag_kdn", "iso_kdn"):
         for T, C in ((24, 8), (21, 8), (5, 8)):
             inp = _random_inputs(variant, 2, T, 2, 8, 6, seed=10 + T)
-            mu = 3.0 if variant == "diag_kdn" else 1.0
+            mu = 3.0 if variant in ("diag_kdn", "iso_kdn") else 1.0
             o1, S1, p1 = rec(variant, mu=mu, **inp)
             o2, S2, p2 = chunk_form(variant, mu=mu, C=C, **inp)
             np.testing.assert_allclose(o1, o2, atol=1e-11, rtol=1e-11)
             np.testing.assert_allclose(S1, S2, atol=1e-11, rtol=1e-11)
-            if variant == "diag_kdn":
+            if p1 is not None:
                 np.testing.assert_allclose(p1, p2, atol=1e-13, rtol=1e-12)
 
 
@@ -394,6 +395,188 @@ def pin_kdn_degenerate_noise(rec):
 
 
 # ---------------------------------------------------------------------------
+# Isotropic KDN: one variance per head ([KDN] "各向同性近似"; [AFS]
+# "Approximation 2: Isotropic KDN").  The reference below is the dense Kalman
+# filter of the filtering section, with its covariance brought back to a
+# multiple of the identity after the predict (mean of the covariance
+# diagonal) and after the update (mean of the precision diagonal, its
+# increment scaled by mu as in the diagonal variant).  It works on d x d
+# matrices, inverses and traces, not on the oracle's scalar arithmetic.
+# ---------------------------------------------------------------------------
+def _iso_case(T, d, seed, key_norms=False):
+    c = _kdn_case(T=T, d=d, seed=seed, onehot=False)
+    g = _rng(seed + 1000)
+    if key_norms:
+        c["k"] = c["k"] * g.uniform(0.3, 2.0, (T, 1))
+    c["p0"] = np.array(g.uniform(0.2, 2.0))
+    return c
+
+
+def _iso_rec(rec, c, mu=1.0, T=None):
+    T = c["k"].shape[0] if T is None else T
+    sl = slice(0, T)
+    o, S, p = rec("iso_kdn", c["q"][None, sl, None], c["k"][None, sl, None],
+                  c["v"][None, sl, None], alpha=c["a"][None, sl, None],
+                  xi=c["xi"][None, sl, None], r=c["r"][None, sl, None],
+                  S0=c["S0"][None, None], p0=np.reshape(c["p0"], (1, 1)), mu=mu)
+    return o[0, :, 0], S[0, 0], p[0, 0]
+
+
+def _projected_kalman(c, mu):
+    """Dense Kalman filter with isotropic projections; returns the memory, the
+    outputs, the final variance and the per-token predicted variances."""
+    S = np.array(c["S0"], np.float64)
+    d = S.shape[0]
+    eye = np.eye(d)
+    P = float(c["p0"]) * eye
+    outs, pms = [], []
+    for t in range(c["k"].shape[0]):
+        D = np.diag(c["a"][t])
+        k = c["k"][t]
+        S = D @ S
+        Pm = D @ P @ D + np.diag(c["xi"][t])
+        Pm = np.trace(Pm) / d * eye
+        pms.append(Pm[0, 0])
+        g = Pm @ k / (k @ Pm @ k + c["r"][t])
+        S = S + np.outer(g, c["v"][t] - S.T @ k)
+        prior = np.linalg.inv(Pm)
+        post = prior + np.outer(k, k) / c["r"][t]
+        lam = np.trace(prior) / d + mu * (np.trace(post) - np.trace(prior)) / d
+        P = eye / lam
+        outs.append(S.T @ c["q"][t])
+    return S, np.array(outs), P[0, 0], np.array(pms)
+
+
+def pin_iso_kdn_is_projected_dense_kalman(rec):
+    for mu in (1.0, 2.5):
+        c = _iso_case(T=20, d=6, seed=60, key_norms=True)
+        o, S, p = _iso_rec(rec, c, mu=mu)
+        S_ref, o_ref, p_ref, _ = _projected_kalman(c, mu)
+        np.testing.assert_allclose(S, S_ref, atol=1e-11, rtol=1e-11)
+        np.testing.assert_allclose(o, o_ref, atol=1e-11, rtol=1e-11)
+        np.testing.assert_allclose(p, p_ref, rtol=1e-12)
+
+
+def pin_iso_kdn_is_kda_with_derived_beta(rec):
+    """The isotropic variant keeps the delta-rule form: it is KDA with the
+    write strength p-/(r + p- |k|^2) taken from the uncertainty recursion."""
+    c = _iso_case(T=18, d=5, seed=61, key_norms=True)
+    o, S, _ = _iso_rec(rec, c, mu=1.7)
+    _, _, _, pms = _projected_kalman(c, 1.7)
+    kk = np.sum(c["k"] ** 2, axis=1)
+    beta = pms / (c["r"] + pms * kk)
+    o2, S2, _ = rec("kda", c["q"][None, :, None], c["k"][None, :, None],
+                    c["v"][None, :, None], alpha=c["a"][None, :, None],
+                    beta=beta[None, :, None], S0=c["S0"][None, None])
+    np.testing.assert_allclose(o, o2[0, :, 0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, S2[0, 0], rtol=1e-12, atol=1e-13)
+
+
+def pin_iso_kdn_first_step_matches_diag(rec):
+    """From p0 = c 1, with one decay and one process noise for every channel,
+    the first isotropic step writes exactly what the diagonal one writes, and
+    its precision is the mean of the diagonal variant's channel precisions."""
+    d = 7
+    for mu in (1.0, 5.0):
+        c = _iso_case(T=1, d=d, seed=62, key_norms=True)
+        c["a"][:] = 0.8
+        c["xi"][:] = 0.15
+        o, S, p = _iso_rec(rec, c, mu=mu)
+        cd = dict(c)
+        cd["p0"] = np.full(d, float(c["p0"]))
+        od, Sd, pd = _kdn_rec(rec, cd, mu=mu)
+        np.testing.assert_allclose(o, od, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(S, Sd, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(1.0 / p, np.mean(1.0 / pd), rtol=1e-13)
+
+
+def pin_iso_kdn_single_channel_is_diag(rec):
+    """With d_k = 1 the two approximations coincide for every token."""
+    c = _kdn_case(T=15, d=1, seed=63, onehot=False)
+    c["k"] = _rng(64).uniform(-2.0, 2.0, (15, 1))
+    for mu in (1.0, 3.0):
+        o, S, p = _kdn_rec(rec, c, mu=mu)
+        ci = dict(c)
+        ci["p0"] = np.array(c["p0"][0])
+        oi, Si, pi = _iso_rec(rec, ci, mu=mu)
+        np.testing.assert_allclose(oi, o, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(Si, S, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(pi, p[0], rtol=1e-13)
+
+
+def pin_iso_kdn_closed_form(rec):
+    """alpha = 1, xi = 0: every token adds mu |k|^2 / (d_k r) to the precision,
+    so 1/p_n = 1/p0 + (mu / d_k) sum_j |k_j|^2 / r_j."""
+    d, n = 6, 9
+    c = _iso_case(T=n, d=d, seed=65, key_norms=True)
+    c["a"][:] = 1.0
+    c["xi"][:] = 0.0
+    kk = np.sum(c["k"] ** 2, axis=1)
+    for mu in (1.0, 4.0):
+        _, _, p = _iso_rec(rec, c, mu=mu)
+        ref = 1.0 / (1.0 / float(c["p0"]) + mu / d * np.sum(kk / c["r"]))
+        np.testing.assert_allclose(p, ref, rtol=1e-13)
+
+
+def pin_iso_kdn_mobius(rec):
+    """The head variance follows the 2x2 Moebius product with mean(a^2),
+    mean(xi) and c = mu |k|^2 / (d_k r) ([KDN] "各向同性近似", last paragraph)."""
+    T, d = 40, 6
+    c = _iso_case(T=T, d=d, seed=66, key_norms=True)
+    for mu in (1.0, 6.0):
+        _, _, p = _iso_rec(rec, c, mu=mu)
+        M = np.eye(2)
+        for t in range(T):
+            a2 = np.mean(c["a"][t] ** 2)
+            xi = np.mean(c["xi"][t])
+            cc = mu * np.sum(c["k"][t] ** 2) / (d * c["r"][t])
+            M = np.array([[a2, xi], [cc * a2, 1.0 + cc * xi]]) @ M
+            M /= np.abs(M).max()
+        num, den = M @ np.array([float(c["p0"]), 1.0])
+        np.testing.assert_allclose(p, num / den, rtol=1e-12)
+
+
+def pin_iso_kdn_gain_range_and_degenerate(rec):
+    """0 <= k^T w < 1 for r > 0; alpha = 1, xi = 0 never grows the variance;
+    r = 0 with k != 0 replaces the value along k exactly and drops the
+    variance to 0; r = 0 with k = 0 writes nothing and only predicts."""
+    g = _rng(67)
+    d = 6
+    for trial in range(20):
+        k = _unit(g.standard_normal(d)) * g.uniform(0.2, 3.0)
+        v = np.zeros(d)
+        v[0] = 1.0
+        o, _, _ = rec("iso_kdn", k[None, None, None], k[None, None, None],
+                      v[None, None, None], alpha=g.uniform(0, 1, (1, 1, 1, d)),
+                      xi=g.uniform(0, 1, (1, 1, 1, d)),
+                      r=np.full((1, 1, 1), g.uniform(0.01, 3)),
+                      p0=np.full((1, 1), g.uniform(0.0, 5.0)))
+        assert 0.0 <= o[0, 0, 0, 0] < 1.0
+    c = _iso_case(T=25, d=d, seed=68)
+    c["a"][:] = 1.0
+    c["xi"][:] = 0.0
+    prev = float(c["p0"])
+    for T in range(1, 26):
+        _, _, p = _iso_rec(rec, c, T=T)
+        assert p < prev
+        prev = p
+    k = np.array([0.0, 2.0, 0.0, -1.0])[None, None, None]
+    v = np.arange(1.0, 5.0)[None, None, None]
+    S0 = _rng(69).standard_normal((1, 1, 4, 4))
+    o, S, p = rec("iso_kdn", k, k, v, alpha=np.full((1, 1, 1, 4), 0.5),
+                  xi=np.full((1, 1, 1, 4), 0.1), r=np.zeros((1, 1, 1)), S0=S0,
+                  p0=np.ones((1, 1)))
+    np.testing.assert_allclose(S[0, 0].T @ k[0, 0, 0], v[0, 0, 0], rtol=1e-14)
+    assert p[0, 0] == 0.0
+    z = np.zeros((1, 1, 1, 4))
+    o, S, p = rec("iso_kdn", z, z, v, alpha=np.full((1, 1, 1, 4), 0.5),
+                  xi=np.full((1, 1, 1, 4), 0.1), r=np.zeros((1, 1, 1)), S0=S0,
+                  p0=np.ones((1, 1)))
+    np.testing.assert_allclose(S[0, 0], 0.5 * S0[0, 0], rtol=0)
+    np.testing.assert_allclose(p[0, 0], 0.25 + 0.1, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
 # Brute force: each token as a dense affine map on vec(S) ([TAB] gated state
 # and delta steps; [KDA] decay before the delta write).
 # ---------------------------------------------------------------------------
@@ -444,14 +627,14 @@ def pin_brute_affine(rec):
 # Resume from a state: the state (S, p) is the whole memory.
 # ---------------------------------------------------------------------------
 def pin_continuation(rec):
-    for variant in ("gated_deltanet", "diag_kdn"):
+    for variant in ("gated_deltanet", "diag_kdn", "iso_kdn"):
         inp = _random_inputs(variant, 2, 30, 2, 5, 4, seed=50)
         o, S, p = rec(variant, mu=1.5, **inp)
         a = {k_: (v_[:, :11] if k_ not in ("S0", "p0") else v_) for k_, v_ in inp.items()}
         o1, S1, p1 = rec(variant, mu=1.5, **a)
         b = {k_: v_[:, 11:] for k_, v_ in inp.items() if k_ not in ("S0", "p0")}
         b["S0"] = S1
-        if variant == "diag_kdn":
+        if p1 is not None:
             b["p0"] = p1
         o2, S2, p2 = rec(variant, mu=1.5, **b)
         np.testing.assert_allclose(np.concatenate([o1, o2], axis=1), o, rtol=1e-13,
@@ -462,11 +645,12 @@ def pin_continuation(rec):
 
 
 def pin_empty_sequence(rec):
-    inp = _random_inputs("diag_kdn", 2, 0, 3, 4, 5, seed=51)
-    o, S, p = rec("diag_kdn", **inp)
-    assert o.shape == (2, 0, 3, 5)
-    np.testing.assert_array_equal(S, inp["S0"])
-    np.testing.assert_array_equal(p, inp["p0"])
+    for variant in ("diag_kdn", "iso_kdn"):
+        inp = _random_inputs(variant, 2, 0, 3, 4, 5, seed=51)
+        o, S, p = rec(variant, **inp)
+        assert o.shape == (2, 0, 3, 5)
+        np.testing.assert_array_equal(S, inp["S0"])
+        np.testing.assert_array_equal(p, inp["p0"])
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

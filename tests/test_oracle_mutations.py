@@ -83,6 +83,27 @@ MUTANTS = {
     "no_decay_scalar_gate": _sub("a[i] = alpha[tok];", "a[i] = 1.0;"),
     "variance_not_carried": _sub("p[i] = (den != 0.0) ? pm[i] * rt / den : pm[i];",
                                  "p[i] = (den != 0.0) ? p[i] : pm[i];"),
+    # isotropic KDN
+    "iso_alpha_not_squared": _sub("a2 += a[i] * a[i];", "a2 += a[i];"),
+    "iso_drops_process_noise": _sub("xm += xi[tok * dk + i];", "xm += 0.0;"),
+    "iso_sum_not_mean": _sub(
+        "const double pmi = (a2 / (double)dk) * p[0] + xm / (double)dk;",
+        "const double pmi = a2 * p[0] + xm;"),
+    "iso_noise_sum_not_mean": _sub(
+        "const double pmi = (a2 / (double)dk) * p[0] + xm / (double)dk;",
+        "const double pmi = (a2 / (double)dk) * p[0] + xm;"),
+    "iso_k_not_squared": _sub("kk += kt[i] * kt[i];", "kk += kt[i];"),
+    "iso_mu_not_over_dk": _sub("(mu / (double)dk) * pmi * kk", "mu * pmi * kk"),
+    "iso_mu_in_gain": _sub("const double s = rt + pmi * kk;",
+                           "const double s = rt + mu * pmi * kk;"),
+    "iso_drops_obs_noise": _sub("const double s = rt + pmi * kk;",
+                                "const double s = pmi * kk;"),
+    "iso_gain_uses_prior": _sub("w[i] = (s != 0.0) ? pmi * kt[i] / s : 0.0;",
+                                "w[i] = (s != 0.0) ? p[0] * kt[i] / s : 0.0;"),
+    "iso_moment_matching": _sub("p[0] = (den != 0.0) ? pmi * rt / den : pmi;",
+                                "p[0] = pmi - pmi * pmi * kk / (s * (double)dk);"),
+    "iso_variance_not_carried": _sub("p[0] = (den != 0.0) ? pmi * rt / den : pmi;",
+                                     "p[0] = (den != 0.0) ? p[0] : pmi;"),
 }
 
 
