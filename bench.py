@@ -1,4 +1,4 @@
-"""Benchmark of the delta-rule / diagonal-KDN hot path on one MI355X.
+"""Benchmark of the delta-rule / Kalman-delta hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--workloads all|headline]
@@ -9,8 +9,8 @@ resident in HBM.  Rank 0 prints ONE JSON line with the headline value
 (prefill tokens/s), the roofline of the prefill kernel (HBM-bound by its
 algorithmic bytes; the MFMA fraction of its algorithmic flops is reported
 next to it), the fp64 oracle timed on the host cores, and the other
-workloads (KDA and diagonal-KDN prefill, diagonal-KDN decode, 16-token
-multi-token decode) each with its own roofline.
+workloads (KDA, diagonal-KDN and isotropic-KDN prefill, diagonal-KDN decode,
+16-token multi-token decode) each with its own roofline.
 """
 from __future__ import annotations
 
@@ -45,11 +45,11 @@ def prefill_bytes(variant, B, T, H, dk, dv, es, has_S0):
     n = tok * (2 * dk + 2 * dv) * es               # q, k, v, o
     if variant == "gated_deltanet":
         n += tok * es
-    elif variant in ("kda", "diag_kdn"):
+    elif variant in ("kda", "diag_kdn", "iso_kdn"):
         n += tok * dk * es
-    if variant == "diag_kdn":
+    if variant in ("diag_kdn", "iso_kdn"):
         n += tok * dk * es + tok * es               # xi, r
-        n += 2 * B * H * dk * 4                     # p0, p_out
+        n += 2 * B * H * (dk if variant == "diag_kdn" else 1) * 4   # p0, p_out
     else:
         n += tok * es                               # beta
     n += B * H * dk * dv * 4 * (2 if has_S0 else 1)
@@ -121,7 +121,7 @@ def bench_prefill(name, steps, warmup, torch, kdn, synth, schedule="two_pass"):
     B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
     o = torch.empty((B, T, H, dv), dtype=inp["q"].dtype, device="cuda")
     S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
-    p = torch.empty_like(inp["p0"]) if c["variant"] == "diag_kdn" else None
+    p = torch.empty_like(inp["p0"]) if inp.get("p0") is not None else None
     # caller-owned workspace of the two-pass schedule, allocated once
     ws = kdn.workspace(c["variant"], inp["q"], inp["v"]) if schedule == "two_pass" else None
 
@@ -263,7 +263,8 @@ def cpu_baseline(name, synth, budget_s=20.0):
                 continue
             parts = [f64(x[b:b + 1, :, h:h + 1]) for (b, h) in heads]
             sl[k] = np.concatenate(parts, axis=2)
-        p0 = None if c["variant"] != "diag_kdn" else np.ones((1, nheads, c["dk"]))
+        p0 = (np.ones((1, nheads, c["dk"])) if c["variant"] == "diag_kdn" else
+              np.ones((1, nheads)) if c["variant"] == "iso_kdn" else None)
         return sl, p0
 
     sl, p0 = sample(1)
@@ -338,7 +339,7 @@ def main():
     }
     if args.workloads == "all":
         w = {}
-        for name in ("kda", "diag_kdn"):
+        for name in ("kda", "diag_kdn", "iso_kdn"):
             w[f"{name}_prefill"] = bench_prefill(name, max(3, args.steps // 2),
                                                  args.warmup, torch, kdn, synth,
                                                  args.schedule)

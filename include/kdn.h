@@ -1,15 +1,20 @@
 /*
- * kdn.h -- C ABI of the MI355X (gfx950) delta-rule / diagonal-KDN library.
+ * kdn.h -- C ABI of the MI355X (gfx950) delta-rule / Kalman-delta library.
  *
  * Per head the library keeps an associative memory S (d_k x d_v, float32)
- * and, for diagonal KDN, a per-channel variance p (d_k, float32).  For each
- * token, in this order:
+ * and, for diagonal KDN, a per-channel variance p (d_k, float32), for
+ * isotropic KDN one variance p per head (float32).  For each token, in this
+ * order:
  *   1. decay vector a: 1 (DeltaNet), alpha_t * 1 (Gated DeltaNet), or the
- *      per-key-channel vector alpha_t (KDA, diagonal KDN);
+ *      per-key-channel vector alpha_t (KDA, diagonal and isotropic KDN);
  *   2. write vector w: beta_t k_t, or for diagonal KDN the Kalman gain
  *        p- = a*a*p + xi_t,  s = r_t + sum_i p-_i k_i^2,  w = p- (.) k / s
  *      (w = 0 if s == 0) followed by the mean-field variance update
  *        p_i = p-_i r_t / (r_t + mu p-_i k_i^2)   (p-_i if that is 0/0);
+ *      for isotropic KDN, with means over the d_k channels,
+ *        p- = mean(a*a) p + mean(xi_t),  w = p- k / (r_t + p- |k|^2)
+ *      (w = 0 if that is 0), then p = p- r_t / (r_t + (mu/d_k) p- |k|^2)
+ *      (p- if that is 0/0);
  *   3. S <- diag(a) S;   4. e = v_t - S^T k_t;   5. S <- S + w e^T;
  *   6. o_t = S^T q_t.
  * Sources (page title, section):
@@ -23,7 +28,8 @@
  *   - "给记忆装一个信任度探测器：Kalman Delta Networks 如何让AI知道自己"记得准不准"",
  *     sections "把记忆问题重新想成一个滤波问题" and "对角近似：把矩阵压扁成一个向量"
  *     (Kalman predict/update, diagonal covariance with exact mean, information
- *     scaling mu).
+ *     scaling mu) and "各向同性近似：把整个头压缩成一个数" (one variance per head,
+ *     the delta rule with a derived write strength).
  *
  * Conventions shared by every entry point:
  *   - All tensor arguments are DEVICE pointers to contiguous row-major data
@@ -31,9 +37,9 @@
  *   - Per-token inputs (q, k, v, alpha, beta, proc_noise, obs_noise) and the
  *     output o use the call's dtype; S and p are always float32.
  *   - Alignment (else KDN_ERR_ALIGN): tensors whose last axis is d_k or d_v
- *     (q, k, v, per-channel alpha, proc_noise, o, S*, p*) start on a 16-byte
- *     boundary; per-head scalars (beta, obs_noise, the Gated DeltaNet alpha)
- *     on their element size.
+ *     (q, k, v, per-channel alpha, proc_noise, o, S*, diagonal-KDN p*) start
+ *     on a 16-byte boundary; per-head scalars (beta, obs_noise, the Gated
+ *     DeltaNet alpha, isotropic-KDN p*) on their element size.
  *   - A pointer the variant does not use must be NULL.  An empty tensor may
  *     be passed as NULL: the per-token tensors when there are no tokens, the
  *     state tensors when there are no heads.
@@ -58,7 +64,8 @@ typedef enum kdn_variant {
     KDN_DELTANET = 0,        /* no decay, write strength beta            */
     KDN_GATED_DELTANET = 1,  /* scalar decay alpha_t per token/head      */
     KDN_KDA = 2,             /* per-key-channel decay alpha_t[d_k]       */
-    KDN_DIAG_KDN = 3         /* per-channel decay + diagonal Kalman gain */
+    KDN_DIAG_KDN = 3,        /* per-channel decay + diagonal Kalman gain */
+    KDN_ISO_KDN = 4          /* per-channel decay + one variance per head */
 } kdn_variant;
 
 typedef enum kdn_dtype {
@@ -72,7 +79,7 @@ typedef enum kdn_status {
                                  variant does not use is non-NULL          */
     KDN_ERR_SHAPE = 2,        /* negative or overflowing sizes             */
     KDN_ERR_UNSUPPORTED = 3,  /* variant/dtype/d_k/d_v/chunk not built      */
-    KDN_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned          */
+    KDN_ERR_ALIGN = 4,        /* a pointer is not aligned as required      */
     KDN_ERR_ALIAS = 5,        /* an output overlaps an input it may not    */
     KDN_ERR_HIP = 6,          /* the HIP runtime refused the launch        */
     KDN_ERR_WORKSPACE = 7     /* workspace smaller than the size query     */
@@ -89,7 +96,7 @@ typedef enum kdn_status {
  *     order (no scratch memory);
  *   - workspace != NULL: the two-pass schedule.  Chunk-parallel kernels write
  *     each chunk's S-independent products (decay-scaled operands, A_qk, the
- *     triangular inverse; for diagonal KDN also the variance at each chunk
+ *     triangular inverse; for KDN also the variance at each chunk
  *     start, from a scan over per-chunk variance maps) to the workspace, then
  *     a sequential pass carries S through the chunks.  This is the fast path
  *     for long sequences.
@@ -97,19 +104,20 @@ typedef enum kdn_status {
  *   q, k        [B, T, H, d_k]  dtype
  *   v           [B, T, H, d_v]  dtype
  *   alpha       NULL (DeltaNet) | [B, T, H] (Gated DeltaNet) |
- *               [B, T, H, d_k] (KDA, diagonal KDN)            dtype
- *   beta        [B, T, H] dtype for DeltaNet / GDN / KDA; NULL for diag KDN
- *   proc_noise  [B, T, H, d_k] dtype, diagonal KDN only (else NULL)
- *   obs_noise   [B, T, H]      dtype, diagonal KDN only (else NULL)
+ *               [B, T, H, d_k] (KDA, diagonal and isotropic KDN)   dtype
+ *   beta        [B, T, H] dtype for DeltaNet / GDN / KDA; NULL for KDN
+ *   proc_noise  [B, T, H, d_k] dtype, KDN only (else NULL)
+ *   obs_noise   [B, T, H]      dtype, KDN only (else NULL)
  *   S0          [B, H, d_k, d_v] float32, or NULL for a zero memory
- *   p0          [B, H, d_k] float32, required for diagonal KDN (else NULL)
+ *   p0          [B, H, d_k] float32 (diagonal KDN), [B, H] float32
+ *               (isotropic KDN), required for KDN (else NULL)
  *   o           [B, T, H, d_v] dtype (output, o_t = S_t^T q_t)
  *   S_out       [B, H, d_k, d_v] float32 (output); may be exactly S0, must not
  *               overlap it otherwise
- *   p_out       [B, H, d_k] float32 (output, diagonal KDN only, else NULL);
- *               must not overlap p0
- *   mu          information scaling of the variance update (diagonal KDN
- *               only; 1 = unscaled)
+ *   p_out       shaped as p0, float32 (output, KDN only, else NULL); must
+ *               not overlap p0
+ *   mu          information scaling of the variance update (KDN only; 1 =
+ *               unscaled)
  *   chunk       chunk length C; 0 picks the library default (64 for bf16,
  *               32 for float32 with d_k = 128, else 64)
  *   workspace   NULL, or device memory of at least workspace_bytes >=
@@ -140,7 +148,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype,
  * sizes (0 when there are no tokens or heads), or 0 with *status set when the
  * combination is invalid or unsupported (status may be NULL).  For bf16,
  * d_k = d_v = 128, C = 64 this is 66,048 bytes per (sequence, head, chunk),
- * plus 2,560 for diagonal KDN.
+ * plus 2,560 for diagonal KDN or 1,044 for isotropic KDN.
  */
 unsigned long long kdn_chunk_prefill_workspace_size(kdn_variant variant, kdn_dtype dtype,
                                                     int B, int T, int H, int d_k,
@@ -154,11 +162,11 @@ unsigned long long kdn_chunk_prefill_workspace_size(kdn_variant variant, kdn_dty
  *
  *   q, k        [N, H, d_k] dtype;   v [N, H, d_v] dtype
  *   alpha       NULL | [N, H] | [N, H, d_k] dtype (as for prefill)
- *   beta        [N, H] dtype, NULL for diagonal KDN
- *   proc_noise  [N, H, d_k] dtype, obs_noise [N, H] dtype (diagonal KDN only)
+ *   beta        [N, H] dtype, NULL for KDN
+ *   proc_noise  [N, H, d_k] dtype, obs_noise [N, H] dtype (KDN only)
  *   S           [N, H, d_k, d_v] float32, read and updated IN PLACE
- *   p           [N, H, d_k] float32, read and updated in place (diag KDN only,
- *               else NULL)
+ *   p           [N, H, d_k] (diagonal KDN) or [N, H] (isotropic KDN) float32,
+ *               read and updated in place (KDN only, else NULL)
  *   o           [N, H, d_v] dtype (output)
  * Supported: d_k, d_v in {64, 128}; dtype KDN_F32 or KDN_BF16; N, H >= 0.
  * o must not overlap any input or S / p.
@@ -182,13 +190,14 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype,
  *
  *   q, k        [N, T, H, d_k] dtype;   v [N, T, H, d_v] dtype
  *   alpha       NULL | [N, T, H] | [N, T, H, d_k] dtype (as for prefill)
- *   beta        [N, T, H] dtype, NULL for diagonal KDN
- *   proc_noise  [N, T, H, d_k] dtype, obs_noise [N, T, H] dtype (diag KDN only)
+ *   beta        [N, T, H] dtype, NULL for KDN
+ *   proc_noise  [N, T, H, d_k] dtype, obs_noise [N, T, H] dtype (KDN only)
  *   S0          [N, H, d_k, d_v] float32 state before the tokens (NULL: zeros)
- *   p0          [N, H, d_k] float32 (diagonal KDN only, else NULL)
+ *   p0          [N, H, d_k] (diagonal KDN) or [N, H] (isotropic KDN) float32
+ *               (KDN only, else NULL)
  *   o           [N, T, H, d_v] dtype (output, one row per token)
  *   S_out       [N, H, d_k, d_v] float32, the state after the T tokens
- *   p_out       [N, H, d_k] float32 (diagonal KDN only, else NULL)
+ *   p_out       shaped as p0 (KDN only, else NULL)
  * S_out may be S0 exactly and p_out may be p0 exactly (update in place);
  * any other overlap between outputs and inputs is KDN_ERR_ALIAS.  With S_out
  * and p_out elsewhere the resident state is left as it was, which is the

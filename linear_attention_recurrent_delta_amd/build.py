@@ -31,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 UNITS = [("kdn_abi.cpp", [], "kdn_abi.o"),
          ("kdn_decode.hip", [], "kdn_decode.o")]
 UNITS += [("kdn_prefill.hip", [f"-DKDN_PREFILL_VARIANT={v}"], f"kdn_prefill_{v}.o")
-          for v in range(4)]
+          for v in range(5)]
 UNITS += [("kdn_prefill.hip", ["-DKDN_PREFILL_DISPATCH"], "kdn_prefill_dispatch.o"),
           ("kdn_prefill_state.hip", [], "kdn_prefill_state.o"),
           ("kdn_variance.hip", [], "kdn_variance.o")]

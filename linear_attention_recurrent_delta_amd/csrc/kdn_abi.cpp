@@ -6,6 +6,7 @@
 #include "kdn_workspace.h"
 
 #include <atomic>
+#include <initializer_list>
 #include <stdint.h>
 
 namespace {
@@ -38,7 +39,15 @@ bool overlap(const void *a, long long na, const void *b, long long nb) {
     return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
-bool valid_variant(int v) { return v >= KDN_DELTANET && v <= KDN_DIAG_KDN; }
+bool valid_variant(int v) { return v >= KDN_DELTANET && v <= KDN_ISO_KDN; }
+bool is_kdn(int v) { return v == KDN_DIAG_KDN || v == KDN_ISO_KDN; }
+// float32 variances per (sequence, head): d_k (diagonal KDN), 1 (isotropic)
+long long p_per_head(int v, int d_k) {
+    return v == KDN_DIAG_KDN ? d_k : (v == KDN_ISO_KDN ? 1 : 0);
+}
+// Alignment of the variance tensors: vectors of d_k floats 16 bytes, the
+// per-head scalar of isotropic KDN one float.
+uintptr_t p_align(int v) { return v == KDN_ISO_KDN ? 4 : 16; }
 bool valid_dtype(int d) { return d == KDN_F32 || d == KDN_BF16; }
 bool valid_dim(int d) { return d == 64 || d == 128; }
 
@@ -47,7 +56,7 @@ bool valid_dim(int d) { return d == 64 || d == 128; }
 kdn_status check_gates(int variant, const void *alpha, const void *beta,
                        const void *xi, const void *r, bool empty) {
     const bool need_alpha = variant != KDN_DELTANET;
-    const bool kdn = variant == KDN_DIAG_KDN;
+    const bool kdn = is_kdn(variant);
     if (!need_alpha && alpha) return KDN_ERR_NULL;
     if (kdn && beta) return KDN_ERR_NULL;
     if (!kdn && (xi || r)) return KDN_ERR_NULL;
@@ -70,7 +79,7 @@ const char *kdn_status_string(kdn_status s) {
     case KDN_ERR_NULL: return "a required pointer is NULL, or a pointer the variant does not use is set";
     case KDN_ERR_SHAPE: return "negative or overflowing sizes";
     case KDN_ERR_UNSUPPORTED: return "unsupported variant, dtype, head dimension or chunk length";
-    case KDN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDN_ERR_ALIGN: return "a pointer is not aligned as required";
     case KDN_ERR_ALIAS: return "an output overlaps an input it may not overlap";
     case KDN_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case KDN_ERR_WORKSPACE: return "the workspace is smaller than kdn_chunk_prefill_workspace_size";
@@ -137,7 +146,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
         return st;
     const long long bh = (long long)B * H;
     const long long tok = bh * T;
-    const bool kdn = variant == KDN_DIAG_KDN;
+    const bool kdn = is_kdn(variant);
     // Empty tensors may be passed as NULL (a zero-size torch tensor has no
     // storage): per-token tensors when B*H*T = 0, state tensors when B*H = 0.
     if (tok > 0 && (!q || !k || !v || !o))
@@ -153,7 +162,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     const long long es = dtype == KDN_BF16 ? 2 : 4;
     // vectors of d_k / d_v elements: 16 bytes; per-head scalars: one element
     const void *vec[] = {q, k, v, variant == KDN_GATED_DELTANET ? nullptr : alpha,
-                         proc_noise, S0, p0, o, S_out, p_out};
+                         proc_noise, S0, o, S_out};
     const void *sca[] = {beta, obs_noise, variant == KDN_GATED_DELTANET ? alpha : nullptr};
     for (const void *x : vec)
         if (x && !aligned(x, 16))
@@ -161,13 +170,16 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     for (const void *x : sca)
         if (x && !aligned(x, (uintptr_t)es))
             return KDN_ERR_ALIGN;
+    for (const void *x : {(const void *)p0, (const void *)p_out})
+        if (x && !aligned(x, p_align(variant)))
+            return KDN_ERR_ALIGN;
 
     const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
     const long long n_a = variant == KDN_GATED_DELTANET ? tok * es
                         : (variant == KDN_DELTANET ? 0 : tok * d_k * es);
     const long long n_b = kdn ? 0 : tok * es;
     const long long n_x = kdn ? tok * d_k * es : 0, n_r = kdn ? tok * es : 0;
-    const long long n_S = bh * d_k * d_v * 4, n_p = kdn ? bh * d_k * 4 : 0;
+    const long long n_S = bh * d_k * d_v * 4, n_p = bh * p_per_head(variant, d_k) * 4;
     // o overlaps no input; S_out may be S0 exactly; p_out must not touch p0.
     struct R { const void *p; long long n; } ins[] = {
         {q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, n_b},
@@ -204,16 +216,22 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.q = q; P.k = k; P.v = v; P.alpha = alpha; P.beta = beta;
     P.xi = proc_noise; P.r = obs_noise;
     P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
-    P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr;
+    P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr; P.ws_stat = nullptr;
     P.cus = device_cus();
     if (n_ws > 0) {
         P.ws = workspace;
-        if (kdn) {
-            const long long nc = kdn::num_chunks(T, C);
-            char *base = static_cast<char *>(workspace) +
-                         kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
+        const long long nc = kdn::num_chunks(T, C);
+        char *base = static_cast<char *>(workspace) +
+                     kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
+        if (variant == KDN_DIAG_KDN) {
             P.ws_mob = reinterpret_cast<float *>(base);
             P.ws_p0 = reinterpret_cast<float *>(base + kdn::WsLayout::mobius_bytes(bh, nc, d_k));
+        } else if (variant == KDN_ISO_KDN) {
+            const long long n_mob = kdn::WsLayout::mobius_bytes(bh, nc, 1);
+            P.ws_mob = reinterpret_cast<float *>(base);
+            P.ws_stat = reinterpret_cast<float *>(base + n_mob);
+            P.ws_p0 = reinterpret_cast<float *>(base + n_mob +
+                                                kdn::WsLayout::stat_bytes(bh, nc, C));
         }
     }
     const hipError_t e = kdn::launch_prefill(P, static_cast<hipStream_t>(stream));
@@ -235,7 +253,7 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype, int N, int
         return KDN_ERR_SHAPE;
     if (!valid_dim(d_k) || !valid_dim(d_v))
         return KDN_ERR_UNSUPPORTED;
-    const bool kdn = variant == KDN_DIAG_KDN;
+    const bool kdn = is_kdn(variant);
     if (nh > 0 && (!q || !k || !v || !o || !S))
         return KDN_ERR_NULL;
     if (kdn_status st = check_gates(variant, alpha, beta, proc_noise, obs_noise, nh == 0))
@@ -246,7 +264,7 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype, int N, int
         return KDN_ERR_NULL;
     const long long es = dtype == KDN_BF16 ? 2 : 4;
     const void *vec[] = {q, k, v, variant == KDN_GATED_DELTANET ? nullptr : alpha,
-                         proc_noise, S, p, o};
+                         proc_noise, S, o};
     const void *sca[] = {beta, obs_noise, variant == KDN_GATED_DELTANET ? alpha : nullptr};
     for (const void *x : vec)
         if (x && !aligned(x, 16))
@@ -254,13 +272,15 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype, int N, int
     for (const void *x : sca)
         if (x && !aligned(x, (uintptr_t)es))
             return KDN_ERR_ALIGN;
+    if (p && !aligned(p, p_align(variant)))
+        return KDN_ERR_ALIGN;
 
     const long long n_qk = nh * d_k * es, n_v = nh * d_v * es;
     const long long n_a = variant == KDN_GATED_DELTANET ? nh * es
                         : (variant == KDN_DELTANET ? 0 : nh * d_k * es);
     const long long n_b = kdn ? 0 : nh * es;
     const long long n_x = kdn ? nh * d_k * es : 0, n_r = kdn ? nh * es : 0;
-    const long long n_S = nh * d_k * d_v * 4, n_p = kdn ? nh * d_k * 4 : 0;
+    const long long n_S = nh * d_k * d_v * 4, n_p = nh * p_per_head(variant, d_k) * 4;
     const long long n_o = nh * d_v * es;
     struct R { const void *p; long long n; } ins[] = {
         {q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, n_b},
@@ -303,7 +323,7 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype, int 
         return KDN_ERR_SHAPE;
     if (!valid_dim(d_k) || !valid_dim(d_v))
         return KDN_ERR_UNSUPPORTED;
-    const bool kdn = variant == KDN_DIAG_KDN;
+    const bool kdn = is_kdn(variant);
     if (tok > 0 && (!q || !k || !v || !o))
         return KDN_ERR_NULL;
     if (kdn_status st = check_gates(variant, alpha, beta, proc_noise, obs_noise, tok == 0))
@@ -316,7 +336,7 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype, int 
         return KDN_ERR_NULL;
     const long long es = dtype == KDN_BF16 ? 2 : 4;
     const void *vec[] = {q, k, v, variant == KDN_GATED_DELTANET ? nullptr : alpha,
-                         proc_noise, S0, p0, o, S_out, p_out};
+                         proc_noise, S0, o, S_out};
     const void *sca[] = {beta, obs_noise, variant == KDN_GATED_DELTANET ? alpha : nullptr};
     for (const void *x : vec)
         if (x && !aligned(x, 16))
@@ -324,13 +344,16 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype, int 
     for (const void *x : sca)
         if (x && !aligned(x, (uintptr_t)es))
             return KDN_ERR_ALIGN;
+    for (const void *x : {(const void *)p0, (const void *)p_out})
+        if (x && !aligned(x, p_align(variant)))
+            return KDN_ERR_ALIGN;
 
     const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
     const long long n_a = variant == KDN_GATED_DELTANET ? tok * es
                         : (variant == KDN_DELTANET ? 0 : tok * d_k * es);
     const long long n_b = kdn ? 0 : tok * es;
     const long long n_x = kdn ? tok * d_k * es : 0, n_r = kdn ? tok * es : 0;
-    const long long n_S = nh * d_k * d_v * 4, n_p = kdn ? nh * d_k * 4 : 0;
+    const long long n_S = nh * d_k * d_v * 4, n_p = nh * p_per_head(variant, d_k) * 4;
     const long long n_o = tok * d_v * es;
     // o overlaps nothing; S_out may be S0 exactly and p_out may be p0 exactly
     // (each workgroup reads its slice before writing it); no other overlap.

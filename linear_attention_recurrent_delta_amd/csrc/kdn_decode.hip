@@ -15,6 +15,10 @@
 // "对角近似：把矩阵压扁成一个向量"):
 //   p- = a*a*p + xi,  s = r + sum_i p-_i k_i^2,  w = p- k / s,
 //   p_i = p-_i r / (r + mu p-_i k_i^2).
+// Isotropic KDN (same page, section "各向同性近似：把整个头压缩成一个数"), one
+// variance p per head:
+//   p- = mean(a^2) p + mean(xi),  w = p- k / (r + p- |k|^2),
+//   p = p- r / (r + (mu / d_k) p- |k|^2).
 //
 // Thread layout: the d_v columns are split in groups of 4 (one float4 per
 // row), the d_k rows in RG groups; thread (rg, cg) holds rows
@@ -42,14 +46,14 @@ struct TokenIn {
             q = to_f32(static_cast<const TIn *>(P.q)[row * DK + tid]);
             if (VAR == GATED_DELTANET)
                 a = to_f32(static_cast<const TIn *>(P.alpha)[row]);
-            else if (VAR == KDA || VAR == DIAG_KDN)
+            else if (VAR == KDA || VAR == DIAG_KDN || VAR == ISO_KDN)
                 a = to_f32(static_cast<const TIn *>(P.alpha)[row * DK + tid]);
-            if (VAR == DIAG_KDN)
+            if (VAR == DIAG_KDN || VAR == ISO_KDN)
                 xi = to_f32(static_cast<const TIn *>(P.xi)[row * DK + tid]);
             else
                 beta = to_f32(static_cast<const TIn *>(P.beta)[row]);
         }
-        if (VAR == DIAG_KDN)
+        if (VAR == DIAG_KDN || VAR == ISO_KDN)
             r = to_f32(static_cast<const TIn *>(P.r)[row]);
         const TIn *vp = static_cast<const TIn *>(P.v) + row * P.dv + 4 * cg;
 #pragma unroll
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
 
     __shared__ float sk[DK], sq[DK], sa[DK], sg[DK];
     __shared__ f32x4 red[RG][CG];
-    __shared__ float part[NT / WAVE];
+    __shared__ float part[3][NT / WAVE];
 
     // The first token's vectors are requested first and the state after
     // them: loads return in order, so the gain below is formed while the
@@ -93,9 +97,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
     TokenIn<TIn, VAR, DK> in;
     if (T > 0)
         in.load(P, row_of(0), tid, cg);
-    float pc = 0.f;                   // variance of channel tid (diagonal KDN)
+    float pc = 0.f;                   // variance of channel tid (diagonal KDN),
+                                      // of the head (isotropic KDN)
     if (VAR == DIAG_KDN && tid < DK)
         pc = P.p0[bh * DK + tid];
+    if (VAR == ISO_KDN)
+        pc = P.p0[bh];
     f32x4 s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
@@ -117,22 +124,51 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
                 pm = in.a * in.a * pc + in.xi;          // predict
                 u = pm * in.k;
                 pk2 = u * in.k;
-            } else {
+            } else if (VAR != ISO_KDN) {
                 sg[tid] = in.beta * in.k;
+            }
+        }
+        if (VAR == ISO_KDN) {
+            // channel sums of a^2, xi and k^2 (block reduction), then the
+            // scalar predict, gain and update in every thread < DK
+            const bool ch = tid < DK;
+            const float wa = wave_sum(ch ? in.a * in.a : 0.f);
+            const float wx = wave_sum(ch ? in.xi : 0.f);
+            const float wk = wave_sum(ch ? in.k * in.k : 0.f);
+            if ((tid & (WAVE - 1)) == 0) {
+                part[0][tid / WAVE] = wa;
+                part[1][tid / WAVE] = wx;
+                part[2][tid / WAVE] = wk;
+            }
+            __syncthreads();
+            if (ch) {
+                float sa = 0.f, sx = 0.f, kk = 0.f;
+#pragma unroll
+                for (int w = 0; w < (DK + WAVE - 1) / WAVE; ++w) {
+                    sa += part[0][w];
+                    sx += part[1][w];
+                    kk += part[2][w];
+                }
+                const float r = in.r;
+                const float pmi = fmaf(sa * (1.f / DK), pc, sx * (1.f / DK));
+                const float s = fmaf(pmi, kk, r);
+                sg[tid] = (s != 0.f) ? pmi / s * in.k : 0.f;   // gain
+                const float den = fmaf(P.mu * (1.f / DK) * pmi, kk, r);
+                pc = (den != 0.f) ? pmi * r / den : pmi;
             }
         }
         if (VAR == DIAG_KDN) {
             // innovation variance s = r + sum_i p-_i k_i^2 (block reduction)
             const float ws = wave_sum(pk2);
             if ((tid & (WAVE - 1)) == 0)
-                part[tid / WAVE] = ws;
+                part[0][tid / WAVE] = ws;
             __syncthreads();
             if (tid < DK) {
                 const float r = in.r;
                 float sum = r;
 #pragma unroll
                 for (int w = 0; w < (DK + WAVE - 1) / WAVE; ++w)
-                    sum += part[w];
+                    sum += part[0][w];
                 sg[tid] = (sum != 0.f) ? u / sum : 0.f;    // gain
                 const float den = r + P.mu * pm * in.k * in.k;
                 pc = (den != 0.f) ? pm * r / den : pm;
@@ -208,6 +244,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
     }
     if (VAR == DIAG_KDN && tid < DK)
         P.p[bh * DK + tid] = pc;
+    if (VAR == ISO_KDN && tid == 0)
+        P.p[bh] = pc;
 }
 
 template <typename TIn, int VAR, bool MULTI>
@@ -235,6 +273,7 @@ static hipError_t launch_decode_t(const DecodeParams &P, hipStream_t st) {
     case GATED_DELTANET: return launch_decode_v<TIn, GATED_DELTANET, MULTI>(P, st);
     case KDA: return launch_decode_v<TIn, KDA, MULTI>(P, st);
     case DIAG_KDN: return launch_decode_v<TIn, DIAG_KDN, MULTI>(P, st);
+    case ISO_KDN: return launch_decode_v<TIn, ISO_KDN, MULTI>(P, st);
     }
     return hipErrorInvalidValue;
 }

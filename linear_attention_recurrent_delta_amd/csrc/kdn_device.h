@@ -13,7 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum Variant { DELTANET = 0, GATED_DELTANET = 1, KDA = 2, DIAG_KDN = 3 };
+enum Variant { DELTANET = 0, GATED_DELTANET = 1, KDA = 2, DIAG_KDN = 3, ISO_KDN = 4 };
 
 constexpr int WAVE = 64;
 
@@ -215,6 +215,55 @@ __device__ __forceinline__ void lds_stn(float *p, const float *f) {
 
 // Fast reciprocal (v_rcp_f32, about 1 ulp).
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Kalman variance step as a linear fractional map of the variance p, held as
+// a 2 x 2 matrix acting on (p, 1) projectively (page "给记忆装一个信任度探测器：
+// Kalman Delta Networks ...", sections "对角近似：把矩阵压扁成一个向量" and
+// "各向同性近似：把整个头压缩成一个数": the recursion is a Mobius map and runs of
+// tokens compose by matrix products).  Entries are >= 0 for admissible
+// inputs, so products have no cancellation and may be rescaled freely.
+struct Map2 {
+    float a, b, c, d;     // [[a, b], [c, d]]
+    // x <- y o x (y applied after x)
+    __device__ __forceinline__ void after(float ya, float yb, float yc, float yd) {
+        const float na = ya * a + yb * c, nb = ya * b + yb * d;
+        const float nc = yc * a + yd * c, nd = yc * b + yd * d;
+        a = na; b = nb; c = nc; d = nd;
+    }
+    // x <- x o y (y applied first)
+    __device__ __forceinline__ void before(float ya, float yb, float yc, float yd) {
+        const float na = a * ya + b * yc, nb = a * yb + b * yd;
+        const float nc = c * ya + d * yc, nd = c * yb + d * yd;
+        a = na; b = nb; c = nc; d = nd;
+    }
+    // divide by the largest entry (the map is unchanged by a common factor)
+    __device__ __forceinline__ void rescale() {
+        const float sc = fast_rcp(fmaxf(fmaxf(a, b), fmaxf(c, d)));
+        a *= sc; b *= sc; c *= sc; d *= sc;
+    }
+    __device__ __forceinline__ float apply(float p) const {
+        return fmaf(a, p, b) / fmaf(c, p, d);
+    }
+};
+
+// One token: predict p- = a2 p + xi, then p = p- r / (r + m p-), where m is
+// the precision gain numerator (mu k_i^2 per channel, or (mu / d_k) |k|^2 for
+// one variance per head).  Divided through by r:
+//   [[a2, xi], [c a2, c xi + 1]],  c = m / r   (r > 0);
+// r = 0: the identity update if m = 0 ([[a2, xi], [0, 1]]), else every p-
+// maps to 0 ([[0, 0], [0, 1]]).
+__device__ __forceinline__ Map2 variance_step_map(float a2, float xi, float m, float r) {
+    Map2 y{a2, xi, 0.f, 1.f};
+    if (r > 0.f) {
+        const float cc = m / r;
+        y.c = cc * a2;
+        y.d = fmaf(cc, xi, 1.f);
+    } else if (m != 0.f) {
+        y.a = 0.f;
+        y.b = 0.f;
+    }
+    return y;
+}
 
 // acc += A[m0:m0+16, 0:K] * B[0:K, n0:n0+16], A given as [row][k] with
 // pitch lda, B as [col][k] with pitch ldb (both in elements).  K must be a

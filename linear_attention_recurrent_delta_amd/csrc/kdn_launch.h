@@ -14,9 +14,10 @@ struct DecodeParams {
     float mu;
     const void *q, *k, *v, *alpha, *beta, *xi, *r;   // [N, T, H, .]
     const float *S0;   // [N, H, dk, dv] state read (NULL: zeros); may equal S
-    const float *p0;   // [N, H, dk] variance read (diagonal KDN); may equal p
+    const float *p0;   // [N, H, dk] (diagonal KDN) or [N, H] (isotropic KDN)
+                       // variance read; may equal p
     float *S;          // [N, H, dk, dv] state written
-    float *p;          // [N, H, dk] variance written (diagonal KDN)
+    float *p;          // variance written, shaped as p0
     void *o;           // [N, T, H, dv]
 };
 
@@ -33,10 +34,12 @@ struct PrefillParams {
     float *S_out;
     float *p_out;      // diagonal KDN
     // Two-pass schedule (null: single pass).  ws holds the per-chunk records
-    // (kdn_workspace.h); ws_mob / ws_p0 the diagonal-KDN variance scan.
+    // (kdn_workspace.h); ws_mob / ws_p0 the KDN variance scan; ws_stat the
+    // isotropic-KDN per-token sums (mean a^2, mean xi, |k|^2, r).
     void *ws;
     float *ws_mob;
     float *ws_p0;
+    float *ws_stat;
     int cus;           // compute units of the current device
 };
 
@@ -49,16 +52,18 @@ hipError_t launch_prefill_v0(const PrefillParams &P, hipStream_t stream, int nv)
 hipError_t launch_prefill_v1(const PrefillParams &P, hipStream_t stream, int nv);
 hipError_t launch_prefill_v2(const PrefillParams &P, hipStream_t stream, int nv);
 hipError_t launch_prefill_v3(const PrefillParams &P, hipStream_t stream, int nv);
+hipError_t launch_prefill_v4(const PrefillParams &P, hipStream_t stream, int nv);
 
 // d_v block width one prefill workgroup owns for this problem.
 int prefill_value_block(const PrefillParams &P);
 
 // Two-pass prefill: chunk-parallel prep kernels (one unit per variant), the
-// diagonal-KDN variance scan, and the sequential state pass.
+// KDN variance scans, and the sequential state pass.
 hipError_t launch_prefill_prep_v0(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_prefill_prep_v1(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_prefill_prep_v2(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_prefill_prep_v3(const PrefillParams &P, hipStream_t stream);
+hipError_t launch_prefill_prep_v4(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_variance_scan(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_prefill_state(const PrefillParams &P, hipStream_t stream);
 

@@ -14,7 +14,11 @@
 // Write vectors: w = beta k (DeltaNet, Gated DeltaNet, KDA) or the diagonal
 // Kalman gain (page "给记忆装一个信任度探测器：Kalman Delta Networks 如何让AI知道自己
 // "记得准不准"", section "对角近似：把矩阵压扁成一个向量"), whose variance recursion
-// does not depend on S and runs per channel inside the chunk.
+// does not depend on S and runs per channel inside the chunk.  Isotropic KDN
+// (same page, section "各向同性近似：把整个头压缩成一个数") is KDA whose write
+// strengths beta_t = p-_t / (r_t + p-_t |k_t|^2) come from one variance per
+// head; inside a chunk its token maps (Mobius form) are scanned across the
+// lanes of one wave.
 //
 // Work split: one workgroup (4 waves) owns one (batch, head, d_v block of NV
 // columns) and walks all chunks in order; the d_k x NV slice of S stays in
@@ -62,8 +66,9 @@ struct PrefillLayout {
     static constexpr int PP = DK + 4;        // pitch of the fp32 KDN u = p- k
     static constexpr int NB = C / 16;        // 16-row blocks per chunk
     static constexpr bool DECAY = VAR != DELTANET;
-    static constexpr bool VDECAY = VAR == KDA || VAR == DIAG_KDN;
+    static constexpr bool VDECAY = VAR == KDA || VAR == DIAG_KDN || VAR == ISO_KDN;
     static constexpr bool KDN = VAR == DIAG_KDN;
+    static constexpr bool ISO = VAR == ISO_KDN;
     // row layout of the decay scan: 8 channels x TPG tokens per thread
     static constexpr int NO = DK / 8;        // channel octets
     static constexpr int NG = 256 / NO < C ? 256 / NO : C; // token groups
@@ -110,7 +115,7 @@ struct PrefillLayout {
     static constexpr int TOTAL = OFF_SM + SZ_SM;
 
     static_assert(TOTAL <= 163840, "prefill LDS budget");
-    static_assert(!KDN || C * PK <= DK * PC, "xi staging alias");
+    static_assert(!(KDN || ISO) || C * PK <= DK * PC, "xi staging alias");
     static_assert(NG * TPG == C && TPG >= 1 && TPG <= 8, "scan layout");
     static_assert(C % 16 == 0 && NV % 16 == 0 && DK % 16 == 0, "tiles");
     static_assert(NB == 2 || NB == 4, "chunk of 32 or 64");
@@ -283,7 +288,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     constexpr int PK = LY::PK, PC = LY::PC, PV = LY::PV, PA = LY::PA,
                   PP = LY::PP, NB = LY::NB;
     constexpr int NO = LY::NO, NG = LY::NG, TPG = LY::TPG;
-    constexpr bool DECAY = LY::DECAY, VDECAY = LY::VDECAY, KDN = LY::KDN;
+    constexpr bool DECAY = LY::DECAY, VDECAY = LY::VDECAY, KDN = LY::KDN, ISO = LY::ISO;
+    // raw xi tile staged in LDS (the isotropic prep kernel reads per-token
+    // sums from the workspace instead)
+    constexpr bool XSTAGE = KDN || (ISO && !PREP);
     // Prep kernel, scalar decay: no per-channel scan; the decay enters as
     // ratios gamma_t / gamma_s in log2 form (section 2s below).
     constexpr bool SPREP = PREP && VAR == GATED_DELTANET;
@@ -316,6 +324,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
           *s_alph = sm + LY::SM_ALPH, *s_invs = sm + LY::SM_INVS,
           *s_gc = sm + LY::SM_GC;
     int *s_flag = reinterpret_cast<int *>(sm + LY::SM_FLAG);
+    // isotropic KDN per-token sums: mean a^2, mean xi, |k|^2 (r in s_r)
+    float *s_ia2 = s_alph, *s_ixm = s_invs, *s_ikk = sm + LY::SM_WSC;
     float *s_gl = s_r;                 // SPREP: log2 gamma over nonzero decays
     float *s_gt = s_invs;              // SPREP: gamma_t
     float *s_wsc = sm + LY::SM_WSC;    // SPREP: beta_s gamma_C / gamma_s
@@ -374,10 +384,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             ST[j * PK + i] = from_f32<E>(sacc[u][r]);
         }
     }
-    float p_reg = 0.f;                 // KDN variance of channel tid
+    float p_reg = 0.f;                 // KDN variance of channel tid (isotropic:
+                                       // of the head, in wave 0)
     float p_nxt = 0.f;                 // PREP: variance at the next unit's start
     if (KDN && tid < DK && !PREP)
         p_reg = P.p0[(long)bh * DK + tid];
+    if (ISO && tid < WAVE && !PREP)
+        p_reg = P.p0[bh];
 
     const long sk_ = (long)H * DK;     // token stride of q/k/alpha/xi
     const long sv_ = (long)H * DV;     // token stride of v/o
@@ -386,19 +399,28 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     TileRegs<E, DK, C, NT> rk, rq, ra, rx;
     TileRegs<E, NV, C, NT> rv;
     E sc_b = from_f32<E>(0.f), sc_r = from_f32<E>(1.f), sc_a = from_f32<E>(1.f);
+    float4 sc_st = make_float4(1.f, 0.f, 0.f, 1.f);   // isotropic prep: token sums
     auto fetch = [&](int bs, int cs) {
         const int Ls = min(C, T - cs);
         const long tk = ((long)(bs / H) * T + cs) * H + bs % H;
         if (PREP && KDN && tid < DK)
             p_nxt = P.ws_p0[((long)bs * NC + cs / C) * DK + tid];
+        if (PREP && ISO && tid < WAVE)
+            p_nxt = P.ws_p0[(long)bs * NC + cs / C];
         rk.fetch(gk + tk * DK, sk_, Ls, tid);
         rq.fetch(gq + tk * DK, sk_, Ls, tid);
         if (VDECAY) ra.fetch(ga + tk * DK, sk_, Ls, tid);
-        if (KDN) rx.fetch(gx + tk * DK, sk_, Ls, tid);
+        if (XSTAGE) rx.fetch(gx + tk * DK, sk_, Ls, tid);
         if (!PREP) rv.fetch(gv + tk * DV + v0, sv_, Ls, tid);
         if (tid < C) {
             const long ti = tk + (long)min(tid, Ls - 1) * H;
-            if (!KDN) sc_b = gb[ti]; else sc_r = gr[ti];
+            if (ISO && PREP)
+                sc_st = reinterpret_cast<const float4 *>(P.ws_stat)[
+                    ((long)bs * NC + cs / C) * C + min(tid, Ls - 1)];
+            else if (KDN || ISO)
+                sc_r = gr[ti];
+            else
+                sc_b = gb[ti];
             if (VAR == GATED_DELTANET) sc_a = ga[ti];
         }
     };
@@ -414,7 +436,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     // Diagonal KDN runs the scan layout on the last NTS threads, alongside
     // the variance chain on the first DK (phase 2).
     static_assert(!KDN || LY::NTS <= NT - DK, "scan threads clear of the variance chain");
-    const int ts = KDN ? tid - (NT - LY::NTS) : tid;   // scan-layout thread, if >= 0
+    static_assert(!ISO || LY::NTS <= NT - WAVE, "scan threads clear of wave 0");
+    const int ts = (KDN || ISO) ? tid - (NT - LY::NTS) : tid;   // scan-layout thread, if >= 0
     const int grp = ts % NG, oc = (ts / NG) % NO;
     const int i0 = oc * 8, t0 = grp * TPG;
     const int gh = tid % NG2, oc2 = tid / NG2;
@@ -459,12 +482,22 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         rk.commit(Kt, PK, 0.f, tid);
         rq.commit(Qt, PK, 0.f, tid);
         if (VDECAY) ra.commit(ALP, PK, 1.f, tid);
-        if (KDN) rx.commit(XR, PK, 0.f, tid);
+        if (XSTAGE) rx.commit(XR, PK, 0.f, tid);
         if (!PREP) rv.commit(VR, PV, 0.f, tid);
         if (tid < C) {
+            // tokens past the end: beta = 0; KDN: a = 1, xi = 0, k = 0, r = 1,
+            // which leaves the variance unchanged
             const bool in = tid < L;
-            if (!KDN) s_beta[tid] = in ? to_f32(sc_b) : 0.f;
-            else s_r[tid] = in ? to_f32(sc_r) : 1.f;
+            if (ISO && PREP) {
+                s_ia2[tid] = in ? sc_st.x : 1.f;
+                s_ixm[tid] = in ? sc_st.y : 0.f;
+                s_ikk[tid] = in ? sc_st.z : 0.f;
+                s_r[tid] = in ? sc_st.w : 1.f;
+            } else if (KDN || ISO) {
+                s_r[tid] = in ? to_f32(sc_r) : 1.f;
+            } else {
+                s_beta[tid] = in ? to_f32(sc_b) : 0.f;
+            }
             if (VAR == GATED_DELTANET) s_alph[tid] = in ? to_f32(sc_a) : 1.f;
         }
         if (tid == 0)
@@ -550,6 +583,76 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                 s_invs[t] = (s != 0.f) ? 1.f / s : 0.f;
             }
         }
+        if constexpr (ISO) {
+            if constexpr (!PREP) {
+                // per-token channel sums: mean a^2, mean xi, |k|^2
+                constexpr int TPR = LY::TPR, CPT = DK / TPR;
+                const int t = tid / TPR, part = tid % TPR;
+                float sa = 0.f, sx = 0.f, sk = 0.f;
+                if (tid < TPR * C) {
+#pragma unroll
+                    for (int c = 0; c < CPT; c += 8) {
+                        float a8[8], x8[8], k8[8];
+                        lds_ld8(ALP + t * PK + part * CPT + c, a8);
+                        lds_ld8(XR + t * PK + part * CPT + c, x8);
+                        lds_ld8(Kt + t * PK + part * CPT + c, k8);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            sa = fmaf(a8[e], a8[e], sa);
+                            sx += x8[e];
+                            sk = fmaf(k8[e], k8[e], sk);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int off = TPR / 2; off >= 1; off >>= 1) {
+                    sa += __shfl_xor(sa, off, WAVE);
+                    sx += __shfl_xor(sx, off, WAVE);
+                    sk += __shfl_xor(sk, off, WAVE);
+                }
+                if (tid < TPR * C && part == 0) {
+                    s_ia2[t] = sa * (1.f / DK);
+                    s_ixm[t] = sx * (1.f / DK);
+                    s_ikk[t] = sk;
+                }
+                __syncthreads();
+            }
+            if (ts >= 0)
+                group_products();          // decays, independent of the variance
+            if (wv == 0) {
+                // Head variance through the chunk: lane t forms token t's map
+                // (predict, then the update with gain numerator (mu/d_k)|k|^2),
+                // an inclusive scan over the lanes composes maps 0..t, and the
+                // chunk-start variance gives p after every token.  Then
+                //   p-_t = mean(a^2) p_{t-1} + mean(xi),
+                //   beta_t = p-_t / (r_t + p-_t |k_t|^2)   (0 if that is 0).
+                const int t = lane;
+                const bool tc = t < C;
+                const float a2 = tc ? s_ia2[t] : 1.f, xm = tc ? s_ixm[t] : 0.f;
+                const float kk = tc ? s_ikk[t] : 0.f, rt = tc ? s_r[t] : 1.f;
+                Map2 m = variance_step_map(a2, xm, P.mu * (1.f / DK) * kk, rt);
+                m.rescale();
+#pragma unroll
+                for (int off = 1; off < C; off <<= 1) {
+                    const float ya = __shfl_up(m.a, off, WAVE), yb = __shfl_up(m.b, off, WAVE);
+                    const float yc = __shfl_up(m.c, off, WAVE), yd = __shfl_up(m.d, off, WAVE);
+                    if (lane >= off) {
+                        m.before(ya, yb, yc, yd);
+                        m.rescale();
+                    }
+                }
+                const float pt = m.apply(p_reg);          // p after token t
+                float pp = __shfl_up(pt, 1, WAVE);        // p after token t - 1
+                if (lane == 0)
+                    pp = p_reg;
+                const float pm = fmaf(a2, pp, xm);
+                const float sv = fmaf(pm, kk, rt);
+                if (tc)
+                    s_beta[t] = (t < L && sv != 0.f) ? pm / sv : 0.f;
+                p_reg = __shfl(pt, C - 1, WAVE);
+            }
+            __syncthreads();
+        }
         bool fb = false;
         // SPREP: raw A-matrix tiles of waves 1.. (tile x = wv-1 + k(NW-1)),
         // computed while wave 0 scans the decays
@@ -602,9 +705,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             }
             __syncthreads();
         } else {
-        // 2a. group products of the decays (diagonal KDN: done in phase 2)
+        // 2a. group products of the decays (KDN: done with the variance above)
         if constexpr (DECAY) {
-            if constexpr (!KDN) {
+            if constexpr (!KDN && !ISO) {
                 if (ts < LY::NTS)
                     group_products();
                 __syncthreads();
@@ -1155,12 +1258,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     }
     if (KDN && vb == 0 && tid < DK)
         P.p_out[(long)bh * DK + tid] = p_reg;
+    if (ISO && vb == 0 && tid == 0)
+        P.p_out[bh] = p_reg;
 }
 #endif  // KDN_PREFILL_VARIANT
 
 // ---------------------------------------------------------------------------
 // Host-side dispatch.  This file is compiled once per variant
-// (KDN_PREFILL_VARIANT = 0..3, each unit instantiates that variant's kernels)
+// (KDN_PREFILL_VARIANT = 0..4, each unit instantiates that variant's kernels)
 // and once with KDN_PREFILL_DISPATCH for the entry point below.
 // ---------------------------------------------------------------------------
 #ifdef KDN_PREFILL_VARIANT
@@ -1258,12 +1363,16 @@ long long prefill_workspace_bytes(int variant, int bf16, long long B, long long 
     long long n = WsLayout::make(bf16, C, dk).records(bh, nc);
     if (variant == DIAG_KDN)
         n += WsLayout::mobius_bytes(bh, nc, dk) + WsLayout::p0_bytes(bh, nc, dk);
+    if (variant == ISO_KDN)
+        n += WsLayout::mobius_bytes(bh, nc, 1) + WsLayout::stat_bytes(bh, nc, C) +
+             WsLayout::p0_bytes(bh, nc, 1);
     return n;
 }
 
 static hipError_t launch_two_pass(const PrefillParams &P, hipStream_t st) {
     hipError_t e = hipSuccess;
-    if (P.variant == DIAG_KDN && (e = launch_variance_scan(P, st)) != hipSuccess)
+    if ((P.variant == DIAG_KDN || P.variant == ISO_KDN) &&
+        (e = launch_variance_scan(P, st)) != hipSuccess)
         return e;
     if (P.T > 0) {
         switch (P.variant) {
@@ -1271,6 +1380,7 @@ static hipError_t launch_two_pass(const PrefillParams &P, hipStream_t st) {
         case GATED_DELTANET: e = launch_prefill_prep_v1(P, st); break;
         case KDA: e = launch_prefill_prep_v2(P, st); break;
         case DIAG_KDN: e = launch_prefill_prep_v3(P, st); break;
+        case ISO_KDN: e = launch_prefill_prep_v4(P, st); break;
         default: e = hipErrorInvalidValue;
         }
         if (e != hipSuccess)
@@ -1290,6 +1400,7 @@ hipError_t launch_prefill(const PrefillParams &P, hipStream_t st) {
     case GATED_DELTANET: return launch_prefill_v1(P, st, nv);
     case KDA: return launch_prefill_v2(P, st, nv);
     case DIAG_KDN: return launch_prefill_v3(P, st, nv);
+    case ISO_KDN: return launch_prefill_v4(P, st, nv);
     }
     return hipErrorInvalidValue;
 }

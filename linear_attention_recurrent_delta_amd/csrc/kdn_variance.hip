@@ -1,4 +1,5 @@
-// kdn_variance.hip -- diagonal-KDN variance scan of the two-pass prefill.
+// kdn_variance.hip -- KDN variance scans of the two-pass prefill (diagonal
+// KDN: one variance per key channel; isotropic KDN: one per head).
 //
 // Per key channel the variance follows a scalar recurrence that does not
 // involve S or the other channels (predict p- = a^2 p + xi, then the
@@ -21,6 +22,12 @@
 // otherwise the update gives 0 for every p- (M = [[0, 0], [0, 1]]).
 // All entries are >= 0, so the products have no cancellation; they are
 // rescaled every four tokens (the map is unchanged by a common factor).
+//
+// Isotropic KDN (page "给记忆装一个信任度探测器 ...", section "各向同性近似：把整个头
+// 压缩成一个数"): one variance per head, the same step with the channel means
+// of a^2 and xi and c = (mu / d_k) |k|^2 / r.  Its chunk kernel also stores
+// each token's (mean a^2, mean xi, |k|^2, r), from which the prep kernel
+// derives the write strengths without re-reading xi.
 #include "kdn_device.h"
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
@@ -29,21 +36,6 @@ namespace kdn {
 
 // Channels per thread: one 16-byte load of k, alpha and xi per token.
 template <typename E> struct VarVec { static constexpr int N = 16 / (int)sizeof(E); };
-
-// 2 x 2 maps, entries >= 0: x <- y x (y applied after x), and a rescale by
-// the largest entry (the map is unchanged by a common factor).
-struct Map2 {
-    float a, b, c, d;     // [[a, b], [c, d]]
-    __device__ __forceinline__ void after(float ya, float yb, float yc, float yd) {
-        const float na = ya * a + yb * c, nb = ya * b + yb * d;
-        const float nc = yc * a + yd * c, nd = yc * b + yd * d;
-        a = na; b = nb; c = nc; d = nd;
-    }
-    __device__ __forceinline__ void rescale() {
-        const float sc = fast_rcp(fmaxf(fmaxf(a, b), fmaxf(c, d)));
-        a *= sc; b *= sc; c *= sc; d *= sc;
-    }
-};
 
 // One wave per (batch*head, chunk): lane = sub * TPU + cg holds channels
 // [cg N, cg N + N) over the sub-th of SUBS equal token ranges of the chunk.
@@ -182,6 +174,146 @@ __global__ __launch_bounds__(256) void variance_scan_kernel(PrefillParams P) {
     }
 }
 
+// Isotropic KDN, one wave per (batch*head, chunk), chunk-major like the
+// diagonal kernel: lane = sub * TPU + g reads channels [g N, g N + N) of the
+// tokens of the sub-th token range; the per-token channel sums are combined
+// across the TPU lanes of a range by a butterfly, every lane of the range
+// composes the token maps, and the ranges are combined in a shuffle tree.
+template <typename E, int DK>
+__global__ __launch_bounds__(256) void iso_variance_chunk_kernel(PrefillParams P) {
+    constexpr int N = VarVec<E>::N;
+    constexpr int TPU = DK / N;
+    constexpr int SUBS = WAVE / TPU;
+    static_assert(TPU * SUBS == WAVE && (SUBS & (SUBS - 1)) == 0, "variance lanes");
+    const int C = P.chunk, T = P.T, H = P.H;
+    const int NC = (T + C - 1) / C;
+    const long unit = (long)blockIdx.x * (256 / WAVE) + threadIdx.x / WAVE;
+    if (unit >= (long)P.B * H * NC)                    // whole waves
+        return;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int sub = lane / TPU, g = lane % TPU, i0 = g * N;
+    const long BH = (long)P.B * H;
+    const int bh = (int)(unit % BH), c = (int)(unit / BH);
+    const int b = bh / H, h = bh % H;
+    const int c0 = c * C, L = min(C, T - c0);
+    const int LS = C / SUBS;
+    const int tb = sub * LS, te = min(tb + LS, L);
+    const E *gk = static_cast<const E *>(P.k);
+    const E *ga = static_cast<const E *>(P.alpha);
+    const E *gx = static_cast<const E *>(P.xi);
+    const E *gr = static_cast<const E *>(P.r);
+    const float mdk = P.mu * (1.f / DK);
+    float4 *stat = reinterpret_cast<float4 *>(P.ws_stat) + ((long)bh * NC + c) * C;
+
+    Map2 m{1.f, 0.f, 0.f, 1.f};
+    const long row0 = ((long)b * T + c0) * H + h;
+#pragma unroll 2
+    for (int t = tb; t < te; ++t) {
+        const long row = row0 + (long)t * H;
+        float k[N], a[N], x[N];
+        load16(gk + row * DK + i0, k);
+        load16(ga + row * DK + i0, a);
+        load16(gx + row * DK + i0, x);
+        const float r = to_f32(gr[row]);
+        float sa = 0.f, sx = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            sa = fmaf(a[e], a[e], sa);
+            sx += x[e];
+            sk = fmaf(k[e], k[e], sk);
+        }
+#pragma unroll
+        for (int off = TPU / 2; off >= 1; off >>= 1) {
+            sa += __shfl_xor(sa, off, WAVE);
+            sx += __shfl_xor(sx, off, WAVE);
+            sk += __shfl_xor(sk, off, WAVE);
+        }
+        const float a2 = sa * (1.f / DK), xm = sx * (1.f / DK);
+        if (g == 0)
+            stat[t] = make_float4(a2, xm, sk, r);
+        const Map2 y = variance_step_map(a2, xm, mdk * sk, r);
+        m.after(y.a, y.b, y.c, y.d);
+        if (((t - tb) & 3) == 3)
+            m.rescale();
+    }
+#pragma unroll
+    for (int off = 1; off < SUBS; off <<= 1) {
+        const bool take = (sub & (2 * off - 1)) == 0;
+        const float ya = __shfl_down(m.a, off * TPU, WAVE);
+        const float yb = __shfl_down(m.b, off * TPU, WAVE);
+        const float yc = __shfl_down(m.c, off * TPU, WAVE);
+        const float yd = __shfl_down(m.d, off * TPU, WAVE);
+        if (take) {
+            m.after(ya, yb, yc, yd);
+            m.rescale();
+        }
+    }
+    if (lane == 0)
+        reinterpret_cast<float4 *>(P.ws_mob)[(long)bh * NC + c] =
+            make_float4(m.a, m.b, m.c, m.d);
+}
+
+// Isotropic KDN, one wave per batch*head: lane = segment of LEN chunks.  Each
+// lane composes its segment's chunk maps, an inclusive scan over the lanes
+// gives the map from p0 to every segment end, and each lane then applies its
+// chunk maps from its segment start, storing the variance at every chunk
+// start.  Dependent chain: LEN + 6 + LEN steps instead of NC.
+__global__ __launch_bounds__(WAVE) void iso_variance_scan_kernel(PrefillParams P) {
+    const int NC = (P.T + P.chunk - 1) / P.chunk;
+    const long bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int LEN = (NC + WAVE - 1) / WAVE;
+    const int cb = min(lane * LEN, NC), ce = min(cb + LEN, NC);
+    const float4 *mob = reinterpret_cast<const float4 *>(P.ws_mob) + bh * NC;
+    float *ps = P.ws_p0 + bh * NC;
+
+    Map2 m{1.f, 0.f, 0.f, 1.f};
+    for (int c = cb; c < ce; ++c) {
+        const float4 y = mob[c];
+        m.after(y.x, y.y, y.z, y.w);
+        if (((c - cb) & 3) == 3)
+            m.rescale();
+    }
+    m.rescale();
+#pragma unroll
+    for (int off = 1; off < WAVE; off <<= 1) {
+        const float ya = __shfl_up(m.a, off, WAVE), yb = __shfl_up(m.b, off, WAVE);
+        const float yc = __shfl_up(m.c, off, WAVE), yd = __shfl_up(m.d, off, WAVE);
+        if (lane >= off) {
+            m.before(ya, yb, yc, yd);
+            m.rescale();
+        }
+    }
+    const float p0 = P.p0[bh];
+    const float pe = m.apply(p0);                      // variance at segment end
+    float p = __shfl_up(pe, 1, WAVE);
+    if (lane == 0)
+        p = p0;
+    if (lane == WAVE - 1)
+        P.p_out[bh] = pe;
+    for (int c = cb; c < ce; ++c) {
+        const float4 y = mob[c];
+        ps[c] = p;
+        p = fmaf(y.x, p, y.y) / fmaf(y.z, p, y.w);
+    }
+}
+
+template <typename E, int DK>
+static hipError_t launch_iso_dk(const PrefillParams &P, hipStream_t st) {
+    const long bh = (long)P.B * P.H;
+    const long nc = (P.T + P.chunk - 1) / P.chunk;
+    if (nc > 0) {
+        constexpr int UPW = 256 / WAVE;
+        const dim3 grid((unsigned)((bh * nc + UPW - 1) / UPW)), block(256);
+        hipLaunchKernelGGL((iso_variance_chunk_kernel<E, DK>), grid, block, 0, st, P);
+        if (hipError_t e = hipGetLastError())
+            return e;
+    }
+    const dim3 grid((unsigned)bh), block(WAVE);
+    hipLaunchKernelGGL(iso_variance_scan_kernel, grid, block, 0, st, P);
+    return hipGetLastError();
+}
+
 template <typename E, int DK>
 static hipError_t launch_variance_dk(const PrefillParams &P, hipStream_t st) {
     const long bh = (long)P.B * P.H;
@@ -199,6 +331,13 @@ static hipError_t launch_variance_dk(const PrefillParams &P, hipStream_t st) {
 }
 
 hipError_t launch_variance_scan(const PrefillParams &P, hipStream_t st) {
+    if (P.variant == ISO_KDN) {
+        if (P.dk == 128)
+            return P.bf16 ? launch_iso_dk<bf16, 128>(P, st) : launch_iso_dk<float, 128>(P, st);
+        if (P.dk == 64)
+            return P.bf16 ? launch_iso_dk<bf16, 64>(P, st) : launch_iso_dk<float, 64>(P, st);
+        return hipErrorInvalidValue;
+    }
     if (P.dk == 128)
         return P.bf16 ? launch_variance_dk<bf16, 128>(P, st) : launch_variance_dk<float, 128>(P, st);
     if (P.dk == 64)

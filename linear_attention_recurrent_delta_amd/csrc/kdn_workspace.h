@@ -26,6 +26,10 @@
 //   Mob  [bh][chunk][DK][4] float32  per-chunk composition of the variance
 //                                    maps (Mobius form, kdn_variance.hip)
 //   P0   [bh][chunk][DK]    float32  variance at each chunk start
+// and for isotropic KDN (one variance per head):
+//   Mob  [bh][chunk][4]     float32
+//   Stat [bh][chunk][C][4]  float32  per token: mean a^2, mean xi, |k|^2, r
+//   P0   [bh][chunk]        float32
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -57,6 +61,7 @@ struct WsLayout {
     __host__ __device__ long records(long bh, long nc) const { return bh * nc * rec; }
     __host__ __device__ static long mobius_bytes(long bh, long nc, int DK) { return bh * nc * DK * 4 * 4; }
     __host__ __device__ static long p0_bytes(long bh, long nc, int DK) { return bh * nc * DK * 4; }
+    __host__ __device__ static long stat_bytes(long bh, long nc, int C) { return bh * nc * C * 16; }
 };
 
 // Number of chunks of a sequence of T tokens.

@@ -17,7 +17,18 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkdn.so")
 
 # kdn_variant / kdn_dtype / kdn_status values of include/kdn.h
-VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "diag_kdn": 3}
+VARIANTS = {"deltanet": 0, "gated_deltanet": 1, "kda": 2, "diag_kdn": 3, "iso_kdn": 4}
+
+
+def _p_shape(vid, N, H, dk):
+    """Shape of the variance tensor p: [N,H,dk] (diagonal KDN), [N,H]
+    (isotropic KDN), or None (no variance)."""
+    return (N, H, dk) if vid == 3 else ((N, H) if vid == 4 else None)
+
+
+def _new_p(vid, N, H, dk, device):
+    shp = _p_shape(vid, N, H, dk)
+    return None if shp is None else torch.empty(shp, dtype=torch.float32, device=device)
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "KDN_OK", 1: "KDN_ERR_NULL", 2: "KDN_ERR_SHAPE",
           3: "KDN_ERR_UNSUPPORTED", 4: "KDN_ERR_ALIGN", 5: "KDN_ERR_ALIAS",
@@ -179,7 +190,8 @@ def prefill(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
             obs_noise=None, S0=None, p0=None, mu=1.0, chunk=0, out=None,
             workspace="auto", stream=None):
     """Chunkwise prefill.  q, k [B,T,H,dk], v [B,T,H,dv] (float32 or bf16).
-    Returns (o, S, p); p is None unless variant is diag_kdn.  ``out`` may pass
+    Returns (o, S, p); p is None unless the variant is a KDN ([B,H,dk] for
+    diag_kdn, [B,H] for iso_kdn).  ``out`` may pass
     preallocated (o, S_out, p_out).  ``workspace``: "auto" allocates one for
     the two-pass schedule, None selects the single-pass kernel, a uint8
     tensor from :func:`workspace` is used as given."""
@@ -190,8 +202,7 @@ def prefill(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
     if out is None:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
         S = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-        p = (torch.empty((B, H, dk), dtype=torch.float32, device=q.device)
-             if vid == 3 else None)
+        p = _new_p(vid, B, H, dk, q.device)
     else:
         o, S, p = out
     if isinstance(workspace, str):
@@ -205,8 +216,8 @@ def prefill(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
 
 def decode(variant, q, k, v, S, p=None, alpha=None, beta=None, proc_noise=None,
            obs_noise=None, mu=1.0, o=None, stream=None):
-    """One decode step; S [N,H,dk,dv] (and p [N,H,dk]) are updated in place.
-    Returns o [N,H,dv]."""
+    """One decode step; S [N,H,dk,dv] (and p: [N,H,dk] for diag_kdn, [N,H]
+    for iso_kdn) are updated in place.  Returns o [N,H,dv]."""
     vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -221,17 +232,16 @@ def decode_multi(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
                  obs_noise=None, S0=None, p0=None, mu=1.0, out=None, stream=None):
     """T decode steps in one pass over the state (speculative verify).
     q, k [N,T,H,dk], v [N,T,H,dv]; S0 [N,H,dk,dv] (None: zeros) and p0
-    [N,H,dk] are read, not modified, unless ``out`` passes them as S_out /
-    p_out (in place).  Returns (o [N,T,H,dv], S_out, p_out); p_out is None
-    unless variant is diag_kdn."""
+    ([N,H,dk] diag_kdn, [N,H] iso_kdn) are read, not modified, unless ``out``
+    passes them as S_out / p_out (in place).  Returns (o [N,T,H,dv], S_out,
+    p_out); p_out is None unless the variant is a KDN."""
     vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     N, T, H, dk = q.shape
     dv = v.shape[-1]
     if out is None:
         o = torch.empty((N, T, H, dv), dtype=q.dtype, device=q.device)
         S = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-        p = (torch.empty((N, H, dk), dtype=torch.float32, device=q.device)
-             if vid == 3 else None)
+        p = _new_p(vid, N, H, dk, q.device)
     else:
         o, S, p = out
     kdn_recurrent_decode_multi(vid, DTYPES[q.dtype], N, T, H, dk, dv, mu, q, k, v,

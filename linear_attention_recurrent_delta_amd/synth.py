@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the delta-rule / diagonal-KDN workloads.
+"""Seeded synthetic inputs for the delta-rule / KDN workloads.
 
 This module holds input distributions only: it draws random tensors, shapes
 them, normalises keys and rounds to the device dtype.  It contains none of the
@@ -13,9 +13,10 @@ sequence lengths inside the 2K-32K range the KDN write-up sweeps (page "ç»™è®°å¿
   DeltaNet case);
 * beta = sigmoid(N(0, 1)) per token and head;
 * Gated DeltaNet retention alpha = exp(-softplus(N(0, 1)) * 0.1) per token/head;
-* KDA / diagonal-KDN retention alpha = exp(-softplus(N(-2, 1))) per channel;
+* KDA / KDN retention alpha = exp(-softplus(N(-2, 1))) per channel;
 * KDN process noise xi = softplus(N(-3, 1)) per channel, observation noise
-  r = softplus(N(0, 1)) per token/head, initial variance p0 = 1.
+  r = softplus(N(0, 1)) per token/head, initial variance p0 = 1 (per channel
+  for diagonal KDN, per head for isotropic KDN).
 
 Draw order: q, k, v, alpha, beta, xi, r (those the variant uses).  Values are
 drawn in float32 and rounded to the device dtype (round-to-nearest-even);
@@ -40,7 +41,11 @@ CONFIGS = {
                      dv=128, dtype="bf16", chunk=64, q_norm=False),
     "decode_diag_kdn": dict(index=4, variant="diag_kdn", N=256, H=32, steps=1024,
                             dk=128, dv=128, dtype="bf16", q_norm=False),
+    "iso_kdn": dict(index=5, variant="iso_kdn", B=2, H=16, T=16384, dk=128,
+                    dv=128, dtype="bf16", chunk=64, q_norm=False),
 }
+
+KDN_VARIANTS = ("diag_kdn", "iso_kdn")
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -63,10 +68,11 @@ def gen_prefill(variant, B, T, H, dk, dv, dtype="bf16", seed=SEED_BASE,
     """Draw one batch of prefill inputs.
 
     Returns a dict with q, k [B,T,H,dk], v [B,T,H,dv] in ``dtype``; ``alpha``
-    ([B,T,H] for gated_deltanet, [B,T,H,dk] for kda/diag_kdn) and ``beta``
-    [B,T,H] (not diag_kdn), ``xi`` [B,T,H,dk] and ``r`` [B,T,H] (diag_kdn) in
-    ``dtype``; ``S0`` [B,H,dk,dv] float32 (None unless ``random_state``) and
-    ``p0`` [B,H,dk] float32 (diag_kdn; ones unless ``random_state``).
+    ([B,T,H] for gated_deltanet, [B,T,H,dk] for kda and the KDNs) and
+    ``beta`` [B,T,H] (not the KDNs), ``xi`` [B,T,H,dk] and ``r`` [B,T,H]
+    (KDNs) in ``dtype``; ``S0`` [B,H,dk,dv] float32 (None unless
+    ``random_state``) and ``p0`` float32, [B,H,dk] for diag_kdn and [B,H] for
+    iso_kdn (ones unless ``random_state``).
     """
     tdt = TORCH_DTYPES[dtype]
     gen = torch.Generator(device=device)
@@ -81,24 +87,25 @@ def gen_prefill(variant, B, T, H, dk, dv, dtype="bf16", seed=SEED_BASE,
     if variant == "gated_deltanet":
         a = _normal(gen, (B, T, H), device=device)
         out["alpha"] = torch.exp(-F.softplus(a) * 0.1).to(tdt)
-    elif variant in ("kda", "diag_kdn"):
+    elif variant in ("kda",) + KDN_VARIANTS:
         a = _normal(gen, (B, T, H, dk), mean=-2.0, device=device)
         out["alpha"] = torch.exp(-F.softplus(a)).to(tdt)
-    if variant != "diag_kdn":
+    if variant not in KDN_VARIANTS:
         out["beta"] = torch.sigmoid(_normal(gen, (B, T, H), device=device)).to(tdt)
     else:
         out["xi"] = F.softplus(_normal(gen, (B, T, H, dk), mean=-3.0,
                                        device=device)).to(tdt)
         out["r"] = F.softplus(_normal(gen, (B, T, H), device=device)).to(tdt)
+    pshape = (B, H, dk) if variant == "diag_kdn" else (B, H)
     if random_state:
         out["S0"] = (0.5 * _normal(gen, (B, H, dk, dv), device=device)).contiguous()
-        if variant == "diag_kdn":
-            out["p0"] = torch.rand((B, H, dk), generator=gen, device=device,
+        if variant in KDN_VARIANTS:
+            out["p0"] = torch.rand(pshape, generator=gen, device=device,
                                    dtype=torch.float32) + 0.5
     else:
         out["S0"] = None
-        if variant == "diag_kdn":
-            out["p0"] = torch.ones((B, H, dk), dtype=torch.float32, device=device)
+        if variant in KDN_VARIANTS:
+            out["p0"] = torch.ones(pshape, dtype=torch.float32, device=device)
     return out
 
 
@@ -125,9 +132,9 @@ def gen_decode(N, H, steps, dk, dv, dtype="bf16", seed=SEED_BASE + 4,
     names = ["q", "k", "v"]
     if variant == "gated_deltanet":
         names += ["alpha"]
-    elif variant in ("kda", "diag_kdn"):
+    elif variant in ("kda",) + KDN_VARIANTS:
         names += ["alpha"]
-    names += ["beta"] if variant != "diag_kdn" else ["xi", "r"]
+    names += ["beta"] if variant not in KDN_VARIANTS else ["xi", "r"]
     out = {}
     for n in names:
         if n in ("beta", "r") or (n == "alpha" and variant == "gated_deltanet"):
@@ -150,10 +157,10 @@ def gen_decode(N, H, steps, dk, dv, dtype="bf16", seed=SEED_BASE + 4,
         if variant == "gated_deltanet":
             a = _normal(gen, (n_, N, H), device=device)
             out["alpha"][s0:s1] = torch.exp(-F.softplus(a) * 0.1).to(tdt)
-        elif variant in ("kda", "diag_kdn"):
+        elif variant in ("kda",) + KDN_VARIANTS:
             a = _normal(gen, (n_, N, H, dk), mean=-2.0, device=device)
             out["alpha"][s0:s1] = torch.exp(-F.softplus(a)).to(tdt)
-        if variant != "diag_kdn":
+        if variant not in KDN_VARIANTS:
             out["beta"][s0:s1] = torch.sigmoid(
                 _normal(gen, (n_, N, H), device=device)).to(tdt)
         else:
@@ -164,6 +171,8 @@ def gen_decode(N, H, steps, dk, dv, dtype="bf16", seed=SEED_BASE + 4,
     out["S0"] = torch.zeros((N, H, dk, dv), dtype=torch.float32, device=device)
     if variant == "diag_kdn":
         out["p0"] = torch.ones((N, H, dk), dtype=torch.float32, device=device)
+    elif variant == "iso_kdn":
+        out["p0"] = torch.ones((N, H), dtype=torch.float32, device=device)
     return out
 
 

@@ -74,7 +74,7 @@ def test_chunk_size_query(lib):
 
 def _prefill_args(variant=1, dtype=1, B=2, T=100, H=4, dk=128, dv=128, chunk=0,
                   **over):
-    kdn_ = variant == 3
+    kdn_ = variant in (3, 4)
     a = dict(q=A, k=A + MB, v=A + 2 * MB,
              alpha=None if variant == 0 else A + 3 * MB,
              beta=None if kdn_ else A + 4 * MB,
@@ -103,6 +103,9 @@ def test_workspace_size_query(lib):
     assert _ws_size(lib) == (2 * 4 * 2 * rec, OK)                # T = 100: 2 chunks
     kdn_extra = 128 * 4 * 4 + 128 * 4                            # variance maps, p0
     assert _ws_size(lib, variant=3) == (2 * 4 * 2 * (rec + kdn_extra), OK)
+    iso_extra = 4 * 4 + 64 * 4 * 4 + 4                           # map, token sums, p0
+    assert iso_extra == 1044
+    assert _ws_size(lib, variant=4) == (2 * 4 * 2 * (rec + iso_extra), OK)
     # float32, d_k = 128: default chunk 32, record rounded up to 256 bytes
     rec32 = 3 * 32 * 128 * 4 + 2 * 32 * 32 * 4 + 128 * 4
     assert _ws_size(lib, dtype=0) == (2 * 4 * 4 * ((rec32 + 255) // 256 * 256), OK)
@@ -137,7 +140,7 @@ def test_workspace_validation(lib):
 
 
 def _decode_args(variant=3, dtype=1, N=8, H=4, dk=128, dv=128, **over):
-    kdn_ = variant == 3
+    kdn_ = variant in (3, 4)
     a = dict(q=A, k=A + MB, v=A + 2 * MB,
              alpha=None if variant == 0 else A + 3 * MB,
              beta=None if kdn_ else A + 4 * MB,
@@ -181,6 +184,15 @@ PREFILL_CASES = [
     ("S_out partially overlaps S0", dict(S_out=A + 7 * MB + 1024), EALIAS),
     ("o overlaps S_out", dict(o=A + 10 * MB + 16), EALIAS),
     ("KDN p_out equals p0", dict(variant=3, p_out=A + 8 * MB), EALIAS),
+    ("iso KDN with beta", dict(variant=4, beta=A + 4 * MB), ENULL),
+    ("iso KDN without proc noise", dict(variant=4, xi=None), ENULL),
+    ("iso KDN without p0", dict(variant=4, p0=None), ENULL),
+    ("iso KDN odd p0", dict(variant=4, p0=A + 8 * MB + 2), EALIGN),
+    # p is [B, H] for isotropic KDN: 4-byte alignment suffices, and 4 bytes
+    # past p0 still overlaps it ([B, H, d_k] needs 16 bytes: misaligned)
+    ("iso KDN p_out 4 B past p0", dict(variant=4, p_out=A + 8 * MB + 4), EALIAS),
+    ("diag KDN p_out 4 B past p0", dict(variant=3, p_out=A + 8 * MB + 4), EALIGN),
+    ("iso KDN p_out overlaps S_out", dict(variant=4, p_out=A + 10 * MB + 12), EALIAS),
 ]
 
 
@@ -203,6 +215,10 @@ DECODE_CASES = [
     ("o overlaps S", dict(o=A + 7 * MB + 512), EALIAS),
     ("S overlaps k", dict(S=A + MB), EALIAS),
     ("p overlaps S", dict(p=A + 7 * MB + 256), EALIAS),
+    ("iso KDN with beta", dict(variant=4, beta=A + 4 * MB), ENULL),
+    ("iso KDN without p", dict(variant=4, p=None), ENULL),
+    ("iso KDN odd p", dict(variant=4, p=A + 8 * MB + 1), EALIGN),
+    ("iso KDN p overlaps o", dict(variant=4, p=A + 9 * MB + 4), EALIAS),
 ]
 
 
@@ -212,7 +228,7 @@ def test_decode_validation(lib, name, over, status):
 
 
 def _multi_args(variant=3, dtype=1, N=8, T=4, H=4, dk=128, dv=128, **over):
-    kdn_ = variant == 3
+    kdn_ = variant in (3, 4)
     a = dict(q=A, k=A + MB, v=A + 2 * MB,
              alpha=None if variant == 0 else A + 3 * MB,
              beta=None if kdn_ else A + 4 * MB,
@@ -247,6 +263,9 @@ MULTI_CASES = [
     ("p_out partially overlaps p0", dict(p_out=A + 8 * MB + 16), EALIAS),
     ("p_out overlaps S0", dict(p_out=A + 7 * MB + 64), EALIAS),
     ("o overlaps p_out", dict(o=A + 11 * MB), EALIAS),
+    ("iso KDN without r", dict(variant=4, r=None), ENULL),
+    ("iso KDN odd p_out", dict(variant=4, p_out=A + 11 * MB + 2), EALIGN),
+    ("iso KDN p_out partially overlaps p0", dict(variant=4, p_out=A + 8 * MB + 4), EALIAS),
 ]
 
 

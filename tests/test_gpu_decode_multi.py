@@ -17,7 +17,7 @@ from linear_attention_recurrent_delta_amd import kdn, synth
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["deltanet", "gated_deltanet", "kda", "diag_kdn"]
+VARIANTS = ["deltanet", "gated_deltanet", "kda", "diag_kdn", "iso_kdn"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -122,7 +122,7 @@ def test_decode_multi_in_place(variant):
         assert torch.equal(p, p_ref)
 
 
-@pytest.mark.parametrize("variant", ["gated_deltanet", "diag_kdn"])
+@pytest.mark.parametrize("variant", ["gated_deltanet", "diag_kdn", "iso_kdn"])
 def test_decode_multi_null_state_is_zero(variant):
     log(f"decode_multi S0 = NULL {variant}")
     inp = _inputs(variant, 2, 4, 2, 128, 128, "bf16", seed=80)
@@ -132,10 +132,11 @@ def test_decode_multi_null_state_is_zero(variant):
         assert (x is None and y is None) or torch.equal(x, y)
 
 
-def test_decode_multi_kdn_mu():
-    log("decode_multi diag_kdn mu = d_k")
-    inp = _inputs("diag_kdn", 3, 9, 2, 128, 128, "f32", seed=90)
-    compare_prefill("diag_kdn", inp, _multi("diag_kdn", inp, mu=128.0), TOL["f32"],
+@pytest.mark.parametrize("variant", ["diag_kdn", "iso_kdn"])
+def test_decode_multi_kdn_mu(variant):
+    log(f"decode_multi {variant} mu = d_k")
+    inp = _inputs(variant, 3, 9, 2, 128, 128, "f32", seed=90)
+    compare_prefill(variant, inp, _multi(variant, inp, mu=128.0), TOL["f32"],
                     mu=128.0)
 
 

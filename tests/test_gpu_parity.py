@@ -20,7 +20,8 @@ from linear_attention_recurrent_delta_amd import kdn, synth
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["deltanet", "gated_deltanet", "kda", "diag_kdn"]
+VARIANTS = ["deltanet", "gated_deltanet", "kda", "diag_kdn", "iso_kdn"]
+KDNS = ("diag_kdn", "iso_kdn")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -71,7 +72,8 @@ def test_prefill_chunk32(variant, dtype):
 
 @pytest.mark.parametrize("T", [0, 1, 2, 15, 16, 63, 64, 65, 128, 129])
 @pytest.mark.parametrize("variant,dtype", [("diag_kdn", "bf16"), ("deltanet", "f32"),
-                                           ("kda", "bf16")])
+                                           ("kda", "bf16"), ("iso_kdn", "bf16"),
+                                           ("iso_kdn", "f32")])
 def test_prefill_lengths(variant, dtype, T):
     log(f"prefill length T={T} {variant} {dtype}")
     inp = _inputs(variant, 2, T, 2, 128, 128, dtype, seed=13 + T)
@@ -79,16 +81,17 @@ def test_prefill_lengths(variant, dtype, T):
     compare_prefill(variant, inp, got, TOL[dtype])
 
 
+@pytest.mark.parametrize("variant", KDNS)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefill_kdn_mu(dtype):
+def test_prefill_kdn_mu(variant, dtype):
     for mu in (128.0, 0.25):
-        log(f"prefill diag_kdn mu={mu} {dtype}")
-        inp = _inputs("diag_kdn", 2, 300, 2, 128, 128, dtype, seed=14)
-        got = gpu_prefill("diag_kdn", inp, mu=mu)
-        compare_prefill("diag_kdn", inp, got, TOL[dtype], mu=mu)
+        log(f"prefill {variant} mu={mu} {dtype}")
+        inp = _inputs(variant, 2, 300, 2, 128, 128, dtype, seed=14)
+        got = gpu_prefill(variant, inp, mu=mu)
+        compare_prefill(variant, inp, got, TOL[dtype], mu=mu)
 
 
-@pytest.mark.parametrize("variant", ["gated_deltanet", "kda", "diag_kdn"])
+@pytest.mark.parametrize("variant", ["gated_deltanet", "kda", "diag_kdn", "iso_kdn"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_alpha_zero(variant, dtype):
     """alpha = 0 (full erase) on some tokens: the chunks containing them take
@@ -105,7 +108,7 @@ def test_prefill_alpha_zero(variant, dtype):
     compare_prefill(variant, inp, got, TOL[dtype])
 
 
-@pytest.mark.parametrize("variant", ["gated_deltanet", "kda", "diag_kdn"])
+@pytest.mark.parametrize("variant", ["gated_deltanet", "kda", "diag_kdn", "iso_kdn"])
 def test_prefill_strong_decay(variant):
     """A chunk whose cumulative decay drops below 2^-90 (tiny alpha)."""
     log(f"prefill strong decay {variant}")
@@ -117,18 +120,28 @@ def test_prefill_strong_decay(variant):
     compare_prefill(variant, inp, got, TOL["bf16"])
 
 
-def test_prefill_kdn_degenerate_values():
-    log("prefill diag_kdn p0 = 0, xi = 0 (zero write); tiny r")
-    inp = _inputs("diag_kdn", 1, 130, 2, 128, 128, "bf16", seed=17)
+@pytest.mark.parametrize("variant", KDNS)
+def test_prefill_kdn_degenerate_values(variant):
+    log(f"prefill {variant} p0 = 0, xi = 0 (zero write); tiny r; r = 0")
+    inp = _inputs(variant, 1, 130, 2, 128, 128, "bf16", seed=17)
     z = dict(inp)
     z["p0"] = torch.zeros_like(inp["p0"])
     z["xi"] = torch.zeros_like(inp["xi"])
-    o, S, p = gpu_prefill("diag_kdn", z)
+    o, S, p = gpu_prefill(variant, z)
     assert torch.count_nonzero(p).item() == 0
-    compare_prefill("diag_kdn", z, (o, S, p), TOL["bf16"])
+    compare_prefill(variant, z, (o, S, p), TOL["bf16"])
     t = dict(inp)
     t["r"] = torch.full_like(inp["r"], 1e-6)
-    compare_prefill("diag_kdn", t, gpu_prefill("diag_kdn", t), TOL["bf16"])
+    compare_prefill(variant, t, gpu_prefill(variant, t), TOL["bf16"])
+    # exact observations on a few tokens (r = 0, keys nonzero): the variance
+    # drops to 0 there and the write replaces the value along k
+    e = dict(inp)
+    r = inp["r"].clone()
+    r[:, 5] = 0
+    r[:, 64:67] = 0
+    r[:, 129] = 0
+    e["r"] = r
+    compare_prefill(variant, e, gpu_prefill(variant, e), TOL["bf16"])
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -138,7 +151,7 @@ def test_prefill_state_in_place(variant):
     ref = oracle_prefill(variant, inp)
     S = inp["S0"].clone()
     o = torch.empty((2, 100, 2, 128), dtype=torch.bfloat16, device="cuda")
-    p = torch.empty_like(inp["p0"]) if variant == "diag_kdn" else None
+    p = torch.empty_like(inp["p0"]) if variant in KDNS else None
     inp2 = dict(inp)
     inp2["S0"] = S
     gpu_prefill(variant, inp2, out=(o, S, p))
@@ -169,11 +182,12 @@ def test_prefill_continuation(variant):
         check("p (two calls)", np64(p2), ref[2], TOL["bf16"])
 
 
-def test_prefill_deterministic():
-    log("prefill bitwise determinism")
-    inp = _inputs("diag_kdn", 2, 500, 4, 128, 128, "bf16", seed=20)
-    a = gpu_prefill("diag_kdn", inp)
-    b = gpu_prefill("diag_kdn", inp)
+@pytest.mark.parametrize("variant", KDNS)
+def test_prefill_deterministic(variant):
+    log(f"prefill bitwise determinism {variant}")
+    inp = _inputs(variant, 2, 500, 4, 128, 128, "bf16", seed=20)
+    a = gpu_prefill(variant, inp)
+    b = gpu_prefill(variant, inp)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
@@ -193,7 +207,7 @@ def test_decode_small(variant, dtype, dk, dv):
                          variant=variant)
     g = torch.Generator(device="cuda").manual_seed(5)
     d["S0"] = 0.5 * torch.randn(d["S0"].shape, generator=g, device="cuda")
-    if variant != "diag_kdn":
+    if variant not in KDNS:
         d.pop("p0", None)
     os_, S, p = gpu_decode_run(variant, d)
     pre = decode_inputs_as_prefill(d)
@@ -209,7 +223,7 @@ def test_prefill_equals_repeated_decode(variant):
     log(f"prefill vs decode {variant}")
     d = synth.gen_decode(3, 2, 70, 128, 128, "bf16", seed=22, device="cuda",
                          variant=variant)
-    if variant != "diag_kdn":
+    if variant not in KDNS:
         d.pop("p0", None)
     os_, S, p = gpu_decode_run(variant, d)
     pre = {k: (v.contiguous() if isinstance(v, torch.Tensor) else v)
@@ -220,7 +234,7 @@ def test_prefill_equals_repeated_decode(variant):
 
 
 # ---------------------------------------------------------------------------
-# The five workloads at full size.
+# The workloads at full size.
 # ---------------------------------------------------------------------------
 def test_workload_deltanet_fp32_full():
     log("workload DeltaNet fp32 B1 H2 T256 d64: every output")
@@ -233,6 +247,7 @@ def test_workload_deltanet_fp32_full():
     ("gated_deltanet", [(0, 0), (3, 15), (2, 7)]),
     ("kda", [(0, 0), (1, 31)]),
     ("diag_kdn", [(0, 0), (1, 15)]),
+    ("iso_kdn", [(0, 0), (1, 9)]),
 ])
 def test_workload_full_size_sampled(name, heads):
     c = synth.CONFIGS[name]
