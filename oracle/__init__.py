@@ -50,6 +50,9 @@ class OracleLib:
         lib.kdn_oracle_recurrence.argtypes = (
             [ctypes.c_int] + [ctypes.c_long] * 5 + [ctypes.c_double]
             + [dp] * 12 + [ctypes.c_int])
+        lib.kdn_oracle_backward.restype = ctypes.c_int
+        lib.kdn_oracle_backward.argtypes = (
+            [ctypes.c_int] + [ctypes.c_long] * 5 + [dp] * 14 + [ctypes.c_int])
         lib.kdn_oracle_max_threads.restype = ctypes.c_int
         lib.kdn_oracle_max_threads.argtypes = []
         self.lib = lib
@@ -62,6 +65,12 @@ class OracleLib:
                    r=None, S0=None, p0=None, mu=1.0, nthreads=0):
         return _run(self.lib, variant, q, k, v, alpha, beta, xi, r, S0, p0, mu,
                     nthreads)
+
+
+    def backward(self, variant, q, k, v, alpha=None, beta=None, S0=None, dO=None,
+                 dS_T=None, nthreads=0):
+        return _run_backward(self.lib, variant, q, k, v, alpha, beta, S0, dO, dS_T,
+                             nthreads)
 
 
 def load() -> OracleLib:
@@ -139,3 +148,46 @@ def _run(lib, variant, q, k, v, alpha, beta, xi, r, S0, p0, mu, nthreads):
     if rc != 0:
         raise RuntimeError(f"kdn_oracle_recurrence failed with code {rc}")
     return o, S, p
+
+
+def backward(variant, q, k, v, alpha=None, beta=None, S0=None, dO=None, dS_T=None,
+             nthreads=0):
+    """Gradients of a scalar loss through the recurrence (DeltaNet, Gated
+    DeltaNet, KDA), given dO = dL/do [B,T,H,dv] and dS_T = dL/dS_final
+    [B,H,dk,dv] (None: zero).
+
+    Returns ``(dq, dk, dv, dalpha, dbeta, dS0)``; dalpha is dL/dalpha
+    ([B,T,H] for Gated DeltaNet, [B,T,H,dk] for KDA, None for DeltaNet).
+    """
+    return load().backward(variant, q, k, v, alpha, beta, S0, dO, dS_T, nthreads)
+
+
+def _run_backward(lib, variant, q, k, v, alpha, beta, S0, dO, dS_T, nthreads):
+    vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    if vid not in (0, 1, 2):
+        raise ValueError("oracle backward: write-strength variants only")
+    q = np.asarray(q)
+    B, T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    q = _f64(q, (B, T, H, dk), "q")
+    k = _f64(k, (B, T, H, dk), "k")
+    v = _f64(v, (B, T, H, dv), "v")
+    ashape = (B, T, H) if vid == 1 else (B, T, H, dk)
+    alpha = _f64(alpha, ashape, "alpha") if vid != 0 else None
+    beta = _f64(beta, (B, T, H), "beta")
+    S0 = _f64(S0, (B, H, dk, dv), "S0") if S0 is not None else None
+    dO = _f64(dO, (B, T, H, dv), "dO")
+    dS_T = _f64(dS_T, (B, H, dk, dv), "dS_T") if dS_T is not None else None
+    dq = np.zeros((B, T, H, dk))
+    dk_ = np.zeros((B, T, H, dk))
+    dv_ = np.zeros((B, T, H, dv))
+    da = np.zeros(ashape) if vid != 0 else None
+    db = np.zeros((B, T, H))
+    dS0 = np.zeros((B, H, dk, dv))
+    rc = lib.kdn_oracle_backward(
+        vid, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(da),
+        _ptr(db), _ptr(dS0), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"kdn_oracle_backward failed with code {rc}")
+    return dq, dk_, dv_, da, db, dS0

@@ -259,3 +259,175 @@ int kdn_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* --------------------------------------------------------------------------
+ * Gradients of the recurrence for the write-strength variants (DeltaNet,
+ * Gated DeltaNet, KDA).
+ *
+ * The pages give no gradient.  What is computed here is the exact derivative
+ * of the recurrence above by reverse-mode differentiation of its steps, token
+ * by token in reverse order.  For a scalar loss L with dL/do_t = do_t and
+ * dL/dS_T = dS_T (S_t: the memory after token t, S_0 the initial one):
+ *   step 6  o_t = S_t^T q_t:         dS_t += q_t do_t^T,  dq_t = S_t do_t
+ *   step 5  S_t = S- + w e^T:        dw = dS_t e_t,  de = dS_t^T w,  dv_t = de
+ *   step 4  e = v_t - S-^T k_t:      dS- = dS_t - k_t de^T,  dk_t = -S- de
+ *   step 2  w = beta_t k_t:          dk_t += beta_t dw,  dbeta_t = k_t . dw
+ *   step 3  S- = diag(a_t) S_{t-1}:  da_t,i = sum_j dS-[i,j] S_{t-1}[i,j],
+ *                                    dS_{t-1} = diag(a_t) dS-
+ * and dS_0 is the gradient of the initial memory.  The decay gradient is
+ * returned per token for Gated DeltaNet (sum over channels of da_t) and per
+ * token and channel for KDA.  The memories S_0 .. S_T of one stream are kept
+ * (T + 1 matrices of dk x dv).
+ * ------------------------------------------------------------------------ */
+
+/* Steps 1-5 of one token for the write-strength variants: S_prev -> S_next,
+ * with S- (the decayed memory) and the error e left in Sm and e. */
+static void step_beta(int variant, long dk, long dv, long tok, const double *k,
+                      const double *v, const double *alpha, const double *beta,
+                      const double *S_prev, double *S_next, double *Sm,
+                      double *a, double *e)
+{
+    const double *kt = k + tok * dk;
+    const double *vt = v + tok * dv;
+    for (long i = 0; i < dk; ++i)
+        a[i] = variant == ORC_DELTANET ? 1.0
+             : (variant == ORC_GATED_DELTANET ? alpha[tok] : alpha[tok * dk + i]);
+    for (long i = 0; i < dk; ++i)
+        for (long j = 0; j < dv; ++j)
+            Sm[i * dv + j] = a[i] * S_prev[i * dv + j];
+    for (long j = 0; j < dv; ++j) {
+        double r = 0.0;
+        for (long i = 0; i < dk; ++i)
+            r += Sm[i * dv + j] * kt[i];
+        e[j] = vt[j] - r;
+    }
+    const double bt = beta[tok];
+    for (long i = 0; i < dk; ++i)
+        for (long j = 0; j < dv; ++j)
+            S_next[i * dv + j] = Sm[i * dv + j] + bt * kt[i] * e[j];
+}
+
+/* Returns 0 on success, a negative code on a bad argument.  S0 and dS_T may
+ * be NULL (zero).  Gradients: dq, dk [B,T,H,dk]; dv [B,T,H,dv]; dalpha
+ * [B,T,H] (Gated DeltaNet) or [B,T,H,dk] (KDA), NULL for DeltaNet; dbeta
+ * [B,T,H]; dS0 [B,H,dk,dv]. */
+int kdn_oracle_backward(int variant, long B, long T, long H, long dk, long dv,
+                        const double *q, const double *k, const double *v,
+                        const double *alpha, const double *beta, const double *S0,
+                        const double *dO, const double *dS_T,
+                        double *dq, double *dk_out, double *dv_out,
+                        double *dalpha, double *dbeta, double *dS0, int nthreads)
+{
+    if (variant < ORC_DELTANET || variant > ORC_KDA)
+        return -1;
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return -2;
+    if (!q || !k || !v || !beta || !dO || !dq || !dk_out || !dv_out || !dbeta || !dS0)
+        return -3;
+    if (variant != ORC_DELTANET && (!alpha || !dalpha))
+        return -4;
+
+    const long BH = B * H, SZ = dk * dv;
+    int fail = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (long bh = 0; bh < BH; ++bh) {
+        const long b = bh / H, h = bh % H;
+        double *Sall = (double *)malloc(sizeof(double) * (T + 1) * SZ);
+        double *buf = (double *)malloc(sizeof(double) * (3 * SZ + 2 * dk + 2 * dv));
+        if (!Sall || !buf) {
+            free(Sall);
+            free(buf);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            fail = 1;
+            continue;
+        }
+        double *Sm = buf, *dS = buf + SZ, *dSm = buf + 2 * SZ;
+        double *a = buf + 3 * SZ, *dw = a + dk, *e = dw + dk, *de = e + dv;
+
+        /* forward: the memories after every token */
+        if (S0)
+            memcpy(Sall, S0 + bh * SZ, sizeof(double) * SZ);
+        else
+            memset(Sall, 0, sizeof(double) * SZ);
+        for (long t = 0; t < T; ++t) {
+            const long tok = (b * T + t) * H + h;
+            step_beta(variant, dk, dv, tok, k, v, alpha, beta, Sall + t * SZ,
+                      Sall + (t + 1) * SZ, Sm, a, e);
+        }
+
+        /* reverse */
+        if (dS_T)
+            memcpy(dS, dS_T + bh * SZ, sizeof(double) * SZ);
+        else
+            memset(dS, 0, sizeof(double) * SZ);
+        for (long t = T - 1; t >= 0; --t) {
+            const long tok = (b * T + t) * H + h;
+            const double *qt = q + tok * dk, *kt = k + tok * dk;
+            const double *dot = dO + tok * dv;
+            const double *St = Sall + (t + 1) * SZ, *Sp = Sall + t * SZ;
+            /* step 6 */
+            for (long i = 0; i < dk; ++i) {
+                double r = 0.0;
+                for (long j = 0; j < dv; ++j) {
+                    dS[i * dv + j] += qt[i] * dot[j];
+                    r += St[i * dv + j] * dot[j];
+                }
+                dq[tok * dk + i] = r;
+            }
+            /* recompute S- and e of this token (dSm receives the recomputed
+             * S_t, unused, and is overwritten below) */
+            step_beta(variant, dk, dv, tok, k, v, alpha, beta, Sp, dSm, Sm, a, e);
+            const double bt = beta[tok];
+            /* step 5 */
+            for (long i = 0; i < dk; ++i) {
+                double r = 0.0;
+                for (long j = 0; j < dv; ++j)
+                    r += dS[i * dv + j] * e[j];
+                dw[i] = r;
+            }
+            for (long j = 0; j < dv; ++j) {
+                double r = 0.0;
+                for (long i = 0; i < dk; ++i)
+                    r += dS[i * dv + j] * bt * kt[i];
+                de[j] = r;
+                dv_out[tok * dv + j] = r;
+            }
+            /* steps 4 and 2 */
+            double db = 0.0;
+            for (long i = 0; i < dk; ++i) {
+                double r = 0.0;
+                for (long j = 0; j < dv; ++j) {
+                    dSm[i * dv + j] = dS[i * dv + j] - kt[i] * de[j];
+                    r += Sm[i * dv + j] * de[j];
+                }
+                dk_out[tok * dk + i] = -r + bt * dw[i];
+                db += kt[i] * dw[i];
+            }
+            dbeta[tok] = db;
+            /* step 3 */
+            double dag = 0.0;
+            for (long i = 0; i < dk; ++i) {
+                double r = 0.0;
+                for (long j = 0; j < dv; ++j) {
+                    r += dSm[i * dv + j] * Sp[i * dv + j];
+                    dS[i * dv + j] = a[i] * dSm[i * dv + j];
+                }
+                if (variant == ORC_KDA)
+                    dalpha[tok * dk + i] = r;
+                dag += r;
+            }
+            if (variant == ORC_GATED_DELTANET)
+                dalpha[tok] = dag;
+        }
+        memcpy(dS0 + bh * SZ, dS, sizeof(double) * SZ);
+        free(Sall);
+        free(buf);
+    }
+    return fail ? -7 : 0;
+}

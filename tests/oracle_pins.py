@@ -654,3 +654,96 @@ def pin_empty_sequence(rec):
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+# ---------------------------------------------------------------------------
+# Gradients (write-strength variants).  The pages give no gradient; the
+# oracle's backward is the exact derivative of the recurrence, pinned here to
+# the (pinned) forward oracle by central differences and to closed forms.
+# Each ``bwd_pin_*`` takes (rec, bwd) with the signatures of
+# ``oracle.recurrence`` and ``oracle.backward``.
+# ---------------------------------------------------------------------------
+BWD_VARIANTS = ("deltanet", "gated_deltanet", "kda")
+GRAD_NAMES = ("q", "k", "v", "alpha", "beta", "S0")
+
+
+def _bwd_inputs(variant, B, T, H, dk, dv, seed):
+    inp = _random_inputs(variant, B, T, H, dk, dv, seed)
+    g = _rng(seed + 500)
+    inp["k"] = inp["k"] * g.uniform(0.5, 1.5, inp["k"].shape[:-1] + (1,))
+    return inp
+
+
+def _grads(bwd, variant, inp, dO, dS):
+    dq, dk, dv, da, db, dS0 = bwd(variant, inp["q"], inp["k"], inp["v"], inp.get("alpha"),
+                                  inp["beta"], inp.get("S0"), dO, dS)
+    return dict(q=dq, k=dk, v=dv, alpha=da, beta=db, S0=dS0)
+
+
+def bwd_pin_finite_differences(rec, bwd):
+    """<grad, delta> equals the central difference of L = <o, R_o> + <S_T, R_S>
+    along a random delta, for every input tensor and every variant."""
+    for vi, variant in enumerate(BWD_VARIANTS):
+        inp = _bwd_inputs(variant, 2, 9, 2, 4, 3, seed=70 + vi)
+        g = _rng(80 + vi)
+        Ro = g.standard_normal(inp["v"].shape)
+        RS = g.standard_normal(inp["S0"].shape)
+
+        def loss(x):
+            o, S, _ = rec(variant, **x)
+            return float(np.sum(o * Ro) + np.sum(S * RS))
+
+        grads = _grads(bwd, variant, inp, Ro, RS)
+        for name in GRAD_NAMES:
+            if grads[name] is None:
+                continue
+            d = g.standard_normal(inp[name].shape)
+            eps = 1e-6
+            xp = dict(inp); xp[name] = inp[name] + eps * d
+            xm = dict(inp); xm[name] = inp[name] - eps * d
+            fd = (loss(xp) - loss(xm)) / (2 * eps)
+            an = float(np.sum(grads[name] * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (variant, name, fd, an)
+
+
+def bwd_pin_deltanet_beta_zero_closed_form(rec, bwd):
+    """beta = 0: the memory stays S0, so dq_t = S0 do_t, dk = dv = 0,
+    dS0 = dS_T + sum_t q_t do_t^T, and dbeta_t = k_t^T G_t (v_t - S0^T k_t)
+    with G_t = dS_T + sum_{r >= t} q_r do_r^T."""
+    inp = _bwd_inputs("deltanet", 1, 7, 1, 5, 4, seed=90)
+    inp["beta"] = np.zeros_like(inp["beta"])
+    g = _rng(91)
+    dO = g.standard_normal(inp["v"].shape)
+    dS = g.standard_normal(inp["S0"].shape)
+    gr = _grads(bwd, "deltanet", inp, dO, dS)
+    S0 = inp["S0"][0, 0]
+    q, k, v, do = inp["q"][0, :, 0], inp["k"][0, :, 0], inp["v"][0, :, 0], dO[0, :, 0]
+    np.testing.assert_allclose(gr["q"][0, :, 0], do @ S0.T, rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(gr["v"], 0.0)
+    np.testing.assert_allclose(gr["k"], 0.0, atol=1e-15)
+    np.testing.assert_allclose(gr["S0"][0, 0], dS[0, 0] + q.T @ do, rtol=1e-13, atol=1e-13)
+    for t in range(7):
+        G = dS[0, 0] + q[t:].T @ do[t:]
+        ref = k[t] @ G @ (v[t] - S0.T @ k[t])
+        np.testing.assert_allclose(gr["beta"][0, t, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+def bwd_pin_no_tokens_and_linearity(rec, bwd):
+    """T = 0 passes dS_T through to dS0; the gradients are linear in the
+    cotangents (dO, dS_T)."""
+    inp = _bwd_inputs("kda", 1, 0, 2, 4, 3, seed=92)
+    dS = _rng(93).standard_normal(inp["S0"].shape)
+    gr = _grads(bwd, "kda", inp, np.zeros(inp["v"].shape), dS)
+    np.testing.assert_array_equal(gr["S0"], dS)
+    inp = _bwd_inputs("gated_deltanet", 1, 6, 1, 4, 3, seed=94)
+    g = _rng(95)
+    o1, o2 = g.standard_normal(inp["v"].shape), g.standard_normal(inp["v"].shape)
+    s1, s2 = g.standard_normal(inp["S0"].shape), g.standard_normal(inp["S0"].shape)
+    a = _grads(bwd, "gated_deltanet", inp, o1, s1)
+    b = _grads(bwd, "gated_deltanet", inp, o2, s2)
+    c = _grads(bwd, "gated_deltanet", inp, o1 + 2 * o2, s1 + 2 * s2)
+    for n in GRAD_NAMES:
+        np.testing.assert_allclose(c[n], a[n] + 2 * b[n], rtol=1e-11, atol=1e-12)
+
+
+BWD_PINS = [v for k, v in sorted(globals().items()) if k.startswith("bwd_pin_")]

@@ -83,6 +83,24 @@ MUTANTS = {
     "no_decay_scalar_gate": _sub("a[i] = alpha[tok];", "a[i] = 1.0;"),
     "variance_not_carried": _sub("p[i] = (den != 0.0) ? pm[i] * rt / den : pm[i];",
                                  "p[i] = (den != 0.0) ? p[i] : pm[i];"),
+    # backward
+    "bwd_dq_from_previous_memory": _sub("r += St[i * dv + j] * dot[j];",
+                                        "r += Sp[i * dv + j] * dot[j];"),
+    "bwd_output_term_dropped": _sub("dS[i * dv + j] += qt[i] * dot[j];",
+                                    "dS[i * dv + j] += 0.0 * qt[i] * dot[j];"),
+    "bwd_de_without_beta": _sub("r += dS[i * dv + j] * bt * kt[i];",
+                                "r += dS[i * dv + j] * kt[i];"),
+    "bwd_read_term_dropped": _sub("dSm[i * dv + j] = dS[i * dv + j] - kt[i] * de[j];",
+                                  "dSm[i * dv + j] = dS[i * dv + j];"),
+    "bwd_dk_sign": _sub("dk_out[tok * dk + i] = -r + bt * dw[i];",
+                        "dk_out[tok * dk + i] = r + bt * dw[i];"),
+    "bwd_dk_without_write_term": _sub("dk_out[tok * dk + i] = -r + bt * dw[i];",
+                                      "dk_out[tok * dk + i] = -r;"),
+    "bwd_decay_grad_from_new_memory": _sub("r += dSm[i * dv + j] * Sp[i * dv + j];",
+                                           "r += dSm[i * dv + j] * St[i * dv + j];"),
+    "bwd_memory_grad_not_decayed": _sub("dS[i * dv + j] = a[i] * dSm[i * dv + j];",
+                                        "dS[i * dv + j] = dSm[i * dv + j];"),
+    "bwd_dbeta_wrong_vector": _sub("db += kt[i] * dw[i];", "db += qt[i] * dw[i];"),
     # isotropic KDN
     "iso_alpha_not_squared": _sub("a2 += a[i] * a[i];", "a2 += a[i];"),
     "iso_drops_process_noise": _sub("xm += xi[tok * dk + i];", "xm += 0.0;"),
@@ -126,9 +144,11 @@ def test_pins_catch_mutant(name, tmpdir_mut):
     oracle.build(src=c, out=so)
     lib = oracle.OracleLib(so)
     caught = []
-    for pin in oracle_pins.ALL_PINS:
+    pins = [(p, (lib.recurrence,)) for p in oracle_pins.ALL_PINS]
+    pins += [(p, (lib.recurrence, lib.backward)) for p in oracle_pins.BWD_PINS]
+    for pin, args in pins:
         try:
-            pin(lib.recurrence)
+            pin(*args)
         except (AssertionError, FloatingPointError, ValueError,
                 ZeroDivisionError, RuntimeError):
             caught.append(pin.__name__)
@@ -141,3 +161,5 @@ def test_unmutated_source_passes_every_pin(tmpdir_mut):
     lib = oracle.OracleLib(so)
     for pin in oracle_pins.ALL_PINS:
         pin(lib.recurrence)
+    for pin in oracle_pins.BWD_PINS:
+        pin(lib.recurrence, lib.backward)
