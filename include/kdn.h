@@ -215,6 +215,59 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype,
                                       const float *S0, const float *p0, void *o,
                                       float *S_out, float *p_out, void *stream);
 
+/*
+ * Gradients of kdn_chunk_prefill for the write-strength variants (DeltaNet,
+ * Gated DeltaNet, KDA; the KDN variants give KDN_ERR_UNSUPPORTED).  The pages
+ * give no gradient ("معماری KDA ...", section "پیاده‌سازی فنی و گذارهای DPLR",
+ * names training as a use of the chunk form); what is computed is the exact
+ * derivative of the recurrence above for a scalar loss L whose cotangents
+ * are d_o = dL/do and dS_out = dL/dS_out, by the reverse of the chunk
+ * algebra.  The call re-runs the forward chunk pass internally (it needs the
+ * state at every chunk start), then a reverse pass over the chunks for the
+ * state gradient, then the chunk-parallel local gradients.
+ *
+ *   q, k, v, alpha, beta, S0, chunk   as for kdn_chunk_prefill (S0 may be NULL)
+ *   d_o         [B, T, H, d_v] dtype, dL/do
+ *   dS_out      [B, H, d_k, d_v] float32, dL/dS_out, or NULL for zero
+ * Outputs, all float32 whatever the dtype:
+ *   dq, dk      [B, T, H, d_k]
+ *   dv          [B, T, H, d_v]
+ *   dlog_alpha  alpha * dL/dalpha (the gradient with respect to log alpha):
+ *               [B, T, H] (Gated DeltaNet), [B, T, H, d_k] (KDA), NULL for
+ *               DeltaNet
+ *   dbeta       [B, T, H]
+ *   dS0         [B, H, d_k, d_v], dL/dS0; may be NULL (not computed)
+ *   workspace   device memory of at least
+ *               kdn_chunk_prefill_backward_workspace_size(...) bytes,
+ *               256-byte aligned, overlapping no argument; required unless
+ *               B*H*T = 0.  Scratch, as for kdn_chunk_prefill.
+ * Outputs overlap no input and no other output (else KDN_ERR_ALIAS).
+ * Alignment: 16 bytes for tensors whose last axis is d_k or d_v, the element
+ * size for per-head scalars.  Validation, asynchrony and errors as for
+ * kdn_chunk_prefill.
+ */
+kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype,
+                                      int B, int T, int H, int d_k, int d_v, int chunk,
+                                      const void *q, const void *k, const void *v,
+                                      const void *alpha, const void *beta, const float *S0,
+                                      const void *d_o, const float *dS_out,
+                                      float *dq, float *dk, float *dv, float *dlog_alpha,
+                                      float *dbeta, float *dS0,
+                                      void *workspace, unsigned long long workspace_bytes,
+                                      void *stream);
+
+/*
+ * Bytes of workspace kdn_chunk_prefill_backward needs (0 when there are no
+ * tokens), or 0 with *status set when the combination is invalid or
+ * unsupported.  It is the forward record size plus two float32 states (S at
+ * each chunk start, dS at each chunk end) per (sequence, head, chunk):
+ * 66,048 + 131,072 bytes per (sequence, head, chunk) for bf16, d = 128, C = 64.
+ */
+unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant,
+                                                             kdn_dtype dtype, int B, int T,
+                                                             int H, int d_k, int d_v,
+                                                             int chunk, kdn_status *status);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kdn_status_string(kdn_status status);
 
@@ -225,7 +278,7 @@ int kdn_chunk_prefill_chunk_size(kdn_dtype dtype, int d_k, int d_v, int chunk);
 /* ABI version of this header (incremented on any incompatible change). */
 int kdn_abi_version(void);
 
-#define KDN_ABI_VERSION 3
+#define KDN_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

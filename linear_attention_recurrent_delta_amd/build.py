@@ -34,7 +34,8 @@ UNITS += [("kdn_prefill.hip", [f"-DKDN_PREFILL_VARIANT={v}"], f"kdn_prefill_{v}.
           for v in range(5)]
 UNITS += [("kdn_prefill.hip", ["-DKDN_PREFILL_DISPATCH"], "kdn_prefill_dispatch.o"),
           ("kdn_prefill_state.hip", [], "kdn_prefill_state.o"),
-          ("kdn_variance.hip", [], "kdn_variance.o")]
+          ("kdn_variance.hip", [], "kdn_variance.o"),
+          ("kdn_backward.hip", [], "kdn_backward.o")]
 
 
 def hipcc() -> str:

@@ -217,6 +217,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.xi = proc_noise; P.r = obs_noise;
     P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
     P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr; P.ws_stat = nullptr;
+    P.states = nullptr;
     P.cus = device_cus();
     if (n_ws > 0) {
         P.ws = workspace;
@@ -379,6 +380,146 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype, int 
     P.xi = proc_noise; P.r = obs_noise;
     P.S0 = S0; P.p0 = p0; P.S = S_out; P.p = p_out; P.o = o;
     const hipError_t e = kdn::launch_decode_multi(P, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Gradients of the chunkwise prefill.
+// ---------------------------------------------------------------------------
+static long long backward_workspace_bytes(int variant, int bf16, long long B, long long T,
+                                          long long H, int d_k, int d_v, int C) {
+    const long long bh = B * H, nc = kdn::num_chunks(T, C);
+    if (bh * T == 0)
+        return 0;
+    const long long rec = kdn::prefill_workspace_bytes(variant, bf16, B, T, H, d_k, C);
+    return rec + 2 * bh * nc * d_k * d_v * 4;
+}
+
+unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant, kdn_dtype dtype,
+                                                             int B, int T, int H, int d_k,
+                                                             int d_v, int chunk,
+                                                             kdn_status *status) {
+    int C = 0;
+    kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C);
+    if (st == KDN_OK && is_kdn(variant))
+        st = KDN_ERR_UNSUPPORTED;
+    if (status)
+        *status = st;
+    if (st != KDN_OK)
+        return 0;
+    return (unsigned long long)backward_workspace_bytes(variant, dtype == KDN_BF16, B, T, H,
+                                                        d_k, d_v, C);
+}
+
+kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int B, int T,
+                                      int H, int d_k, int d_v, int chunk,
+                                      const void *q, const void *k, const void *v,
+                                      const void *alpha, const void *beta, const float *S0,
+                                      const void *d_o, const float *dS_out,
+                                      float *dq, float *dk, float *dv, float *dlog_alpha,
+                                      float *dbeta, float *dS0, void *workspace,
+                                      unsigned long long workspace_bytes, void *stream) {
+    int C = 0;
+    if (kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C))
+        return st;
+    if (is_kdn(variant))
+        return KDN_ERR_UNSUPPORTED;
+    const long long bh = (long long)B * H;
+    const long long tok = bh * T;
+    const bool gdn = variant == KDN_GATED_DELTANET, dn = variant == KDN_DELTANET;
+    if (tok > 0 && (!q || !k || !v || !d_o || !dq || !dk || !dv || !dbeta))
+        return KDN_ERR_NULL;
+    if (kdn_status st = check_gates(variant, alpha, beta, nullptr, nullptr, tok == 0))
+        return st;
+    if (dn && dlog_alpha)
+        return KDN_ERR_NULL;
+    if (!dn && tok > 0 && !dlog_alpha)
+        return KDN_ERR_NULL;
+    const long long es = dtype == KDN_BF16 ? 2 : 4;
+    const void *vec[] = {q, k, v, gdn ? nullptr : alpha, S0, d_o, dS_out, dq, dk, dv,
+                         gdn ? nullptr : dlog_alpha, dS0};
+    for (const void *x : vec)
+        if (x && !aligned(x, 16))
+            return KDN_ERR_ALIGN;
+    for (const void *x : {beta, gdn ? alpha : nullptr})
+        if (x && !aligned(x, (uintptr_t)es))
+            return KDN_ERR_ALIGN;
+    for (const void *x : {(const void *)dbeta, (const void *)(gdn ? dlog_alpha : nullptr)})
+        if (x && !aligned(x, 4))
+            return KDN_ERR_ALIGN;
+
+    const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
+    const long long n_a = gdn ? tok * es : (dn ? 0 : tok * d_k * es);
+    const long long n_S = bh * d_k * d_v * 4;
+    struct R { const void *p; long long n; };
+    const R ins[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, tok * es},
+                     {S0, n_S}, {d_o, n_v}, {dS_out, n_S}};
+    const R outs[] = {{dq, tok * d_k * 4}, {dk, tok * d_k * 4}, {dv, tok * d_v * 4},
+                      {dlog_alpha, gdn ? tok * 4 : (dn ? 0 : tok * d_k * 4)},
+                      {dbeta, tok * 4}, {dS0, n_S}};
+    // outputs overlap no input and no other output
+    for (int i = 0; i < 6; ++i) {
+        for (const R &x : ins)
+            if (overlap(outs[i].p, outs[i].n, x.p, x.n)) return KDN_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return KDN_ERR_ALIAS;
+    }
+    const long long n_ws = backward_workspace_bytes(variant, dtype == KDN_BF16, B, T, H, d_k,
+                                                    d_v, C);
+    if (n_ws > 0) {
+        if (!workspace || (long long)workspace_bytes < n_ws)
+            return KDN_ERR_WORKSPACE;
+        if (!aligned(workspace, 256))
+            return KDN_ERR_ALIGN;
+        for (const R &x : ins)
+            if (overlap(workspace, n_ws, x.p, x.n)) return KDN_ERR_ALIAS;
+        for (const R &x : outs)
+            if (overlap(workspace, n_ws, x.p, x.n)) return KDN_ERR_ALIAS;
+    }
+    if (bh == 0)
+        return KDN_OK;
+
+    // forward: records, then S at every chunk start
+    const long long nc = kdn::num_chunks(T, C);
+    const long long n_rec = kdn::prefill_workspace_bytes(variant, dtype == KDN_BF16, B, T, H,
+                                                         d_k, C);
+    char *base = static_cast<char *>(workspace);
+    kdn::PrefillParams F;
+    F.variant = variant;
+    F.bf16 = dtype == KDN_BF16;
+    F.B = B; F.T = T; F.H = H; F.dk = d_k; F.dv = d_v; F.chunk = C;
+    F.mu = 1.f;
+    F.q = q; F.k = k; F.v = v; F.alpha = alpha; F.beta = beta; F.xi = nullptr; F.r = nullptr;
+    F.S0 = S0; F.p0 = nullptr; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
+    F.ws = n_ws > 0 ? base : nullptr;
+    F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
+    F.states = n_ws > 0 ? reinterpret_cast<float *>(base + n_rec) : nullptr;
+    F.cus = device_cus();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (tok > 0) {
+        switch (variant) {
+        case KDN_DELTANET: e = kdn::launch_prefill_prep_v0(F, st); break;
+        case KDN_GATED_DELTANET: e = kdn::launch_prefill_prep_v1(F, st); break;
+        default: e = kdn::launch_prefill_prep_v2(F, st); break;
+        }
+        if (e == hipSuccess)
+            e = kdn::launch_prefill_state(F, st);
+        if (e != hipSuccess)
+            return KDN_ERR_HIP;
+    }
+    kdn::BackwardParams G;
+    G.variant = variant;
+    G.bf16 = dtype == KDN_BF16;
+    G.B = B; G.T = T; G.H = H; G.dk = d_k; G.dv = d_v; G.chunk = C;
+    G.q = q; G.k = k; G.v = v; G.alpha = alpha; G.beta = beta; G.S0 = S0;
+    G.dO = d_o; G.dS_out = dS_out;
+    G.dq = dq; G.dk_ = dk; G.dv_ = dv; G.dla = dlog_alpha; G.dbeta = dbeta; G.dS0 = dS0;
+    G.ws = F.ws;
+    G.states = F.states;
+    G.dstates = n_ws > 0 ? F.states + bh * nc * d_k * d_v : nullptr;
+    G.cus = F.cus;
+    e = kdn::launch_backward(G, st);
     return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;
 }
 

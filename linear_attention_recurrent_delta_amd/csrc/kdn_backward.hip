@@ -1,0 +1,702 @@
+// kdn_backward.hip -- gradients of the chunkwise prefill (gfx950), for the
+// write-strength variants (DeltaNet, Gated DeltaNet, KDA).
+//
+// The forward chunk algebra (page "معماری KDA: حذف تداخل حافظه با قانون دلتا در
+// توالی‌های بلند", section "حل مشکل وابستگی علی"), per chunk entering with state S:
+//   U = V - K~ S,  E = T U,  O = Q~ S + A_qk E,  S' = diag(gamma_C) S + W~^T E,
+// with T = (I + A_kk)^-1.  Its exact reverse, for cotangents dO of the outputs
+// and dS' of the state leaving the chunk:
+//   dE = A_qk^T dO + W~ dS',   dU = T^T dE,   dV = dU,
+//   dS = diag(gamma_C) dS' + Q~^T dO - K~^T dU                    (state pass)
+//   dA_qk = tril(dO E^T),  dA_kk = strict tril(-dU E^T)          (local)
+//   dQ~ = dO S^T + dA_qk W',  dK~ = -dU S^T + dA_kk W',
+//   dW' = dA_qk^T Q~ + dA_kk^T K~ + diag(gamma_C) E dS'^T,
+// where A_kk = K~ W'^T, A_qk = Q~ W'^T, W' = w / gamma, W~ = gamma_C W'.  Back
+// through the decay scaling (K~ = gamma k, Q~ = gamma q, w = beta k):
+//   dq = gamma dQ~,  dw = dW' / gamma,  dk = gamma dK~ + beta dw,  dbeta = k . dw,
+//   d log gamma_t = k (gamma dK~) + q dq - w dw  (+ the gamma_C terms at the
+//   chunk end), and d log a_r = sum over t >= r of d log gamma_t.
+//
+// Three launches after the forward pass (which saves S at every chunk start):
+//   backward_state_kernel: one workgroup per (batch*head, value block) walks
+//     the chunks in reverse, dS in registers, and saves dS' of every chunk;
+//   backward_chunk_kernel: one workgroup per (batch*head, chunk) forms the
+//     chunk's local gradients from S, dS', the tiles and the forward record.
+#include "kdn_device.h"
+#include "kdn_launch.h"
+#include "kdn_workspace.h"
+
+namespace kdn {
+
+#ifdef KDN_DECAY_FLOOR
+#undef KDN_DECAY_FLOOR
+#endif
+// Below this cumulative in-chunk decay the 1/gamma operand scaling is not
+// used; the chunk takes the exact elementwise path.
+#define KDN_DECAY_FLOOR 8.077935669463161e-28f   /* 2^-90 */
+
+// Copy a record matrix X[R][K], stored in fragment order (kdn_workspace.h),
+// to LDS.  TRANS: dst[k * pitch + r] = sgn X[r][k]; else dst[r * pitch + k].
+template <typename E, int R, int K, int NT, bool TRANS>
+__device__ __forceinline__ void defrag(E *dst, int pitch, const char *src, float sgn, int tid) {
+    constexpr int EPU = 16 / (int)sizeof(E);
+    constexpr int KG = sizeof(E) == 2 ? 32 : 16;
+    constexpr int NU = R * K / EPU;
+    const uint4 *s = reinterpret_cast<const uint4 *>(src);
+    for (int u = tid; u < NU; u += NT) {
+        const int l = u & 63, grp = u >> 6;
+        const int m = grp / (K / KG), g = grp % (K / KG);
+        const int row = m * 16 + (l & 15);
+        const uint4 v = s[u];
+        const E *e = reinterpret_cast<const E *>(&v);
+#pragma unroll
+        for (int x = 0; x < EPU; ++x) {
+            const int col = sizeof(E) == 2 ? g * 32 + (l >> 4) * 8 + x : g * 16 + x * 4 + (l >> 4);
+            const E val = from_f32<E>(sgn * to_f32(e[x]));
+            if (TRANS)
+                dst[col * pitch + row] = val;
+            else
+                dst[row * pitch + col] = val;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse state pass.  Per chunk, from the chunk's record:
+//   dE = A_qk^T dO + W~ dS,  dU = T^T dE,  dS <- diag(gamma_C) dS + Q~^T dO - K~^T dU.
+// LDS operands (row = MFMA row, k contiguous): A_qk^T [s][t], W~ [s][i],
+// T^T [t][s], Q~^T [i][t], -K~^T [i][t]; the B operands dO^T, dS^T, dE^T,
+// dU^T as [column][k].
+// ---------------------------------------------------------------------------
+template <typename E, bool DECAY, int DK, int NV, int C>
+__global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
+    constexpr int NT = 512, NW = 8;
+    constexpr int PADE = 16 / (int)sizeof(E);
+    constexpr int PK = DK + PADE, PC = C + PADE;
+    constexpr int NTJ = NV / 16, NTI = DK / 16, NTC = C / 16;
+    constexpr int NSS = (NTI * NTJ + NW - 1) / NW;   // dS tiles per wave
+    constexpr int NSE = (NTC * NTJ + NW - 1) / NW;   // dE / dU tiles per wave
+
+    __shared__ __attribute__((aligned(16))) E AQT[C * PC];
+    __shared__ __attribute__((aligned(16))) E WR[C * PK];
+    __shared__ __attribute__((aligned(16))) E TT[C * PC];
+    __shared__ __attribute__((aligned(16))) E QT[DK * PC];
+    __shared__ __attribute__((aligned(16))) E KT[DK * PC];
+    __shared__ __attribute__((aligned(16))) E DOT[NV * PC];
+    __shared__ __attribute__((aligned(16))) E DST[NV * PK];
+    __shared__ __attribute__((aligned(16))) E DET[NV * PC];
+    __shared__ __attribute__((aligned(16))) E DUT[NV * PC];
+    __shared__ float GC[DK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nvb = P.dv / NV;
+    const int bh = blockIdx.x / nvb, vb = blockIdx.x % nvb;
+    const int b = bh / P.H, h = bh % P.H;
+    const int v0 = vb * NV;
+    const int T = P.T, H = P.H, DV = P.dv;
+    const int NC = (T + C - 1) / C;
+    const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
+    const char *ws = static_cast<const char *>(P.ws) + (long)bh * NC * LW.rec;
+    const E *gdo = static_cast<const E *>(P.dO);
+
+    // dS tiles: tau = wv + NW k -> (key tile, column tile) = (tau / NTJ, tau % NTJ)
+    f32x4 dacc[NSS];
+#pragma unroll
+    for (int k = 0; k < NSS; ++k) {
+        const int tau = wv + NW * k;
+        if (tau >= NTI * NTJ) continue;
+        const int i0 = (tau / NTJ) * 16 + (lane >> 4) * 4, j = (tau % NTJ) * 16 + (lane & 15);
+        float s4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dacc[k][r] = P.dS_out ? P.dS_out[((long)bh * DK + i0 + r) * DV + v0 + j] : 0.f;
+            s4[r] = dacc[k][r];
+        }
+        lds_stn<4>(DST + j * PK + i0, s4);
+    }
+
+    for (int c = NC - 1; c >= 0; --c) {
+        const int L = min(C, T - c * C);
+        const char *rec = ws + (long)c * LW.rec;
+        // dS leaving this chunk, for the local-gradient kernel
+        float *sv = P.dstates + ((long)bh * NC + c) * DK * DV;
+#pragma unroll
+        for (int k = 0; k < NSS; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NTI * NTJ) continue;
+            const int i0 = (tau / NTJ) * 16 + (lane >> 4) * 4, j = (tau % NTJ) * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sv[(long)(i0 + r) * DV + v0 + j] = dacc[k][r];
+        }
+        defrag<E, C, C, NT, true>(AQT, PC, rec + LW.off_aqk, 1.f, tid);
+        defrag<E, DK, C, NT, true>(WR, PK, rec + LW.off_wdt, 1.f, tid);
+        defrag<E, C, C, NT, true>(TT, PC, rec + LW.off_tm, 1.f, tid);
+        defrag<E, C, DK, NT, true>(QT, PC, rec + LW.off_qd, 1.f, tid);
+        defrag<E, C, DK, NT, true>(KT, PC, rec + LW.off_kd, -1.f, tid);
+        if (DECAY && tid < DK)
+            GC[tid] = reinterpret_cast<const float *>(rec + LW.off_gc)[tid];
+        // dO^T tile (rows past the sequence end are 0)
+        for (int x = tid; x < C * NV; x += NT) {
+            const int t = x / NV, j = x % NV;
+            const long row = ((long)b * T + c * C + t) * H + h;
+            DOT[j * PC + t] = t < L ? gdo[row * DV + v0 + j] : from_f32<E>(0.f);
+        }
+        __syncthreads();
+        // dE = A_qk^T dO + W~ dS  -> dE^T
+#pragma unroll
+        for (int k = 0; k < NSE; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NTC * NTJ) continue;
+            const int ms = tau / NTJ, nj = tau % NTJ;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_tile_k<E, C>(acc, AQT + ms * 16 * PC, PC, DOT + nj * 16 * PC, PC, lane);
+            mma_tile_k<E, DK>(acc, WR + ms * 16 * PK, PK, DST + nj * 16 * PK, PK, lane);
+            float e4[4] = {acc[0], acc[1], acc[2], acc[3]};
+            lds_stn<4>(DET + (nj * 16 + (lane & 15)) * PC + ms * 16 + (lane >> 4) * 4, e4);
+        }
+        __syncthreads();
+        // dU = T^T dE  -> dU^T
+#pragma unroll
+        for (int k = 0; k < NSE; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NTC * NTJ) continue;
+            const int mt = tau / NTJ, nj = tau % NTJ;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_tile_k<E, C>(acc, TT + mt * 16 * PC, PC, DET + nj * 16 * PC, PC, lane);
+            float u4[4] = {acc[0], acc[1], acc[2], acc[3]};
+            lds_stn<4>(DUT + (nj * 16 + (lane & 15)) * PC + mt * 16 + (lane >> 4) * 4, u4);
+        }
+        __syncthreads();
+        // dS <- diag(gamma_C) dS + Q~^T dO - K~^T dU
+#pragma unroll
+        for (int k = 0; k < NSS; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NTI * NTJ) continue;
+            const int mi = tau / NTJ, nj = tau % NTJ;
+            const int i0 = mi * 16 + (lane >> 4) * 4, j = nj * 16 + (lane & 15);
+            if (DECAY) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dacc[k][r] *= GC[i0 + r];
+            }
+            mma_tile_k<E, C>(dacc[k], QT + mi * 16 * PC, PC, DOT + nj * 16 * PC, PC, lane);
+            mma_tile_k<E, C>(dacc[k], KT + mi * 16 * PC, PC, DUT + nj * 16 * PC, PC, lane);
+            float s4[4] = {dacc[k][0], dacc[k][1], dacc[k][2], dacc[k][3]};
+            lds_stn<4>(DST + j * PK + i0, s4);
+        }
+        __syncthreads();
+    }
+    if (P.dS0) {
+#pragma unroll
+        for (int k = 0; k < NSS; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NTI * NTJ) continue;
+            const int i0 = (tau / NTJ) * 16 + (lane >> 4) * 4, j = (tau % NTJ) * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                P.dS0[((long)bh * DK + i0 + r) * DV + v0 + j] = dacc[k][r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Local gradients of one chunk.  The value columns are taken in halves of DVH;
+// per half (j: the half's columns)
+//   U = V - K~ S,  E = T U,  dE = A_qk^T dO + W~ dS',  dU = T^T dE  (dv = dU)
+// and the products summed over j go to registers:
+//   dQ~ += dO S^T,  dK~ -= dU S^T,  dW~ += E dS'^T,  dA_qk += dO E^T,
+//   dA_kk -= dU E^T,  and sum_j S dS' per key channel.
+// Then the decay-scaled products dQ~ += dA_qk W', dK~ += dA_kk W',
+// dW' = gamma_C dW~ + dA_kk^T K~ + dA_qk^T Q~ (exact elementwise sums over the
+// decay ratios when a channel's in-chunk decay drops below 2^-90), and the
+// elementwise step to dq, dk, dbeta and d log gamma; finally the reverse sum
+// over the chunk's tokens gives d log alpha.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int C, int DVH>
+struct BwdLayout {
+    static constexpr int ES = (int)sizeof(E), PADE = 16 / ES;
+    static constexpr int PK = DK + PADE, PC = C + PADE, PH = DVH + PADE, PF = DK + 4;
+    static constexpr int SZ_CK = C * PK * ES, SZ_CC = C * PC * ES, SZ_KC = DK * PC * ES;
+    static constexpr int SZ_HC = DVH * PC * ES, SZ_CH = C * PH * ES, SZ_KH = DK * PH * ES;
+    static constexpr int SZ_SB1 = (DVH * PK > DK * PH ? DVH * PK : DK * PH) * ES;
+    static constexpr int SZ_F = C * PF * 4;
+    static constexpr int OFF_WR = 0;
+    static constexpr int BASE = SZ_CK;
+    // chunk and half phases
+    static constexpr int OFF_KR = BASE, OFF_TR = OFF_KR + SZ_CK, OFF_TT = OFF_TR + SZ_CC,
+                         OFF_AQT = OFF_TT + SZ_CC, OFF_SB1 = OFF_AQT + SZ_CC,
+                         OFF_SB2 = OFF_SB1 + SZ_SB1, OFF_UE = OFF_SB2 + SZ_KH,
+                         OFF_EH = OFF_UE + SZ_HC, OFF_DOT = OFF_EH + SZ_CH,
+                         OFF_DOH = OFF_DOT + SZ_HC, OFF_DUH = OFF_DOH + SZ_CH,
+                         END_A = OFF_DUH + SZ_CH;
+    // decay-scaled products and the elementwise step (over the same bytes)
+    static constexpr int OFF_DAQ = BASE, OFF_DAQT = OFF_DAQ + SZ_CC, OFF_DAK = OFF_DAQT + SZ_CC,
+                         OFF_DAKT = OFF_DAK + SZ_CC, OFF_WPT = OFF_DAKT + SZ_CC,
+                         OFF_QTT = OFF_WPT + SZ_KC, OFF_KTT = OFF_QTT + SZ_KC,
+                         OFF_GAM = OFF_KTT + SZ_KC, END_F = OFF_GAM + SZ_F;
+    static constexpr int OFF_DG = BASE;   // over the dA matrices and W'^T, Q~^T, K~^T
+    static constexpr int END = END_A > END_F ? END_A : END_F;
+    static constexpr int OFF_SM = END;
+    static constexpr int SM_GC = 0, SM_DGC = DK, SM_SDS = 2 * DK, SM_DB = 3 * DK,
+                         SM_DLA = 3 * DK + C, SM_FLAG = 3 * DK + 2 * C;
+    static constexpr int TOTAL = OFF_SM + (3 * DK + 2 * C + 4) * 4;
+    static_assert(OFF_DG + SZ_F <= OFF_GAM, "d log gamma clear of gamma");
+    static_assert(TOTAL <= 163840, "backward LDS budget");
+};
+
+template <typename E, int VAR, int DK, int C, int DVH>
+__global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
+    using LY = BwdLayout<E, DK, C, DVH>;
+    constexpr int NT = 512, NW = 8;
+    constexpr int PK = LY::PK, PC = LY::PC, PH = LY::PH, PF = LY::PF;
+    constexpr int NB = C / 16, NTI = DK / 16, NTH = DVH / 16;
+    constexpr int NSH = (NB * NTH + NW - 1) / NW;     // half-phase tiles per wave
+    constexpr int NS3 = (NB * NTI + NW - 1) / NW;     // dQ~ / dK~ / dW~ tiles per wave
+    constexpr int NL = NB * (NB + 1) / 2;             // dA tiles on or below the diagonal
+    constexpr int NSA = (NL + NW - 1) / NW;
+    constexpr bool DECAY = VAR != DELTANET;
+
+    __shared__ __attribute__((aligned(16))) char smem[LY::TOTAL];
+    E *WR = reinterpret_cast<E *>(smem + LY::OFF_WR);
+    E *KR = reinterpret_cast<E *>(smem + LY::OFF_KR);
+    E *TR = reinterpret_cast<E *>(smem + LY::OFF_TR);
+    E *TT = reinterpret_cast<E *>(smem + LY::OFF_TT);
+    E *AQT = reinterpret_cast<E *>(smem + LY::OFF_AQT);
+    E *SB1 = reinterpret_cast<E *>(smem + LY::OFF_SB1);
+    E *SB2 = reinterpret_cast<E *>(smem + LY::OFF_SB2);
+    E *UE = reinterpret_cast<E *>(smem + LY::OFF_UE);
+    E *EH = reinterpret_cast<E *>(smem + LY::OFF_EH);
+    E *DOT = reinterpret_cast<E *>(smem + LY::OFF_DOT);
+    E *DOH = reinterpret_cast<E *>(smem + LY::OFF_DOH);
+    E *DUH = reinterpret_cast<E *>(smem + LY::OFF_DUH);
+    E *DAQ = reinterpret_cast<E *>(smem + LY::OFF_DAQ);
+    E *DAQT = reinterpret_cast<E *>(smem + LY::OFF_DAQT);
+    E *DAK = reinterpret_cast<E *>(smem + LY::OFF_DAK);
+    E *DAKT = reinterpret_cast<E *>(smem + LY::OFF_DAKT);
+    E *WPT = reinterpret_cast<E *>(smem + LY::OFF_WPT);
+    E *QTT = reinterpret_cast<E *>(smem + LY::OFF_QTT);
+    E *KTT = reinterpret_cast<E *>(smem + LY::OFF_KTT);
+    float *GAM = reinterpret_cast<float *>(smem + LY::OFF_GAM);
+    float *DG = reinterpret_cast<float *>(smem + LY::OFF_DG);
+    float *sm = reinterpret_cast<float *>(smem + LY::OFF_SM);
+    float *s_gc = sm + LY::SM_GC, *s_dgc = sm + LY::SM_DGC, *s_sds = sm + LY::SM_SDS,
+          *s_db = sm + LY::SM_DB, *s_dla = sm + LY::SM_DLA;
+    int *s_flag = reinterpret_cast<int *>(sm + LY::SM_FLAG);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = P.T, H = P.H, DV = P.dv;
+    const int NC = (T + C - 1) / C;
+    const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+    const int b = bh / H, h = bh % H;
+    const int c0 = c * C, L = min(C, T - c0);
+    const long tok0 = ((long)b * T + c0) * H + h;      // row of (b, c0, h)
+    const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
+    const char *rec = static_cast<const char *>(P.ws) + ((long)bh * NC + c) * LW.rec;
+    const float *Sg = P.states + ((long)bh * NC + c) * DK * DV;
+    const float *dSg = P.dstates + ((long)bh * NC + c) * DK * DV;
+    const E *gq = static_cast<const E *>(P.q);
+    const E *gk = static_cast<const E *>(P.k);
+    const E *gv = static_cast<const E *>(P.v);
+    const E *ga = static_cast<const E *>(P.alpha);
+    const E *gb = static_cast<const E *>(P.beta);
+    const E *gdo = static_cast<const E *>(P.dO);
+    auto row = [&](int t) { return tok0 + (long)t * H; };
+
+    // ---- chunk operands from the forward record
+    defrag<E, DK, C, NT, true>(WR, PK, rec + LW.off_wdt, 1.f, tid);    // W~   [s][i]
+    defrag<E, C, DK, NT, false>(KR, PK, rec + LW.off_kd, 1.f, tid);    // K~   [t][i]
+    defrag<E, C, C, NT, false>(TR, PC, rec + LW.off_tm, 1.f, tid);     // T    [t][s]
+    defrag<E, C, C, NT, true>(TT, PC, rec + LW.off_tm, 1.f, tid);      // T^T  [t][s]
+    defrag<E, C, C, NT, true>(AQT, PC, rec + LW.off_aqk, 1.f, tid);    // A_qk^T [s][t]
+    if (tid < DK) {
+        s_gc[tid] = DECAY ? reinterpret_cast<const float *>(rec + LW.off_gc)[tid] : 1.f;
+        s_dgc[tid] = 0.f;
+        s_sds[tid] = 0.f;
+    }
+    if (tid < C) {
+        s_db[tid] = 0.f;
+        s_dla[tid] = 0.f;
+    }
+    if (tid == 0)
+        *s_flag = 0;
+
+    f32x4 dq3[NS3], dk3[NS3], dw3[NS3], daq[NSA], dak[NSA];
+#pragma unroll
+    for (int k = 0; k < NS3; ++k)
+        dq3[k] = dk3[k] = dw3[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NSA; ++k)
+        daq[k] = dak[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto tri = [](int x, int &bi, int &bj) {          // x-th block on or below the diagonal
+        int mi = 0;
+        while (x > mi) { x -= mi + 1; ++mi; }
+        bi = mi;
+        bj = x;
+    };
+
+    for (int jh = 0; jh < DV; jh += DVH) {
+        // ---- S^T of the half, dO^T and dO
+        for (int x = tid; x < DK * DVH; x += NT) {
+            const int i = x / DVH, j = x % DVH;
+            SB1[j * PK + i] = from_f32<E>(Sg[(long)i * DV + jh + j]);
+        }
+        for (int x = tid; x < C * DVH; x += NT) {
+            const int t = x / DVH, j = x % DVH;
+            const E d = t < L ? gdo[row(t) * DV + jh + j] : from_f32<E>(0.f);
+            DOT[j * PC + t] = d;
+            DOH[t * PH + j] = d;
+        }
+        __syncthreads();
+        // ---- U = V - K~ S  -> U^T
+#pragma unroll
+        for (int k = 0; k < NSH; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTH) continue;
+            const int mt = tau / NTH, nj = tau % NTH;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_tile_k<E, DK>(acc, KR + mt * 16 * PK, PK, SB1 + nj * 16 * PK, PK, lane);
+            const int j = nj * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
+            float u[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                u[r] = (t0 + r < L ? to_f32(gv[row(t0 + r) * DV + jh + j]) : 0.f) - acc[r];
+            lds_stn<4>(UE + j * PC + t0, u);
+        }
+        __syncthreads();
+        // ---- E = T U  -> E (row-major);  dS'^T of the half
+#pragma unroll
+        for (int k = 0; k < NSH; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTH) continue;
+            const int mt = tau / NTH, nj = tau % NTH;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_tile_k<E, C>(acc, TR + mt * 16 * PC, PC, UE + nj * 16 * PC, PC, lane);
+            const int j = nj * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                EH[(t0 + r) * PH + j] = from_f32<E>(acc[r]);
+        }
+        for (int x = tid; x < DK * DVH; x += NT) {
+            const int i = x / DVH, j = x % DVH;
+            SB1[j * PK + i] = from_f32<E>(dSg[(long)i * DV + jh + j]);
+        }
+        __syncthreads();
+        // ---- dE = A_qk^T dO + W~ dS'  -> dE^T
+#pragma unroll
+        for (int k = 0; k < NSH; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTH) continue;
+            const int ms = tau / NTH, nj = tau % NTH;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_tile_k<E, C>(acc, AQT + ms * 16 * PC, PC, DOT + nj * 16 * PC, PC, lane);
+            mma_tile_k<E, DK>(acc, WR + ms * 16 * PK, PK, SB1 + nj * 16 * PK, PK, lane);
+            float e4[4] = {acc[0], acc[1], acc[2], acc[3]};
+            lds_stn<4>(UE + (nj * 16 + (lane & 15)) * PC + ms * 16 + (lane >> 4) * 4, e4);
+        }
+        __syncthreads();
+        // ---- dU = T^T dE  -> dv and dU (row-major);  S and dS' of the half
+        //      (row-major) and sum_j S dS'
+#pragma unroll
+        for (int k = 0; k < NSH; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTH) continue;
+            const int mt = tau / NTH, nj = tau % NTH;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            mma_tile_k<E, C>(acc, TT + mt * 16 * PC, PC, UE + nj * 16 * PC, PC, lane);
+            const int j = nj * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                DUH[(t0 + r) * PH + j] = from_f32<E>(acc[r]);
+                if (t0 + r < L)
+                    P.dv_[row(t0 + r) * DV + jh + j] = acc[r];
+            }
+        }
+        for (int x = tid; x < DK * DVH; x += NT) {
+            const int i = x / DVH, j = x % DVH;
+            const float sv = Sg[(long)i * DV + jh + j], dsv = dSg[(long)i * DV + jh + j];
+            SB1[i * PH + j] = from_f32<E>(sv);
+            SB2[i * PH + j] = from_f32<E>(dsv);
+            if (DECAY)
+                atomicAdd(&s_sds[i], sv * dsv);
+        }
+        __syncthreads();
+        // ---- sums over the half's columns
+#pragma unroll
+        for (int k = 0; k < NS3; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTI) continue;
+            const int mt = tau / NTI, ni = tau % NTI;
+            mma_tile_k<E, DVH>(dq3[k], DOH + mt * 16 * PH, PH, SB1 + ni * 16 * PH, PH, lane);
+            mma_tile_k<E, DVH>(dk3[k], DUH + mt * 16 * PH, PH, SB1 + ni * 16 * PH, PH, lane);
+            mma_tile_k<E, DVH>(dw3[k], EH + mt * 16 * PH, PH, SB2 + ni * 16 * PH, PH, lane);
+        }
+#pragma unroll
+        for (int k = 0; k < NSA; ++k) {
+            const int x = wv + NW * k;
+            if (x >= NL) continue;
+            int bi, bj;
+            tri(x, bi, bj);
+            mma_tile_k<E, DVH>(daq[k], DOH + bi * 16 * PH, PH, EH + bj * 16 * PH, PH, lane);
+            mma_tile_k<E, DVH>(dak[k], DUH + bi * 16 * PH, PH, EH + bj * 16 * PH, PH, lane);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < NS3; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dk3[k][r] = -dk3[k][r];
+
+    // ---- decays gamma_t per channel; W'^T = (beta k / gamma)^T, Q~^T, K~^T;
+    //      the dA matrices (masked) and their transposes; sum_s W~ dW~
+    if (tid < DK) {
+        const int i = tid;
+        float g = 1.f;
+        for (int t = 0; t < C; ++t) {
+            const bool in = t < L;
+            float a = 1.f;
+            if (in && VAR == GATED_DELTANET) a = to_f32(ga[row(t)]);
+            if (in && VAR == KDA) a = to_f32(ga[row(t) * DK + i]);
+            g *= a;
+            const float kk = in ? to_f32(gk[row(t) * DK + i]) : 0.f;
+            const float qq = in ? to_f32(gq[row(t) * DK + i]) : 0.f;
+            const float bt = in ? to_f32(gb[row(t)]) : 0.f;
+            GAM[t * PF + i] = g;
+            WPT[i * PC + t] = from_f32<E>(g > 0.f ? bt * kk / g : 0.f);
+            QTT[i * PC + t] = from_f32<E>(g * qq);
+            KTT[i * PC + t] = from_f32<E>(g * kk);
+        }
+        if (DECAY && !(g >= KDN_DECAY_FLOOR))
+            *s_flag = 1;
+    }
+    for (int x = tid; x < C * C; x += NT) {            // blocks above the diagonal
+        const int t = x / C, s = x % C;
+        if ((s >> 4) > (t >> 4)) {
+            DAQ[t * PC + s] = DAK[t * PC + s] = from_f32<E>(0.f);
+            DAQT[s * PC + t] = DAKT[s * PC + t] = from_f32<E>(0.f);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NSA; ++k) {
+        const int x = wv + NW * k;
+        if (x >= NL) continue;
+        int bi, bj;
+        tri(x, bi, bj);
+        const int s = bj * 16 + (lane & 15), t0 = bi * 16 + (lane >> 4) * 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + r;
+            const E vq = from_f32<E>(s <= t ? daq[k][r] : 0.f);
+            const E vk = from_f32<E>(s < t ? -dak[k][r] : 0.f);
+            DAQ[t * PC + s] = vq;
+            DAQT[s * PC + t] = vq;
+            DAK[t * PC + s] = vk;
+            DAKT[s * PC + t] = vk;
+        }
+    }
+    if (DECAY) {
+        // sum_s W~_s,i dW~_s,i (the W~ term of d log gamma_C)
+#pragma unroll
+        for (int k = 0; k < NS3; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTI) continue;
+            const int mt = tau / NTI, ni = tau % NTI;
+            const int i = ni * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc += to_f32(WR[(t0 + r) * PK + i]) * dw3[k][r];
+            acc += __shfl_xor(acc, 16, WAVE);
+            acc += __shfl_xor(acc, 32, WAVE);
+            if (lane < 16)
+                atomicAdd(&s_dgc[i], acc);
+        }
+    }
+    __syncthreads();
+    const bool exact = *s_flag != 0;
+
+    // ---- decay-scaled products (or their exact elementwise sums)
+    if (!exact) {
+#pragma unroll
+        for (int k = 0; k < NS3; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTI) continue;
+            const int mt = tau / NTI, ni = tau % NTI;
+            const int i0 = ni * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dw3[k][r] *= s_gc[i0];
+            mma_tile_k<E, C>(dq3[k], DAQ + mt * 16 * PC, PC, WPT + ni * 16 * PC, PC, lane);
+            mma_tile_k<E, C>(dk3[k], DAK + mt * 16 * PC, PC, WPT + ni * 16 * PC, PC, lane);
+            mma_tile_k<E, C>(dw3[k], DAKT + mt * 16 * PC, PC, KTT + ni * 16 * PC, PC, lane);
+            mma_tile_k<E, C>(dw3[k], DAQT + mt * 16 * PC, PC, QTT + ni * 16 * PC, PC, lane);
+        }
+    } else {
+        // Exact: with R(t, s) = prod_{s < r <= t} a_r (per channel),
+        //   dq_t = gamma_t dQ~S_t + sum_{s<=t} dA_qk[t,s] w_s R(t,s),
+        //   gamma_t dK~_t likewise with dA_kk (s < t),
+        //   dw_s = R(C-1,s) dW~_s + sum_{t>s} dA_kk[t,s] k_t R(t,s)
+        //          + sum_{t>=s} dA_qk[t,s] q_t R(t,s),
+        // stored already scaled (dq3 <- dq, dk3 <- gamma dK~, dw3 <- dw).
+        auto dec = [&](int t, int i) {
+            if (t >= L) return 1.f;
+            return VAR == GATED_DELTANET ? to_f32(ga[row(t)])
+                 : (VAR == KDA ? to_f32(ga[row(t) * DK + i]) : 1.f);
+        };
+        auto wval = [&](int s, int i) {
+            return s < L ? to_f32(gb[row(s)]) * to_f32(gk[row(s) * DK + i]) : 0.f;
+        };
+#pragma unroll
+        for (int k = 0; k < NS3; ++k) {
+            const int tau = wv + NW * k;
+            if (tau >= NB * NTI) continue;
+            const int mt = tau / NTI, ni = tau % NTI;
+            const int i = ni * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = mt * 16 + (lane >> 4) * 4 + r;
+                const float g = GAM[t * PF + i];
+                float xq = g * dq3[k][r], xk = g * dk3[k][r];
+                float R = 1.f;
+                for (int s = t; s >= 0; --s) {
+                    const float w = wval(s, i);
+                    xq += to_f32(DAQ[t * PC + s]) * w * R;
+                    if (s < t)
+                        xk += to_f32(DAK[t * PC + s]) * w * R;
+                    R *= dec(s, i);
+                }
+                float rc = 1.f;                           // R(C-1, t)
+                for (int u = t + 1; u < C; ++u)
+                    rc *= dec(u, i);
+                float xw = rc * dw3[k][r];
+                R = 1.f;
+                for (int u = t; u < C; ++u) {
+                    if (u > t)
+                        R *= dec(u, i);
+                    const float kk = u < L ? to_f32(gk[row(u) * DK + i]) : 0.f;
+                    const float qq = u < L ? to_f32(gq[row(u) * DK + i]) : 0.f;
+                    if (u > t)
+                        xw += to_f32(DAK[u * PC + t]) * kk * R;
+                    xw += to_f32(DAQ[u * PC + t]) * qq * R;
+                }
+                dq3[k][r] = xq;
+                dk3[k][r] = xk;
+                dw3[k][r] = xw;
+            }
+        }
+    }
+    __syncthreads();                                   // dA, W'^T read; DG overwrites them
+
+    // ---- elementwise: dq, dk, dbeta, d log gamma
+#pragma unroll
+    for (int k = 0; k < NS3; ++k) {
+        const int tau = wv + NW * k;
+        if (tau >= NB * NTI) continue;
+        const int mt = tau / NTI, ni = tau % NTI;
+        const int i = ni * 16 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = mt * 16 + (lane >> 4) * 4 + r;
+            const bool in = t < L;
+            const float g = GAM[t * PF + i];
+            const float kk = in ? to_f32(gk[row(t) * DK + i]) : 0.f;
+            const float qq = in ? to_f32(gq[row(t) * DK + i]) : 0.f;
+            const float bt = in ? to_f32(gb[row(t)]) : 0.f;
+            const float dq = exact ? dq3[k][r] : g * dq3[k][r];
+            const float dkd = exact ? dk3[k][r] : g * dk3[k][r];
+            const float dw = exact ? dw3[k][r] : (g > 0.f ? dw3[k][r] / g : 0.f);
+            if (in) {
+                P.dq[row(t) * DK + i] = dq;
+                P.dk_[row(t) * DK + i] = dkd + bt * dw;
+            }
+            float db = kk * dw;
+            db += __shfl_xor(db, 1, WAVE);
+            db += __shfl_xor(db, 2, WAVE);
+            db += __shfl_xor(db, 4, WAVE);
+            db += __shfl_xor(db, 8, WAVE);
+            if ((lane & 15) == 0)
+                atomicAdd(&s_db[t], db);
+            if (DECAY)
+                DG[t * PF + i] = kk * dkd + qq * dq - bt * kk * dw;
+        }
+    }
+    __syncthreads();
+    // ---- d log alpha: reverse sum over the chunk's tokens, plus the gamma_C terms
+    if (DECAY && tid < DK) {
+        const int i = tid;
+        float acc = s_dgc[i] + s_gc[i] * s_sds[i];
+        for (int t = C - 1; t >= 0; --t) {
+            acc += DG[t * PF + i];
+            if (VAR == KDA && t < L)
+                P.dla[row(t) * DK + i] = acc;
+            if (VAR == GATED_DELTANET)
+                atomicAdd(&s_dla[t], acc);
+        }
+    }
+    __syncthreads();
+    if (tid < L) {
+        P.dbeta[row(tid)] = s_db[tid];
+        if (VAR == GATED_DELTANET)
+            P.dla[row(tid)] = s_dla[tid];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+template <typename E, int VAR, int DK, int C>
+static hipError_t launch_bwd_vc(const BackwardParams &P, hipStream_t st) {
+    const long heads = (long)P.B * P.H;
+    const long nc = (P.T + C - 1) / C;
+    constexpr bool DECAY = VAR != DELTANET;
+    // reverse state pass: value blocks of 32 (bf16) or 16 columns
+    if (sizeof(E) == 2 && P.dv % 32 == 0) {
+        const dim3 grid((unsigned)(heads * (P.dv / 32))), block(512);
+        hipLaunchKernelGGL((backward_state_kernel<E, DECAY, DK, 32, C>), grid, block, 0, st, P);
+    } else {
+        const dim3 grid((unsigned)(heads * (P.dv / 16))), block(512);
+        hipLaunchKernelGGL((backward_state_kernel<E, DECAY, DK, 16, C>), grid, block, 0, st, P);
+    }
+    if (hipError_t e = hipGetLastError())
+        return e;
+    if (nc == 0)
+        return hipSuccess;
+    constexpr int DVH = sizeof(E) == 2 ? 64 : 32;
+    const dim3 grid((unsigned)(heads * nc)), block(512);
+    hipLaunchKernelGGL((backward_chunk_kernel<E, VAR, DK, C, DVH>), grid, block, 0, st, P);
+    return hipGetLastError();
+}
+
+template <typename E, int VAR>
+static hipError_t launch_bwd_v(const BackwardParams &P, hipStream_t st) {
+    if (P.dk == 128 && P.chunk == 64) {
+        if constexpr (sizeof(E) == 2)
+            return launch_bwd_vc<E, VAR, 128, 64>(P, st);
+        return hipErrorInvalidValue;
+    }
+    if (P.dk == 128 && P.chunk == 32) return launch_bwd_vc<E, VAR, 128, 32>(P, st);
+    if (P.dk == 64 && P.chunk == 64) return launch_bwd_vc<E, VAR, 64, 64>(P, st);
+    if (P.dk == 64 && P.chunk == 32) return launch_bwd_vc<E, VAR, 64, 32>(P, st);
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+static hipError_t launch_bwd_e(const BackwardParams &P, hipStream_t st) {
+    switch (P.variant) {
+    case DELTANET: return launch_bwd_v<E, DELTANET>(P, st);
+    case GATED_DELTANET: return launch_bwd_v<E, GATED_DELTANET>(P, st);
+    case KDA: return launch_bwd_v<E, KDA>(P, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward(const BackwardParams &P, hipStream_t st) {
+    if ((long)P.B * P.H == 0)
+        return hipSuccess;
+    return P.bf16 ? launch_bwd_e<bf16>(P, st) : launch_bwd_e<float>(P, st);
+}
+
+}  // namespace kdn

@@ -40,7 +40,31 @@ struct PrefillParams {
     float *ws_mob;
     float *ws_p0;
     float *ws_stat;
+    // Gradient computation: S at every chunk start is saved here by the state
+    // pass ([batch*head][chunk][dk][dv] float32; null otherwise).
+    float *states;
     int cus;           // compute units of the current device
+};
+
+// Gradients of the chunkwise prefill (write-strength variants).  All gradient
+// outputs are float32.
+struct BackwardParams {
+    int variant;
+    int bf16;
+    int B, T, H, dk, dv;
+    int chunk;
+    const void *q, *k, *v, *alpha, *beta;   // [B, T, H, .] in the call's dtype
+    const float *S0;                        // may be null (zero)
+    const void *dO;                         // [B, T, H, dv] call dtype
+    const float *dS_out;                    // [B, H, dk, dv], may be null (zero)
+    float *dq, *dk_, *dv_;                  // [B, T, H, dk / dv]
+    float *dla;                             // d log alpha: [B,T,H] (GDN), [B,T,H,dk] (KDA)
+    float *dbeta;                           // [B, T, H]
+    float *dS0;                             // [B, H, dk, dv], may be null
+    void *ws;                               // forward records (kdn_workspace.h)
+    float *states;                          // S at every chunk start
+    float *dstates;                         // dS leaving every chunk
+    int cus;
 };
 
 hipError_t launch_decode(const DecodeParams &P, hipStream_t stream);
@@ -70,5 +94,9 @@ hipError_t launch_prefill_state(const PrefillParams &P, hipStream_t stream);
 // Bytes of workspace the two-pass schedule needs (0 when there is no chunk).
 long long prefill_workspace_bytes(int variant, int bf16, long long B, long long T,
                                   long long H, int dk, int C);
+
+// Gradient kernels (after the forward prep and the state pass with states
+// saved): the reverse state pass, then the chunk-parallel local gradients.
+hipError_t launch_backward(const BackwardParams &P, hipStream_t stream);
 
 }  // namespace kdn

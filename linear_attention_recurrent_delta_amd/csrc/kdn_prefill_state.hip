@@ -18,6 +18,10 @@
 // ahead, and the record two chunks ahead is prefetched into L2, so the only
 // LDS traffic is the S / U / E exchange between the MFMA output and operand
 // layouts.  Three barriers per chunk.
+//
+// SAVE (the forward pass of the gradient computation): S at the start of every
+// chunk is written to P.states ([batch*head][chunk][d_k][d_v], float32), and
+// neither o nor S_out is written.
 #include "kdn_device.h"
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
@@ -95,7 +99,7 @@ template <> __device__ __forceinline__ void buf_store<float>(__amdgpu_buffer_rsr
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, (int)voff, 0, 0);
 }
 
-template <typename E, bool DECAY, int DK, int NV, int C>
+template <typename E, bool DECAY, int DK, int NV, int C, bool SAVE>
 __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
     constexpr int KG = FragMma<E>::KG;
     constexpr int NB = C / 16;          // token blocks of a chunk
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
     // c = -1 (before the first chunk) stores through an empty descriptor:
     // every store is dropped, and no branch guards it.
     auto finish_output = [&](int c) {
-        const auto orr = c >= 0 ? row_rsrc(go, c) : buf_rsrc(go, 0u);
+        const auto orr = (!SAVE && c >= 0) ? row_rsrc(go, c) : buf_rsrc(go, 0u);
         const E *ET = ETB[c & 1];
 #pragma unroll
         for (int nj = 0; nj < NTJ; ++nj) {
@@ -277,6 +281,18 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
     };
 
     auto compute = [&](const Chunk &X, int c) {
+        if constexpr (SAVE) {
+            float *sv = P.states + ((long)bh * NC + c) * DK * DV;
+#pragma unroll
+            for (int k = 0; k < NSW; ++k) {
+                const int tau = wv + 8 * k;
+                if (NSTT % 8 != 0 && tau >= NSTT) continue;
+                const int j = (tau / NIBT) * 16 + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sv[(long)(i0 + r) * DV + v0 + j] = sacc[k][r];
+            }
+        }
         // phase 1: chain waves U = V - K~ S; output waves finish chunk c-1
         // and start Q~ S of chunk c
         if (chain) {
@@ -370,6 +386,8 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
     }
     if (outw && NC > 0)
         finish_output(NC - 1);
+    if constexpr (SAVE)
+        return;
 
 #pragma unroll
     for (int k = 0; k < NSW; ++k) {
@@ -386,7 +404,12 @@ template <typename E, bool DECAY, int DK, int NV, int C>
 static hipError_t launch_state_one(const PrefillParams &P, hipStream_t st) {
     const long heads = (long)P.B * P.H;
     const dim3 grid((unsigned)(heads * (P.dv / NV))), block(512);
-    hipLaunchKernelGGL((prefill_state_kernel<E, DECAY, DK, NV, C>), grid, block, 0, st, P);
+    if (P.states)
+        hipLaunchKernelGGL((prefill_state_kernel<E, DECAY, DK, NV, C, true>), grid, block, 0,
+                           st, P);
+    else
+        hipLaunchKernelGGL((prefill_state_kernel<E, DECAY, DK, NV, C, false>), grid, block, 0,
+                           st, P);
     return hipGetLastError();
 }
 

@@ -62,6 +62,10 @@ def load(path: str = LIB_PATH):
     lib.kdn_recurrent_decode.argtypes = [i, i, i, i, i, i, f] + [vp] * 11
     lib.kdn_recurrent_decode_multi.restype = i
     lib.kdn_recurrent_decode_multi.argtypes = [i, i, i, i, i, i, i, f] + [vp] * 13
+    lib.kdn_chunk_prefill_backward.restype = i
+    lib.kdn_chunk_prefill_backward.argtypes = [i] * 8 + [vp] * 14 + [vp, u64, vp]
+    lib.kdn_chunk_prefill_backward_workspace_size.restype = u64
+    lib.kdn_chunk_prefill_backward_workspace_size.argtypes = [i] * 8 + [ctypes.POINTER(i)]
     lib.kdn_status_string.restype = ctypes.c_char_p
     lib.kdn_status_string.argtypes = [i]
     lib.kdn_chunk_prefill_chunk_size.restype = i
@@ -141,6 +145,33 @@ def kdn_chunk_prefill_workspace_size(variant, dtype, B, T, H, d_k, d_v, chunk):
     n = lib.kdn_chunk_prefill_workspace_size(int(variant), int(dtype), int(B), int(T),
                                              int(H), int(d_k), int(d_v), int(chunk),
                                              ctypes.byref(st))
+    _check(lib, st.value)
+    return int(n)
+
+
+def kdn_chunk_prefill_backward(variant, dtype, B, T, H, d_k, d_v, chunk, q, k, v,
+                               alpha, beta, S0, d_o, dS_out, dq, dk, dv, dlog_alpha,
+                               dbeta, dS0, workspace=None, workspace_bytes=0,
+                               stream=None):
+    """Raw entry point: same arguments as the C function."""
+    lib = load()
+    if workspace is not None and not isinstance(workspace, int) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.kdn_chunk_prefill_backward(
+        int(variant), int(dtype), int(B), int(T), int(H), int(d_k), int(d_v), int(chunk),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(d_o),
+        _ptr(dS_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_alpha), _ptr(dbeta),
+        _ptr(dS0), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check(lib, st)
+
+
+def kdn_chunk_prefill_backward_workspace_size(variant, dtype, B, T, H, d_k, d_v, chunk):
+    """Bytes of workspace the gradient call needs; raises on invalid sizes."""
+    lib = load()
+    st = ctypes.c_int(0)
+    n = lib.kdn_chunk_prefill_backward_workspace_size(
+        int(variant), int(dtype), int(B), int(T), int(H), int(d_k), int(d_v), int(chunk),
+        ctypes.byref(st))
     _check(lib, st.value)
     return int(n)
 
@@ -248,3 +279,35 @@ def decode_multi(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
                                alpha, beta, proc_noise, obs_noise, S0, p0, o, S, p,
                                stream)
     return o, S, p
+
+
+def prefill_backward(variant, q, k, v, d_o, alpha=None, beta=None, S0=None, dS_out=None,
+                     chunk=0, out=None, workspace=None, stream=None):
+    """Gradients of :func:`prefill` (DeltaNet, Gated DeltaNet, KDA) for the
+    cotangents d_o [B,T,H,dv] and dS_out [B,H,dk,dv] (None: zero).  Returns
+    float32 (dq, dk, dv, dlog_alpha, dbeta, dS0); dlog_alpha = alpha dL/dalpha
+    ([B,T,H] for gated_deltanet, [B,T,H,dk] for kda, None for deltanet).
+    ``workspace``: a uint8 tensor of at least the queried size, or None to
+    allocate one."""
+    vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = DTYPES[q.dtype]
+    dev = q.device
+    if out is None:
+        f = torch.float32
+        gq = torch.empty((B, T, H, dk), dtype=f, device=dev)
+        gk = torch.empty((B, T, H, dk), dtype=f, device=dev)
+        gv = torch.empty((B, T, H, dv), dtype=f, device=dev)
+        ga = (None if vid == 0 else
+              torch.empty((B, T, H) if vid == 1 else (B, T, H, dk), dtype=f, device=dev))
+        gb = torch.empty((B, T, H), dtype=f, device=dev)
+        gS = torch.empty((B, H, dk, dv), dtype=f, device=dev)
+    else:
+        gq, gk, gv, ga, gb, gS = out
+    if workspace is None:
+        n = kdn_chunk_prefill_backward_workspace_size(vid, dt, B, T, H, dk, dv, chunk)
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    kdn_chunk_prefill_backward(vid, dt, B, T, H, dk, dv, chunk, q, k, v, alpha, beta, S0,
+                               d_o, dS_out, gq, gk, gv, ga, gb, gS, workspace, 0, stream)
+    return gq, gk, gv, ga, gb, gS

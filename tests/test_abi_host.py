@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kdn_chunk_prefill", "kdn_recurrent_decode", "kdn_status_string",
-              "kdn_recurrent_decode_multi",
+              "kdn_recurrent_decode_multi", "kdn_chunk_prefill_backward",
+              "kdn_chunk_prefill_backward_workspace_size",
               "kdn_chunk_prefill_chunk_size", "kdn_abi_version",
               "kdn_chunk_prefill_workspace_size"):
         assert n in names
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.kdn_abi_version() == 3
+    assert lib.kdn_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -282,6 +283,61 @@ def test_decode_multi_accepts_in_place_and_empty(lib):
     assert lib.kdn_recurrent_decode_multi(*_multi_args(H=0, T=0)) == OK
     assert lib.kdn_recurrent_decode_multi(
         *_multi_args(N=0, q=None, k=None, v=None, o=None, S0=None)) == OK
+
+
+def _bwd_args(variant=1, dtype=1, B=2, T=100, H=4, dk=128, dv=128, chunk=0, **over):
+    a = dict(q=A, k=A + MB, v=A + 2 * MB, alpha=None if variant == 0 else A + 3 * MB,
+             beta=A + 4 * MB, S0=A + 5 * MB, do=A + 6 * MB, dS=A + 7 * MB,
+             gq=A + 8 * MB, gk=A + 9 * MB, gv=A + 10 * MB,
+             da=None if variant == 0 else A + 11 * MB, db=A + 12 * MB, dS0=A + 13 * MB,
+             ws=A + 16 * MB, ws_bytes=1 << 40)
+    a.update(over)
+    return (variant, dtype, B, T, H, dk, dv, chunk, a["q"], a["k"], a["v"], a["alpha"],
+            a["beta"], a["S0"], a["do"], a["dS"], a["gq"], a["gk"], a["gv"], a["da"],
+            a["db"], a["dS0"], a["ws"], a["ws_bytes"], None)
+
+
+BWD_CASES = [
+    ("diagonal KDN", dict(variant=3, beta=None), EUNSUP),
+    ("isotropic KDN", dict(variant=4, beta=None), EUNSUP),
+    ("bad dtype", dict(dtype=2), EUNSUP),
+    ("negative T", dict(T=-1), ESHAPE),
+    ("d_k 32", dict(dk=32), EUNSUP),
+    ("d_o NULL", dict(do=None), ENULL),
+    ("dq NULL", dict(gq=None), ENULL),
+    ("dbeta NULL", dict(db=None), ENULL),
+    ("GDN without dlog_alpha", dict(da=None), ENULL),
+    ("DeltaNet with dlog_alpha", dict(variant=0, da=A + 11 * MB), ENULL),
+    ("GDN without beta", dict(beta=None), ENULL),
+    ("misaligned dk", dict(gk=A + 9 * MB + 8), EALIGN),
+    ("misaligned dS_out", dict(dS=A + 7 * MB + 4), EALIGN),
+    ("odd dbeta", dict(db=A + 12 * MB + 2), EALIGN),
+    ("KDA misaligned dlog_alpha", dict(variant=2, da=A + 11 * MB + 4), EALIGN),
+    ("no workspace", dict(ws=None, ws_bytes=0), EWS),
+    ("small workspace", dict(ws_bytes=1000), EWS),
+    ("misaligned workspace", dict(ws=A + 16 * MB + 64), EALIGN),
+    ("dq overlaps q", dict(gq=A + 1024), EALIAS),
+    ("dk overlaps dq", dict(gk=A + 8 * MB + 4096), EALIAS),
+    ("dS0 overlaps dS_out", dict(dS0=A + 7 * MB), EALIAS),
+    ("workspace overlaps dv", dict(ws=A + 10 * MB), EALIAS),
+]
+
+
+@pytest.mark.parametrize("name,over,status", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_validation(lib, name, over, status):
+    assert lib.kdn_chunk_prefill_backward(*_bwd_args(**over)) == status
+
+
+def test_backward_workspace_size(lib):
+    st = ctypes.c_int(-1)
+    f = lib.kdn_chunk_prefill_backward_workspace_size
+    rec = 66048
+    n = f(1, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
+    assert st.value == OK and n == 2 * 4 * 2 * (rec + 2 * 128 * 128 * 4)
+    assert f(3, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st)) == 0 and st.value == EUNSUP
+    assert f(1, 1, 2, 0, 4, 128, 128, 0, ctypes.byref(st)) == 0 and st.value == OK
+    # no tokens: nothing to launch for B*H = 0, and no workspace is needed
+    assert lib.kdn_chunk_prefill_backward(*_bwd_args(B=0, ws=None, ws_bytes=0)) == OK
 
 
 def test_binding_raises_with_status(lib):

@@ -1,0 +1,155 @@
+"""Gradients of the chunkwise prefill on the GPU (kdn_chunk_prefill_backward)
+against the fp64 oracle's reverse-mode backward.
+
+Every case draws seeded inputs and cotangents (dO, dS_out), runs the library,
+runs the oracle on exactly the same rounded values, and compares each
+gradient tensor (dq, dk, dv, dlog_alpha, dbeta, dS0) by
+max|gpu - ref| / max|ref| against TOL (1e-4 for float32 inputs, 2e-2 for
+bfloat16 inputs with float32 state, as for the forward pass).  The oracle's
+decay gradient dL/dalpha is compared as alpha * dL/dalpha, the quantity the
+library returns.
+"""
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, check, log, np64
+from linear_attention_recurrent_delta_amd import kdn, synth
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ["deltanet", "gated_deltanet", "kda"]
+NAMES = ("q", "k", "v", "log_alpha", "beta", "S0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kdn.ensure_built()
+    yield
+
+
+def _inputs(variant, B, T, H, dk, dv, dtype, seed, state=True, ds=True):
+    inp = synth.gen_prefill(variant, B, T, H, dk, dv, dtype, seed=seed, device="cuda",
+                            random_state=state)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    inp["dO"] = torch.randn((B, T, H, dv), generator=g, device="cuda").to(inp["q"].dtype)
+    inp["dS"] = torch.randn((B, H, dk, dv), generator=g, device="cuda") if ds else None
+    return inp
+
+
+def _ref(variant, inp, heads=None):
+    f = lambda x: None if x is None else np64(x)
+    sl = lambda x, b, h, state: None if x is None else (
+        x[b:b + 1, h:h + 1] if state else x[b:b + 1, :, h:h + 1])
+    if heads is None:
+        parts = [(inp, None)]
+    else:
+        parts = [({k: sl(v, b, h, k in ("S0", "dS")) for k, v in inp.items()}, (b, h))
+                 for (b, h) in heads]
+    out = []
+    for x, key in parts:
+        dq, dk, dv, da, db, dS0 = oracle.backward(
+            variant, f(x["q"]), f(x["k"]), f(x["v"]), f(x.get("alpha")), f(x["beta"]),
+            f(x.get("S0")), f(x["dO"]), f(x.get("dS")))
+        if da is not None:
+            da = da * f(x["alpha"])
+        out.append((key, dict(zip(NAMES, (dq, dk, dv, da, db, dS0)))))
+    return out
+
+
+def _gpu(variant, inp, chunk=0):
+    got = kdn.prefill_backward(variant, inp["q"], inp["k"], inp["v"], inp["dO"],
+                               alpha=inp.get("alpha"), beta=inp.get("beta"),
+                               S0=inp.get("S0"), dS_out=inp.get("dS"), chunk=chunk)
+    torch.cuda.synchronize()
+    return dict(zip(NAMES, got))
+
+
+def _compare(variant, inp, tol, chunk=0, heads=None):
+    got = _gpu(variant, inp, chunk)
+    for n in NAMES:
+        if got[n] is not None:
+            assert torch.isfinite(got[n]).all(), f"d{n} not finite"
+    for key, ref in _ref(variant, inp, heads):
+        for n in NAMES:
+            if ref[n] is None:
+                assert got[n] is None
+                continue
+            g = got[n]
+            if key is not None:
+                b, h = key
+                g = g[b:b + 1, h:h + 1] if n == "S0" else g[b:b + 1, :, h:h + 1]
+            check(f"d{n}" + ("" if key is None else f"[b={key[0]},h={key[1]}]"),
+                  np64(g), ref[n], tol)
+
+
+CASES = [(v, dt, dk, dv) for v in VARIANTS for dt in ("bf16", "f32")
+         for (dk, dv) in ((128, 128), (64, 64), (128, 64), (64, 128))]
+
+
+@pytest.mark.parametrize("variant,dtype,dk,dv", CASES,
+                         ids=[f"{v}-{d}-k{a}v{b}" for v, d, a, b in CASES])
+def test_backward_small(variant, dtype, dk, dv):
+    log(f"backward {variant} {dtype} dk={dk} dv={dv} B2 T200 H2")
+    inp = _inputs(variant, 2, 200, 2, dk, dv, dtype, seed=101)
+    _compare(variant, inp, TOL[dtype])
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_backward_chunk32(variant):
+    log(f"backward chunk 32 {variant} bf16")
+    inp = _inputs(variant, 1, 150, 3, 128, 128, "bf16", seed=102)
+    _compare(variant, inp, TOL["bf16"], chunk=32)
+
+
+@pytest.mark.parametrize("T", [0, 1, 2, 63, 64, 65, 129])
+@pytest.mark.parametrize("variant,dtype", [("gated_deltanet", "bf16"), ("kda", "f32")])
+def test_backward_lengths(variant, dtype, T):
+    log(f"backward length T={T} {variant} {dtype}")
+    inp = _inputs(variant, 2, T, 2, 128, 128 if dtype == "bf16" else 64, dtype, seed=103 + T)
+    _compare(variant, inp, TOL[dtype])
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_backward_without_state_cotangent(variant):
+    log(f"backward S0 = NULL, dS_out = NULL {variant}")
+    inp = _inputs(variant, 2, 140, 2, 128, 128, "bf16", seed=104, state=False, ds=False)
+    _compare(variant, inp, TOL["bf16"])
+
+
+@pytest.mark.parametrize("variant", ["gated_deltanet", "kda"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_alpha_zero(variant, dtype):
+    """alpha = 0 on some tokens: those chunks take the exact elementwise path."""
+    log(f"backward alpha=0 {variant} {dtype}")
+    inp = _inputs(variant, 1, 200, 2, 64, 64, dtype, seed=105)
+    a = inp["alpha"].float()
+    a[:, 10] = 0.0
+    a[:, 100:103] = 0.0
+    if a.dim() == 4:
+        a[:, 150, :, :32] = 0.0
+    inp["alpha"] = a.to(inp["alpha"].dtype)
+    _compare(variant, inp, TOL[dtype])
+
+
+@pytest.mark.parametrize("variant", ["gated_deltanet", "kda"])
+def test_backward_strong_decay(variant):
+    """A chunk whose cumulative decay drops below 2^-90."""
+    log(f"backward strong decay {variant}")
+    inp = _inputs(variant, 1, 192, 2, 128, 128, "bf16", seed=106)
+    a = inp["alpha"].float()
+    a[:, 64:128] = 0.2
+    inp["alpha"] = a.to(inp["alpha"].dtype)
+    _compare(variant, inp, TOL["bf16"])
+
+
+def test_backward_workload_sampled():
+    """Gated DeltaNet workload (B4 H16 T4096, d = 128, bf16): every head on the
+    GPU, sampled heads against the oracle at full length."""
+    c = synth.CONFIGS["gated_deltanet"]
+    log(f"backward workload gated_deltanet B{c['B']} H{c['H']} T{c['T']}: sampled heads")
+    inp = _inputs("gated_deltanet", c["B"], c["T"], c["H"], c["dk"], c["dv"], c["dtype"],
+                  seed=synth.seed_of("gated_deltanet"), state=False)
+    _compare("gated_deltanet", inp, TOL["bf16"], heads=[(0, 0), (3, 15)])
