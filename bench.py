@@ -9,8 +9,9 @@ resident in HBM.  Rank 0 prints ONE JSON line with the headline value
 (prefill tokens/s), the roofline of the prefill kernel (HBM-bound by its
 algorithmic bytes; the MFMA fraction of its algorithmic flops is reported
 next to it), the fp64 oracle timed on the host cores, and the other
-workloads (KDA, diagonal-KDN and isotropic-KDN prefill, diagonal-KDN decode,
-16-token multi-token decode) each with its own roofline.
+workloads (KDA, diagonal-KDN and isotropic-KDN prefill, the Gated DeltaNet
+gradient call, diagonal-KDN decode, 16-token multi-token decode) each with its
+own roofline.
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ METRIC = "prefill tokens/s + decode steps/s per head-state; % MFMA / % HBM roofl
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
-KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_variance.hip",
+KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_variance.hip", "kdn_backward.hip",
                   "kdn_decode.hip", "kdn_device.h", "kdn_launch.h", "kdn_workspace.h"]
 
 
@@ -60,6 +61,31 @@ def prefill_flops_per_head_token(C, dk, dv):
     # A_kk, A_qk (2 C dk), T solve (C^2/3), products with T ((C-1)(dk+dv)),
     # A_qk E ((C+1) dv), K~S, Q~S, W~^T E (6 dk dv); triangles counted as half.
     return 2 * C * dk + C * C / 3 + (C - 1) * (dk + dv) + (C + 1) * dv + 6 * dk * dv
+
+
+def backward_bytes(variant, B, T, H, dk, dv, es):
+    """Gradient call: q, k, v, dO (and alpha, beta) read in the call dtype;
+    dq, dk, dv, dbeta (and dlog_alpha) written as float32; S0 = dS_out = NULL."""
+    tok = B * T * H
+    n = tok * (2 * dk + 2 * dv) * es + tok * es             # q, k, v, dO, beta
+    n += tok * (2 * dk + dv) * 4 + tok * 4                  # dq, dk, dv, dbeta
+    if variant == "gated_deltanet":
+        n += tok * es + tok * 4
+    elif variant == "kda":
+        n += tok * dk * es + tok * dk * 4
+    n += B * H * dk * dv * 4                                # dS0
+    return n
+
+
+def backward_flops_per_head_token(C, dk, dv):
+    """The forward chunk pass it re-runs, then per token (multiply-adds, x2):
+    the reverse state pass A_qk^T dO, W~ dS, T^T dE, Q~^T dO, K~^T dU
+    (C dv + 3 dk dv) and the local gradients U, E, dE, dU, dO S^T, dU S^T,
+    E dS^T, dO E^T, dU E^T and the four decay-scaled C x C x dk products
+    (5 dk dv + 2.5 C dv + 2 C dk); triangles counted as half."""
+    state = C * dv + 3 * dk * dv
+    local = 5 * dk * dv + 2.5 * C * dv + 2 * C * dk
+    return prefill_flops_per_head_token(C, dk, dv) + 2 * (state + local)
 
 
 def decode_bytes(N, H, dk, dv, es):
@@ -156,6 +182,60 @@ def bench_prefill(name, steps, warmup, torch, kdn, synth, schedule="two_pass"):
                  "algorithmic_flops": flops},
     }
     del inp, o, S, p, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_backward(name, steps, warmup, torch, kdn, synth):
+    c = synth.CONFIGS[name]
+    variant = c["variant"]
+    inp = synth.gen_config(name, device="cuda")
+    B, T, H, dk, dv = c["B"], c["T"], c["H"], c["dk"], c["dv"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.seed_of(name) + 7)
+    d_o = torch.randn((B, T, H, dv), generator=g, device="cuda").to(inp["q"].dtype)
+    f = torch.float32
+    out = (torch.empty((B, T, H, dk), dtype=f, device="cuda"),
+           torch.empty((B, T, H, dk), dtype=f, device="cuda"),
+           torch.empty((B, T, H, dv), dtype=f, device="cuda"),
+           None if variant == "deltanet" else torch.empty(
+               (B, T, H) if variant == "gated_deltanet" else (B, T, H, dk), dtype=f,
+               device="cuda"),
+           torch.empty((B, T, H), dtype=f, device="cuda"),
+           torch.empty((B, H, dk, dv), dtype=f, device="cuda"))
+    dt = 1 if c["dtype"] == "bf16" else 0
+    C = kdn.kdn_chunk_prefill_chunk_size(dt, dk, dv, 0)
+    n = kdn.kdn_chunk_prefill_backward_workspace_size(kdn.VARIANTS[variant], dt, B, T, H,
+                                                      dk, dv, 0)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def step():
+        kdn.prefill_backward(variant, inp["q"], inp["k"], inp["v"], d_o,
+                             alpha=inp.get("alpha"), beta=inp.get("beta"), out=out,
+                             workspace=ws)
+
+    wall, gpu = time_launches(step, steps, warmup, torch)
+    es = 2 if c["dtype"] == "bf16" else 4
+    nbytes = backward_bytes(variant, B, T, H, dk, dv, es)
+    flops = backward_flops_per_head_token(C, dk, dv) * B * H * T
+    launch_s = gpu / steps
+    res = {
+        "value": B * T * steps / wall, "unit": "tokens/s",
+        "head_tokens_per_s": B * H * T * steps / wall,
+        "ms_per_step": wall / steps * 1e3,
+        "config": {"workload": f"{name}_backward", "variant": variant, "B": B, "T": T,
+                   "H": H, "d_k": dk, "d_v": dv, "chunk": C, "dtype": c["dtype"],
+                   "gradients": "float32", "workspace_bytes": n},
+        "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": load_traffic(f"backward_{name}"), "algorithmic_bytes": nbytes,
+                     "kernel_ms": launch_s * 1e3},
+        "mfma": {"achieved": flops / launch_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": flops / launch_s / 1e12 / BF16_PEAK_TFLOPS,
+                 "algorithmic_flops": flops},
+    }
+    del inp, d_o, out, ws
     torch.cuda.empty_cache()
     return res
 
@@ -343,6 +423,8 @@ def main():
             w[f"{name}_prefill"] = bench_prefill(name, max(3, args.steps // 2),
                                                  args.warmup, torch, kdn, synth,
                                                  args.schedule)
+        w["gated_deltanet_backward"] = bench_backward("gated_deltanet", max(3, args.steps // 2),
+                                                      args.warmup, torch, kdn, synth)
         w["decode_diag_kdn"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
         w["verify16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth)
         out["workloads"] = w

@@ -35,30 +35,66 @@ namespace kdn {
 // used; the chunk takes the exact elementwise path.
 #define KDN_DECAY_FLOOR 8.077935669463161e-28f   /* 2^-90 */
 
-// Copy a record matrix X[R][K], stored in fragment order (kdn_workspace.h),
-// to LDS.  TRANS: dst[k * pitch + r] = sgn X[r][k]; else dst[r * pitch + k].
-template <typename E, int R, int K, int NT, bool TRANS>
-__device__ __forceinline__ void defrag(E *dst, int pitch, const char *src, float sgn, int tid) {
-    constexpr int EPU = 16 / (int)sizeof(E);
-    constexpr int KG = sizeof(E) == 2 ? 32 : 16;
-    constexpr int NU = R * K / EPU;
-    const uint4 *s = reinterpret_cast<const uint4 *>(src);
-    for (int u = tid; u < NU; u += NT) {
-        const int l = u & 63, grp = u >> 6;
-        const int m = grp / (K / KG), g = grp % (K / KG);
-        const int row = m * 16 + (l & 15);
-        const uint4 v = s[u];
-        const E *e = reinterpret_cast<const E *>(&v);
+// The 16-byte units of a record matrix X[R][K] (fragment order,
+// kdn_workspace.h) that thread tid moves: units tid + NT n.  load() issues all
+// of them before any is used; store() writes X to LDS as dst[r * pitch + k]
+// or, TRANS, as X^T: dst[k * pitch + r] (times sgn).
+template <typename E, int R, int K, int NT>
+struct RecUnits {
+    static constexpr int EPU = 16 / (int)sizeof(E);
+    static constexpr int KG = sizeof(E) == 2 ? 32 : 16;
+    static constexpr int NU = R * K / EPU;
+    static constexpr int NPT = (NU + NT - 1) / NT;
+    uint4 u[NPT];
+    __device__ __forceinline__ void load(const char *src, int tid) {
+        const uint4 *s = reinterpret_cast<const uint4 *>(src);
 #pragma unroll
-        for (int x = 0; x < EPU; ++x) {
-            const int col = sizeof(E) == 2 ? g * 32 + (l >> 4) * 8 + x : g * 16 + x * 4 + (l >> 4);
-            const E val = from_f32<E>(sgn * to_f32(e[x]));
-            if (TRANS)
-                dst[col * pitch + row] = val;
-            else
-                dst[row * pitch + col] = val;
+        for (int n = 0; n < NPT; ++n) {
+            const int x = tid + NT * n;
+            if (NU % NT == 0 || x < NU)
+                u[n] = s[x];
         }
     }
+    template <bool TRANS>
+    __device__ __forceinline__ void store(E *dst, int pitch, float sgn, int tid) const {
+#pragma unroll
+        for (int n = 0; n < NPT; ++n) {
+            const int x = tid + NT * n;
+            if (!(NU % NT == 0 || x < NU)) continue;
+            const int l = x & 63, grp = x >> 6;
+            const int m = grp / (K / KG), g = grp % (K / KG);
+            const int row = m * 16 + (l & 15);
+            if (!TRANS && sizeof(E) == 2 && sgn == 1.f) {
+                *reinterpret_cast<uint4 *>(dst + row * pitch + g * 32 + (l >> 4) * 8) = u[n];
+                continue;
+            }
+            const uint4 v = u[n];
+            const E *e = reinterpret_cast<const E *>(&v);
+#pragma unroll
+            for (int xx = 0; xx < EPU; ++xx) {
+                const int col = sizeof(E) == 2 ? g * 32 + (l >> 4) * 8 + xx
+                                               : g * 16 + xx * 4 + (l >> 4);
+                const E val = from_f32<E>(sgn * to_f32(e[xx]));
+                if (TRANS)
+                    dst[col * pitch + row] = val;
+                else
+                    dst[row * pitch + col] = val;
+            }
+        }
+    }
+};
+
+// Four consecutive elements of E from global memory as floats.
+__device__ __forceinline__ void gload4(const float *p, float (&f)[4]) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
+__device__ __forceinline__ void gload4(const bf16 *p, float (&f)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
 }
 
 // ---------------------------------------------------------------------------
@@ -116,9 +152,37 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
         lds_stn<4>(DST + j * PK + i0, s4);
     }
 
-    for (int c = NC - 1; c >= 0; --c) {
-        const int L = min(C, T - c * C);
+    // One chunk's record units and dO elements, loaded one chunk ahead.
+    constexpr int NDO = (C * NV + NT - 1) / NT;
+    struct Rec {
+        RecUnits<E, C, C, NT> aq, tm;
+        RecUnits<E, DK, C, NT> wt;
+        RecUnits<E, C, DK, NT> qd, kd;
+        float gc;
+        E dov[NDO];
+    };
+    auto load = [&](Rec &X, int c) {
         const char *rec = ws + (long)c * LW.rec;
+        X.aq.load(rec + LW.off_aqk, tid);
+        X.wt.load(rec + LW.off_wdt, tid);
+        X.tm.load(rec + LW.off_tm, tid);
+        X.qd.load(rec + LW.off_qd, tid);
+        X.kd.load(rec + LW.off_kd, tid);
+        X.gc = (DECAY && tid < DK) ? reinterpret_cast<const float *>(rec + LW.off_gc)[tid] : 1.f;
+        const int L = min(C, T - c * C);
+#pragma unroll
+        for (int n = 0; n < NDO; ++n) {
+            const int x = tid + NT * n, t = x / NV, j = x % NV;
+            const long row = ((long)b * T + c * C + t) * H + h;
+            X.dov[n] = ((C * NV) % NT == 0 || x < C * NV) && t < L ? gdo[row * DV + v0 + j]
+                                                                  : from_f32<E>(0.f);
+        }
+    };
+    Rec X;
+    if (NC > 0)
+        load(X, NC - 1);
+
+    for (int c = NC - 1; c >= 0; --c) {
         // dS leaving this chunk, for the local-gradient kernel
         float *sv = P.dstates + ((long)bh * NC + c) * DK * DV;
 #pragma unroll
@@ -130,19 +194,21 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
             for (int r = 0; r < 4; ++r)
                 sv[(long)(i0 + r) * DV + v0 + j] = dacc[k][r];
         }
-        defrag<E, C, C, NT, true>(AQT, PC, rec + LW.off_aqk, 1.f, tid);
-        defrag<E, DK, C, NT, true>(WR, PK, rec + LW.off_wdt, 1.f, tid);
-        defrag<E, C, C, NT, true>(TT, PC, rec + LW.off_tm, 1.f, tid);
-        defrag<E, C, DK, NT, true>(QT, PC, rec + LW.off_qd, 1.f, tid);
-        defrag<E, C, DK, NT, true>(KT, PC, rec + LW.off_kd, -1.f, tid);
+        X.aq.template store<true>(AQT, PC, 1.f, tid);
+        X.wt.template store<true>(WR, PK, 1.f, tid);
+        X.tm.template store<true>(TT, PC, 1.f, tid);
+        X.qd.template store<true>(QT, PC, 1.f, tid);
+        X.kd.template store<true>(KT, PC, -1.f, tid);
         if (DECAY && tid < DK)
-            GC[tid] = reinterpret_cast<const float *>(rec + LW.off_gc)[tid];
-        // dO^T tile (rows past the sequence end are 0)
-        for (int x = tid; x < C * NV; x += NT) {
-            const int t = x / NV, j = x % NV;
-            const long row = ((long)b * T + c * C + t) * H + h;
-            DOT[j * PC + t] = t < L ? gdo[row * DV + v0 + j] : from_f32<E>(0.f);
+            GC[tid] = X.gc;
+#pragma unroll
+        for (int n = 0; n < NDO; ++n) {                // dO^T (rows past the end are 0)
+            const int x = tid + NT * n;
+            if ((C * NV) % NT == 0 || x < C * NV)
+                DOT[(x % NV) * PC + x / NV] = X.dov[n];
         }
+        if (c > 0)
+            load(X, c - 1);                            // in flight during this chunk
         __syncthreads();
         // dE = A_qk^T dO + W~ dS  -> dE^T
 #pragma unroll
@@ -306,11 +372,20 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     auto row = [&](int t) { return tok0 + (long)t * H; };
 
     // ---- chunk operands from the forward record
-    defrag<E, DK, C, NT, true>(WR, PK, rec + LW.off_wdt, 1.f, tid);    // W~   [s][i]
-    defrag<E, C, DK, NT, false>(KR, PK, rec + LW.off_kd, 1.f, tid);    // K~   [t][i]
-    defrag<E, C, C, NT, false>(TR, PC, rec + LW.off_tm, 1.f, tid);     // T    [t][s]
-    defrag<E, C, C, NT, true>(TT, PC, rec + LW.off_tm, 1.f, tid);      // T^T  [t][s]
-    defrag<E, C, C, NT, true>(AQT, PC, rec + LW.off_aqk, 1.f, tid);    // A_qk^T [s][t]
+    {
+        RecUnits<E, DK, C, NT> wt;
+        RecUnits<E, C, DK, NT> kd;
+        RecUnits<E, C, C, NT> tm, aq;
+        wt.load(rec + LW.off_wdt, tid);
+        kd.load(rec + LW.off_kd, tid);
+        tm.load(rec + LW.off_tm, tid);
+        aq.load(rec + LW.off_aqk, tid);
+        wt.template store<true>(WR, PK, 1.f, tid);     // W~     [s][i]
+        kd.template store<false>(KR, PK, 1.f, tid);    // K~     [t][i]
+        tm.template store<false>(TR, PC, 1.f, tid);    // T      [t][s]
+        tm.template store<true>(TT, PC, 1.f, tid);     // T^T    [t][s]
+        aq.template store<true>(AQT, PC, 1.f, tid);    // A_qk^T [s][t]
+    }
     if (tid < DK) {
         s_gc[tid] = DECAY ? reinterpret_cast<const float *>(rec + LW.off_gc)[tid] : 1.f;
         s_dgc[tid] = 0.f;
@@ -337,17 +412,49 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
         bj = x;
     };
 
+    // fp32 [DK][DV] state blocks are read 4 columns at a time; NS4 units per thread
+    constexpr int G4 = DVH / 4, NS4 = DK * G4 / NT;
+    static_assert(NS4 * NT == DK * G4, "state staging");
+    constexpr int NO4 = (C * G4 + NT - 1) / NT;
+    // S^T (or dS'^T) of columns [jh, jh + DVH) into SB1 as [j][i]
+    auto stage_t = [&](const float *src, int jh) {
+        float v[NS4][4];
+#pragma unroll
+        for (int n = 0; n < NS4; ++n) {
+            const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
+            gload4(src + (long)i * DV + jh + j4, v[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < NS4; ++n) {
+            const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                SB1[(j4 + e) * PK + i] = from_f32<E>(v[n][e]);
+        }
+    };
+
     for (int jh = 0; jh < DV; jh += DVH) {
         // ---- S^T of the half, dO^T and dO
-        for (int x = tid; x < DK * DVH; x += NT) {
-            const int i = x / DVH, j = x % DVH;
-            SB1[j * PK + i] = from_f32<E>(Sg[(long)i * DV + jh + j]);
-        }
-        for (int x = tid; x < C * DVH; x += NT) {
-            const int t = x / DVH, j = x % DVH;
-            const E d = t < L ? gdo[row(t) * DV + jh + j] : from_f32<E>(0.f);
-            DOT[j * PC + t] = d;
-            DOH[t * PH + j] = d;
+        stage_t(Sg, jh);
+        {
+            float d[NO4][4];
+#pragma unroll
+            for (int n = 0; n < NO4; ++n) {
+                const int x = tid + NT * n, t = x / G4, j4 = (x % G4) * 4;
+                if (((C * G4) % NT == 0 || x < C * G4) && t < L)
+                    gload4(gdo + row(t) * DV + jh + j4, d[n]);
+                else
+                    d[n][0] = d[n][1] = d[n][2] = d[n][3] = 0.f;
+            }
+#pragma unroll
+            for (int n = 0; n < NO4; ++n) {
+                const int x = tid + NT * n, t = x / G4, j4 = (x % G4) * 4;
+                if (!((C * G4) % NT == 0 || x < C * G4)) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    DOT[(j4 + e) * PC + t] = from_f32<E>(d[n][e]);
+                lds_stn<4>(DOH + t * PH + j4, d[n]);
+            }
         }
         __syncthreads();
         // ---- U = V - K~ S  -> U^T
@@ -379,10 +486,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             for (int r = 0; r < 4; ++r)
                 EH[(t0 + r) * PH + j] = from_f32<E>(acc[r]);
         }
-        for (int x = tid; x < DK * DVH; x += NT) {
-            const int i = x / DVH, j = x % DVH;
-            SB1[j * PK + i] = from_f32<E>(dSg[(long)i * DV + jh + j]);
-        }
+        stage_t(dSg, jh);
         __syncthreads();
         // ---- dE = A_qk^T dO + W~ dS'  -> dE^T
 #pragma unroll
@@ -414,13 +518,30 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                     P.dv_[row(t0 + r) * DV + jh + j] = acc[r];
             }
         }
-        for (int x = tid; x < DK * DVH; x += NT) {
-            const int i = x / DVH, j = x % DVH;
-            const float sv = Sg[(long)i * DV + jh + j], dsv = dSg[(long)i * DV + jh + j];
-            SB1[i * PH + j] = from_f32<E>(sv);
-            SB2[i * PH + j] = from_f32<E>(dsv);
-            if (DECAY)
-                atomicAdd(&s_sds[i], sv * dsv);
+        {
+            float sv[NS4][4], dsv[NS4][4];
+#pragma unroll
+            for (int n = 0; n < NS4; ++n) {
+                const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
+                gload4(Sg + (long)i * DV + jh + j4, sv[n]);
+                gload4(dSg + (long)i * DV + jh + j4, dsv[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < NS4; ++n) {
+                const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
+                lds_stn<4>(SB1 + i * PH + j4, sv[n]);
+                lds_stn<4>(SB2 + i * PH + j4, dsv[n]);
+                if (DECAY) {
+                    // sum over the G4 lanes of key channel i, then one atomic
+                    float p = sv[n][0] * dsv[n][0] + sv[n][1] * dsv[n][1] +
+                              sv[n][2] * dsv[n][2] + sv[n][3] * dsv[n][3];
+#pragma unroll
+                    for (int off = G4 / 2; off >= 1; off >>= 1)
+                        p += __shfl_xor(p, off, WAVE);
+                    if (lane % G4 == 0)
+                        atomicAdd(&s_sds[i], p);
+                }
+            }
         }
         __syncthreads();
         // ---- sums over the half's columns
@@ -452,25 +573,20 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 
     // ---- decays gamma_t per channel; W'^T = (beta k / gamma)^T, Q~^T, K~^T;
     //      the dA matrices (masked) and their transposes; sum_s W~ dW~
-    if (tid < DK) {
-        const int i = tid;
-        float g = 1.f;
-        for (int t = 0; t < C; ++t) {
-            const bool in = t < L;
-            float a = 1.f;
-            if (in && VAR == GATED_DELTANET) a = to_f32(ga[row(t)]);
-            if (in && VAR == KDA) a = to_f32(ga[row(t) * DK + i]);
-            g *= a;
-            const float kk = in ? to_f32(gk[row(t) * DK + i]) : 0.f;
-            const float qq = in ? to_f32(gq[row(t) * DK + i]) : 0.f;
-            const float bt = in ? to_f32(gb[row(t)]) : 0.f;
-            GAM[t * PF + i] = g;
-            WPT[i * PC + t] = from_f32<E>(g > 0.f ? bt * kk / g : 0.f);
-            QTT[i * PC + t] = from_f32<E>(g * qq);
-            KTT[i * PC + t] = from_f32<E>(g * kk);
+    // decays into GAM (a_t per channel; 1 past the sequence end)
+    constexpr int GK4 = DK / 4, NK4 = C * GK4 / NT;
+    static_assert(NK4 * NT == C * GK4, "chunk tile units");
+#pragma unroll
+    for (int n = 0; n < NK4; ++n) {
+        const int x = tid + NT * n, t = x / GK4, i4 = (x % GK4) * 4;
+        float a[4] = {1.f, 1.f, 1.f, 1.f};
+        if (t < L) {
+            if (VAR == KDA)
+                gload4(ga + row(t) * DK + i4, a);
+            if (VAR == GATED_DELTANET)
+                a[0] = a[1] = a[2] = a[3] = to_f32(ga[row(t)]);
         }
-        if (DECAY && !(g >= KDN_DECAY_FLOOR))
-            *s_flag = 1;
+        *reinterpret_cast<float4 *>(GAM + t * PF + i4) = make_float4(a[0], a[1], a[2], a[3]);
     }
     for (int x = tid; x < C * C; x += NT) {            // blocks above the diagonal
         const int t = x / C, s = x % C;
@@ -513,6 +629,44 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             acc += __shfl_xor(acc, 32, WAVE);
             if (lane < 16)
                 atomicAdd(&s_dgc[i], acc);
+        }
+    }
+    __syncthreads();
+    // gamma_t = prod_{r <= t} a_r per channel, in place
+    if (DECAY && tid < DK) {
+        const int i = tid;
+        float a[C];
+#pragma unroll
+        for (int t = 0; t < C; ++t)
+            a[t] = GAM[t * PF + i];
+        float g = 1.f;
+#pragma unroll
+        for (int t = 0; t < C; ++t) {
+            g *= a[t];
+            GAM[t * PF + i] = g;
+        }
+        if (!(g >= KDN_DECAY_FLOOR))
+            *s_flag = 1;
+    }
+    __syncthreads();
+    // W'^T = (beta k / gamma)^T, Q~^T = (gamma q)^T, K~^T = (gamma k)^T
+#pragma unroll
+    for (int n = 0; n < NK4; ++n) {
+        const int x = tid + NT * n, t = x / GK4, i4 = (x % GK4) * 4;
+        float kk[4] = {0.f, 0.f, 0.f, 0.f}, qq[4] = {0.f, 0.f, 0.f, 0.f};
+        float bt = 0.f;
+        if (t < L) {
+            gload4(gk + row(t) * DK + i4, kk);
+            gload4(gq + row(t) * DK + i4, qq);
+            bt = to_f32(gb[row(t)]);
+        }
+        const float4 g4 = *reinterpret_cast<const float4 *>(GAM + t * PF + i4);
+        const float g[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            WPT[(i4 + e) * PC + t] = from_f32<E>(g[e] > 0.f ? bt * kk[e] / g[e] : 0.f);
+            QTT[(i4 + e) * PC + t] = from_f32<E>(g[e] * qq[e]);
+            KTT[(i4 + e) * PC + t] = from_f32<E>(g[e] * kk[e]);
         }
     }
     __syncthreads();
@@ -625,23 +779,50 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     }
     __syncthreads();
     // ---- d log alpha: reverse sum over the chunk's tokens, plus the gamma_C terms
-    if (DECAY && tid < DK) {
+    if (VAR == KDA && tid < DK) {
         const int i = tid;
+        float dg[C];
+#pragma unroll
+        for (int t = 0; t < C; ++t)
+            dg[t] = DG[t * PF + i];
         float acc = s_dgc[i] + s_gc[i] * s_sds[i];
+#pragma unroll
         for (int t = C - 1; t >= 0; --t) {
-            acc += DG[t * PF + i];
-            if (VAR == KDA && t < L)
+            acc += dg[t];
+            if (t < L)
                 P.dla[row(t) * DK + i] = acc;
-            if (VAR == GATED_DELTANET)
-                atomicAdd(&s_dla[t], acc);
         }
     }
-    __syncthreads();
-    if (tid < L) {
-        P.dbeta[row(tid)] = s_db[tid];
-        if (VAR == GATED_DELTANET)
-            P.dla[row(tid)] = s_dla[tid];
+    if (VAR == GATED_DELTANET) {
+        // one decay per token: sum the channels first (a wave per row), then a
+        // suffix sum over the tokens across the lanes of wave 0
+        for (int t = wv; t < C; t += NW) {
+            float x = 0.f;
+            for (int i = lane; i < DK; i += WAVE)
+                x += DG[t * PF + i];
+            x = wave_sum(x);
+            if (lane == 0)
+                s_dla[t] = x;
+        }
+        __syncthreads();
+        if (wv == 0) {
+            float gcs = 0.f;
+            for (int i = lane; i < DK; i += WAVE)
+                gcs += s_dgc[i] + s_gc[i] * s_sds[i];
+            gcs = wave_sum(gcs);
+            float v = lane < C ? s_dla[lane] : 0.f;
+#pragma unroll
+            for (int off = 1; off < WAVE; off <<= 1) {
+                const float y = __shfl_down(v, off, WAVE);
+                if (lane + off < WAVE)
+                    v += y;
+            }
+            if (lane < L)
+                P.dla[row(lane)] = v + gcs;
+        }
     }
+    if (tid < L)
+        P.dbeta[row(tid)] = s_db[tid];
 }
 
 // ---------------------------------------------------------------------------
