@@ -416,9 +416,9 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     constexpr int G4 = DVH / 4, NS4 = DK * G4 / NT;
     static_assert(NS4 * NT == DK * G4, "state staging");
     constexpr int NO4 = (C * G4 + NT - 1) / NT;
-    // S^T (or dS'^T) of columns [jh, jh + DVH) into SB1 as [j][i]
-    auto stage_t = [&](const float *src, int jh) {
-        float v[NS4][4];
+    // S^T (or dS'^T) of columns [jh, jh + DVH) into SB1 as [j][i]; the values
+    // stay in v for the row-major copy later in the half
+    auto stage_t = [&](const float *src, int jh, float (&v)[NS4][4]) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
             const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
@@ -434,8 +434,9 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     };
 
     for (int jh = 0; jh < DV; jh += DVH) {
+        float sv[NS4][4], dsv[NS4][4];
         // ---- S^T of the half, dO^T and dO
-        stage_t(Sg, jh);
+        stage_t(Sg, jh, sv);
         {
             float d[NO4][4];
 #pragma unroll
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             for (int r = 0; r < 4; ++r)
                 EH[(t0 + r) * PH + j] = from_f32<E>(acc[r]);
         }
-        stage_t(dSg, jh);
+        stage_t(dSg, jh, dsv);
         __syncthreads();
         // ---- dE = A_qk^T dO + W~ dS'  -> dE^T
 #pragma unroll
@@ -519,13 +520,6 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             }
         }
         {
-            float sv[NS4][4], dsv[NS4][4];
-#pragma unroll
-            for (int n = 0; n < NS4; ++n) {
-                const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
-                gload4(Sg + (long)i * DV + jh + j4, sv[n]);
-                gload4(dSg + (long)i * DV + jh + j4, dsv[n]);
-            }
 #pragma unroll
             for (int n = 0; n < NS4; ++n) {
                 const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
