@@ -431,3 +431,115 @@ int kdn_oracle_backward(int variant, long B, long T, long H, long dk, long dv,
     }
     return fail ? -7 : 0;
 }
+
+/* --------------------------------------------------------------------------
+ * Gradients for isotropic KDN.  The write strength is derived, per token,
+ * from the head variance (forward step 2, isotropic branch):
+ *   p- = a2 p + xm,  s = r + p- kk,  beta = p- / s (0 if s = 0),
+ *   den = r + m p- kk (m = mu / dk),  p' = p- r / den (p- if den = 0),
+ * with a2 = mean(a^2), xm = mean(xi), kk = |k|^2.  Reverse mode: the memory
+ * part is the write-strength backward above with that beta, giving dbeta_t;
+ * then, with dp the gradient of p' (from the later tokens, dp_T at the end):
+ *   s != 0:   dp- += dbeta r / s^2,  dkk -= dbeta p-^2 / s^2,  dr -= dbeta p- / s^2
+ *   den != 0: dp- += dp r^2 / den^2, dkk -= dp m p-^2 r / den^2,
+ *             dr += dp m p-^2 kk / den^2;        den = 0: dp- += dp
+ *   da2 = dp- p,  dxm = dp-,  and the gradient of the previous p is dp- a2;
+ *   dalpha_i += da2 2 a_i / dk,  dxi_i = dxm / dk,  dk_i += dkk 2 k_i.
+ * dp0 is the gradient of the initial variance.
+ * ------------------------------------------------------------------------ */
+int kdn_oracle_backward_iso(long B, long T, long H, long dk, long dv, double mu,
+                            const double *q, const double *k, const double *v,
+                            const double *alpha, const double *xi, const double *r,
+                            const double *S0, const double *p0,
+                            const double *dO, const double *dS_T, const double *dp_T,
+                            double *dq, double *dk_out, double *dv_out, double *dalpha,
+                            double *dxi, double *dr, double *dS0, double *dp0,
+                            int nthreads)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return -2;
+    if (!q || !k || !v || !alpha || !xi || !r || !p0 || !dO || !dq || !dk_out ||
+        !dv_out || !dalpha || !dxi || !dr || !dS0 || !dp0)
+        return -3;
+    const long BH = B * H, SZ = dk * dv;
+    const long NTOK = B * T * H;
+    /* the derived write strengths, as a beta tensor for the memory part */
+    double *beta = (double *)malloc(sizeof(double) * (NTOK > 0 ? NTOK : 1));
+    double *dbeta = (double *)malloc(sizeof(double) * (NTOK > 0 ? NTOK : 1));
+    double *pprev = (double *)malloc(sizeof(double) * (NTOK > 0 ? NTOK : 1));
+    if (!beta || !dbeta || !pprev) {
+        free(beta); free(dbeta); free(pprev);
+        return -7;
+    }
+    const double m = mu / (double)dk;
+    for (long bh = 0; bh < BH; ++bh) {
+        const long b = bh / H, h = bh % H;
+        double p = p0[bh];
+        for (long t = 0; t < T; ++t) {
+            const long tok = (b * T + t) * H + h;
+            double a2 = 0.0, xm = 0.0, kk = 0.0;
+            for (long i = 0; i < dk; ++i) {
+                a2 += alpha[tok * dk + i] * alpha[tok * dk + i];
+                xm += xi[tok * dk + i];
+                kk += k[tok * dk + i] * k[tok * dk + i];
+            }
+            a2 /= (double)dk;
+            xm /= (double)dk;
+            pprev[tok] = p;
+            const double pm = a2 * p + xm;
+            const double s = r[tok] + pm * kk;
+            beta[tok] = (s != 0.0) ? pm / s : 0.0;
+            const double den = r[tok] + m * pm * kk;
+            p = (den != 0.0) ? pm * r[tok] / den : pm;
+        }
+    }
+    int rc = kdn_oracle_backward(ORC_KDA, B, T, H, dk, dv, q, k, v, alpha, beta, S0, dO,
+                                 dS_T, dq, dk_out, dv_out, dalpha, dbeta, dS0, nthreads);
+    if (rc == 0) {
+        for (long bh = 0; bh < BH; ++bh) {
+            const long b = bh / H, h = bh % H;
+            double dp = dp_T ? dp_T[bh] : 0.0;
+            for (long t = T - 1; t >= 0; --t) {
+                const long tok = (b * T + t) * H + h;
+                double a2 = 0.0, xm = 0.0, kk = 0.0;
+                for (long i = 0; i < dk; ++i) {
+                    a2 += alpha[tok * dk + i] * alpha[tok * dk + i];
+                    xm += xi[tok * dk + i];
+                    kk += k[tok * dk + i] * k[tok * dk + i];
+                }
+                a2 /= (double)dk;
+                xm /= (double)dk;
+                const double pp = pprev[tok], rt = r[tok];
+                const double pm = a2 * pp + xm;
+                const double s = rt + pm * kk, den = rt + m * pm * kk;
+                const double db = dbeta[tok];
+                double dpm = 0.0, dkk = 0.0, drt = 0.0;
+                if (s != 0.0) {
+                    dpm += db * rt / (s * s);
+                    dkk -= db * pm * pm / (s * s);
+                    drt -= db * pm / (s * s);
+                }
+                if (den != 0.0) {
+                    dpm += dp * rt * rt / (den * den);
+                    dkk -= dp * m * pm * pm * rt / (den * den);
+                    drt += dp * m * pm * pm * kk / (den * den);
+                } else {
+                    dpm += dp;
+                }
+                const double da2 = dpm * pp;
+                for (long i = 0; i < dk; ++i) {
+                    dalpha[tok * dk + i] += da2 * 2.0 * alpha[tok * dk + i] / (double)dk;
+                    dxi[tok * dk + i] = dpm / (double)dk;
+                    dk_out[tok * dk + i] += dkk * 2.0 * k[tok * dk + i];
+                }
+                dr[tok] = drt;
+                dp = dpm * a2;
+            }
+            dp0[bh] = dp;
+        }
+    }
+    free(beta);
+    free(dbeta);
+    free(pprev);
+    return rc;
+}

@@ -660,8 +660,8 @@ ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 # Gradients (write-strength variants).  The pages give no gradient; the
 # oracle's backward is the exact derivative of the recurrence, pinned here to
 # the (pinned) forward oracle by central differences and to closed forms.
-# Each ``bwd_pin_*`` takes (rec, bwd) with the signatures of
-# ``oracle.recurrence`` and ``oracle.backward``.
+# Each ``bwd_pin_*`` takes the oracle (the module or an ``OracleLib``) and uses
+# its ``recurrence``, ``backward`` and ``backward_iso``.
 # ---------------------------------------------------------------------------
 BWD_VARIANTS = ("deltanet", "gated_deltanet", "kda")
 GRAD_NAMES = ("q", "k", "v", "alpha", "beta", "S0")
@@ -680,7 +680,7 @@ def _grads(bwd, variant, inp, dO, dS):
     return dict(q=dq, k=dk, v=dv, alpha=da, beta=db, S0=dS0)
 
 
-def bwd_pin_finite_differences(rec, bwd):
+def bwd_pin_finite_differences(lib):
     """<grad, delta> equals the central difference of L = <o, R_o> + <S_T, R_S>
     along a random delta, for every input tensor and every variant."""
     for vi, variant in enumerate(BWD_VARIANTS):
@@ -690,10 +690,10 @@ def bwd_pin_finite_differences(rec, bwd):
         RS = g.standard_normal(inp["S0"].shape)
 
         def loss(x):
-            o, S, _ = rec(variant, **x)
+            o, S, _ = lib.recurrence(variant, **x)
             return float(np.sum(o * Ro) + np.sum(S * RS))
 
-        grads = _grads(bwd, variant, inp, Ro, RS)
+        grads = _grads(lib.backward, variant, inp, Ro, RS)
         for name in GRAD_NAMES:
             if grads[name] is None:
                 continue
@@ -706,7 +706,7 @@ def bwd_pin_finite_differences(rec, bwd):
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (variant, name, fd, an)
 
 
-def bwd_pin_deltanet_beta_zero_closed_form(rec, bwd):
+def bwd_pin_deltanet_beta_zero_closed_form(lib):
     """beta = 0: the memory stays S0, so dq_t = S0 do_t, dk = dv = 0,
     dS0 = dS_T + sum_t q_t do_t^T, and dbeta_t = k_t^T G_t (v_t - S0^T k_t)
     with G_t = dS_T + sum_{r >= t} q_r do_r^T."""
@@ -715,7 +715,7 @@ def bwd_pin_deltanet_beta_zero_closed_form(rec, bwd):
     g = _rng(91)
     dO = g.standard_normal(inp["v"].shape)
     dS = g.standard_normal(inp["S0"].shape)
-    gr = _grads(bwd, "deltanet", inp, dO, dS)
+    gr = _grads(lib.backward, "deltanet", inp, dO, dS)
     S0 = inp["S0"][0, 0]
     q, k, v, do = inp["q"][0, :, 0], inp["k"][0, :, 0], inp["v"][0, :, 0], dO[0, :, 0]
     np.testing.assert_allclose(gr["q"][0, :, 0], do @ S0.T, rtol=1e-13, atol=1e-13)
@@ -728,22 +728,54 @@ def bwd_pin_deltanet_beta_zero_closed_form(rec, bwd):
         np.testing.assert_allclose(gr["beta"][0, t, 0], ref, rtol=1e-12, atol=1e-13)
 
 
-def bwd_pin_no_tokens_and_linearity(rec, bwd):
+def bwd_pin_no_tokens_and_linearity(lib):
     """T = 0 passes dS_T through to dS0; the gradients are linear in the
     cotangents (dO, dS_T)."""
     inp = _bwd_inputs("kda", 1, 0, 2, 4, 3, seed=92)
     dS = _rng(93).standard_normal(inp["S0"].shape)
-    gr = _grads(bwd, "kda", inp, np.zeros(inp["v"].shape), dS)
+    gr = _grads(lib.backward, "kda", inp, np.zeros(inp["v"].shape), dS)
     np.testing.assert_array_equal(gr["S0"], dS)
     inp = _bwd_inputs("gated_deltanet", 1, 6, 1, 4, 3, seed=94)
     g = _rng(95)
     o1, o2 = g.standard_normal(inp["v"].shape), g.standard_normal(inp["v"].shape)
     s1, s2 = g.standard_normal(inp["S0"].shape), g.standard_normal(inp["S0"].shape)
-    a = _grads(bwd, "gated_deltanet", inp, o1, s1)
-    b = _grads(bwd, "gated_deltanet", inp, o2, s2)
-    c = _grads(bwd, "gated_deltanet", inp, o1 + 2 * o2, s1 + 2 * s2)
+    a = _grads(lib.backward, "gated_deltanet", inp, o1, s1)
+    b = _grads(lib.backward, "gated_deltanet", inp, o2, s2)
+    c = _grads(lib.backward, "gated_deltanet", inp, o1 + 2 * o2, s1 + 2 * s2)
     for n in GRAD_NAMES:
         np.testing.assert_allclose(c[n], a[n] + 2 * b[n], rtol=1e-11, atol=1e-12)
+
+
+ISO_GRAD_NAMES = ("q", "k", "v", "alpha", "xi", "r", "S0", "p0")
+
+
+def bwd_pin_iso_finite_differences(lib):
+    """Isotropic KDN: <grad, delta> equals the central difference of
+    L = <o, R_o> + <S_T, R_S> + <p_T, R_p> for every input, including xi, r
+    and p0, at mu = 1 and mu = 3, with some exact observations (r = 0)."""
+    for mu in (1.0, 3.0):
+        inp = _bwd_inputs("iso_kdn", 2, 9, 2, 4, 3, seed=96)
+        inp["r"][0, 4, 1] = 0.0
+        g = _rng(97)
+        Ro = g.standard_normal(inp["v"].shape)
+        RS = g.standard_normal(inp["S0"].shape)
+        Rp = g.standard_normal(inp["p0"].shape)
+
+        def loss(x):
+            o, S, p = lib.recurrence("iso_kdn", mu=mu, **x)
+            return float(np.sum(o * Ro) + np.sum(S * RS) + np.sum(p * Rp))
+
+        grads = dict(zip(ISO_GRAD_NAMES, lib.backward_iso(
+            inp["q"], inp["k"], inp["v"], inp["alpha"], inp["xi"], inp["r"], inp["p0"],
+            inp["S0"], Ro, RS, Rp, mu=mu)))
+        for name in ISO_GRAD_NAMES:
+            d = g.standard_normal(inp[name].shape)
+            eps = 1e-6
+            xp = dict(inp); xp[name] = inp[name] + eps * d
+            xm = dict(inp); xm[name] = inp[name] - eps * d
+            fd = (loss(xp) - loss(xm)) / (2 * eps)
+            an = float(np.sum(grads[name] * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (mu, name, fd, an)
 
 
 BWD_PINS = [v for k, v in sorted(globals().items()) if k.startswith("bwd_pin_")]

@@ -101,6 +101,19 @@ MUTANTS = {
     "bwd_memory_grad_not_decayed": _sub("dS[i * dv + j] = a[i] * dSm[i * dv + j];",
                                         "dS[i * dv + j] = dSm[i * dv + j];"),
     "bwd_dbeta_wrong_vector": _sub("db += kt[i] * dw[i];", "db += qt[i] * dw[i];"),
+    # isotropic-KDN backward (the variance chain)
+    "iso_bwd_gain_term_sign": _sub("dpm += db * rt / (s * s);", "dpm -= db * rt / (s * s);"),
+    "iso_bwd_update_not_squared": _sub("dpm += dp * rt * rt / (den * den);",
+                                       "dpm += dp * rt / den;"),
+    "iso_bwd_variance_not_decayed": _sub("dp = dpm * a2;", "dp = dpm;"),
+    "iso_bwd_noise_not_averaged": _sub("dxi[tok * dk + i] = dpm / (double)dk;",
+                                       "dxi[tok * dk + i] = dpm;"),
+    "iso_bwd_key_norm_factor": _sub("dk_out[tok * dk + i] += dkk * 2.0 * k[tok * dk + i];",
+                                    "dk_out[tok * dk + i] += dkk * k[tok * dk + i];"),
+    "iso_bwd_obs_noise_update_term": _sub("drt += dp * m * pm * pm * kk / (den * den);",
+                                          "drt += 0.0 * dp;"),
+    "iso_bwd_decay_from_new_variance": _sub("const double da2 = dpm * pp;",
+                                            "const double da2 = dpm * pm;"),
     # isotropic KDN
     "iso_alpha_not_squared": _sub("a2 += a[i] * a[i];", "a2 += a[i];"),
     "iso_drops_process_noise": _sub("xm += xi[tok * dk + i];", "xm += 0.0;"),
@@ -145,7 +158,7 @@ def test_pins_catch_mutant(name, tmpdir_mut):
     lib = oracle.OracleLib(so)
     caught = []
     pins = [(p, (lib.recurrence,)) for p in oracle_pins.ALL_PINS]
-    pins += [(p, (lib.recurrence, lib.backward)) for p in oracle_pins.BWD_PINS]
+    pins += [(p, (lib,)) for p in oracle_pins.BWD_PINS]
     for pin, args in pins:
         try:
             pin(*args)
@@ -162,4 +175,4 @@ def test_unmutated_source_passes_every_pin(tmpdir_mut):
     for pin in oracle_pins.ALL_PINS:
         pin(lib.recurrence)
     for pin in oracle_pins.BWD_PINS:
-        pin(lib.recurrence, lib.backward)
+        pin(lib)

@@ -12,4 +12,4 @@ def test_pin(pin):
 
 @pytest.mark.parametrize("pin", oracle_pins.BWD_PINS, ids=lambda f: f.__name__)
 def test_backward_pin(pin):
-    pin(oracle.recurrence, oracle.backward)
+    pin(oracle)
