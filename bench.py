@@ -195,14 +195,12 @@ def bench_backward(name, steps, warmup, torch, kdn, synth):
     g.manual_seed(synth.seed_of(name) + 7)
     d_o = torch.randn((B, T, H, dv), generator=g, device="cuda").to(inp["q"].dtype)
     f = torch.float32
-    out = (torch.empty((B, T, H, dk), dtype=f, device="cuda"),
-           torch.empty((B, T, H, dk), dtype=f, device="cuda"),
-           torch.empty((B, T, H, dv), dtype=f, device="cuda"),
-           None if variant == "deltanet" else torch.empty(
-               (B, T, H) if variant == "gated_deltanet" else (B, T, H, dk), dtype=f,
-               device="cuda"),
-           torch.empty((B, T, H), dtype=f, device="cuda"),
-           torch.empty((B, H, dk, dv), dtype=f, device="cuda"))
+    new = lambda *shape: torch.empty(shape, dtype=f, device="cuda")
+    out = dict(dq=new(B, T, H, dk), dk=new(B, T, H, dk), dv=new(B, T, H, dv),
+               dlog_alpha=None if variant == "deltanet" else (
+                   new(B, T, H) if variant == "gated_deltanet" else new(B, T, H, dk)),
+               dbeta=new(B, T, H), dS0=new(B, H, dk, dv), dproc_noise=None,
+               dobs_noise=None, dp0=None)
     dt = 1 if c["dtype"] == "bf16" else 0
     C = kdn.kdn_chunk_prefill_chunk_size(dt, dk, dv, 0)
     n = kdn.kdn_chunk_prefill_backward_workspace_size(kdn.VARIANTS[variant], dt, B, T, H,

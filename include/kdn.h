@@ -216,27 +216,35 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype,
                                       float *S_out, float *p_out, void *stream);
 
 /*
- * Gradients of kdn_chunk_prefill for the write-strength variants (DeltaNet,
- * Gated DeltaNet, KDA; the KDN variants give KDN_ERR_UNSUPPORTED).  The pages
- * give no gradient ("معماری KDA ...", section "پیاده‌سازی فنی و گذارهای DPLR",
- * names training as a use of the chunk form); what is computed is the exact
+ * Gradients of kdn_chunk_prefill for DeltaNet, Gated DeltaNet, KDA and
+ * isotropic KDN (diagonal KDN gives KDN_ERR_UNSUPPORTED).  The pages give no
+ * gradient ("معماری KDA ...", section "پیاده‌سازی فنی و گذارهای DPLR", names
+ * training as a use of the chunk form); what is computed is the exact
  * derivative of the recurrence above for a scalar loss L whose cotangents
- * are d_o = dL/do and dS_out = dL/dS_out, by the reverse of the chunk
- * algebra.  The call re-runs the forward chunk pass internally (it needs the
- * state at every chunk start), then a reverse pass over the chunks for the
- * state gradient, then the chunk-parallel local gradients.
+ * are d_o = dL/do, dS_out = dL/dS_out and (isotropic KDN) dp_out = dL/dp_out,
+ * by the reverse of the chunk algebra.  The call re-runs the forward chunk
+ * pass internally (it needs the state at every chunk start), then a reverse
+ * pass over the chunks for the state gradient, then the chunk-parallel local
+ * gradients; for isotropic KDN (whose write strength is derived from the
+ * head variance, "给记忆装一个信任度探测器 ...", section "各向同性近似：把整个头压缩成一个数")
+ * also the reverse of the variance recursion.
  *
- *   q, k, v, alpha, beta, S0, chunk   as for kdn_chunk_prefill (S0 may be NULL)
+ *   q, k, v, alpha, beta, proc_noise, obs_noise, S0, p0, mu, chunk
+ *               as for kdn_chunk_prefill (S0 may be NULL)
  *   d_o         [B, T, H, d_v] dtype, dL/do
  *   dS_out      [B, H, d_k, d_v] float32, dL/dS_out, or NULL for zero
+ *   dp_out      isotropic KDN: [B, H] float32, dL/dp_out, or NULL for zero;
+ *               else NULL
  * Outputs, all float32 whatever the dtype:
  *   dq, dk      [B, T, H, d_k]
  *   dv          [B, T, H, d_v]
  *   dlog_alpha  alpha * dL/dalpha (the gradient with respect to log alpha):
- *               [B, T, H] (Gated DeltaNet), [B, T, H, d_k] (KDA), NULL for
- *               DeltaNet
- *   dbeta       [B, T, H]
+ *               [B, T, H] (Gated DeltaNet), [B, T, H, d_k] (KDA, isotropic
+ *               KDN), NULL for DeltaNet
+ *   dbeta       [B, T, H] (DeltaNet, Gated DeltaNet, KDA; NULL for KDN)
+ *   dproc_noise [B, T, H, d_k], dobs_noise [B, T, H] (isotropic KDN; else NULL)
  *   dS0         [B, H, d_k, d_v], dL/dS0; may be NULL (not computed)
+ *   dp0         isotropic KDN: [B, H], dL/dp0, may be NULL; else NULL
  *   workspace   device memory of at least
  *               kdn_chunk_prefill_backward_workspace_size(...) bytes,
  *               256-byte aligned, overlapping no argument; required unless
@@ -248,20 +256,27 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype,
  */
 kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype,
                                       int B, int T, int H, int d_k, int d_v, int chunk,
+                                      float mu,
                                       const void *q, const void *k, const void *v,
-                                      const void *alpha, const void *beta, const float *S0,
+                                      const void *alpha, const void *beta,
+                                      const void *proc_noise, const void *obs_noise,
+                                      const float *S0, const float *p0,
                                       const void *d_o, const float *dS_out,
+                                      const float *dp_out,
                                       float *dq, float *dk, float *dv, float *dlog_alpha,
-                                      float *dbeta, float *dS0,
+                                      float *dbeta, float *dproc_noise, float *dobs_noise,
+                                      float *dS0, float *dp0,
                                       void *workspace, unsigned long long workspace_bytes,
                                       void *stream);
 
 /*
  * Bytes of workspace kdn_chunk_prefill_backward needs (0 when there are no
  * tokens), or 0 with *status set when the combination is invalid or
- * unsupported.  It is the forward record size plus two float32 states (S at
- * each chunk start, dS at each chunk end) per (sequence, head, chunk):
- * 66,048 + 131,072 bytes per (sequence, head, chunk) for bf16, d = 128, C = 64.
+ * unsupported.  It is the forward pass's workspace plus two float32 states
+ * (S at each chunk start, dS at each chunk end) per (sequence, head, chunk):
+ * 66,048 + 131,072 bytes per (sequence, head, chunk) for bf16, d = 128, C = 64,
+ * each section rounded up to 256 bytes; isotropic KDN adds 8 bytes per token
+ * and 12 per chunk.
  */
 unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant,
                                                              kdn_dtype dtype, int B, int T,

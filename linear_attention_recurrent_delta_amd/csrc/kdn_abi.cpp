@@ -218,6 +218,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
     P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr; P.ws_stat = nullptr;
     P.states = nullptr;
+    P.beta_out = nullptr;
     P.cus = device_cus();
     if (n_ws > 0) {
         P.ws = workspace;
@@ -386,14 +387,36 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype, int 
 // ---------------------------------------------------------------------------
 // Gradients of the chunkwise prefill.
 // ---------------------------------------------------------------------------
-static long long backward_workspace_bytes(int variant, int bf16, long long B, long long T,
-                                          long long H, int d_k, int d_v, int C) {
-    const long long bh = B * H, nc = kdn::num_chunks(T, C);
-    if (bh * T == 0)
-        return 0;
-    const long long rec = kdn::prefill_workspace_bytes(variant, bf16, B, T, H, d_k, C);
-    return rec + 2 * bh * nc * d_k * d_v * 4;
+namespace {
+// Workspace of the gradient call, sections 256-byte aligned: the forward's
+// two-pass workspace, S at every chunk start, dS at every chunk end, and for
+// isotropic KDN the derived write strengths, their gradients, the chain's
+// chunk maps and its gradient at every chunk end.
+struct BwdWs {
+    long long fwd, states, dstates, beta, dbeta, cmap, cdp, total;
+};
+long long up256(long long n) { return (n + 255) / 256 * 256; }
+BwdWs backward_ws(int variant, int bf16, long long B, long long T, long long H, int d_k,
+                  int d_v, int C) {
+    BwdWs w{};
+    const long long bh = B * H, nc = kdn::num_chunks(T, C), tok = bh * T;
+    if (tok == 0)
+        return w;
+    const bool iso = variant == KDN_ISO_KDN;
+    long long o = up256(kdn::prefill_workspace_bytes(variant, bf16, B, T, H, d_k, C));
+    w.fwd = 0;
+    w.states = o;  o += up256(bh * nc * d_k * d_v * 4);
+    w.dstates = o; o += up256(bh * nc * d_k * d_v * 4);
+    if (iso) {
+        w.beta = o;  o += up256(tok * 4);
+        w.dbeta = o; o += up256(tok * 4);
+        w.cmap = o;  o += up256(bh * nc * 8);
+        w.cdp = o;   o += up256(bh * nc * 4);
+    }
+    w.total = o;
+    return w;
 }
+}  // namespace
 
 unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant, kdn_dtype dtype,
                                                              int B, int T, int H, int d_k,
@@ -401,50 +424,62 @@ unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant
                                                              kdn_status *status) {
     int C = 0;
     kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C);
-    if (st == KDN_OK && is_kdn(variant))
+    if (st == KDN_OK && variant == KDN_DIAG_KDN)
         st = KDN_ERR_UNSUPPORTED;
     if (status)
         *status = st;
     if (st != KDN_OK)
         return 0;
-    return (unsigned long long)backward_workspace_bytes(variant, dtype == KDN_BF16, B, T, H,
-                                                        d_k, d_v, C);
+    return (unsigned long long)backward_ws(variant, dtype == KDN_BF16, B, T, H, d_k, d_v, C).total;
 }
 
 kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int B, int T,
-                                      int H, int d_k, int d_v, int chunk,
+                                      int H, int d_k, int d_v, int chunk, float mu,
                                       const void *q, const void *k, const void *v,
-                                      const void *alpha, const void *beta, const float *S0,
-                                      const void *d_o, const float *dS_out,
+                                      const void *alpha, const void *beta,
+                                      const void *proc_noise, const void *obs_noise,
+                                      const float *S0, const float *p0,
+                                      const void *d_o, const float *dS_out, const float *dp_out,
                                       float *dq, float *dk, float *dv, float *dlog_alpha,
-                                      float *dbeta, float *dS0, void *workspace,
+                                      float *dbeta, float *dproc_noise, float *dobs_noise,
+                                      float *dS0, float *dp0, void *workspace,
                                       unsigned long long workspace_bytes, void *stream) {
     int C = 0;
     if (kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C))
         return st;
-    if (is_kdn(variant))
+    if (variant == KDN_DIAG_KDN)
         return KDN_ERR_UNSUPPORTED;
+    const bool iso = variant == KDN_ISO_KDN;
     const long long bh = (long long)B * H;
     const long long tok = bh * T;
     const bool gdn = variant == KDN_GATED_DELTANET, dn = variant == KDN_DELTANET;
-    if (tok > 0 && (!q || !k || !v || !d_o || !dq || !dk || !dv || !dbeta))
+    if (tok > 0 && (!q || !k || !v || !d_o || !dq || !dk || !dv))
         return KDN_ERR_NULL;
-    if (kdn_status st = check_gates(variant, alpha, beta, nullptr, nullptr, tok == 0))
+    if (kdn_status st = check_gates(variant, alpha, beta, proc_noise, obs_noise, tok == 0))
         return st;
     if (dn && dlog_alpha)
         return KDN_ERR_NULL;
     if (!dn && tok > 0 && !dlog_alpha)
         return KDN_ERR_NULL;
+    if (iso) {
+        if (dbeta || (bh > 0 && !p0) || (tok > 0 && (!dproc_noise || !dobs_noise)))
+            return KDN_ERR_NULL;
+    } else {
+        if ((tok > 0 && !dbeta) || p0 || dp_out || dproc_noise || dobs_noise || dp0)
+            return KDN_ERR_NULL;
+    }
     const long long es = dtype == KDN_BF16 ? 2 : 4;
-    const void *vec[] = {q, k, v, gdn ? nullptr : alpha, S0, d_o, dS_out, dq, dk, dv,
-                         gdn ? nullptr : dlog_alpha, dS0};
+    const void *vec[] = {q, k, v, gdn ? nullptr : alpha, proc_noise, S0, d_o, dS_out, dq, dk,
+                         dv, gdn ? nullptr : dlog_alpha, dproc_noise, dS0};
     for (const void *x : vec)
         if (x && !aligned(x, 16))
             return KDN_ERR_ALIGN;
-    for (const void *x : {beta, gdn ? alpha : nullptr})
+    for (const void *x : {beta, obs_noise, gdn ? alpha : nullptr})
         if (x && !aligned(x, (uintptr_t)es))
             return KDN_ERR_ALIGN;
-    for (const void *x : {(const void *)dbeta, (const void *)(gdn ? dlog_alpha : nullptr)})
+    for (const void *x : {(const void *)dbeta, (const void *)(gdn ? dlog_alpha : nullptr),
+                          (const void *)dobs_noise, (const void *)p0, (const void *)dp_out,
+                          (const void *)dp0})
         if (x && !aligned(x, 4))
             return KDN_ERR_ALIGN;
 
@@ -452,56 +487,75 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     const long long n_a = gdn ? tok * es : (dn ? 0 : tok * d_k * es);
     const long long n_S = bh * d_k * d_v * 4;
     struct R { const void *p; long long n; };
-    const R ins[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, tok * es},
-                     {S0, n_S}, {d_o, n_v}, {dS_out, n_S}};
+    const R ins[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, iso ? 0 : tok * es},
+                     {proc_noise, iso ? n_qk : 0}, {obs_noise, iso ? tok * es : 0},
+                     {S0, n_S}, {p0, iso ? bh * 4 : 0}, {d_o, n_v}, {dS_out, n_S},
+                     {dp_out, iso ? bh * 4 : 0}};
     const R outs[] = {{dq, tok * d_k * 4}, {dk, tok * d_k * 4}, {dv, tok * d_v * 4},
                       {dlog_alpha, gdn ? tok * 4 : (dn ? 0 : tok * d_k * 4)},
-                      {dbeta, tok * 4}, {dS0, n_S}};
+                      {dbeta, iso ? 0 : tok * 4}, {dproc_noise, iso ? tok * d_k * 4 : 0},
+                      {dobs_noise, iso ? tok * 4 : 0}, {dS0, n_S}, {dp0, iso ? bh * 4 : 0}};
+    constexpr int NO = (int)(sizeof(outs) / sizeof(outs[0]));
     // outputs overlap no input and no other output
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < NO; ++i) {
         for (const R &x : ins)
             if (overlap(outs[i].p, outs[i].n, x.p, x.n)) return KDN_ERR_ALIAS;
-        for (int j = i + 1; j < 6; ++j)
+        for (int j = i + 1; j < NO; ++j)
             if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return KDN_ERR_ALIAS;
     }
-    const long long n_ws = backward_workspace_bytes(variant, dtype == KDN_BF16, B, T, H, d_k,
-                                                    d_v, C);
-    if (n_ws > 0) {
-        if (!workspace || (long long)workspace_bytes < n_ws)
+    const BwdWs W = backward_ws(variant, dtype == KDN_BF16, B, T, H, d_k, d_v, C);
+    if (W.total > 0) {
+        if (!workspace || (long long)workspace_bytes < W.total)
             return KDN_ERR_WORKSPACE;
         if (!aligned(workspace, 256))
             return KDN_ERR_ALIGN;
         for (const R &x : ins)
-            if (overlap(workspace, n_ws, x.p, x.n)) return KDN_ERR_ALIAS;
+            if (overlap(workspace, W.total, x.p, x.n)) return KDN_ERR_ALIAS;
         for (const R &x : outs)
-            if (overlap(workspace, n_ws, x.p, x.n)) return KDN_ERR_ALIAS;
+            if (overlap(workspace, W.total, x.p, x.n)) return KDN_ERR_ALIAS;
     }
     if (bh == 0)
         return KDN_OK;
 
-    // forward: records, then S at every chunk start
+    // forward: records (isotropic KDN: its variance pass first), then S at
+    // every chunk start
     const long long nc = kdn::num_chunks(T, C);
-    const long long n_rec = kdn::prefill_workspace_bytes(variant, dtype == KDN_BF16, B, T, H,
-                                                         d_k, C);
     char *base = static_cast<char *>(workspace);
     kdn::PrefillParams F;
     F.variant = variant;
     F.bf16 = dtype == KDN_BF16;
     F.B = B; F.T = T; F.H = H; F.dk = d_k; F.dv = d_v; F.chunk = C;
-    F.mu = 1.f;
-    F.q = q; F.k = k; F.v = v; F.alpha = alpha; F.beta = beta; F.xi = nullptr; F.r = nullptr;
-    F.S0 = S0; F.p0 = nullptr; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
-    F.ws = n_ws > 0 ? base : nullptr;
-    F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
-    F.states = n_ws > 0 ? reinterpret_cast<float *>(base + n_rec) : nullptr;
+    F.mu = mu;
+    F.q = q; F.k = k; F.v = v; F.alpha = alpha; F.beta = iso ? nullptr : beta;
+    F.xi = proc_noise; F.r = obs_noise;
+    F.S0 = S0; F.p0 = p0; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
+    F.ws = nullptr; F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
+    F.states = nullptr; F.beta_out = nullptr;
     F.cus = device_cus();
+    if (W.total > 0) {
+        F.ws = base;
+        F.states = reinterpret_cast<float *>(base + W.states);
+        if (iso) {
+            char *vb = base + kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
+            const long long n_mob = kdn::WsLayout::mobius_bytes(bh, nc, 1);
+            F.ws_mob = reinterpret_cast<float *>(vb);
+            F.ws_stat = reinterpret_cast<float *>(vb + n_mob);
+            F.ws_p0 = reinterpret_cast<float *>(vb + n_mob + kdn::WsLayout::stat_bytes(bh, nc, C));
+            F.beta_out = reinterpret_cast<float *>(base + W.beta);
+        }
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (tok > 0) {
-        switch (variant) {
-        case KDN_DELTANET: e = kdn::launch_prefill_prep_v0(F, st); break;
-        case KDN_GATED_DELTANET: e = kdn::launch_prefill_prep_v1(F, st); break;
-        default: e = kdn::launch_prefill_prep_v2(F, st); break;
+        if (iso)
+            e = kdn::launch_variance_scan(F, st);
+        if (e == hipSuccess) {
+            switch (variant) {
+            case KDN_DELTANET: e = kdn::launch_prefill_prep_v0(F, st); break;
+            case KDN_GATED_DELTANET: e = kdn::launch_prefill_prep_v1(F, st); break;
+            case KDN_KDA: e = kdn::launch_prefill_prep_v2(F, st); break;
+            default: e = kdn::launch_prefill_prep_v4(F, st); break;
+            }
         }
         if (e == hipSuccess)
             e = kdn::launch_prefill_state(F, st);
@@ -512,12 +566,22 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     G.variant = variant;
     G.bf16 = dtype == KDN_BF16;
     G.B = B; G.T = T; G.H = H; G.dk = d_k; G.dv = d_v; G.chunk = C;
-    G.q = q; G.k = k; G.v = v; G.alpha = alpha; G.beta = beta; G.S0 = S0;
+    G.mu = mu;
+    G.q = q; G.k = k; G.v = v; G.alpha = alpha; G.beta = iso ? nullptr : beta;
+    G.xi = proc_noise; G.r = obs_noise; G.p0 = p0;
+    G.beta_f32 = F.beta_out;
+    G.S0 = S0;
     G.dO = d_o; G.dS_out = dS_out;
-    G.dq = dq; G.dk_ = dk; G.dv_ = dv; G.dla = dlog_alpha; G.dbeta = dbeta; G.dS0 = dS0;
+    G.dq = dq; G.dk_ = dk; G.dv_ = dv; G.dla = dlog_alpha;
+    G.dbeta = iso ? (W.total > 0 ? reinterpret_cast<float *>(base + W.dbeta) : nullptr) : dbeta;
+    G.dS0 = dS0;
+    G.dp_out = dp_out; G.dxi = dproc_noise; G.dr = dobs_noise; G.dp0 = dp0;
     G.ws = F.ws;
     G.states = F.states;
-    G.dstates = n_ws > 0 ? F.states + bh * nc * d_k * d_v : nullptr;
+    G.dstates = W.total > 0 ? reinterpret_cast<float *>(base + W.dstates) : nullptr;
+    G.ws_stat = F.ws_stat; G.ws_p0 = F.ws_p0;
+    G.chain_map = iso && W.total > 0 ? reinterpret_cast<float *>(base + W.cmap) : nullptr;
+    G.chain_dp = iso && W.total > 0 ? reinterpret_cast<float *>(base + W.cdp) : nullptr;
     G.cus = F.cus;
     e = kdn::launch_backward(G, st);
     return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;

@@ -370,6 +370,10 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     const E *gb = static_cast<const E *>(P.beta);
     const E *gdo = static_cast<const E *>(P.dO);
     auto row = [&](int t) { return tok0 + (long)t * H; };
+    // write strength of token t (isotropic KDN: derived, saved by the forward)
+    auto beta_at = [&](int t) {
+        return P.beta_f32 ? P.beta_f32[row(t)] : to_f32(gb[row(t)]);
+    };
 
     // ---- chunk operands from the forward record
     {
@@ -652,7 +656,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
         if (t < L) {
             gload4(gk + row(t) * DK + i4, kk);
             gload4(gq + row(t) * DK + i4, qq);
-            bt = to_f32(gb[row(t)]);
+            bt = beta_at(t);
         }
         const float4 g4 = *reinterpret_cast<const float4 *>(GAM + t * PF + i4);
         const float g[4] = {g4.x, g4.y, g4.z, g4.w};
@@ -695,7 +699,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                  : (VAR == KDA ? to_f32(ga[row(t) * DK + i]) : 1.f);
         };
         auto wval = [&](int s, int i) {
-            return s < L ? to_f32(gb[row(s)]) * to_f32(gk[row(s) * DK + i]) : 0.f;
+            return s < L ? beta_at(s) * to_f32(gk[row(s) * DK + i]) : 0.f;
         };
 #pragma unroll
         for (int k = 0; k < NS3; ++k) {
@@ -752,7 +756,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             const float g = GAM[t * PF + i];
             const float kk = in ? to_f32(gk[row(t) * DK + i]) : 0.f;
             const float qq = in ? to_f32(gq[row(t) * DK + i]) : 0.f;
-            const float bt = in ? to_f32(gb[row(t)]) : 0.f;
+            const float bt = in ? beta_at(t) : 0.f;
             const float dq = exact ? dq3[k][r] : g * dq3[k][r];
             const float dkd = exact ? dk3[k][r] : g * dk3[k][r];
             const float dw = exact ? dw3[k][r] : (g > 0.f ? dw3[k][r] / g : 0.f);
@@ -820,6 +824,178 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// Isotropic KDN: the adjoint of the head-variance chain.  Per token, forward
+//   p- = a2 p + xm,  s = r + p- kk,  beta = p- / s,  den = r + m p- kk,
+//   p' = p- r / den   (m = mu / d_k; s = 0: beta = 0; den = 0: p' = p-),
+// the gradient of the variance before the token is affine in the gradient dp
+// of p' once dbeta is known (the memory part of the backward gives it):
+//   dp- = dbeta r / s^2 + dp c,  c = r^2 / den^2 (1 if den = 0),
+//   d(previous p) = a2 dp- = A dp + Bc,  A = a2 c,  Bc = a2 dbeta r / s^2.
+// Kernel 1 composes each chunk's token maps; kernel 2 runs the chunk maps
+// backwards from dp_out, giving dp at every chunk end and dp0; kernel 3
+// forms every token's dp and its gradients:
+//   dkk = -dbeta p-^2 / s^2 - dp m p-^2 r / den^2,
+//   dr = -dbeta p- / s^2 + dp m p-^2 kk / den^2,  da2 = dp- p,  dxm = dp-,
+// added to dk (2 dkk k), d log alpha (2 da2 a^2 / d_k) and written to dxi
+// (dxm / d_k) and dr.
+// ---------------------------------------------------------------------------
+struct ChainTok {
+    float a2, xm, kk, r, pp, pm, s, den, db, A, Bc;
+};
+
+// Lane t of a wave: token t of chunk c of head bh (identity past the end).
+// The variance before each token comes from the chunk-start variance by the
+// same scan of the token maps as the forward pass.
+__device__ __forceinline__ ChainTok chain_token(const BackwardParams &P, int bh, int c,
+                                                int NC, int C, int lane) {
+    const int T = P.T, H = P.H;
+    const int b = bh / H, h = bh % H, c0 = c * C, L = min(C, T - c0);
+    const bool in = lane < L;
+    ChainTok x;
+    const float4 st = in ? reinterpret_cast<const float4 *>(P.ws_stat)[((long)bh * NC + c) * C + lane]
+                         : make_float4(1.f, 0.f, 0.f, 1.f);
+    x.a2 = st.x; x.xm = st.y; x.kk = st.z; x.r = st.w;
+    const float mdk = P.mu * (1.f / P.dk);
+    Map2 M = variance_step_map(x.a2, x.xm, mdk * x.kk, x.r);
+    M.rescale();
+    for (int off = 1; off < C; off <<= 1) {
+        const float ya = __shfl_up(M.a, off, WAVE), yb = __shfl_up(M.b, off, WAVE);
+        const float yc = __shfl_up(M.c, off, WAVE), yd = __shfl_up(M.d, off, WAVE);
+        if (lane >= off) {
+            M.before(ya, yb, yc, yd);
+            M.rescale();
+        }
+    }
+    const float p0 = P.ws_p0[(long)bh * NC + c];
+    const float pt = M.apply(p0);
+    float pp = __shfl_up(pt, 1, WAVE);
+    if (lane == 0)
+        pp = p0;
+    x.pp = pp;
+    x.pm = fmaf(x.a2, pp, x.xm);
+    x.s = fmaf(x.pm, x.kk, x.r);
+    x.den = fmaf(mdk * x.pm, x.kk, x.r);
+    x.db = in ? P.dbeta[((long)b * T + c0 + lane) * H + h] : 0.f;
+    const float cc = x.den != 0.f ? (x.r * x.r) / (x.den * x.den) : 1.f;
+    x.A = x.a2 * cc;
+    x.Bc = x.s != 0.f ? x.a2 * x.db * x.r / (x.s * x.s) : 0.f;
+    if (!in) {
+        x.A = 1.f;
+        x.Bc = 0.f;
+    }
+    return x;
+}
+
+// Suffix composition over the lanes: lane t gets f_t o f_{t+1} o ... o f_{C-1}
+// (f applied last-token first).
+__device__ __forceinline__ void chain_suffix(float &A, float &Bc, int C, int lane) {
+    for (int off = 1; off < C; off <<= 1) {
+        const float ya = __shfl_down(A, off, WAVE), yb = __shfl_down(Bc, off, WAVE);
+        if (lane + off < C) {
+            Bc = fmaf(A, yb, Bc);
+            A *= ya;
+        }
+    }
+}
+
+// Kernel 1: one wave per (head, chunk), chunk maps to chain_map [bh][c][2].
+__global__ __launch_bounds__(256) void iso_chain_map_kernel(BackwardParams P) {
+    const int C = P.chunk, NC = (P.T + C - 1) / C;
+    const long unit = (long)blockIdx.x * 4 + threadIdx.x / WAVE;
+    if (unit >= (long)P.B * P.H * NC)
+        return;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int bh = (int)(unit / NC), c = (int)(unit % NC);
+    ChainTok x = chain_token(P, bh, c, NC, C, lane);
+    float A = x.A, Bc = x.Bc;
+    chain_suffix(A, Bc, C, lane);
+    if (lane == 0) {
+        P.chain_map[unit * 2] = A;
+        P.chain_map[unit * 2 + 1] = Bc;
+    }
+}
+
+// Kernel 2: one lane per head, the chunk maps from the last chunk to the
+// first: dp at every chunk end, and dp0.
+__global__ __launch_bounds__(64) void iso_chain_scan_kernel(BackwardParams P) {
+    const long bh = (long)blockIdx.x * 64 + threadIdx.x;
+    if (bh >= (long)P.B * P.H)
+        return;
+    const int NC = (P.T + P.chunk - 1) / P.chunk;
+    float dp = P.dp_out ? P.dp_out[bh] : 0.f;
+    for (int c = NC - 1; c >= 0; --c) {
+        P.chain_dp[bh * NC + c] = dp;
+        dp = fmaf(P.chain_map[(bh * NC + c) * 2], dp, P.chain_map[(bh * NC + c) * 2 + 1]);
+    }
+    if (P.dp0)
+        P.dp0[bh] = dp;
+}
+
+// Kernel 3: one wave per (head, chunk): every token's dp, its scalar
+// gradients, then the per-channel ones (lanes over the channels).
+template <typename E>
+__global__ __launch_bounds__(256) void iso_chain_grad_kernel(BackwardParams P) {
+    __shared__ float sg[4][3][64];                 // per wave: dkk, da2, dxm of each token
+    const int C = P.chunk, NC = (P.T + C - 1) / C;
+    const int w = threadIdx.x / WAVE;
+    const long unit = (long)blockIdx.x * 4 + w;
+    if (unit >= (long)P.B * P.H * NC)
+        return;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int bh = (int)(unit / NC), c = (int)(unit % NC);
+    const int T = P.T, H = P.H, DK = P.dk;
+    const int b = bh / H, h = bh % H, c0 = c * C, L = min(C, T - c0);
+    ChainTok x = chain_token(P, bh, c, NC, C, lane);
+    float A = x.A, Bc = x.Bc;
+    chain_suffix(A, Bc, C, lane);
+    // dp of token t = (f_{t+1} o ... o f_{C-1})(dp at the chunk end)
+    float An = __shfl_down(A, 1, WAVE), Bn = __shfl_down(Bc, 1, WAVE);
+    if (lane + 1 >= C) {
+        An = 1.f;
+        Bn = 0.f;
+    }
+    const float dpe = P.chain_dp[(long)bh * NC + c];
+    const float dp = fmaf(An, dpe, Bn);
+    const float mdk = P.mu * (1.f / DK);
+    const float s2 = x.s * x.s, d2 = x.den * x.den, pm2 = x.pm * x.pm;
+    float dpm = 0.f, dkk = 0.f, dr = 0.f;
+    if (x.s != 0.f) {
+        dpm += x.db * x.r / s2;
+        dkk -= x.db * pm2 / s2;
+        dr -= x.db * x.pm / s2;
+    }
+    if (x.den != 0.f) {
+        dpm += dp * x.r * x.r / d2;
+        dkk -= dp * mdk * pm2 * x.r / d2;
+        dr += dp * mdk * pm2 * x.kk / d2;
+    } else {
+        dpm += dp;
+    }
+    const long tok = ((long)b * T + c0 + lane) * H + h;
+    if (lane < L)
+        P.dr[tok] = dr;
+    if (lane < C) {
+        sg[w][0][lane] = dkk;
+        sg[w][1][lane] = dpm * x.pp;                 // da2
+        sg[w][2][lane] = dpm;                        // dxm
+    }
+    __builtin_amdgcn_wave_barrier();
+    const E *gk = static_cast<const E *>(P.k);
+    const E *ga = static_cast<const E *>(P.alpha);
+    const float inv = 1.f / DK;
+    for (int t = 0; t < L; ++t) {
+        const long rt = ((long)b * T + c0 + t) * H + h;
+        const float tkk = sg[w][0][t], ta2 = sg[w][1][t], txm = sg[w][2][t];
+        for (int i = lane; i < DK; i += WAVE) {
+            const float kv = to_f32(gk[rt * DK + i]), av = to_f32(ga[rt * DK + i]);
+            P.dxi[rt * DK + i] = txm * inv;
+            P.dk_[rt * DK + i] += 2.f * tkk * kv;
+            P.dla[rt * DK + i] += 2.f * ta2 * av * av * inv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 template <typename E, int VAR, int DK, int C>
@@ -864,6 +1040,28 @@ static hipError_t launch_bwd_e(const BackwardParams &P, hipStream_t st) {
     case DELTANET: return launch_bwd_v<E, DELTANET>(P, st);
     case GATED_DELTANET: return launch_bwd_v<E, GATED_DELTANET>(P, st);
     case KDA: return launch_bwd_v<E, KDA>(P, st);
+    case ISO_KDN: {
+        // the memory part as KDA with the derived write strengths, then the
+        // variance chain
+        if (hipError_t e = launch_bwd_v<E, KDA>(P, st))
+            return e;
+        const long bh = (long)P.B * P.H, nc = (P.T + P.chunk - 1) / P.chunk;
+        if (nc > 0) {
+            const dim3 g1((unsigned)((bh * nc + 3) / 4)), b1(256);
+            hipLaunchKernelGGL(iso_chain_map_kernel, g1, b1, 0, st, P);
+            if (hipError_t e = hipGetLastError())
+                return e;
+        }
+        hipLaunchKernelGGL(iso_chain_scan_kernel, dim3((unsigned)((bh + 63) / 64)), dim3(64), 0,
+                           st, P);
+        if (hipError_t e = hipGetLastError())
+            return e;
+        if (nc > 0) {
+            const dim3 g3((unsigned)((bh * nc + 3) / 4)), b3(256);
+            hipLaunchKernelGGL((iso_chain_grad_kernel<E>), g3, b3, 0, st, P);
+        }
+        return hipGetLastError();
+    }
     }
     return hipErrorInvalidValue;
 }

@@ -43,6 +43,9 @@ struct PrefillParams {
     // Gradient computation: S at every chunk start is saved here by the state
     // pass ([batch*head][chunk][dk][dv] float32; null otherwise).
     float *states;
+    // Isotropic KDN, gradient computation: the derived write strengths
+    // [B, T, H] (float32) are saved here by the prep kernel (null otherwise).
+    float *beta_out;
     int cus;           // compute units of the current device
 };
 
@@ -53,7 +56,11 @@ struct BackwardParams {
     int bf16;
     int B, T, H, dk, dv;
     int chunk;
+    float mu;
     const void *q, *k, *v, *alpha, *beta;   // [B, T, H, .] in the call's dtype
+    const void *xi, *r;                     // isotropic KDN: process / observation noise
+    const float *p0;                        // isotropic KDN: [B, H]
+    const float *beta_f32;                  // isotropic KDN: derived write strengths
     const float *S0;                        // may be null (zero)
     const void *dO;                         // [B, T, H, dv] call dtype
     const float *dS_out;                    // [B, H, dk, dv], may be null (zero)
@@ -61,9 +68,16 @@ struct BackwardParams {
     float *dla;                             // d log alpha: [B,T,H] (GDN), [B,T,H,dk] (KDA)
     float *dbeta;                           // [B, T, H]
     float *dS0;                             // [B, H, dk, dv], may be null
+    const float *dp_out;                    // isotropic KDN: dL/dp_final [B, H], may be null
+    float *dxi, *dr, *dp0;                  // isotropic KDN gradients
     void *ws;                               // forward records (kdn_workspace.h)
     float *states;                          // S at every chunk start
     float *dstates;                         // dS leaving every chunk
+    // isotropic KDN: the forward variance pass's per-token sums (mean a^2,
+    // mean xi, |k|^2, r) and chunk-start variances; the chain's chunk maps
+    // and the variance gradient at every chunk end
+    const float *ws_stat, *ws_p0;
+    float *chain_map, *chain_dp;
     int cus;
 };
 

@@ -647,8 +647,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                     pp = p_reg;
                 const float pm = fmaf(a2, pp, xm);
                 const float sv = fmaf(pm, kk, rt);
+                const float bt = (t < L && sv != 0.f) ? pm / sv : 0.f;
                 if (tc)
-                    s_beta[t] = (t < L && sv != 0.f) ? pm / sv : 0.f;
+                    s_beta[t] = bt;
+                if (PREP && P.beta_out && t < L)      // for the gradient pass
+                    P.beta_out[tok0 + (long)t * H] = bt;
                 p_reg = __shfl(pt, C - 1, WAVE);
             }
             __syncthreads();

@@ -162,7 +162,8 @@ __global__ __launch_bounds__(256) void variance_scan_kernel(PrefillParams P) {
             const float4 y = segmap[s][ch];
             p = fmaf(y.x, p, y.y) / fmaf(y.z, p, y.w);
         }
-        P.p_out[bh * DK + i] = p;
+        if (P.p_out)                                   // not kept by the gradient pass
+            P.p_out[bh * DK + i] = p;
     }
     __syncthreads();
     float p = pstart[seg][ch];
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(WAVE) void iso_variance_scan_kernel(PrefillParams P
     float p = __shfl_up(pe, 1, WAVE);
     if (lane == 0)
         p = p0;
-    if (lane == WAVE - 1)
+    if (lane == WAVE - 1 && P.p_out)                   // not kept by the gradient pass
         P.p_out[bh] = pe;
     for (int c = cb; c < ce; ++c) {
         const float4 y = mob[c];

@@ -63,7 +63,7 @@ def load(path: str = LIB_PATH):
     lib.kdn_recurrent_decode_multi.restype = i
     lib.kdn_recurrent_decode_multi.argtypes = [i, i, i, i, i, i, i, f] + [vp] * 13
     lib.kdn_chunk_prefill_backward.restype = i
-    lib.kdn_chunk_prefill_backward.argtypes = [i] * 8 + [vp] * 14 + [vp, u64, vp]
+    lib.kdn_chunk_prefill_backward.argtypes = [i] * 8 + [f] + [vp] * 21 + [vp, u64, vp]
     lib.kdn_chunk_prefill_backward_workspace_size.restype = u64
     lib.kdn_chunk_prefill_backward_workspace_size.argtypes = [i] * 8 + [ctypes.POINTER(i)]
     lib.kdn_status_string.restype = ctypes.c_char_p
@@ -149,9 +149,10 @@ def kdn_chunk_prefill_workspace_size(variant, dtype, B, T, H, d_k, d_v, chunk):
     return int(n)
 
 
-def kdn_chunk_prefill_backward(variant, dtype, B, T, H, d_k, d_v, chunk, q, k, v,
-                               alpha, beta, S0, d_o, dS_out, dq, dk, dv, dlog_alpha,
-                               dbeta, dS0, workspace=None, workspace_bytes=0,
+def kdn_chunk_prefill_backward(variant, dtype, B, T, H, d_k, d_v, chunk, mu, q, k, v,
+                               alpha, beta, proc_noise, obs_noise, S0, p0, d_o, dS_out,
+                               dp_out, dq, dk, dv, dlog_alpha, dbeta, dproc_noise,
+                               dobs_noise, dS0, dp0, workspace=None, workspace_bytes=0,
                                stream=None):
     """Raw entry point: same arguments as the C function."""
     lib = load()
@@ -159,9 +160,11 @@ def kdn_chunk_prefill_backward(variant, dtype, B, T, H, d_k, d_v, chunk, q, k, v
         workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib.kdn_chunk_prefill_backward(
         int(variant), int(dtype), int(B), int(T), int(H), int(d_k), int(d_v), int(chunk),
-        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(d_o),
-        _ptr(dS_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_alpha), _ptr(dbeta),
-        _ptr(dS0), _ptr(workspace), int(workspace_bytes), _stream(stream))
+        float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(proc_noise),
+        _ptr(obs_noise), _ptr(S0), _ptr(p0), _ptr(d_o), _ptr(dS_out), _ptr(dp_out),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_alpha), _ptr(dbeta), _ptr(dproc_noise),
+        _ptr(dobs_noise), _ptr(dS0), _ptr(dp0), _ptr(workspace), int(workspace_bytes),
+        _stream(stream))
     _check(lib, st)
 
 
@@ -281,33 +284,38 @@ def decode_multi(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
     return o, S, p
 
 
-def prefill_backward(variant, q, k, v, d_o, alpha=None, beta=None, S0=None, dS_out=None,
+def prefill_backward(variant, q, k, v, d_o, alpha=None, beta=None, proc_noise=None,
+                     obs_noise=None, S0=None, p0=None, dS_out=None, dp_out=None, mu=1.0,
                      chunk=0, out=None, workspace=None, stream=None):
-    """Gradients of :func:`prefill` (DeltaNet, Gated DeltaNet, KDA) for the
-    cotangents d_o [B,T,H,dv] and dS_out [B,H,dk,dv] (None: zero).  Returns
-    float32 (dq, dk, dv, dlog_alpha, dbeta, dS0); dlog_alpha = alpha dL/dalpha
-    ([B,T,H] for gated_deltanet, [B,T,H,dk] for kda, None for deltanet).
-    ``workspace``: a uint8 tensor of at least the queried size, or None to
-    allocate one."""
+    """Gradients of :func:`prefill` (DeltaNet, Gated DeltaNet, KDA, isotropic
+    KDN) for the cotangents d_o [B,T,H,dv], dS_out [B,H,dk,dv] and (iso_kdn)
+    dp_out [B,H] (None: zero).  Returns a dict of float32 tensors: dq, dk, dv,
+    dlog_alpha (alpha dL/dalpha: [B,T,H] for gated_deltanet, [B,T,H,dk] for
+    kda and iso_kdn, None for deltanet), dbeta (None for iso_kdn), dS0, and
+    for iso_kdn dproc_noise, dobs_noise, dp0.  ``workspace``: a uint8 tensor
+    of at least the queried size, or None to allocate one."""
     vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    iso = vid == 4
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = DTYPES[q.dtype]
     dev = q.device
     if out is None:
         f = torch.float32
-        gq = torch.empty((B, T, H, dk), dtype=f, device=dev)
-        gk = torch.empty((B, T, H, dk), dtype=f, device=dev)
-        gv = torch.empty((B, T, H, dv), dtype=f, device=dev)
-        ga = (None if vid == 0 else
-              torch.empty((B, T, H) if vid == 1 else (B, T, H, dk), dtype=f, device=dev))
-        gb = torch.empty((B, T, H), dtype=f, device=dev)
-        gS = torch.empty((B, H, dk, dv), dtype=f, device=dev)
-    else:
-        gq, gk, gv, ga, gb, gS = out
+        new = lambda *shape: torch.empty(shape, dtype=f, device=dev)
+        out = dict(dq=new(B, T, H, dk), dk=new(B, T, H, dk), dv=new(B, T, H, dv),
+                   dlog_alpha=None if vid == 0 else (new(B, T, H) if vid == 1
+                                                     else new(B, T, H, dk)),
+                   dbeta=None if iso else new(B, T, H), dS0=new(B, H, dk, dv),
+                   dproc_noise=new(B, T, H, dk) if iso else None,
+                   dobs_noise=new(B, T, H) if iso else None,
+                   dp0=new(B, H) if iso else None)
     if workspace is None:
         n = kdn_chunk_prefill_backward_workspace_size(vid, dt, B, T, H, dk, dv, chunk)
         workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
-    kdn_chunk_prefill_backward(vid, dt, B, T, H, dk, dv, chunk, q, k, v, alpha, beta, S0,
-                               d_o, dS_out, gq, gk, gv, ga, gb, gS, workspace, 0, stream)
-    return gq, gk, gv, ga, gb, gS
+    kdn_chunk_prefill_backward(vid, dt, B, T, H, dk, dv, chunk, mu, q, k, v, alpha, beta,
+                               proc_noise, obs_noise, S0, p0, d_o, dS_out, dp_out,
+                               out["dq"], out["dk"], out["dv"], out["dlog_alpha"],
+                               out["dbeta"], out["dproc_noise"], out["dobs_noise"],
+                               out["dS0"], out["dp0"], workspace, 0, stream)
+    return out

@@ -286,20 +286,34 @@ def test_decode_multi_accepts_in_place_and_empty(lib):
 
 
 def _bwd_args(variant=1, dtype=1, B=2, T=100, H=4, dk=128, dv=128, chunk=0, **over):
+    iso = variant == 4
     a = dict(q=A, k=A + MB, v=A + 2 * MB, alpha=None if variant == 0 else A + 3 * MB,
-             beta=A + 4 * MB, S0=A + 5 * MB, do=A + 6 * MB, dS=A + 7 * MB,
+             beta=None if iso else A + 4 * MB, xi=A + 14 * MB if iso else None,
+             r=A + 15 * MB if iso else None, S0=A + 5 * MB,
+             p0=A + 17 * MB if iso else None, do=A + 6 * MB, dS=A + 7 * MB,
+             dp=A + 18 * MB if iso else None,
              gq=A + 8 * MB, gk=A + 9 * MB, gv=A + 10 * MB,
-             da=None if variant == 0 else A + 11 * MB, db=A + 12 * MB, dS0=A + 13 * MB,
-             ws=A + 16 * MB, ws_bytes=1 << 40)
+             da=None if variant == 0 else A + 11 * MB, db=None if iso else A + 12 * MB,
+             dxi=A + 19 * MB if iso else None, dr=A + 20 * MB if iso else None,
+             dS0=A + 13 * MB, dp0=A + 21 * MB if iso else None,
+             ws=A + 32 * MB, ws_bytes=1 << 40)
     a.update(over)
-    return (variant, dtype, B, T, H, dk, dv, chunk, a["q"], a["k"], a["v"], a["alpha"],
-            a["beta"], a["S0"], a["do"], a["dS"], a["gq"], a["gk"], a["gv"], a["da"],
-            a["db"], a["dS0"], a["ws"], a["ws_bytes"], None)
+    return (variant, dtype, B, T, H, dk, dv, chunk, 1.0, a["q"], a["k"], a["v"], a["alpha"],
+            a["beta"], a["xi"], a["r"], a["S0"], a["p0"], a["do"], a["dS"], a["dp"],
+            a["gq"], a["gk"], a["gv"], a["da"], a["db"], a["dxi"], a["dr"], a["dS0"],
+            a["dp0"], a["ws"], a["ws_bytes"], None)
 
 
 BWD_CASES = [
-    ("diagonal KDN", dict(variant=3, beta=None), EUNSUP),
-    ("isotropic KDN", dict(variant=4, beta=None), EUNSUP),
+    ("diagonal KDN", dict(variant=3, beta=None, xi=A + 14 * MB, r=A + 15 * MB), EUNSUP),
+    ("iso KDN with beta", dict(variant=4, beta=A + 4 * MB), ENULL),
+    ("iso KDN with dbeta", dict(variant=4, db=A + 12 * MB), ENULL),
+    ("iso KDN without p0", dict(variant=4, p0=None), ENULL),
+    ("iso KDN without dproc_noise", dict(variant=4, dxi=None), ENULL),
+    ("iso KDN odd dp0", dict(variant=4, dp0=A + 21 * MB + 2), EALIGN),
+    ("iso KDN dobs_noise overlaps dbeta area", dict(variant=4, dr=A + 8 * MB), EALIAS),
+    ("GDN with p0", dict(p0=A + 17 * MB), ENULL),
+    ("GDN with dp0", dict(dp0=A + 21 * MB), ENULL),
     ("bad dtype", dict(dtype=2), EUNSUP),
     ("negative T", dict(T=-1), ESHAPE),
     ("d_k 32", dict(dk=32), EUNSUP),
@@ -335,6 +349,8 @@ def test_backward_workspace_size(lib):
     n = f(1, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
     assert st.value == OK and n == 2 * 4 * 2 * (rec + 2 * 128 * 128 * 4)
     assert f(3, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st)) == 0 and st.value == EUNSUP
+    n_iso = f(4, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
+    assert st.value == OK and n_iso > n
     assert f(1, 1, 2, 0, 4, 128, 128, 0, ctypes.byref(st)) == 0 and st.value == OK
     # no tokens: nothing to launch for B*H = 0, and no workspace is needed
     assert lib.kdn_chunk_prefill_backward(*_bwd_args(B=0, ws=None, ws_bytes=0)) == OK
