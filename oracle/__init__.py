@@ -56,6 +56,9 @@ class OracleLib:
         lib.kdn_oracle_backward_iso.restype = ctypes.c_int
         lib.kdn_oracle_backward_iso.argtypes = (
             [ctypes.c_long] * 5 + [ctypes.c_double] + [dp] * 19 + [ctypes.c_int])
+        lib.kdn_oracle_backward_diag.restype = ctypes.c_int
+        lib.kdn_oracle_backward_diag.argtypes = (
+            [ctypes.c_long] * 5 + [ctypes.c_double] + [dp] * 19)
         lib.kdn_oracle_max_threads.restype = ctypes.c_int
         lib.kdn_oracle_max_threads.argtypes = []
         self.lib = lib
@@ -75,9 +78,14 @@ class OracleLib:
         return _run_backward(self.lib, variant, q, k, v, alpha, beta, S0, dO, dS_T,
                              nthreads)
 
+    def backward_diag(self, q, k, v, alpha, xi, r, p0, S0=None, dO=None, dS_T=None,
+                      dp_T=None, mu=1.0):
+        return _run_backward_kdn(self.lib, 3, q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T,
+                                 mu, 0)
+
     def backward_iso(self, q, k, v, alpha, xi, r, p0, S0=None, dO=None, dS_T=None,
                      dp_T=None, mu=1.0, nthreads=0):
-        return _run_backward_iso(self.lib, q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T,
+        return _run_backward_kdn(self.lib, 4, q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T,
                                  mu, nthreads)
 
 
@@ -209,7 +217,15 @@ def backward_iso(q, k, v, alpha, xi, r, p0, S0=None, dO=None, dS_T=None, dp_T=No
     return load().backward_iso(q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T, mu, nthreads)
 
 
-def _run_backward_iso(lib, q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T, mu, nthreads):
+def backward_diag(q, k, v, alpha, xi, r, p0, S0=None, dO=None, dS_T=None, dp_T=None,
+                  mu=1.0):
+    """Gradients through diagonal KDN, given dO [B,T,H,dv], dS_T [B,H,dk,dv]
+    and dp_T [B,H,dk] (None: zero).  Returns ``(dq, dk, dv, dalpha, dxi, dr,
+    dS0, dp0)`` with dalpha = dL/dalpha [B,T,H,dk] and dp0 [B,H,dk]."""
+    return load().backward_diag(q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T, mu)
+
+
+def _run_backward_kdn(lib, vid, q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T, mu, nthreads):
     q = np.asarray(q)
     B, T, H, dk = q.shape
     dv = np.asarray(v).shape[-1]
@@ -219,21 +235,25 @@ def _run_backward_iso(lib, q, k, v, alpha, xi, r, p0, S0, dO, dS_T, dp_T, mu, nt
     alpha = _f64(alpha, (B, T, H, dk), "alpha")
     xi = _f64(xi, (B, T, H, dk), "xi")
     r = _f64(r, (B, T, H), "r")
-    p0 = _f64(p0, (B, H), "p0")
+    pshape = (B, H) if vid == 4 else (B, H, dk)
+    p0 = _f64(p0, pshape, "p0")
     S0 = _f64(S0, (B, H, dk, dv), "S0") if S0 is not None else None
     dO = _f64(dO, (B, T, H, dv), "dO")
     dS_T = _f64(dS_T, (B, H, dk, dv), "dS_T") if dS_T is not None else None
-    dp_T = _f64(dp_T, (B, H), "dp_T") if dp_T is not None else None
+    dp_T = _f64(dp_T, pshape, "dp_T") if dp_T is not None else None
     out = dict(dq=np.zeros((B, T, H, dk)), dk=np.zeros((B, T, H, dk)),
                dv=np.zeros((B, T, H, dv)), da=np.zeros((B, T, H, dk)),
                dxi=np.zeros((B, T, H, dk)), dr=np.zeros((B, T, H)),
-               dS0=np.zeros((B, H, dk, dv)), dp0=np.zeros((B, H)))
-    rc = lib.kdn_oracle_backward_iso(
-        B, T, H, dk, dv, float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(xi),
-        _ptr(r), _ptr(S0), _ptr(p0), _ptr(dO), _ptr(dS_T), _ptr(dp_T), _ptr(out["dq"]),
-        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["da"]), _ptr(out["dxi"]), _ptr(out["dr"]),
-        _ptr(out["dS0"]), _ptr(out["dp0"]), int(nthreads))
+               dS0=np.zeros((B, H, dk, dv)), dp0=np.zeros(pshape))
+    args = (B, T, H, dk, dv, float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(xi),
+            _ptr(r), _ptr(S0), _ptr(p0), _ptr(dO), _ptr(dS_T), _ptr(dp_T), _ptr(out["dq"]),
+            _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["da"]), _ptr(out["dxi"]),
+            _ptr(out["dr"]), _ptr(out["dS0"]), _ptr(out["dp0"]))
+    if vid == 4:
+        rc = lib.kdn_oracle_backward_iso(*args, int(nthreads))
+    else:
+        rc = lib.kdn_oracle_backward_diag(*args)
     if rc != 0:
-        raise RuntimeError(f"kdn_oracle_backward_iso failed with code {rc}")
+        raise RuntimeError(f"kdn_oracle backward (variant {vid}) failed with code {rc}")
     return (out["dq"], out["dk"], out["dv"], out["da"], out["dxi"], out["dr"], out["dS0"],
             out["dp0"])

@@ -543,3 +543,218 @@ int kdn_oracle_backward_iso(long B, long T, long H, long dk, long dv, double mu,
     free(pprev);
     return rc;
 }
+
+/* --------------------------------------------------------------------------
+ * Gradients for diagonal KDN.  Per token the write vector is the gain
+ *   p-_i = a_i^2 p_i + xi_i,  s = r + sum_i p-_i k_i^2,  w_i = p-_i k_i / s,
+ * and the variance update is p'_i = p-_i r / den_i, den_i = r + mu p-_i k_i^2
+ * (s = 0: w = 0; den_i = 0: p'_i = p-_i).  Reverse mode: first the memory with
+ * the write vector as given (as in the write-strength backward, without the
+ * beta factor), which yields dw_t; then, per token in reverse, with dp_i the
+ * gradient of p'_i from the later tokens (dp_T at the end):
+ *   u_i = p-_i k_i:  du_i = dw_i / s,  ds = -sum_i dw_i u_i / s^2   (s != 0)
+ *   dp-_i = du_i k_i + ds k_i^2 + dp_i r^2 / den_i^2    (dp_i if den_i = 0)
+ *   dk_i += du_i p-_i + 2 ds p-_i k_i - 2 dp_i mu p-_i^2 r k_i / den_i^2
+ *   dr = ds + sum_i dp_i mu p-_i^2 k_i^2 / den_i^2
+ *   dalpha_i += 2 a_i p_i dp-_i,  dxi_i = dp-_i,  previous dp_i = a_i^2 dp-_i.
+ * dp0 is the gradient of the initial variances.
+ * ------------------------------------------------------------------------ */
+
+/* Memory part for a given write vector W [B,T,H,dk] and per-channel decay:
+ * the write-strength backward's steps 6, 5, 4 and 3 with w = W_t; returns dW
+ * in place of dbeta and only the read term in dk. */
+static int backward_memory_w(long B, long T, long H, long dk, long dv,
+                             const double *q, const double *k, const double *v,
+                             const double *alpha, const double *W, const double *S0,
+                             const double *dO, const double *dS_T, double *dq,
+                             double *dk_out, double *dv_out, double *dalpha, double *dW,
+                             double *dS0)
+{
+    const long BH = B * H, SZ = dk * dv;
+    for (long bh = 0; bh < BH; ++bh) {
+        const long b = bh / H, h = bh % H;
+        double *Sall = (double *)malloc(sizeof(double) * (T + 1) * SZ);
+        double *buf = (double *)malloc(sizeof(double) * (3 * SZ + 2 * dv));
+        if (!Sall || !buf) {
+            free(Sall);
+            free(buf);
+            return -7;
+        }
+        double *Sm = buf, *dS = buf + SZ, *dSm = buf + 2 * SZ, *e = buf + 3 * SZ, *de = e + dv;
+        if (S0)
+            memcpy(Sall, S0 + bh * SZ, sizeof(double) * SZ);
+        else
+            memset(Sall, 0, sizeof(double) * SZ);
+        /* forward: S_t = diag(a) S_{t-1} + w (v - (diag(a) S_{t-1})^T k)^T */
+        for (long t = 0; t < T; ++t) {
+            const long tok = (b * T + t) * H + h;
+            const double *Sp = Sall + t * SZ;
+            double *Sn = Sall + (t + 1) * SZ;
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    Sm[i * dv + j] = alpha[tok * dk + i] * Sp[i * dv + j];
+            for (long j = 0; j < dv; ++j) {
+                double rr = 0.0;
+                for (long i = 0; i < dk; ++i)
+                    rr += Sm[i * dv + j] * k[tok * dk + i];
+                e[j] = v[tok * dv + j] - rr;
+            }
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    Sn[i * dv + j] = Sm[i * dv + j] + W[tok * dk + i] * e[j];
+        }
+        if (dS_T)
+            memcpy(dS, dS_T + bh * SZ, sizeof(double) * SZ);
+        else
+            memset(dS, 0, sizeof(double) * SZ);
+        for (long t = T - 1; t >= 0; --t) {
+            const long tok = (b * T + t) * H + h;
+            const double *qt = q + tok * dk, *kt = k + tok * dk, *wt = W + tok * dk;
+            const double *dot = dO + tok * dv;
+            const double *St = Sall + (t + 1) * SZ, *Sp = Sall + t * SZ;
+            for (long i = 0; i < dk; ++i) {
+                double rr = 0.0;
+                for (long j = 0; j < dv; ++j) {
+                    dS[i * dv + j] += qt[i] * dot[j];
+                    rr += St[i * dv + j] * dot[j];
+                }
+                dq[tok * dk + i] = rr;
+            }
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    Sm[i * dv + j] = alpha[tok * dk + i] * Sp[i * dv + j];
+            for (long j = 0; j < dv; ++j) {
+                double rr = 0.0, rd = 0.0;
+                for (long i = 0; i < dk; ++i) {
+                    rr += Sm[i * dv + j] * kt[i];
+                    rd += dS[i * dv + j] * wt[i];
+                }
+                e[j] = v[tok * dv + j] - rr;
+                de[j] = rd;
+                dv_out[tok * dv + j] = rd;
+            }
+            for (long i = 0; i < dk; ++i) {
+                double rw = 0.0, rk = 0.0;
+                for (long j = 0; j < dv; ++j) {
+                    rw += dS[i * dv + j] * e[j];
+                    dSm[i * dv + j] = dS[i * dv + j] - kt[i] * de[j];
+                    rk += Sm[i * dv + j] * de[j];
+                }
+                dW[tok * dk + i] = rw;
+                dk_out[tok * dk + i] = -rk;
+            }
+            for (long i = 0; i < dk; ++i) {
+                double ra = 0.0;
+                for (long j = 0; j < dv; ++j) {
+                    ra += dSm[i * dv + j] * Sp[i * dv + j];
+                    dS[i * dv + j] = alpha[tok * dk + i] * dSm[i * dv + j];
+                }
+                dalpha[tok * dk + i] = ra;
+            }
+        }
+        memcpy(dS0 + bh * SZ, dS, sizeof(double) * SZ);
+        free(Sall);
+        free(buf);
+    }
+    return 0;
+}
+
+int kdn_oracle_backward_diag(long B, long T, long H, long dk, long dv, double mu,
+                             const double *q, const double *k, const double *v,
+                             const double *alpha, const double *xi, const double *r,
+                             const double *S0, const double *p0,
+                             const double *dO, const double *dS_T, const double *dp_T,
+                             double *dq, double *dk_out, double *dv_out, double *dalpha,
+                             double *dxi, double *dr, double *dS0, double *dp0)
+{
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return -2;
+    if (!q || !k || !v || !alpha || !xi || !r || !p0 || !dO || !dq || !dk_out ||
+        !dv_out || !dalpha || !dxi || !dr || !dS0 || !dp0)
+        return -3;
+    const long BH = B * H, NTOK = B * T * H;
+    const long NV = (NTOK > 0 ? NTOK : 1) * dk;
+    double *W = (double *)malloc(sizeof(double) * NV);
+    double *dW = (double *)malloc(sizeof(double) * NV);
+    double *pprev = (double *)malloc(sizeof(double) * NV);
+    double *dp = (double *)malloc(sizeof(double) * dk);
+    if (!W || !dW || !pprev || !dp) {
+        free(W); free(dW); free(pprev); free(dp);
+        return -7;
+    }
+    /* forward: the gains and the variances before every token */
+    for (long bh = 0; bh < BH; ++bh) {
+        const long b = bh / H, h = bh % H;
+        for (long i = 0; i < dk; ++i)
+            dp[i] = p0[bh * dk + i];                       /* running p */
+        for (long t = 0; t < T; ++t) {
+            const long tok = (b * T + t) * H + h;
+            const double *a = alpha + tok * dk, *kt = k + tok * dk, *x = xi + tok * dk;
+            double s = r[tok];
+            for (long i = 0; i < dk; ++i) {
+                pprev[tok * dk + i] = dp[i];
+                const double pm = a[i] * a[i] * dp[i] + x[i];
+                s += pm * kt[i] * kt[i];
+            }
+            for (long i = 0; i < dk; ++i) {
+                const double pm = a[i] * a[i] * dp[i] + x[i];
+                W[tok * dk + i] = (s != 0.0) ? pm * kt[i] / s : 0.0;
+                const double den = r[tok] + mu * pm * kt[i] * kt[i];
+                dp[i] = (den != 0.0) ? pm * r[tok] / den : pm;
+            }
+        }
+    }
+    int rc = backward_memory_w(B, T, H, dk, dv, q, k, v, alpha, W, S0, dO, dS_T, dq, dk_out,
+                               dv_out, dalpha, dW, dS0);
+    if (rc == 0) {
+        for (long bh = 0; bh < BH; ++bh) {
+            const long b = bh / H, h = bh % H;
+            for (long i = 0; i < dk; ++i)
+                dp[i] = dp_T ? dp_T[bh * dk + i] : 0.0;
+            for (long t = T - 1; t >= 0; --t) {
+                const long tok = (b * T + t) * H + h;
+                const double *a = alpha + tok * dk, *kt = k + tok * dk, *x = xi + tok * dk;
+                const double *pp = pprev + tok * dk, *dwt = dW + tok * dk;
+                const double rt = r[tok];
+                double s = rt;
+                for (long i = 0; i < dk; ++i) {
+                    const double pm = a[i] * a[i] * pp[i] + x[i];
+                    s += pm * kt[i] * kt[i];
+                }
+                double ds = 0.0;
+                if (s != 0.0)
+                    for (long i = 0; i < dk; ++i) {
+                        const double pm = a[i] * a[i] * pp[i] + x[i];
+                        ds -= dwt[i] * pm * kt[i] / (s * s);
+                    }
+                double drt = ds;
+                for (long i = 0; i < dk; ++i) {
+                    const double pm = a[i] * a[i] * pp[i] + x[i];
+                    const double du = (s != 0.0) ? dwt[i] / s : 0.0;
+                    const double den = rt + mu * pm * kt[i] * kt[i];
+                    double dpm = du * kt[i] + ds * kt[i] * kt[i];
+                    double dki = du * pm + 2.0 * ds * pm * kt[i];
+                    if (den != 0.0) {
+                        dpm += dp[i] * rt * rt / (den * den);
+                        dki -= 2.0 * dp[i] * mu * pm * pm * rt * kt[i] / (den * den);
+                        drt += dp[i] * mu * pm * pm * kt[i] * kt[i] / (den * den);
+                    } else {
+                        dpm += dp[i];
+                    }
+                    dk_out[tok * dk + i] += dki;
+                    dalpha[tok * dk + i] += 2.0 * a[i] * pp[i] * dpm;
+                    dxi[tok * dk + i] = dpm;
+                    dp[i] = a[i] * a[i] * dpm;
+                }
+                dr[tok] = drt;
+            }
+            for (long i = 0; i < dk; ++i)
+                dp0[bh * dk + i] = dp[i];
+        }
+    }
+    free(W);
+    free(dW);
+    free(pprev);
+    free(dp);
+    return rc;
+}

@@ -778,4 +778,35 @@ def bwd_pin_iso_finite_differences(lib):
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (mu, name, fd, an)
 
 
+def bwd_pin_diag_finite_differences(lib):
+    """Diagonal KDN: <grad, delta> equals the central difference of
+    L = <o, R_o> + <S_T, R_S> + <p_T, R_p> for every input (p0 and the
+    cotangent R_p per channel), at mu = 1 and mu = 3, with an exact
+    observation (r = 0) and a key with zero channels in the sequence."""
+    for mu in (1.0, 3.0):
+        inp = _bwd_inputs("diag_kdn", 2, 9, 2, 4, 3, seed=98)
+        inp["r"][1, 3, 0] = 0.0
+        inp["k"][0, 5, 1, :2] = 0.0
+        g = _rng(99)
+        Ro = g.standard_normal(inp["v"].shape)
+        RS = g.standard_normal(inp["S0"].shape)
+        Rp = g.standard_normal(inp["p0"].shape)
+
+        def loss(x):
+            o, S, p = lib.recurrence("diag_kdn", mu=mu, **x)
+            return float(np.sum(o * Ro) + np.sum(S * RS) + np.sum(p * Rp))
+
+        grads = dict(zip(ISO_GRAD_NAMES, lib.backward_diag(
+            inp["q"], inp["k"], inp["v"], inp["alpha"], inp["xi"], inp["r"], inp["p0"],
+            inp["S0"], Ro, RS, Rp, mu=mu)))
+        for name in ISO_GRAD_NAMES:
+            d = g.standard_normal(inp[name].shape)
+            eps = 1e-6
+            xp = dict(inp); xp[name] = inp[name] + eps * d
+            xm = dict(inp); xm[name] = inp[name] - eps * d
+            fd = (loss(xp) - loss(xm)) / (2 * eps)
+            an = float(np.sum(grads[name] * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (mu, name, fd, an)
+
+
 BWD_PINS = [v for k, v in sorted(globals().items()) if k.startswith("bwd_pin_")]

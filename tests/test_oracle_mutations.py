@@ -114,6 +114,20 @@ MUTANTS = {
                                           "drt += 0.0 * dp;"),
     "iso_bwd_decay_from_new_variance": _sub("const double da2 = dpm * pp;",
                                             "const double da2 = dpm * pm;"),
+    # diagonal-KDN backward
+    "diag_bwd_error_grad_uses_key": _sub("rd += dS[i * dv + j] * wt[i];",
+                                         "rd += dS[i * dv + j] * kt[i];"),
+    "diag_bwd_innovation_sign": _sub("ds -= dwt[i] * pm * kt[i] / (s * s);",
+                                     "ds += dwt[i] * pm * kt[i] / (s * s);"),
+    "diag_bwd_gain_key_term_dropped": _sub("double dki = du * pm + 2.0 * ds * pm * kt[i];",
+                                           "double dki = du * pm;"),
+    "diag_bwd_update_term_not_squared": _sub("dpm += dp[i] * rt * rt / (den * den);",
+                                             "dpm += dp[i] * rt / den;"),
+    "diag_bwd_obs_noise_gain_term": _sub("double drt = ds;", "double drt = 0.0;"),
+    "diag_bwd_variance_not_decayed": _sub("dp[i] = a[i] * a[i] * dpm;", "dp[i] = dpm;"),
+    "diag_bwd_decay_grad_missing_factor": _sub(
+        "dalpha[tok * dk + i] += 2.0 * a[i] * pp[i] * dpm;",
+        "dalpha[tok * dk + i] += a[i] * pp[i] * dpm;"),
     # isotropic KDN
     "iso_alpha_not_squared": _sub("a2 += a[i] * a[i];", "a2 += a[i];"),
     "iso_drops_process_noise": _sub("xm += xi[tok * dk + i];", "xm += 0.0;"),
