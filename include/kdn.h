@@ -216,35 +216,35 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype,
                                       float *S_out, float *p_out, void *stream);
 
 /*
- * Gradients of kdn_chunk_prefill for DeltaNet, Gated DeltaNet, KDA and
- * isotropic KDN (diagonal KDN gives KDN_ERR_UNSUPPORTED).  The pages give no
+ * Gradients of kdn_chunk_prefill for every variant.  The pages give no
  * gradient ("معماری KDA ...", section "پیاده‌سازی فنی و گذارهای DPLR", names
  * training as a use of the chunk form); what is computed is the exact
  * derivative of the recurrence above for a scalar loss L whose cotangents
- * are d_o = dL/do, dS_out = dL/dS_out and (isotropic KDN) dp_out = dL/dp_out,
+ * are d_o = dL/do, dS_out = dL/dS_out and (KDN) dp_out = dL/dp_out,
  * by the reverse of the chunk algebra.  The call re-runs the forward chunk
  * pass internally (it needs the state at every chunk start), then a reverse
  * pass over the chunks for the state gradient, then the chunk-parallel local
- * gradients; for isotropic KDN (whose write strength is derived from the
- * head variance, "给记忆装一个信任度探测器 ...", section "各向同性近似：把整个头压缩成一个数")
- * also the reverse of the variance recursion.
+ * gradients; for KDN (whose write vector is derived from the variance,
+ * "给记忆装一个信任度探测器 ...", sections "对角近似：把矩阵压扁成一个向量" and
+ * "各向同性近似：把整个头压缩成一个数") also the reverse of the variance
+ * recursion.
  *
  *   q, k, v, alpha, beta, proc_noise, obs_noise, S0, p0, mu, chunk
  *               as for kdn_chunk_prefill (S0 may be NULL)
  *   d_o         [B, T, H, d_v] dtype, dL/do
  *   dS_out      [B, H, d_k, d_v] float32, dL/dS_out, or NULL for zero
- *   dp_out      isotropic KDN: [B, H] float32, dL/dp_out, or NULL for zero;
+ *   dp_out      KDN: shaped as p0, float32, dL/dp_out, or NULL for zero;
  *               else NULL
  * Outputs, all float32 whatever the dtype:
  *   dq, dk      [B, T, H, d_k]
  *   dv          [B, T, H, d_v]
  *   dlog_alpha  alpha * dL/dalpha (the gradient with respect to log alpha):
- *               [B, T, H] (Gated DeltaNet), [B, T, H, d_k] (KDA, isotropic
- *               KDN), NULL for DeltaNet
+ *               [B, T, H] (Gated DeltaNet), [B, T, H, d_k] (KDA, KDN), NULL
+ *               for DeltaNet
  *   dbeta       [B, T, H] (DeltaNet, Gated DeltaNet, KDA; NULL for KDN)
- *   dproc_noise [B, T, H, d_k], dobs_noise [B, T, H] (isotropic KDN; else NULL)
+ *   dproc_noise [B, T, H, d_k], dobs_noise [B, T, H] (KDN; else NULL)
  *   dS0         [B, H, d_k, d_v], dL/dS0; may be NULL (not computed)
- *   dp0         isotropic KDN: [B, H], dL/dp0, may be NULL; else NULL
+ *   dp0         KDN: shaped as p0, dL/dp0, may be NULL; else NULL
  *   workspace   device memory of at least
  *               kdn_chunk_prefill_backward_workspace_size(...) bytes,
  *               256-byte aligned, overlapping no argument; required unless
@@ -276,7 +276,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype,
  * (S at each chunk start, dS at each chunk end) per (sequence, head, chunk):
  * 66,048 + 131,072 bytes per (sequence, head, chunk) for bf16, d = 128, C = 64,
  * each section rounded up to 256 bytes; isotropic KDN adds 8 bytes per token
- * and 12 per chunk.
+ * and 12 per chunk, diagonal KDN 8 d_k bytes per token and 12 d_k per chunk.
  */
 unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant,
                                                              kdn_dtype dtype, int B, int T,

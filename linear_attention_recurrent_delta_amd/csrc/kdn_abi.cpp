@@ -219,6 +219,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr; P.ws_stat = nullptr;
     P.states = nullptr;
     P.beta_out = nullptr;
+    P.w_out = nullptr;
     P.cus = device_cus();
     if (n_ws > 0) {
         P.ws = workspace;
@@ -389,11 +390,12 @@ kdn_status kdn_recurrent_decode_multi(kdn_variant variant, kdn_dtype dtype, int 
 // ---------------------------------------------------------------------------
 namespace {
 // Workspace of the gradient call, sections 256-byte aligned: the forward's
-// two-pass workspace, S at every chunk start, dS at every chunk end, and for
-// isotropic KDN the derived write strengths, their gradients, the chain's
+// two-pass workspace, S at every chunk start, dS at every chunk end; for
+// isotropic KDN the derived write strengths and their gradients, for
+// diagonal KDN the gains and their gradients; for both the variance chain's
 // chunk maps and its gradient at every chunk end.
 struct BwdWs {
-    long long fwd, states, dstates, beta, dbeta, cmap, cdp, total;
+    long long fwd, states, dstates, beta, dbeta, w, dw, cmap, cdp, total;
 };
 long long up256(long long n) { return (n + 255) / 256 * 256; }
 BwdWs backward_ws(int variant, int bf16, long long B, long long T, long long H, int d_k,
@@ -402,7 +404,7 @@ BwdWs backward_ws(int variant, int bf16, long long B, long long T, long long H, 
     const long long bh = B * H, nc = kdn::num_chunks(T, C), tok = bh * T;
     if (tok == 0)
         return w;
-    const bool iso = variant == KDN_ISO_KDN;
+    const bool iso = variant == KDN_ISO_KDN, diag = variant == KDN_DIAG_KDN;
     long long o = up256(kdn::prefill_workspace_bytes(variant, bf16, B, T, H, d_k, C));
     w.fwd = 0;
     w.states = o;  o += up256(bh * nc * d_k * d_v * 4);
@@ -412,6 +414,12 @@ BwdWs backward_ws(int variant, int bf16, long long B, long long T, long long H, 
         w.dbeta = o; o += up256(tok * 4);
         w.cmap = o;  o += up256(bh * nc * 8);
         w.cdp = o;   o += up256(bh * nc * 4);
+    }
+    if (diag) {
+        w.w = o;     o += up256(tok * d_k * 4);
+        w.dw = o;    o += up256(tok * d_k * 4);
+        w.cmap = o;  o += up256(bh * nc * d_k * 8);
+        w.cdp = o;   o += up256(bh * nc * d_k * 4);
     }
     w.total = o;
     return w;
@@ -424,8 +432,6 @@ unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant
                                                              kdn_status *status) {
     int C = 0;
     kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C);
-    if (st == KDN_OK && variant == KDN_DIAG_KDN)
-        st = KDN_ERR_UNSUPPORTED;
     if (status)
         *status = st;
     if (st != KDN_OK)
@@ -447,9 +453,8 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     int C = 0;
     if (kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C))
         return st;
-    if (variant == KDN_DIAG_KDN)
-        return KDN_ERR_UNSUPPORTED;
-    const bool iso = variant == KDN_ISO_KDN;
+    const bool iso = variant == KDN_ISO_KDN, diag = variant == KDN_DIAG_KDN;
+    const bool kdn = iso || diag;
     const long long bh = (long long)B * H;
     const long long tok = bh * T;
     const bool gdn = variant == KDN_GATED_DELTANET, dn = variant == KDN_DELTANET;
@@ -461,7 +466,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
         return KDN_ERR_NULL;
     if (!dn && tok > 0 && !dlog_alpha)
         return KDN_ERR_NULL;
-    if (iso) {
+    if (kdn) {
         if (dbeta || (bh > 0 && !p0) || (tok > 0 && (!dproc_noise || !dobs_noise)))
             return KDN_ERR_NULL;
     } else {
@@ -470,7 +475,9 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     }
     const long long es = dtype == KDN_BF16 ? 2 : 4;
     const void *vec[] = {q, k, v, gdn ? nullptr : alpha, proc_noise, S0, d_o, dS_out, dq, dk,
-                         dv, gdn ? nullptr : dlog_alpha, dproc_noise, dS0};
+                         dv, gdn ? nullptr : dlog_alpha, dproc_noise, dS0,
+                         diag ? (const void *)p0 : nullptr, diag ? (const void *)dp_out : nullptr,
+                         diag ? (const void *)dp0 : nullptr};
     for (const void *x : vec)
         if (x && !aligned(x, 16))
             return KDN_ERR_ALIGN;
@@ -486,15 +493,15 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
     const long long n_a = gdn ? tok * es : (dn ? 0 : tok * d_k * es);
     const long long n_S = bh * d_k * d_v * 4;
+    const long long n_p = bh * p_per_head(variant, d_k) * 4;
     struct R { const void *p; long long n; };
-    const R ins[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, iso ? 0 : tok * es},
-                     {proc_noise, iso ? n_qk : 0}, {obs_noise, iso ? tok * es : 0},
-                     {S0, n_S}, {p0, iso ? bh * 4 : 0}, {d_o, n_v}, {dS_out, n_S},
-                     {dp_out, iso ? bh * 4 : 0}};
+    const R ins[] = {{q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, kdn ? 0 : tok * es},
+                     {proc_noise, kdn ? n_qk : 0}, {obs_noise, kdn ? tok * es : 0},
+                     {S0, n_S}, {p0, n_p}, {d_o, n_v}, {dS_out, n_S}, {dp_out, n_p}};
     const R outs[] = {{dq, tok * d_k * 4}, {dk, tok * d_k * 4}, {dv, tok * d_v * 4},
                       {dlog_alpha, gdn ? tok * 4 : (dn ? 0 : tok * d_k * 4)},
-                      {dbeta, iso ? 0 : tok * 4}, {dproc_noise, iso ? tok * d_k * 4 : 0},
-                      {dobs_noise, iso ? tok * 4 : 0}, {dS0, n_S}, {dp0, iso ? bh * 4 : 0}};
+                      {dbeta, kdn ? 0 : tok * 4}, {dproc_noise, kdn ? tok * d_k * 4 : 0},
+                      {dobs_noise, kdn ? tok * 4 : 0}, {dS0, n_S}, {dp0, n_p}};
     constexpr int NO = (int)(sizeof(outs) / sizeof(outs[0]));
     // outputs overlap no input and no other output
     for (int i = 0; i < NO; ++i) {
@@ -530,7 +537,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     F.xi = proc_noise; F.r = obs_noise;
     F.S0 = S0; F.p0 = p0; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
     F.ws = nullptr; F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
-    F.states = nullptr; F.beta_out = nullptr;
+    F.states = nullptr; F.beta_out = nullptr; F.w_out = nullptr;
     F.cus = device_cus();
     if (W.total > 0) {
         F.ws = base;
@@ -543,17 +550,24 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
             F.ws_p0 = reinterpret_cast<float *>(vb + n_mob + kdn::WsLayout::stat_bytes(bh, nc, C));
             F.beta_out = reinterpret_cast<float *>(base + W.beta);
         }
+        if (diag) {
+            char *vb = base + kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
+            F.ws_mob = reinterpret_cast<float *>(vb);
+            F.ws_p0 = reinterpret_cast<float *>(vb + kdn::WsLayout::mobius_bytes(bh, nc, d_k));
+            F.w_out = reinterpret_cast<float *>(base + W.w);
+        }
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (tok > 0) {
-        if (iso)
+        if (kdn)
             e = kdn::launch_variance_scan(F, st);
         if (e == hipSuccess) {
             switch (variant) {
             case KDN_DELTANET: e = kdn::launch_prefill_prep_v0(F, st); break;
             case KDN_GATED_DELTANET: e = kdn::launch_prefill_prep_v1(F, st); break;
             case KDN_KDA: e = kdn::launch_prefill_prep_v2(F, st); break;
+            case KDN_DIAG_KDN: e = kdn::launch_prefill_prep_v3(F, st); break;
             default: e = kdn::launch_prefill_prep_v4(F, st); break;
             }
         }
@@ -567,21 +581,24 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     G.bf16 = dtype == KDN_BF16;
     G.B = B; G.T = T; G.H = H; G.dk = d_k; G.dv = d_v; G.chunk = C;
     G.mu = mu;
-    G.q = q; G.k = k; G.v = v; G.alpha = alpha; G.beta = iso ? nullptr : beta;
+    G.q = q; G.k = k; G.v = v; G.alpha = alpha; G.beta = kdn ? nullptr : beta;
     G.xi = proc_noise; G.r = obs_noise; G.p0 = p0;
     G.beta_f32 = F.beta_out;
+    G.w_f32 = F.w_out;
+    G.dw_out = diag && W.total > 0 ? reinterpret_cast<float *>(base + W.dw) : nullptr;
     G.S0 = S0;
     G.dO = d_o; G.dS_out = dS_out;
     G.dq = dq; G.dk_ = dk; G.dv_ = dv; G.dla = dlog_alpha;
-    G.dbeta = iso ? (W.total > 0 ? reinterpret_cast<float *>(base + W.dbeta) : nullptr) : dbeta;
+    G.dbeta = iso ? (W.total > 0 ? reinterpret_cast<float *>(base + W.dbeta) : nullptr)
+                  : (diag ? nullptr : dbeta);
     G.dS0 = dS0;
     G.dp_out = dp_out; G.dxi = dproc_noise; G.dr = dobs_noise; G.dp0 = dp0;
     G.ws = F.ws;
     G.states = F.states;
     G.dstates = W.total > 0 ? reinterpret_cast<float *>(base + W.dstates) : nullptr;
     G.ws_stat = F.ws_stat; G.ws_p0 = F.ws_p0;
-    G.chain_map = iso && W.total > 0 ? reinterpret_cast<float *>(base + W.cmap) : nullptr;
-    G.chain_dp = iso && W.total > 0 ? reinterpret_cast<float *>(base + W.cdp) : nullptr;
+    G.chain_map = kdn && W.total > 0 ? reinterpret_cast<float *>(base + W.cmap) : nullptr;
+    G.chain_dp = kdn && W.total > 0 ? reinterpret_cast<float *>(base + W.cdp) : nullptr;
     G.cus = F.cus;
     e = kdn::launch_backward(G, st);
     return e == hipSuccess ? KDN_OK : KDN_ERR_HIP;

@@ -374,6 +374,9 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     auto beta_at = [&](int t) {
         return P.beta_f32 ? P.beta_f32[row(t)] : to_f32(gb[row(t)]);
     };
+    // diagonal KDN: the write vector is the gain w (saved by the forward),
+    // and dw goes out for the variance chain instead of into dk and dbeta
+    const bool gw = P.w_f32 != nullptr;
 
     // ---- chunk operands from the forward record
     {
@@ -652,17 +655,24 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     for (int n = 0; n < NK4; ++n) {
         const int x = tid + NT * n, t = x / GK4, i4 = (x % GK4) * 4;
         float kk[4] = {0.f, 0.f, 0.f, 0.f}, qq[4] = {0.f, 0.f, 0.f, 0.f};
-        float bt = 0.f;
+        float ww[4] = {0.f, 0.f, 0.f, 0.f};
         if (t < L) {
             gload4(gk + row(t) * DK + i4, kk);
             gload4(gq + row(t) * DK + i4, qq);
-            bt = beta_at(t);
+            if (gw) {
+                gload4(P.w_f32 + row(t) * DK + i4, ww);
+            } else {
+                const float bt = beta_at(t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ww[e] = bt * kk[e];
+            }
         }
         const float4 g4 = *reinterpret_cast<const float4 *>(GAM + t * PF + i4);
         const float g[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            WPT[(i4 + e) * PC + t] = from_f32<E>(g[e] > 0.f ? bt * kk[e] / g[e] : 0.f);
+            WPT[(i4 + e) * PC + t] = from_f32<E>(g[e] > 0.f ? ww[e] / g[e] : 0.f);
             QTT[(i4 + e) * PC + t] = from_f32<E>(g[e] * qq[e]);
             KTT[(i4 + e) * PC + t] = from_f32<E>(g[e] * kk[e]);
         }
@@ -699,7 +709,8 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                  : (VAR == KDA ? to_f32(ga[row(t) * DK + i]) : 1.f);
         };
         auto wval = [&](int s, int i) {
-            return s < L ? beta_at(s) * to_f32(gk[row(s) * DK + i]) : 0.f;
+            if (s >= L) return 0.f;
+            return gw ? P.w_f32[row(s) * DK + i] : beta_at(s) * to_f32(gk[row(s) * DK + i]);
         };
 #pragma unroll
         for (int k = 0; k < NS3; ++k) {
@@ -756,15 +767,18 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             const float g = GAM[t * PF + i];
             const float kk = in ? to_f32(gk[row(t) * DK + i]) : 0.f;
             const float qq = in ? to_f32(gq[row(t) * DK + i]) : 0.f;
-            const float bt = in ? beta_at(t) : 0.f;
+            const float bt = (in && !gw) ? beta_at(t) : 0.f;
+            const float wv = in ? (gw ? P.w_f32[row(t) * DK + i] : bt * kk) : 0.f;
             const float dq = exact ? dq3[k][r] : g * dq3[k][r];
             const float dkd = exact ? dk3[k][r] : g * dk3[k][r];
             const float dw = exact ? dw3[k][r] : (g > 0.f ? dw3[k][r] / g : 0.f);
             if (in) {
                 P.dq[row(t) * DK + i] = dq;
                 P.dk_[row(t) * DK + i] = dkd + bt * dw;
+                if (gw)
+                    P.dw_out[row(t) * DK + i] = dw;
             }
-            float db = kk * dw;
+            float db = gw ? 0.f : kk * dw;
             db += __shfl_xor(db, 1, WAVE);
             db += __shfl_xor(db, 2, WAVE);
             db += __shfl_xor(db, 4, WAVE);
@@ -772,7 +786,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             if ((lane & 15) == 0)
                 atomicAdd(&s_db[t], db);
             if (DECAY)
-                DG[t * PF + i] = kk * dkd + qq * dq - bt * kk * dw;
+                DG[t * PF + i] = kk * dkd + qq * dq - wv * dw;
         }
     }
     __syncthreads();
@@ -819,7 +833,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                 P.dla[row(lane)] = v + gcs;
         }
     }
-    if (tid < L)
+    if (tid < L && P.dbeta)
         P.dbeta[row(tid)] = s_db[tid];
 }
 
@@ -996,6 +1010,230 @@ __global__ __launch_bounds__(256) void iso_chain_grad_kernel(BackwardParams P) {
 }
 
 // ---------------------------------------------------------------------------
+// Diagonal KDN: the adjoint of the per-channel variance chain.  Per token,
+// forward (channel i; s couples the channels):
+//   p-_i = a_i^2 p_i + xi_i,  s = r + sum_i p-_i k_i^2,  w_i = p-_i k_i / s,
+//   den_i = r + mu p-_i k_i^2,  p'_i = p-_i r / den_i
+// (s = 0: w = 0; den_i = 0: p'_i = p-_i).  With dw from the memory part,
+//   du_i = dw_i / s,  ds = -sum_i dw_i w_i / s          (0 if s = 0)
+//   dp-_i = du_i k_i + ds k_i^2 + dp_i c_i,  c_i = r^2 / den_i^2 (1 if 0)
+//   d(previous p_i) = a_i^2 dp-_i,
+// affine in dp_i: A = a^2 c, Bc = a^2 (du k + ds k^2).  The three kernels
+// mirror the isotropic ones, one thread per key channel; the gradients:
+//   dk_i += du_i p-_i + 2 ds p-_i k_i - 2 dp_i mu p-_i^2 r k_i / den_i^2,
+//   dr = ds + sum_i dp_i mu p-_i^2 k_i^2 / den_i^2,
+//   d log alpha_i += 2 a_i^2 p_i dp-_i,  dxi_i = dp-_i.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int C>
+struct DiagChainSmem {
+    float pm[C][DK], pp[C][DK];     // p- and the variance before each token
+    E kv[C][DK], av[C][DK];         // k, a
+    float s[C], ds[C], r[C];
+};
+
+// The chunk's forward variance chain (thread i = channel i, from the
+// chunk-start variance of the forward pass) and the per-token sums s, ds.
+template <typename E, int DK, int C>
+__device__ __forceinline__ void diag_chain_setup(const BackwardParams &P, int bh, int c, int NC,
+                                                 DiagChainSmem<E, DK, C> &M) {
+    const int i = threadIdx.x, lane = i & (WAVE - 1), wv = i / WAVE;
+    constexpr int NWV = DK / WAVE;
+    const int T = P.T, H = P.H;
+    const int b = bh / H, h = bh % H, c0 = c * C, L = min(C, T - c0);
+    const long tok0 = ((long)b * T + c0) * H + h;
+    const E *gk = static_cast<const E *>(P.k);
+    const E *ga = static_cast<const E *>(P.alpha);
+    const E *gx = static_cast<const E *>(P.xi);
+    const E *gr = static_cast<const E *>(P.r);
+    const float mu = P.mu;
+    float p = P.ws_p0[((long)bh * NC + c) * DK + i];
+    constexpr int G = 8;                                  // tokens loaded ahead
+#pragma unroll 1
+    for (int tb = 0; tb < C; tb += G) {
+        float kk[G], aa[G], xx[G], rr[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int t = tb + g;
+            const bool in = t < L;
+            const long row = tok0 + (long)t * H;
+            kk[g] = in ? to_f32(gk[row * DK + i]) : 0.f;
+            aa[g] = in ? to_f32(ga[row * DK + i]) : 1.f;
+            xx[g] = in ? to_f32(gx[row * DK + i]) : 0.f;
+            rr[g] = in ? to_f32(gr[row]) : 1.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int t = tb + g;
+            const float pm = fmaf(aa[g] * aa[g], p, xx[g]);
+            M.pm[t][i] = pm;
+            M.pp[t][i] = p;
+            M.kv[t][i] = from_f32<E>(kk[g]);
+            M.av[t][i] = from_f32<E>(aa[g]);
+            if (i == 0)
+                M.r[t] = rr[g];
+            const float den = fmaf(mu * kk[g] * kk[g], pm, rr[g]);
+            p = den != 0.f ? pm * rr[g] / den : pm;
+        }
+    }
+    __syncthreads();
+    // s_t = r_t + sum_i p-_i k_i^2 and ds_t = -sum_i dw_i w_i / s_t, a wave per token
+    for (int t = wv; t < C; t += NWV) {
+        float a = 0.f, d = 0.f;
+        const long row = tok0 + (long)t * H;
+        const bool in = t < L;
+        for (int j = lane; j < DK; j += WAVE) {
+            const float kj = to_f32(M.kv[t][j]);
+            a += M.pm[t][j] * kj * kj;
+            if (in)
+                d += P.dw_out[row * DK + j] * P.w_f32[row * DK + j];
+        }
+        a = wave_sum(a);
+        d = wave_sum(d);
+        if (lane == 0) {
+            const float sv = M.r[t] + a;
+            M.s[t] = sv;
+            M.ds[t] = sv != 0.f ? -d / sv : 0.f;
+        }
+    }
+    __syncthreads();
+}
+
+// The affine map of token t, channel i.
+template <typename E, int DK, int C>
+__device__ __forceinline__ void diag_token_map(const BackwardParams &P, const DiagChainSmem<E, DK, C> &M,
+                                               int t, int i, float dw, float &A, float &Bc) {
+    const float kk = to_f32(M.kv[t][i]), a = to_f32(M.av[t][i]);
+    const float pm = M.pm[t][i], r = M.r[t], sv = M.s[t], ds = M.ds[t];
+    const float du = sv != 0.f ? dw / sv : 0.f;
+    const float den = fmaf(P.mu * kk * kk, pm, r);
+    const float cc = den != 0.f ? (r * r) / (den * den) : 1.f;
+    A = a * a * cc;
+    Bc = a * a * (du * kk + ds * kk * kk);
+}
+
+// Kernel 1: one workgroup (thread per channel) per (head, chunk): chunk maps
+// to chain_map [bh][c][i][2].
+template <typename E, int DK, int C>
+__global__ __launch_bounds__(DK) void diag_chain_map_kernel(BackwardParams P) {
+    __shared__ DiagChainSmem<E, DK, C> M;
+    const int NC = (P.T + C - 1) / C;
+    const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+    diag_chain_setup<E, DK, C>(P, bh, c, NC, M);
+    const int i = threadIdx.x;
+    const int b = bh / P.H, h = bh % P.H, c0 = c * C, L = min(C, P.T - c0);
+    const long tok0 = ((long)b * P.T + c0) * P.H + h;
+    float A = 1.f, Bc = 0.f;                            // f_t o ... o f_{C-1}
+    for (int t = L - 1; t >= 0; --t) {
+        float at, bt;
+        diag_token_map<E, DK, C>(P, M, t, i, P.dw_out[(tok0 + (long)t * P.H) * DK + i], at, bt);
+        Bc = fmaf(at, Bc, bt);
+        A *= at;
+    }
+    float *dst = P.chain_map + (((long)bh * NC + c) * DK + i) * 2;
+    dst[0] = A;
+    dst[1] = Bc;
+}
+
+// Kernel 2: one thread per (head, channel), the chunk maps from the last
+// chunk back: dp at every chunk end, and dp0.
+__global__ __launch_bounds__(256) void diag_chain_scan_kernel(BackwardParams P) {
+    const long x = (long)blockIdx.x * 256 + threadIdx.x;
+    const int DK = P.dk;
+    if (x >= (long)P.B * P.H * DK)
+        return;
+    const long bh = x / DK;
+    const int i = (int)(x % DK);
+    const int NC = (P.T + P.chunk - 1) / P.chunk;
+    float dp = P.dp_out ? P.dp_out[bh * DK + i] : 0.f;
+    for (int c = NC - 1; c >= 0; --c) {
+        const long u = (bh * NC + c) * DK + i;
+        P.chain_dp[u] = dp;
+        dp = fmaf(P.chain_map[u * 2], dp, P.chain_map[u * 2 + 1]);
+    }
+    if (P.dp0)
+        P.dp0[bh * DK + i] = dp;
+}
+
+// Kernel 3: the per-token gradients of the chain.
+template <typename E, int DK, int C>
+__global__ __launch_bounds__(DK) void diag_chain_grad_kernel(BackwardParams P) {
+    __shared__ DiagChainSmem<E, DK, C> M;
+    const int NC = (P.T + C - 1) / C;
+    const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+    diag_chain_setup<E, DK, C>(P, bh, c, NC, M);
+    const int i = threadIdx.x, lane = i & (WAVE - 1), wv = i / WAVE;
+    constexpr int NWV = DK / WAVE;
+    const int b = bh / P.H, h = bh % P.H, c0 = c * C, L = min(C, P.T - c0);
+    const long tok0 = ((long)b * P.T + c0) * P.H + h;
+    const float mu = P.mu;
+    float dp = P.chain_dp[((long)bh * NC + c) * DK + i];
+    for (int t = L - 1; t >= 0; --t) {
+        const long rt = tok0 + (long)t * P.H;
+        const float kk = to_f32(M.kv[t][i]), a = to_f32(M.av[t][i]);
+        const float pm = M.pm[t][i], pp = M.pp[t][i], r = M.r[t], sv = M.s[t], ds = M.ds[t];
+        const float du = sv != 0.f ? P.dw_out[rt * DK + i] / sv : 0.f;
+        const float den = fmaf(mu * kk * kk, pm, r);
+        float dpm = du * kk + ds * kk * kk;
+        float dki = du * pm + 2.f * ds * pm * kk;
+        float drp = 0.f;
+        if (den != 0.f) {
+            const float d2 = den * den;
+            dpm += dp * r * r / d2;
+            dki -= 2.f * dp * mu * pm * pm * r * kk / d2;
+            drp = dp * mu * pm * pm * kk * kk / d2;
+        } else {
+            dpm += dp;
+        }
+        M.pp[t][i] = drp;                 // pp[t][i] is read only above: dr parts
+        P.dk_[rt * DK + i] += dki;
+        P.dla[rt * DK + i] += 2.f * a * a * pp * dpm;
+        P.dxi[rt * DK + i] = dpm;
+        dp = a * a * dpm;
+    }
+    __syncthreads();
+    for (int t = wv; t < L; t += NWV) {
+        float x = 0.f;
+        for (int j = lane; j < DK; j += WAVE)
+            x += M.pp[t][j];
+        x = wave_sum(x);
+        if (lane == 0)
+            P.dr[tok0 + (long)t * P.H] = M.ds[t] + x;
+    }
+}
+
+template <typename E, int DK, int C>
+static hipError_t launch_diag_chain(const BackwardParams &P, hipStream_t st) {
+    const long bh = (long)P.B * P.H, nc = (P.T + C - 1) / C;
+    if (nc > 0) {
+        hipLaunchKernelGGL((diag_chain_map_kernel<E, DK, C>), dim3((unsigned)(bh * nc)), dim3(DK),
+                           0, st, P);
+        if (hipError_t e = hipGetLastError())
+            return e;
+    }
+    hipLaunchKernelGGL(diag_chain_scan_kernel, dim3((unsigned)((bh * DK + 255) / 256)),
+                       dim3(256), 0, st, P);
+    if (hipError_t e = hipGetLastError())
+        return e;
+    if (nc > 0)
+        hipLaunchKernelGGL((diag_chain_grad_kernel<E, DK, C>), dim3((unsigned)(bh * nc)), dim3(DK),
+                           0, st, P);
+    return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t launch_diag_chain_e(const BackwardParams &P, hipStream_t st) {
+    if (P.dk == 128 && P.chunk == 64) {
+        if constexpr (sizeof(E) == 2)
+            return launch_diag_chain<E, 128, 64>(P, st);
+        return hipErrorInvalidValue;
+    }
+    if (P.dk == 128 && P.chunk == 32) return launch_diag_chain<E, 128, 32>(P, st);
+    if (P.dk == 64 && P.chunk == 64) return launch_diag_chain<E, 64, 64>(P, st);
+    if (P.dk == 64 && P.chunk == 32) return launch_diag_chain<E, 64, 32>(P, st);
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 template <typename E, int VAR, int DK, int C>
@@ -1040,6 +1278,13 @@ static hipError_t launch_bwd_e(const BackwardParams &P, hipStream_t st) {
     case DELTANET: return launch_bwd_v<E, DELTANET>(P, st);
     case GATED_DELTANET: return launch_bwd_v<E, GATED_DELTANET>(P, st);
     case KDA: return launch_bwd_v<E, KDA>(P, st);
+    case DIAG_KDN: {
+        // the memory part with the gains as write vectors, then the
+        // per-channel variance chain
+        if (hipError_t e = launch_bwd_v<E, KDA>(P, st))
+            return e;
+        return launch_diag_chain_e<E>(P, st);
+    }
     case ISO_KDN: {
         // the memory part as KDA with the derived write strengths, then the
         // variance chain

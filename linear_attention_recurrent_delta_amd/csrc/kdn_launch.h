@@ -46,6 +46,8 @@ struct PrefillParams {
     // Isotropic KDN, gradient computation: the derived write strengths
     // [B, T, H] (float32) are saved here by the prep kernel (null otherwise).
     float *beta_out;
+    // Diagonal KDN, gradient computation: the gains w [B, T, H, dk] (float32).
+    float *w_out;
     int cus;           // compute units of the current device
 };
 
@@ -61,6 +63,8 @@ struct BackwardParams {
     const void *xi, *r;                     // isotropic KDN: process / observation noise
     const float *p0;                        // isotropic KDN: [B, H]
     const float *beta_f32;                  // isotropic KDN: derived write strengths
+    const float *w_f32;                     // diagonal KDN: gains [B, T, H, dk]
+    float *dw_out;                          // diagonal KDN: dL/dw [B, T, H, dk]
     const float *S0;                        // may be null (zero)
     const void *dO;                         // [B, T, H, dv] call dtype
     const float *dS_out;                    // [B, H, dk, dv], may be null (zero)

@@ -781,6 +781,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
                         w[tt][c] = uu[c] * inv;
+                    if (PREP && P.w_out && t < L) {     // gains, for the gradient pass
+                        float *wo = P.w_out + (tok0 + (long)t * H) * DK + j0;
+                        *reinterpret_cast<float4 *>(wo) =
+                            make_float4(w[tt][0], w[tt][1], w[tt][2], w[tt][3]);
+                        *reinterpret_cast<float4 *>(wo + 4) =
+                            make_float4(w[tt][4], w[tt][5], w[tt][6], w[tt][7]);
+                    }
                 } else {
                     const float bt = s_beta[t];
 #pragma unroll

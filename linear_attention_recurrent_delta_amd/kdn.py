@@ -287,15 +287,15 @@ def decode_multi(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
 def prefill_backward(variant, q, k, v, d_o, alpha=None, beta=None, proc_noise=None,
                      obs_noise=None, S0=None, p0=None, dS_out=None, dp_out=None, mu=1.0,
                      chunk=0, out=None, workspace=None, stream=None):
-    """Gradients of :func:`prefill` (DeltaNet, Gated DeltaNet, KDA, isotropic
-    KDN) for the cotangents d_o [B,T,H,dv], dS_out [B,H,dk,dv] and (iso_kdn)
-    dp_out [B,H] (None: zero).  Returns a dict of float32 tensors: dq, dk, dv,
-    dlog_alpha (alpha dL/dalpha: [B,T,H] for gated_deltanet, [B,T,H,dk] for
-    kda and iso_kdn, None for deltanet), dbeta (None for iso_kdn), dS0, and
-    for iso_kdn dproc_noise, dobs_noise, dp0.  ``workspace``: a uint8 tensor
-    of at least the queried size, or None to allocate one."""
+    """Gradients of :func:`prefill` (every variant) for the cotangents
+    d_o [B,T,H,dv], dS_out [B,H,dk,dv] and (KDN) dp_out shaped as p0 (None:
+    zero).  Returns a dict of float32 tensors: dq, dk, dv, dlog_alpha
+    (alpha dL/dalpha: [B,T,H] for gated_deltanet, [B,T,H,dk] for kda and the
+    KDNs, None for deltanet), dbeta (None for the KDNs), dS0, and for the KDNs
+    dproc_noise, dobs_noise, dp0.  ``workspace``: a uint8 tensor of at least
+    the queried size, or None to allocate one."""
     vid = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    iso = vid == 4
+    iso = vid in (3, 4)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dt = DTYPES[q.dtype]
@@ -309,7 +309,7 @@ def prefill_backward(variant, q, k, v, d_o, alpha=None, beta=None, proc_noise=No
                    dbeta=None if iso else new(B, T, H), dS0=new(B, H, dk, dv),
                    dproc_noise=new(B, T, H, dk) if iso else None,
                    dobs_noise=new(B, T, H) if iso else None,
-                   dp0=new(B, H) if iso else None)
+                   dp0=(new(B, H, dk) if vid == 3 else new(B, H)) if iso else None)
     if workspace is None:
         n = kdn_chunk_prefill_backward_workspace_size(vid, dt, B, T, H, dk, dv, chunk)
         workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None

@@ -305,7 +305,11 @@ def _bwd_args(variant=1, dtype=1, B=2, T=100, H=4, dk=128, dv=128, chunk=0, **ov
 
 
 BWD_CASES = [
-    ("diagonal KDN", dict(variant=3, beta=None, xi=A + 14 * MB, r=A + 15 * MB), EUNSUP),
+    ("diag KDN with beta", dict(variant=3, xi=A + 14 * MB, r=A + 15 * MB,
+                                p0=A + 17 * MB, da=A + 11 * MB), ENULL),
+    ("diag KDN misaligned p0", dict(variant=3, beta=None, xi=A + 14 * MB, r=A + 15 * MB,
+                                    p0=A + 17 * MB + 4, db=None, dxi=A + 19 * MB,
+                                    dr=A + 20 * MB), EALIGN),
     ("iso KDN with beta", dict(variant=4, beta=A + 4 * MB), ENULL),
     ("iso KDN with dbeta", dict(variant=4, db=A + 12 * MB), ENULL),
     ("iso KDN without p0", dict(variant=4, p0=None), ENULL),
@@ -348,7 +352,8 @@ def test_backward_workspace_size(lib):
     rec = 66048
     n = f(1, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
     assert st.value == OK and n == 2 * 4 * 2 * (rec + 2 * 128 * 128 * 4)
-    assert f(3, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st)) == 0 and st.value == EUNSUP
+    n_diag = f(3, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
+    assert st.value == OK and n_diag > n
     n_iso = f(4, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
     assert st.value == OK and n_iso > n
     assert f(1, 1, 2, 0, 4, 128, 128, 0, ctypes.byref(st)) == 0 and st.value == OK

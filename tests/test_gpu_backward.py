@@ -156,30 +156,33 @@ def test_backward_workload_sampled():
 
 
 # ---------------------------------------------------------------------------
-# Isotropic KDN: the memory part with the derived write strengths, then the
-# head-variance chain (gradients of xi, r, p0 and the extra alpha, k terms).
+# KDN: the memory part with the derived write vectors (isotropic: beta k from
+# the head variance; diagonal: the gain), then the variance chain (gradients
+# of xi, r, p0 and the extra alpha, k terms).
 # ---------------------------------------------------------------------------
-ISO_NAMES = ("q", "k", "v", "log_alpha", "proc_noise", "obs_noise", "S0", "p0")
+KDN_NAMES = ("q", "k", "v", "log_alpha", "proc_noise", "obs_noise", "S0", "p0")
+KDNS = ["diag_kdn", "iso_kdn"]
 
 
-def _iso_inputs(B, T, H, dk, dv, dtype, seed, state=True, ds=True):
-    inp = _inputs("iso_kdn", B, T, H, dk, dv, dtype, seed, state=state, ds=ds)
+def _kdn_inputs(variant, B, T, H, dk, dv, dtype, seed, state=True, ds=True):
+    inp = _inputs(variant, B, T, H, dk, dv, dtype, seed, state=state, ds=ds)
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 11)
-    inp["dp"] = torch.randn((B, H), generator=g, device="cuda") if ds else None
+    inp["dp"] = torch.randn(tuple(inp["p0"].shape), generator=g, device="cuda") if ds else None
     return inp
 
 
-def _iso_compare(inp, tol, mu=1.0, chunk=0, heads=None):
-    got = kdn.prefill_backward("iso_kdn", inp["q"], inp["k"], inp["v"], inp["dO"],
+def _kdn_compare(variant, inp, tol, mu=1.0, chunk=0, heads=None):
+    got = kdn.prefill_backward(variant, inp["q"], inp["k"], inp["v"], inp["dO"],
                                alpha=inp["alpha"], proc_noise=inp["xi"], obs_noise=inp["r"],
                                S0=inp.get("S0"), p0=inp["p0"], dS_out=inp.get("dS"),
                                dp_out=inp.get("dp"), mu=mu, chunk=chunk)
     torch.cuda.synchronize()
-    got = {n: got["d" + n] for n in ISO_NAMES}
-    for n in ISO_NAMES:
+    got = {n: got["d" + n] for n in KDN_NAMES}
+    for n in KDN_NAMES:
         assert torch.isfinite(got[n]).all(), f"d{n} not finite"
     f = lambda x: None if x is None else np64(x)
+    ref_fn = oracle.backward_iso if variant == "iso_kdn" else oracle.backward_diag
     if heads is None:
         parts = [(inp, None)]
     else:
@@ -188,12 +191,12 @@ def _iso_compare(inp, tol, mu=1.0, chunk=0, heads=None):
         parts = [({k: sl(v, b, h, k in ("S0", "dS", "p0", "dp")) for k, v in inp.items()},
                   (b, h)) for (b, h) in heads]
     for x, key in parts:
-        ref = oracle.backward_iso(f(x["q"]), f(x["k"]), f(x["v"]), f(x["alpha"]), f(x["xi"]),
-                                  f(x["r"]), f(x["p0"]), f(x.get("S0")), f(x["dO"]),
-                                  f(x.get("dS")), f(x.get("dp")), mu=mu)
-        ref = dict(zip(ISO_NAMES, ref))
+        ref = ref_fn(f(x["q"]), f(x["k"]), f(x["v"]), f(x["alpha"]), f(x["xi"]), f(x["r"]),
+                     f(x["p0"]), f(x.get("S0")), f(x["dO"]), f(x.get("dS")), f(x.get("dp")),
+                     mu=mu)
+        ref = dict(zip(KDN_NAMES, ref))
         ref["log_alpha"] = ref["log_alpha"] * f(x["alpha"])
-        for n in ISO_NAMES:
+        for n in KDN_NAMES:
             g = got[n]
             if key is not None:
                 b, h = key
@@ -202,44 +205,50 @@ def _iso_compare(inp, tol, mu=1.0, chunk=0, heads=None):
                   np64(g), ref[n], tol)
 
 
-ISO_CASES = [(dt, dk, dv) for dt in ("bf16", "f32")
+KDN_CASES = [(v, dt, dk, dv) for v in KDNS for dt in ("bf16", "f32")
              for (dk, dv) in ((128, 128), (64, 64), (128, 64), (64, 128))]
 
 
-@pytest.mark.parametrize("dtype,dk,dv", ISO_CASES,
-                         ids=[f"{d}-k{a}v{b}" for d, a, b in ISO_CASES])
-def test_backward_iso_small(dtype, dk, dv):
-    log(f"backward iso_kdn {dtype} dk={dk} dv={dv} B2 T200 H2")
-    _iso_compare(_iso_inputs(2, 200, 2, dk, dv, dtype, seed=111), TOL[dtype])
+@pytest.mark.parametrize("variant,dtype,dk,dv", KDN_CASES,
+                         ids=[f"{v}-{d}-k{a}v{b}" for v, d, a, b in KDN_CASES])
+def test_backward_kdn_small(variant, dtype, dk, dv):
+    log(f"backward {variant} {dtype} dk={dk} dv={dv} B2 T200 H2")
+    _kdn_compare(variant, _kdn_inputs(variant, 2, 200, 2, dk, dv, dtype, seed=111), TOL[dtype])
 
 
 @pytest.mark.parametrize("T", [0, 1, 63, 64, 65, 130])
-def test_backward_iso_lengths(T):
-    log(f"backward iso_kdn length T={T}")
-    _iso_compare(_iso_inputs(2, T, 2, 128, 128, "bf16", seed=112 + T), TOL["bf16"])
+@pytest.mark.parametrize("variant", KDNS)
+def test_backward_kdn_lengths(variant, T):
+    log(f"backward {variant} length T={T}")
+    _kdn_compare(variant, _kdn_inputs(variant, 2, T, 2, 128, 128, "bf16", seed=112 + T),
+                 TOL["bf16"])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_backward_iso_mu_and_exact_observations(dtype):
-    log(f"backward iso_kdn mu = d_k, r = 0 on some tokens {dtype}")
-    inp = _iso_inputs(1, 180, 2, 128, 128 if dtype == "bf16" else 64, dtype, seed=113)
+@pytest.mark.parametrize("variant", KDNS)
+def test_backward_kdn_mu_and_exact_observations(variant, dtype):
+    log(f"backward {variant} mu = d_k, r = 0 on some tokens {dtype}")
+    inp = _kdn_inputs(variant, 1, 180, 2, 128, 128 if dtype == "bf16" else 64, dtype,
+                      seed=113)
     r = inp["r"].clone()
     r[:, 7] = 0
     r[:, 64:66] = 0
     inp["r"] = r
-    _iso_compare(inp, TOL[dtype], mu=128.0)
+    _kdn_compare(variant, inp, TOL[dtype], mu=128.0)
 
 
-def test_backward_iso_without_cotangents():
-    log("backward iso_kdn S0, dS_out, dp_out = NULL")
-    _iso_compare(_iso_inputs(2, 150, 2, 128, 128, "bf16", seed=114, state=False, ds=False),
-                 TOL["bf16"])
+@pytest.mark.parametrize("variant", KDNS)
+def test_backward_kdn_without_cotangents(variant):
+    log(f"backward {variant} S0, dS_out, dp_out = NULL")
+    _kdn_compare(variant, _kdn_inputs(variant, 2, 150, 2, 128, 128, "bf16", seed=114,
+                                      state=False, ds=False), TOL["bf16"])
 
 
-def test_backward_iso_long_sampled():
-    """Isotropic KDN at the workload's heads and head size (B2 H16, d = 128,
-    bf16) over 2048 tokens: every head on the GPU, sampled heads against the
-    oracle (whose backward keeps every memory of a stream)."""
-    log("backward iso_kdn B2 H16 T2048: sampled heads")
-    inp = _iso_inputs(2, 2048, 16, 128, 128, "bf16", seed=synth.seed_of("iso_kdn"))
-    _iso_compare(inp, TOL["bf16"], heads=[(0, 0), (1, 9)])
+@pytest.mark.parametrize("variant", KDNS)
+def test_backward_kdn_long_sampled(variant):
+    """KDN at the workload's heads and head size (B2 H16, d = 128, bf16) over
+    2048 tokens: every head on the GPU, sampled heads against the oracle
+    (whose backward keeps every memory of a stream)."""
+    log(f"backward {variant} B2 H16 T2048: sampled heads")
+    inp = _kdn_inputs(variant, 2, 2048, 16, 128, 128, "bf16", seed=synth.seed_of(variant))
+    _kdn_compare(variant, inp, TOL["bf16"], heads=[(0, 0), (1, 9)])
