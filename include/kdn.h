@@ -276,7 +276,8 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype,
  * (S at each chunk start, dS at each chunk end) per (sequence, head, chunk):
  * 66,048 + 131,072 bytes per (sequence, head, chunk) for bf16, d = 128, C = 64,
  * each section rounded up to 256 bytes; isotropic KDN adds 8 bytes per token
- * and 12 per chunk, diagonal KDN 8 d_k bytes per token and 12 d_k per chunk.
+ * and 12 per chunk, diagonal KDN 12 d_k + 8 bytes per token and 12 d_k per
+ * chunk.
  */
 unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant,
                                                              kdn_dtype dtype, int B, int T,

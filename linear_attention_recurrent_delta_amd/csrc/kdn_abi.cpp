@@ -220,6 +220,7 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.states = nullptr;
     P.beta_out = nullptr;
     P.w_out = nullptr;
+    P.invs_out = nullptr;
     P.cus = device_cus();
     if (n_ws > 0) {
         P.ws = workspace;
@@ -392,10 +393,11 @@ namespace {
 // Workspace of the gradient call, sections 256-byte aligned: the forward's
 // two-pass workspace, S at every chunk start, dS at every chunk end; for
 // isotropic KDN the derived write strengths and their gradients, for
-// diagonal KDN the gains and their gradients; for both the variance chain's
+// diagonal KDN the gains and their gradients, 1/s and sum_i w_i dw_i per
+// token and the variance before every token; for both the variance chain's
 // chunk maps and its gradient at every chunk end.
 struct BwdWs {
-    long long fwd, states, dstates, beta, dbeta, w, dw, cmap, cdp, total;
+    long long fwd, states, dstates, beta, dbeta, w, dw, invs, wdw, pp, cmap, cdp, total;
 };
 long long up256(long long n) { return (n + 255) / 256 * 256; }
 BwdWs backward_ws(int variant, int bf16, long long B, long long T, long long H, int d_k,
@@ -418,6 +420,9 @@ BwdWs backward_ws(int variant, int bf16, long long B, long long T, long long H, 
     if (diag) {
         w.w = o;     o += up256(tok * d_k * 4);
         w.dw = o;    o += up256(tok * d_k * 4);
+        w.invs = o;  o += up256(tok * 4);
+        w.wdw = o;   o += up256(tok * 4);
+        w.pp = o;    o += up256(tok * d_k * 4);
         w.cmap = o;  o += up256(bh * nc * d_k * 8);
         w.cdp = o;   o += up256(bh * nc * d_k * 4);
     }
@@ -537,7 +542,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     F.xi = proc_noise; F.r = obs_noise;
     F.S0 = S0; F.p0 = p0; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
     F.ws = nullptr; F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
-    F.states = nullptr; F.beta_out = nullptr; F.w_out = nullptr;
+    F.states = nullptr; F.beta_out = nullptr; F.w_out = nullptr; F.invs_out = nullptr;
     F.cus = device_cus();
     if (W.total > 0) {
         F.ws = base;
@@ -555,6 +560,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
             F.ws_mob = reinterpret_cast<float *>(vb);
             F.ws_p0 = reinterpret_cast<float *>(vb + kdn::WsLayout::mobius_bytes(bh, nc, d_k));
             F.w_out = reinterpret_cast<float *>(base + W.w);
+            F.invs_out = reinterpret_cast<float *>(base + W.invs);
         }
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -585,7 +591,11 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     G.xi = proc_noise; G.r = obs_noise; G.p0 = p0;
     G.beta_f32 = F.beta_out;
     G.w_f32 = F.w_out;
-    G.dw_out = diag && W.total > 0 ? reinterpret_cast<float *>(base + W.dw) : nullptr;
+    const bool dws = diag && W.total > 0;
+    G.dw_out = dws ? reinterpret_cast<float *>(base + W.dw) : nullptr;
+    G.invs = F.invs_out;
+    G.wdw = dws ? reinterpret_cast<float *>(base + W.wdw) : nullptr;
+    G.pp = dws ? reinterpret_cast<float *>(base + W.pp) : nullptr;
     G.S0 = S0;
     G.dO = d_o; G.dS_out = dS_out;
     G.dq = dq; G.dk_ = dk; G.dv_ = dv; G.dla = dlog_alpha;

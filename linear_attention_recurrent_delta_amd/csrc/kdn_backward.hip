@@ -778,7 +778,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                 if (gw)
                     P.dw_out[row(t) * DK + i] = dw;
             }
-            float db = gw ? 0.f : kk * dw;
+            float db = (gw ? wv : kk) * dw;           // diagonal KDN: sum w dw
             db += __shfl_xor(db, 1, WAVE);
             db += __shfl_xor(db, 2, WAVE);
             db += __shfl_xor(db, 4, WAVE);
@@ -833,8 +833,9 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                 P.dla[row(lane)] = v + gcs;
         }
     }
-    if (tid < L && P.dbeta)
-        P.dbeta[row(tid)] = s_db[tid];
+    float *const dbo = gw ? P.wdw : P.dbeta;
+    if (tid < L && dbo)
+        dbo[row(tid)] = s_db[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -929,22 +930,6 @@ __global__ __launch_bounds__(256) void iso_chain_map_kernel(BackwardParams P) {
     }
 }
 
-// Kernel 2: one lane per head, the chunk maps from the last chunk to the
-// first: dp at every chunk end, and dp0.
-__global__ __launch_bounds__(64) void iso_chain_scan_kernel(BackwardParams P) {
-    const long bh = (long)blockIdx.x * 64 + threadIdx.x;
-    if (bh >= (long)P.B * P.H)
-        return;
-    const int NC = (P.T + P.chunk - 1) / P.chunk;
-    float dp = P.dp_out ? P.dp_out[bh] : 0.f;
-    for (int c = NC - 1; c >= 0; --c) {
-        P.chain_dp[bh * NC + c] = dp;
-        dp = fmaf(P.chain_map[(bh * NC + c) * 2], dp, P.chain_map[(bh * NC + c) * 2 + 1]);
-    }
-    if (P.dp0)
-        P.dp0[bh] = dp;
-}
-
 // Kernel 3: one wave per (head, chunk): every token's dp, its scalar
 // gradients, then the per-channel ones (lanes over the channels).
 template <typename E>
@@ -1018,215 +1003,282 @@ __global__ __launch_bounds__(256) void iso_chain_grad_kernel(BackwardParams P) {
 //   du_i = dw_i / s,  ds = -sum_i dw_i w_i / s          (0 if s = 0)
 //   dp-_i = du_i k_i + ds k_i^2 + dp_i c_i,  c_i = r^2 / den_i^2 (1 if 0)
 //   d(previous p_i) = a_i^2 dp-_i,
-// affine in dp_i: A = a^2 c, Bc = a^2 (du k + ds k^2).  The three kernels
-// mirror the isotropic ones, one thread per key channel; the gradients:
+// affine in dp_i: A = a^2 c, Bc = a^2 (du k + ds k^2).  The gradients:
 //   dk_i += du_i p-_i + 2 ds p-_i k_i - 2 dp_i mu p-_i^2 r k_i / den_i^2,
 //   dr = ds + sum_i dp_i mu p-_i^2 k_i^2 / den_i^2,
 //   d log alpha_i += 2 a_i^2 p_i dp-_i,  dxi_i = dp-_i.
+// The forward pass saved 1/s per token and the memory part sum_i w_i dw_i,
+// so given those the channels are independent: one wave per (head, chunk),
+// lane l holding channels NJ l .. NJ l + NJ - 1, every token's inputs read a
+// group of tokens ahead so the loads stay off the sequential chain.
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int C>
-struct DiagChainSmem {
-    float pm[C][DK], pp[C][DK];     // p- and the variance before each token
-    E kv[C][DK], av[C][DK];         // k, a
-    float s[C], ds[C], r[C];
-};
+template <int NJ, typename E>
+__device__ __forceinline__ void ld_ch(const E *p, float (&x)[NJ]) {
+    if constexpr (NJ == 1) {
+        x[0] = to_f32(p[0]);
+    } else if constexpr (sizeof(E) == 2) {
+        const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+        x[0] = __uint_as_float(u << 16);
+        x[1] = __uint_as_float(u & 0xffff0000u);
+    } else {
+        const float2 f = *reinterpret_cast<const float2 *>(p);
+        x[0] = f.x;
+        x[1] = f.y;
+    }
+}
+template <int NJ>
+__device__ __forceinline__ void st_ch(float *p, const float (&x)[NJ]) {
+    if constexpr (NJ == 1)
+        p[0] = x[0];
+    else
+        *reinterpret_cast<float2 *>(p) = make_float2(x[0], x[1]);
+}
+__device__ __forceinline__ float lane_bcast(float x, int t) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), t));
+}
 
-// The chunk's forward variance chain (thread i = channel i, from the
-// chunk-start variance of the forward pass) and the per-token sums s, ds.
+// Unit (head, chunk) of a diagonal-chain wave, with lane t holding token t's
+// observation noise, 1/s and ds (1, 0, 0 past the chunk's end).
+struct DiagUnit {
+    long unit, tok0;
+    int L;
+    float r, invs, ds;
+};
+template <typename E>
+__device__ __forceinline__ bool diag_unit(const BackwardParams &P, int C, DiagUnit &U) {
+    const int NC = (P.T + C - 1) / C;
+    U.unit = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (U.unit >= (long)P.B * P.H * NC)
+        return false;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int bh = (int)(U.unit / NC), c = (int)(U.unit % NC);
+    const int b = bh / P.H, h = bh % P.H, c0 = c * C;
+    U.L = min(C, P.T - c0);
+    U.tok0 = ((long)b * P.T + c0) * P.H + h;
+    U.r = 1.f;
+    U.invs = 0.f;
+    U.ds = 0.f;
+    if (lane < U.L) {
+        const long row = U.tok0 + (long)lane * P.H;
+        U.r = to_f32(static_cast<const E *>(P.r)[row]);
+        U.invs = P.invs[row];
+        U.ds = -U.invs * P.wdw[row];
+    }
+    return true;
+}
+
+// Kernel 2 (both KDN variants): the chain's chunk maps composed from the
+// last chunk back.  Sequence s (a head, or a head's key channel: nch per
+// head) has NC maps, map c at chain_map[((s / nch) NC + c) nch + s % nch]
+// (pairs A, B: dp before chunk c = A dp after it + B).  One wave per
+// sequence takes 64 chunks at a time: a suffix composition over the lanes
+// gives every chunk-end gradient of the block from the one at its end.
+__global__ __launch_bounds__(256) void chain_scan_kernel(BackwardParams P, int nch) {
+    const long s = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (s >= (long)P.B * P.H * nch)
+        return;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const long bh = s / nch;
+    const int i = (int)(s % nch);
+    const int NC = (P.T + P.chunk - 1) / P.chunk;
+    const float2 *maps = reinterpret_cast<const float2 *>(P.chain_map);
+    float carry = P.dp_out ? P.dp_out[s] : 0.f;
+    for (int hi = NC; hi > 0; hi -= WAVE) {
+        const int c = hi - WAVE + lane;
+        const long u = (bh * NC + c) * nch + i;
+        float A = 1.f, Bc = 0.f;
+        if (c >= 0) {
+            const float2 m = maps[u];
+            A = m.x;
+            Bc = m.y;
+        }
+        chain_suffix(A, Bc, WAVE, lane);           // lane l: m_l o ... o m_63
+        float EA = __shfl_down(A, 1, WAVE), EB = __shfl_down(Bc, 1, WAVE);
+        if (lane == WAVE - 1) {
+            EA = 1.f;
+            EB = 0.f;
+        }
+        if (c >= 0)
+            P.chain_dp[u] = fmaf(EA, carry, EB);
+        carry = fmaf(lane_bcast(A, 0), carry, lane_bcast(Bc, 0));
+    }
+    if (lane == 0 && P.dp0)
+        P.dp0[s] = carry;
+}
+
+// Kernel 1: the chain through the chunk from its start variance (the same
+// arithmetic as the forward pass), saving the variance before each token,
+// and the chunk map F = f_0 o ... o f_{L-1} composed in token order, to
+// chain_map [bh][c][dk][2].
 template <typename E, int DK, int C>
-__device__ __forceinline__ void diag_chain_setup(const BackwardParams &P, int bh, int c, int NC,
-                                                 DiagChainSmem<E, DK, C> &M) {
-    const int i = threadIdx.x, lane = i & (WAVE - 1), wv = i / WAVE;
-    constexpr int NWV = DK / WAVE;
-    const int T = P.T, H = P.H;
-    const int b = bh / H, h = bh % H, c0 = c * C, L = min(C, T - c0);
-    const long tok0 = ((long)b * T + c0) * H + h;
+__global__ __launch_bounds__(256) void diag_chain_map_kernel(BackwardParams P) {
+    constexpr int NJ = DK / WAVE, G = 8;
+    DiagUnit U;
+    if (!diag_unit<E>(P, C, U))
+        return;
+    const int i0 = (threadIdx.x & (WAVE - 1)) * NJ;
+    const long H = P.H;
     const E *gk = static_cast<const E *>(P.k);
     const E *ga = static_cast<const E *>(P.alpha);
     const E *gx = static_cast<const E *>(P.xi);
-    const E *gr = static_cast<const E *>(P.r);
     const float mu = P.mu;
-    float p = P.ws_p0[((long)bh * NC + c) * DK + i];
-    constexpr int G = 8;                                  // tokens loaded ahead
+    float p[NJ], FA[NJ], FB[NJ];
+    ld_ch<NJ>(P.ws_p0 + U.unit * DK + i0, p);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        FA[j] = 1.f;
+        FB[j] = 0.f;
+    }
 #pragma unroll 1
-    for (int tb = 0; tb < C; tb += G) {
-        float kk[G], aa[G], xx[G], rr[G];
+    for (int tb = 0; tb < U.L; tb += G) {
+        float kk[G][NJ], aa[G][NJ], xx[G][NJ], dw[G][NJ];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const long row = U.tok0 + (long)(tb + g) * H;
+            if (tb + g < U.L) {
+                ld_ch<NJ>(gk + row * DK + i0, kk[g]);
+                ld_ch<NJ>(ga + row * DK + i0, aa[g]);
+                ld_ch<NJ>(gx + row * DK + i0, xx[g]);
+                ld_ch<NJ>(P.dw_out + row * DK + i0, dw[g]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    kk[g][j] = 0.f; aa[g][j] = 1.f; xx[g][j] = 0.f; dw[g][j] = 0.f;
+                }
+            }
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int t = tb + g;
-            const bool in = t < L;
-            const long row = tok0 + (long)t * H;
-            kk[g] = in ? to_f32(gk[row * DK + i]) : 0.f;
-            aa[g] = in ? to_f32(ga[row * DK + i]) : 1.f;
-            xx[g] = in ? to_f32(gx[row * DK + i]) : 0.f;
-            rr[g] = in ? to_f32(gr[row]) : 1.f;
-        }
+            const float r = lane_bcast(U.r, t), invs = lane_bcast(U.invs, t);
+            const float ds = lane_bcast(U.ds, t);
+            if (t < U.L)
+                st_ch<NJ>(P.pp + (U.tok0 + (long)t * H) * DK + i0, p);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int t = tb + g;
-            const float pm = fmaf(aa[g] * aa[g], p, xx[g]);
-            M.pm[t][i] = pm;
-            M.pp[t][i] = p;
-            M.kv[t][i] = from_f32<E>(kk[g]);
-            M.av[t][i] = from_f32<E>(aa[g]);
-            if (i == 0)
-                M.r[t] = rr[g];
-            const float den = fmaf(mu * kk[g] * kk[g], pm, rr[g]);
-            p = den != 0.f ? pm * rr[g] / den : pm;
+            for (int j = 0; j < NJ; ++j) {
+                const float k = kk[g][j], a2 = aa[g][j] * aa[g][j];
+                const float pm = fmaf(a2, p[j], xx[g][j]);
+                const float den = fmaf(mu * k * k, pm, r);
+                p[j] = den != 0.f ? pm * r * fast_rcp(den) : pm;
+                const float cc = den != 0.f ? (r * r) / (den * den) : 1.f;
+                const float du = dw[g][j] * invs;
+                FB[j] = fmaf(FA[j], a2 * fmaf(ds * k, k, du * k), FB[j]);
+                FA[j] *= a2 * cc;
+            }
         }
     }
-    __syncthreads();
-    // s_t = r_t + sum_i p-_i k_i^2 and ds_t = -sum_i dw_i w_i / s_t, a wave per token
-    for (int t = wv; t < C; t += NWV) {
-        float a = 0.f, d = 0.f;
-        const long row = tok0 + (long)t * H;
-        const bool in = t < L;
-        for (int j = lane; j < DK; j += WAVE) {
-            const float kj = to_f32(M.kv[t][j]);
-            a += M.pm[t][j] * kj * kj;
-            if (in)
-                d += P.dw_out[row * DK + j] * P.w_f32[row * DK + j];
-        }
-        a = wave_sum(a);
-        d = wave_sum(d);
-        if (lane == 0) {
-            const float sv = M.r[t] + a;
-            M.s[t] = sv;
-            M.ds[t] = sv != 0.f ? -d / sv : 0.f;
-        }
-    }
-    __syncthreads();
+    float *dst = P.chain_map + (U.unit * DK + i0) * 2;
+    if constexpr (NJ == 2)
+        *reinterpret_cast<float4 *>(dst) = make_float4(FA[0], FB[0], FA[1], FB[1]);
+    else
+        *reinterpret_cast<float2 *>(dst) = make_float2(FA[0], FB[0]);
 }
 
-// The affine map of token t, channel i.
+// Kernel 3: from dp at the chunk end, the tokens in reverse: every token's
+// dp and gradients (dk and d log alpha added to the memory part's).
 template <typename E, int DK, int C>
-__device__ __forceinline__ void diag_token_map(const BackwardParams &P, const DiagChainSmem<E, DK, C> &M,
-                                               int t, int i, float dw, float &A, float &Bc) {
-    const float kk = to_f32(M.kv[t][i]), a = to_f32(M.av[t][i]);
-    const float pm = M.pm[t][i], r = M.r[t], sv = M.s[t], ds = M.ds[t];
-    const float du = sv != 0.f ? dw / sv : 0.f;
-    const float den = fmaf(P.mu * kk * kk, pm, r);
-    const float cc = den != 0.f ? (r * r) / (den * den) : 1.f;
-    A = a * a * cc;
-    Bc = a * a * (du * kk + ds * kk * kk);
-}
-
-// Kernel 1: one workgroup (thread per channel) per (head, chunk): chunk maps
-// to chain_map [bh][c][i][2].
-template <typename E, int DK, int C>
-__global__ __launch_bounds__(DK) void diag_chain_map_kernel(BackwardParams P) {
-    __shared__ DiagChainSmem<E, DK, C> M;
-    const int NC = (P.T + C - 1) / C;
-    const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
-    diag_chain_setup<E, DK, C>(P, bh, c, NC, M);
-    const int i = threadIdx.x;
-    const int b = bh / P.H, h = bh % P.H, c0 = c * C, L = min(C, P.T - c0);
-    const long tok0 = ((long)b * P.T + c0) * P.H + h;
-    float A = 1.f, Bc = 0.f;                            // f_t o ... o f_{C-1}
-    for (int t = L - 1; t >= 0; --t) {
-        float at, bt;
-        diag_token_map<E, DK, C>(P, M, t, i, P.dw_out[(tok0 + (long)t * P.H) * DK + i], at, bt);
-        Bc = fmaf(at, Bc, bt);
-        A *= at;
-    }
-    float *dst = P.chain_map + (((long)bh * NC + c) * DK + i) * 2;
-    dst[0] = A;
-    dst[1] = Bc;
-}
-
-// Kernel 2: one thread per (head, channel), the chunk maps from the last
-// chunk back: dp at every chunk end, and dp0.
-__global__ __launch_bounds__(256) void diag_chain_scan_kernel(BackwardParams P) {
-    const long x = (long)blockIdx.x * 256 + threadIdx.x;
-    const int DK = P.dk;
-    if (x >= (long)P.B * P.H * DK)
+__global__ __launch_bounds__(256) void diag_chain_grad_kernel(BackwardParams P) {
+    constexpr int NJ = DK / WAVE, G = 4;
+    DiagUnit U;
+    if (!diag_unit<E>(P, C, U))
         return;
-    const long bh = x / DK;
-    const int i = (int)(x % DK);
-    const int NC = (P.T + P.chunk - 1) / P.chunk;
-    float dp = P.dp_out ? P.dp_out[bh * DK + i] : 0.f;
-    for (int c = NC - 1; c >= 0; --c) {
-        const long u = (bh * NC + c) * DK + i;
-        P.chain_dp[u] = dp;
-        dp = fmaf(P.chain_map[u * 2], dp, P.chain_map[u * 2 + 1]);
-    }
-    if (P.dp0)
-        P.dp0[bh * DK + i] = dp;
-}
-
-// Kernel 3: the per-token gradients of the chain.
-template <typename E, int DK, int C>
-__global__ __launch_bounds__(DK) void diag_chain_grad_kernel(BackwardParams P) {
-    __shared__ DiagChainSmem<E, DK, C> M;
-    const int NC = (P.T + C - 1) / C;
-    const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
-    diag_chain_setup<E, DK, C>(P, bh, c, NC, M);
-    const int i = threadIdx.x, lane = i & (WAVE - 1), wv = i / WAVE;
-    constexpr int NWV = DK / WAVE;
-    const int b = bh / P.H, h = bh % P.H, c0 = c * C, L = min(C, P.T - c0);
-    const long tok0 = ((long)b * P.T + c0) * P.H + h;
+    const int lane = threadIdx.x & (WAVE - 1), i0 = lane * NJ;
+    const long H = P.H;
+    const E *gk = static_cast<const E *>(P.k);
+    const E *ga = static_cast<const E *>(P.alpha);
+    const E *gx = static_cast<const E *>(P.xi);
     const float mu = P.mu;
-    float dp = P.chain_dp[((long)bh * NC + c) * DK + i];
-    for (int t = L - 1; t >= 0; --t) {
-        const long rt = tok0 + (long)t * P.H;
-        const float kk = to_f32(M.kv[t][i]), a = to_f32(M.av[t][i]);
-        const float pm = M.pm[t][i], pp = M.pp[t][i], r = M.r[t], sv = M.s[t], ds = M.ds[t];
-        const float du = sv != 0.f ? P.dw_out[rt * DK + i] / sv : 0.f;
-        const float den = fmaf(mu * kk * kk, pm, r);
-        float dpm = du * kk + ds * kk * kk;
-        float dki = du * pm + 2.f * ds * pm * kk;
-        float drp = 0.f;
-        if (den != 0.f) {
-            const float d2 = den * den;
-            dpm += dp * r * r / d2;
-            dki -= 2.f * dp * mu * pm * pm * r * kk / d2;
-            drp = dp * mu * pm * pm * kk * kk / d2;
-        } else {
-            dpm += dp;
+    float dp[NJ];
+    ld_ch<NJ>(P.chain_dp + U.unit * DK + i0, dp);
+#pragma unroll 1
+    for (int tb = (U.L - 1) / G * G; tb >= 0; tb -= G) {
+        float kk[G][NJ], aa[G][NJ], xx[G][NJ], dw[G][NJ], pv[G][NJ], gk_[G][NJ], gl[G][NJ];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const long o = (U.tok0 + (long)(tb + g) * H) * DK + i0;
+            if (tb + g < U.L) {
+                ld_ch<NJ>(gk + o, kk[g]);
+                ld_ch<NJ>(ga + o, aa[g]);
+                ld_ch<NJ>(gx + o, xx[g]);
+                ld_ch<NJ>(P.dw_out + o, dw[g]);
+                ld_ch<NJ>(P.pp + o, pv[g]);
+                ld_ch<NJ>(P.dk_ + o, gk_[g]);
+                ld_ch<NJ>(P.dla + o, gl[g]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    kk[g][j] = 0.f; aa[g][j] = 1.f; xx[g][j] = 0.f; dw[g][j] = 0.f;
+                    pv[g][j] = 0.f; gk_[g][j] = 0.f; gl[g][j] = 0.f;
+                }
+            }
         }
-        M.pp[t][i] = drp;                 // pp[t][i] is read only above: dr parts
-        P.dk_[rt * DK + i] += dki;
-        P.dla[rt * DK + i] += 2.f * a * a * pp * dpm;
-        P.dxi[rt * DK + i] = dpm;
-        dp = a * a * dpm;
-    }
-    __syncthreads();
-    for (int t = wv; t < L; t += NWV) {
-        float x = 0.f;
-        for (int j = lane; j < DK; j += WAVE)
-            x += M.pp[t][j];
-        x = wave_sum(x);
-        if (lane == 0)
-            P.dr[tok0 + (long)t * P.H] = M.ds[t] + x;
+        float drs[G];
+#pragma unroll
+        for (int g = G - 1; g >= 0; --g) {
+            const int t = tb + g;
+            const float r = lane_bcast(U.r, t), invs = lane_bcast(U.invs, t);
+            const float ds = lane_bcast(U.ds, t);
+            float dxi[NJ];
+            drs[g] = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float k = kk[g][j], a2 = aa[g][j] * aa[g][j], pp = pv[g][j];
+                const float pm = fmaf(a2, pp, xx[g][j]);
+                const float den = fmaf(mu * k * k, pm, r);
+                const float du = dw[g][j] * invs;
+                float dpm = fmaf(ds * k, k, du * k);
+                float dki = fmaf(2.f * ds * pm, k, du * pm);
+                if (den != 0.f) {
+                    const float q = dp[j] / (den * den);
+                    dpm = fmaf(q, r * r, dpm);
+                    dki -= 2.f * q * mu * pm * pm * r * k;
+                    drs[g] = fmaf(q * mu * pm * pm, k * k, drs[g]);
+                } else {
+                    dpm += dp[j];
+                }
+                gk_[g][j] += dki;
+                gl[g][j] = fmaf(2.f * a2 * pp, dpm, gl[g][j]);
+                dxi[j] = dpm;
+                dp[j] = a2 * dpm;
+            }
+            if (t < U.L) {
+                const long o = (U.tok0 + (long)t * H) * DK + i0;
+                st_ch<NJ>(P.dk_ + o, gk_[g]);
+                st_ch<NJ>(P.dla + o, gl[g]);
+                st_ch<NJ>(P.dxi + o, dxi);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int t = tb + g;
+            const float x = wave_sum(drs[g]);
+            if (lane == 0 && t < U.L)
+                P.dr[U.tok0 + (long)t * H] = lane_bcast(U.ds, t) + x;
+        }
     }
 }
 
 template <typename E, int DK, int C>
 static hipError_t launch_diag_chain(const BackwardParams &P, hipStream_t st) {
     const long bh = (long)P.B * P.H, nc = (P.T + C - 1) / C;
+    const dim3 g((unsigned)((bh * nc + 3) / 4)), blk(256);
     if (nc > 0) {
-        hipLaunchKernelGGL((diag_chain_map_kernel<E, DK, C>), dim3((unsigned)(bh * nc)), dim3(DK),
-                           0, st, P);
+        hipLaunchKernelGGL((diag_chain_map_kernel<E, DK, C>), g, blk, 0, st, P);
         if (hipError_t e = hipGetLastError())
             return e;
     }
-    hipLaunchKernelGGL(diag_chain_scan_kernel, dim3((unsigned)((bh * DK + 255) / 256)),
-                       dim3(256), 0, st, P);
+    hipLaunchKernelGGL(chain_scan_kernel, dim3((unsigned)((bh * DK + 3) / 4)), dim3(256), 0, st,
+                       P, DK);
     if (hipError_t e = hipGetLastError())
         return e;
     if (nc > 0)
-        hipLaunchKernelGGL((diag_chain_grad_kernel<E, DK, C>), dim3((unsigned)(bh * nc)), dim3(DK),
-                           0, st, P);
+        hipLaunchKernelGGL((diag_chain_grad_kernel<E, DK, C>), g, blk, 0, st, P);
     return hipGetLastError();
 }
 
 template <typename E>
 static hipError_t launch_diag_chain_e(const BackwardParams &P, hipStream_t st) {
-    if (P.dk == 128 && P.chunk == 64) {
-        if constexpr (sizeof(E) == 2)
-            return launch_diag_chain<E, 128, 64>(P, st);
-        return hipErrorInvalidValue;
-    }
+    if (P.dk == 128 && P.chunk == 64) return launch_diag_chain<E, 128, 64>(P, st);
     if (P.dk == 128 && P.chunk == 32) return launch_diag_chain<E, 128, 32>(P, st);
     if (P.dk == 64 && P.chunk == 64) return launch_diag_chain<E, 64, 64>(P, st);
     if (P.dk == 64 && P.chunk == 32) return launch_diag_chain<E, 64, 32>(P, st);
@@ -1297,8 +1349,8 @@ static hipError_t launch_bwd_e(const BackwardParams &P, hipStream_t st) {
             if (hipError_t e = hipGetLastError())
                 return e;
         }
-        hipLaunchKernelGGL(iso_chain_scan_kernel, dim3((unsigned)((bh + 63) / 64)), dim3(64), 0,
-                           st, P);
+        hipLaunchKernelGGL(chain_scan_kernel, dim3((unsigned)((bh + 3) / 4)), dim3(256), 0, st,
+                           P, 1);
         if (hipError_t e = hipGetLastError())
             return e;
         if (nc > 0) {

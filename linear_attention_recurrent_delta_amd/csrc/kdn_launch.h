@@ -46,8 +46,10 @@ struct PrefillParams {
     // Isotropic KDN, gradient computation: the derived write strengths
     // [B, T, H] (float32) are saved here by the prep kernel (null otherwise).
     float *beta_out;
-    // Diagonal KDN, gradient computation: the gains w [B, T, H, dk] (float32).
+    // Diagonal KDN, gradient computation: the gains w [B, T, H, dk] and the
+    // reciprocal innovation variances 1/s [B, T, H] (0 where s = 0), float32.
     float *w_out;
+    float *invs_out;
     int cus;           // compute units of the current device
 };
 
@@ -65,6 +67,9 @@ struct BackwardParams {
     const float *beta_f32;                  // isotropic KDN: derived write strengths
     const float *w_f32;                     // diagonal KDN: gains [B, T, H, dk]
     float *dw_out;                          // diagonal KDN: dL/dw [B, T, H, dk]
+    const float *invs;                      // diagonal KDN: 1/s [B, T, H] (0 if s = 0)
+    float *wdw;                             // diagonal KDN: sum_i w_i dw_i [B, T, H]
+    float *pp;                              // diagonal KDN: variance before each token [B,T,H,dk]
     const float *S0;                        // may be null (zero)
     const void *dO;                         // [B, T, H, dv] call dtype
     const float *dS_out;                    // [B, H, dk, dv], may be null (zero)

@@ -580,7 +580,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                 acc += __shfl_xor(acc, off, WAVE);
             if (tid < TPR * C && part == 0) {
                 const float s = s_r[t] + acc;
-                s_invs[t] = (s != 0.f) ? 1.f / s : 0.f;
+                const float invs = (s != 0.f) ? 1.f / s : 0.f;
+                s_invs[t] = invs;
+                if (PREP && P.invs_out && t < L)     // for the gradient pass
+                    P.invs_out[tok0 + (long)t * H] = invs;
             }
         }
         if constexpr (ISO) {
