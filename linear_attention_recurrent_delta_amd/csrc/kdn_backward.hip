@@ -312,7 +312,13 @@ struct BwdLayout {
     static_assert(TOTAL <= 163840, "backward LDS budget");
 };
 
-template <typename E, int VAR, int DK, int C, int DVH>
+// Source of the write vector w of each token: beta k with beta given (the
+// write-strength variants), beta k with beta derived by the forward pass
+// (isotropic KDN, float32), or the gain saved by the forward pass (diagonal
+// KDN).  A template argument, so every load of the kernel is unconditional.
+enum WriteSrc { WS_BETA = 0, WS_BETA_F32 = 1, WS_GAIN = 2 };
+
+template <typename E, int VAR, int DK, int C, int DVH, int WSRC>
 __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     using LY = BwdLayout<E, DK, C, DVH>;
     constexpr int NT = 512, NW = 8;
@@ -372,27 +378,12 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     auto row = [&](int t) { return tok0 + (long)t * H; };
     // write strength of token t (isotropic KDN: derived, saved by the forward)
     auto beta_at = [&](int t) {
-        return P.beta_f32 ? P.beta_f32[row(t)] : to_f32(gb[row(t)]);
+        return WSRC == WS_BETA_F32 ? P.beta_f32[row(t)] : to_f32(gb[row(t)]);
     };
     // diagonal KDN: the write vector is the gain w (saved by the forward),
     // and dw goes out for the variance chain instead of into dk and dbeta
-    const bool gw = P.w_f32 != nullptr;
+    constexpr bool gw = WSRC == WS_GAIN;
 
-    // ---- chunk operands from the forward record
-    {
-        RecUnits<E, DK, C, NT> wt;
-        RecUnits<E, C, DK, NT> kd;
-        RecUnits<E, C, C, NT> tm, aq;
-        wt.load(rec + LW.off_wdt, tid);
-        kd.load(rec + LW.off_kd, tid);
-        tm.load(rec + LW.off_tm, tid);
-        aq.load(rec + LW.off_aqk, tid);
-        wt.template store<true>(WR, PK, 1.f, tid);     // W~     [s][i]
-        kd.template store<false>(KR, PK, 1.f, tid);    // K~     [t][i]
-        tm.template store<false>(TR, PC, 1.f, tid);    // T      [t][s]
-        tm.template store<true>(TT, PC, 1.f, tid);     // T^T    [t][s]
-        aq.template store<true>(AQT, PC, 1.f, tid);    // A_qk^T [s][t]
-    }
     if (tid < DK) {
         s_gc[tid] = DECAY ? reinterpret_cast<const float *>(rec + LW.off_gc)[tid] : 1.f;
         s_dgc[tid] = 0.f;
@@ -423,14 +414,35 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     constexpr int G4 = DVH / 4, NS4 = DK * G4 / NT;
     static_assert(NS4 * NT == DK * G4, "state staging");
     constexpr int NO4 = (C * G4 + NT - 1) / NT;
-    // S^T (or dS'^T) of columns [jh, jh + DVH) into SB1 as [j][i]; the values
-    // stay in v for the row-major copy later in the half
-    auto stage_t = [&](const float *src, int jh, float (&v)[NS4][4]) {
+    // A half's global inputs, all issued before any is used: S and dS' of
+    // its columns, dO, and V in the U-tile layout.  Rows past the sequence
+    // end read the last row (every load unconditional, so they are all in
+    // flight together) and are zeroed where used.
+    float sv[NS4][4], dsv[NS4][4], dov[NO4][4], vv[NSH][4];
+    auto load_half = [&](int jh) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
             const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
-            gload4(src + (long)i * DV + jh + j4, v[n]);
+            gload4(Sg + (long)i * DV + jh + j4, sv[n]);
+            gload4(dSg + (long)i * DV + jh + j4, dsv[n]);
         }
+#pragma unroll
+        for (int n = 0; n < NO4; ++n) {
+            const int x = tid + NT * n, t = min(x / G4, L - 1), j4 = (x % G4) * 4;
+            gload4(gdo + row(t) * DV + jh + j4, dov[n]);
+        }
+#pragma unroll
+        for (int k = 0; k < NSH; ++k) {
+            const int tau = wv + NW * k;
+            const int mt = tau / NTH, nj = tau % NTH;
+            const int j = nj * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vv[k][r] = to_f32(gv[row(min(t0 + r, L - 1)) * DV + jh + j]);
+        }
+    };
+    // S^T (or dS'^T) of the half into SB1 as [j][i]
+    auto stage_t = [&](const float (&v)[NS4][4]) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
             const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
@@ -440,29 +452,37 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
         }
     };
 
+    // ---- chunk operands from the forward record, with the first half's
+    //      inputs in flight behind them
+    {
+        RecUnits<E, DK, C, NT> wt;
+        RecUnits<E, C, DK, NT> kd;
+        RecUnits<E, C, C, NT> tm, aq;
+        wt.load(rec + LW.off_wdt, tid);
+        kd.load(rec + LW.off_kd, tid);
+        tm.load(rec + LW.off_tm, tid);
+        aq.load(rec + LW.off_aqk, tid);
+        load_half(0);
+        wt.template store<true>(WR, PK, 1.f, tid);     // W~     [s][i]
+        kd.template store<false>(KR, PK, 1.f, tid);    // K~     [t][i]
+        tm.template store<false>(TR, PC, 1.f, tid);    // T      [t][s]
+        tm.template store<true>(TT, PC, 1.f, tid);     // T^T    [t][s]
+        aq.template store<true>(AQT, PC, 1.f, tid);    // A_qk^T [s][t]
+    }
     for (int jh = 0; jh < DV; jh += DVH) {
-        float sv[NS4][4], dsv[NS4][4];
         // ---- S^T of the half, dO^T and dO
-        stage_t(Sg, jh, sv);
-        {
-            float d[NO4][4];
+        stage_t(sv);
 #pragma unroll
-            for (int n = 0; n < NO4; ++n) {
-                const int x = tid + NT * n, t = x / G4, j4 = (x % G4) * 4;
-                if (((C * G4) % NT == 0 || x < C * G4) && t < L)
-                    gload4(gdo + row(t) * DV + jh + j4, d[n]);
-                else
-                    d[n][0] = d[n][1] = d[n][2] = d[n][3] = 0.f;
+        for (int n = 0; n < NO4; ++n) {
+            const int x = tid + NT * n, t = x / G4, j4 = (x % G4) * 4;
+            if (!((C * G4) % NT == 0 || x < C * G4)) continue;
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d[e] = t < L ? dov[n][e] : 0.f;
+                DOT[(j4 + e) * PC + t] = from_f32<E>(d[e]);
             }
-#pragma unroll
-            for (int n = 0; n < NO4; ++n) {
-                const int x = tid + NT * n, t = x / G4, j4 = (x % G4) * 4;
-                if (!((C * G4) % NT == 0 || x < C * G4)) continue;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    DOT[(j4 + e) * PC + t] = from_f32<E>(d[n][e]);
-                lds_stn<4>(DOH + t * PH + j4, d[n]);
-            }
+            lds_stn<4>(DOH + t * PH + j4, d);
         }
         __syncthreads();
         // ---- U = V - K~ S  -> U^T
@@ -477,7 +497,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             float u[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                u[r] = (t0 + r < L ? to_f32(gv[row(t0 + r) * DV + jh + j]) : 0.f) - acc[r];
+                u[r] = (t0 + r < L ? vv[k][r] : 0.f) - acc[r];
             lds_stn<4>(UE + j * PC + t0, u);
         }
         __syncthreads();
@@ -494,7 +514,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             for (int r = 0; r < 4; ++r)
                 EH[(t0 + r) * PH + j] = from_f32<E>(acc[r]);
         }
-        stage_t(dSg, jh, dsv);
+        stage_t(dsv);
         __syncthreads();
         // ---- dE = A_qk^T dO + W~ dS'  -> dE^T
 #pragma unroll
@@ -544,6 +564,8 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                 }
             }
         }
+        if (jh + DVH < DV)
+            load_half(jh + DVH);                       // in flight during the sums
         __syncthreads();
         // ---- sums over the half's columns
 #pragma unroll
@@ -577,17 +599,44 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     // decays into GAM (a_t per channel; 1 past the sequence end)
     constexpr int GK4 = DK / 4, NK4 = C * GK4 / NT;
     static_assert(NK4 * NT == C * GK4, "chunk tile units");
+    static_assert(NS3 * NW == NB * NTI, "one element set per thread");
+    // The thread's elements of the [C][DK] tiles (tile tau = wv + NW k, row r:
+    // t = mt 16 + (lane >> 4) 4 + r, i = ni 16 + (lane & 15)): k, q and the
+    // gain (diagonal KDN) or beta, read once with the decays for the scaled
+    // operands and the elementwise step.
+    float ek[NS3][4], eq[NS3][4], ew[NS3][4];
+    {
+        float a4[NK4][4];
 #pragma unroll
-    for (int n = 0; n < NK4; ++n) {
-        const int x = tid + NT * n, t = x / GK4, i4 = (x % GK4) * 4;
-        float a[4] = {1.f, 1.f, 1.f, 1.f};
-        if (t < L) {
+        for (int n = 0; n < NK4; ++n) {
+            const int x = tid + NT * n, t = min(x / GK4, L - 1), i4 = (x % GK4) * 4;
+            a4[n][0] = a4[n][1] = a4[n][2] = a4[n][3] = 1.f;
             if (VAR == KDA)
-                gload4(ga + row(t) * DK + i4, a);
+                gload4(ga + row(t) * DK + i4, a4[n]);
             if (VAR == GATED_DELTANET)
-                a[0] = a[1] = a[2] = a[3] = to_f32(ga[row(t)]);
+                a4[n][0] = a4[n][1] = a4[n][2] = a4[n][3] = to_f32(ga[row(t)]);
         }
-        *reinterpret_cast<float4 *>(GAM + t * PF + i4) = make_float4(a[0], a[1], a[2], a[3]);
+#pragma unroll
+        for (int k = 0; k < NS3; ++k) {
+            const int tau = wv + NW * k;
+            const int mt = tau / NTI, ni = tau % NTI;
+            const int i = ni * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = min(mt * 16 + (lane >> 4) * 4 + r, L - 1);
+                ek[k][r] = to_f32(gk[row(t) * DK + i]);
+                eq[k][r] = to_f32(gq[row(t) * DK + i]);
+                ew[k][r] = gw ? P.w_f32[row(t) * DK + i] : beta_at(t);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NK4; ++n) {
+            const int x = tid + NT * n, t = x / GK4, i4 = (x % GK4) * 4;
+            const bool in = t < L;
+            *reinterpret_cast<float4 *>(GAM + t * PF + i4) =
+                make_float4(in ? a4[n][0] : 1.f, in ? a4[n][1] : 1.f, in ? a4[n][2] : 1.f,
+                            in ? a4[n][3] : 1.f);
+        }
     }
     for (int x = tid; x < C * C; x += NT) {            // blocks above the diagonal
         const int t = x / C, s = x % C;
@@ -650,32 +699,27 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             *s_flag = 1;
     }
     __syncthreads();
-    // W'^T = (beta k / gamma)^T, Q~^T = (gamma q)^T, K~^T = (gamma k)^T
+    // W'^T = (w / gamma)^T, Q~^T = (gamma q)^T, K~^T = (gamma k)^T, four
+    // consecutive tokens of one channel per store
 #pragma unroll
-    for (int n = 0; n < NK4; ++n) {
-        const int x = tid + NT * n, t = x / GK4, i4 = (x % GK4) * 4;
-        float kk[4] = {0.f, 0.f, 0.f, 0.f}, qq[4] = {0.f, 0.f, 0.f, 0.f};
-        float ww[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t < L) {
-            gload4(gk + row(t) * DK + i4, kk);
-            gload4(gq + row(t) * DK + i4, qq);
-            if (gw) {
-                gload4(P.w_f32 + row(t) * DK + i4, ww);
-            } else {
-                const float bt = beta_at(t);
+    for (int k = 0; k < NS3; ++k) {
+        const int tau = wv + NW * k;
+        const int mt = tau / NTI, ni = tau % NTI;
+        const int i = ni * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
+        float wp[4], qt[4], kt[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ww[e] = bt * kk[e];
-            }
+        for (int r = 0; r < 4; ++r) {
+            if (t0 + r >= L)                           // rows past the end: zero
+                ek[k][r] = eq[k][r] = ew[k][r] = 0.f;
+            const float g = GAM[(t0 + r) * PF + i];
+            const float w = gw ? ew[k][r] : ew[k][r] * ek[k][r];
+            wp[r] = g > 0.f ? w / g : 0.f;
+            qt[r] = g * eq[k][r];
+            kt[r] = g * ek[k][r];
         }
-        const float4 g4 = *reinterpret_cast<const float4 *>(GAM + t * PF + i4);
-        const float g[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            WPT[(i4 + e) * PC + t] = from_f32<E>(g[e] > 0.f ? ww[e] / g[e] : 0.f);
-            QTT[(i4 + e) * PC + t] = from_f32<E>(g[e] * qq[e]);
-            KTT[(i4 + e) * PC + t] = from_f32<E>(g[e] * kk[e]);
-        }
+        lds_stn<4>(WPT + i * PC + t0, wp);
+        lds_stn<4>(QTT + i * PC + t0, qt);
+        lds_stn<4>(KTT + i * PC + t0, kt);
     }
     __syncthreads();
     const bool exact = *s_flag != 0;
@@ -765,10 +809,9 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             const int t = mt * 16 + (lane >> 4) * 4 + r;
             const bool in = t < L;
             const float g = GAM[t * PF + i];
-            const float kk = in ? to_f32(gk[row(t) * DK + i]) : 0.f;
-            const float qq = in ? to_f32(gq[row(t) * DK + i]) : 0.f;
-            const float bt = (in && !gw) ? beta_at(t) : 0.f;
-            const float wv = in ? (gw ? P.w_f32[row(t) * DK + i] : bt * kk) : 0.f;
+            const float kk = ek[k][r], qq = eq[k][r];
+            const float bt = gw ? 0.f : ew[k][r];
+            const float wv = gw ? ew[k][r] : bt * kk;
             const float dq = exact ? dq3[k][r] : g * dq3[k][r];
             const float dkd = exact ? dk3[k][r] : g * dk3[k][r];
             const float dw = exact ? dw3[k][r] : (g > 0.f ? dw3[k][r] / g : 0.f);
@@ -1307,7 +1350,20 @@ static hipError_t launch_bwd_vc(const BackwardParams &P, hipStream_t st) {
         return hipSuccess;
     constexpr int DVH = sizeof(E) == 2 ? 64 : 32;
     const dim3 grid((unsigned)(heads * nc)), block(512);
-    hipLaunchKernelGGL((backward_chunk_kernel<E, VAR, DK, C, DVH>), grid, block, 0, st, P);
+    if constexpr (VAR == KDA) {
+        if (P.w_f32)
+            hipLaunchKernelGGL((backward_chunk_kernel<E, VAR, DK, C, DVH, WS_GAIN>), grid, block,
+                               0, st, P);
+        else if (P.beta_f32)
+            hipLaunchKernelGGL((backward_chunk_kernel<E, VAR, DK, C, DVH, WS_BETA_F32>), grid,
+                               block, 0, st, P);
+        else
+            hipLaunchKernelGGL((backward_chunk_kernel<E, VAR, DK, C, DVH, WS_BETA>), grid, block,
+                               0, st, P);
+    } else {
+        hipLaunchKernelGGL((backward_chunk_kernel<E, VAR, DK, C, DVH, WS_BETA>), grid, block, 0,
+                           st, P);
+    }
     return hipGetLastError();
 }
 
