@@ -84,6 +84,25 @@ struct RecUnits {
     }
 };
 
+// Four consecutive elements of E from global memory, held raw (as loaded)
+// and converted where used, so no wait follows the load.
+template <typename E> struct Raw4;
+template <> struct Raw4<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const float4 *>(p); }
+    __device__ __forceinline__ float operator[](int e) const {
+        return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    }
+};
+template <> struct Raw4<bf16> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ float operator[](int e) const {
+        const uint32_t w = e < 2 ? v.x : v.y;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
 // Four consecutive elements of E from global memory as floats.
 __device__ __forceinline__ void gload4(const float *p, float (&f)[4]) {
     const float4 v = *reinterpret_cast<const float4 *>(p);
@@ -418,7 +437,9 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     // its columns, dO, and V in the U-tile layout.  Rows past the sequence
     // end read the last row (every load unconditional, so they are all in
     // flight together) and are zeroed where used.
-    float sv[NS4][4], dsv[NS4][4], dov[NO4][4], vv[NSH][4];
+    float sv[NS4][4], dsv[NS4][4];
+    Raw4<E> dov[NO4];
+    E vv[NSH][4];
     auto load_half = [&](int jh) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
@@ -429,7 +450,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int n = 0; n < NO4; ++n) {
             const int x = tid + NT * n, t = min(x / G4, L - 1), j4 = (x % G4) * 4;
-            gload4(gdo + row(t) * DV + jh + j4, dov[n]);
+            dov[n].load(gdo + row(t) * DV + jh + j4);
         }
 #pragma unroll
         for (int k = 0; k < NSH; ++k) {
@@ -438,7 +459,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             const int j = nj * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                vv[k][r] = to_f32(gv[row(min(t0 + r, L - 1)) * DV + jh + j]);
+                vv[k][r] = gv[row(min(t0 + r, L - 1)) * DV + jh + j];
         }
     };
     // S^T (or dS'^T) of the half into SB1 as [j][i]
@@ -497,7 +518,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
             float u[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                u[r] = (t0 + r < L ? vv[k][r] : 0.f) - acc[r];
+                u[r] = (t0 + r < L ? to_f32(vv[k][r]) : 0.f) - acc[r];
             lds_stn<4>(UE + j * PC + t0, u);
         }
         __syncthreads();
@@ -556,11 +577,17 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                     // sum over the G4 lanes of key channel i, then one atomic
                     float p = sv[n][0] * dsv[n][0] + sv[n][1] * dsv[n][1] +
                               sv[n][2] * dsv[n][2] + sv[n][3] * dsv[n][3];
+                    if constexpr (G4 == 16) {
+                        p = row16_sum_last(p);
+                        if (lane % 16 == 15)
+                            atomicAdd(&s_sds[i], p);
+                    } else {
 #pragma unroll
-                    for (int off = G4 / 2; off >= 1; off >>= 1)
-                        p += __shfl_xor(p, off, WAVE);
-                    if (lane % G4 == 0)
-                        atomicAdd(&s_sds[i], p);
+                        for (int off = G4 / 2; off >= 1; off >>= 1)
+                            p += __shfl_xor(p, off, WAVE);
+                        if (lane % G4 == 0)
+                            atomicAdd(&s_sds[i], p);
+                    }
                 }
             }
         }

@@ -51,6 +51,16 @@ __device__ __forceinline__ void load16<bf16>(const bf16 *p, float (&out)[8]) {
     }
 }
 
+// Sum over each row of 16 lanes by DPP row shifts (no LDS traffic); lane 15
+// of the row holds the total, the other lanes partial sums.
+__device__ __forceinline__ float row16_sum_last(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+    return x;
+}
+
 // Sum over the 64 lanes of a wave; every lane gets the total.  Fixed
 // butterfly order, so results are deterministic.
 __device__ __forceinline__ float wave_sum(float x) {
