@@ -9,9 +9,9 @@ resident in HBM.  Rank 0 prints ONE JSON line with the headline value
 (prefill tokens/s), the roofline of the prefill kernel (HBM-bound by its
 algorithmic bytes; the MFMA fraction of its algorithmic flops is reported
 next to it), the fp64 oracle timed on the host cores, and the other
-workloads (KDA, diagonal-KDN and isotropic-KDN prefill, the Gated DeltaNet
-gradient call, diagonal-KDN decode, 16-token multi-token decode) each with its
-own roofline.
+workloads (KDA, diagonal-KDN and isotropic-KDN prefill, the gradient calls of
+Gated DeltaNet, KDA and both KDN variants, diagonal-KDN decode, 16-token
+multi-token decode) each with its own roofline.
 """
 from __future__ import annotations
 
@@ -64,15 +64,22 @@ def prefill_flops_per_head_token(C, dk, dv):
 
 
 def backward_bytes(variant, B, T, H, dk, dv, es):
-    """Gradient call: q, k, v, dO (and alpha, beta) read in the call dtype;
-    dq, dk, dv, dbeta (and dlog_alpha) written as float32; S0 = dS_out = NULL."""
+    """Gradient call: q, k, v, dO and the gates (beta, alpha; KDN: alpha, the
+    noises and p0) read in the call dtype (p0 float32); dq, dk, dv and the
+    gates' gradients written as float32; S0 = dS_out = dp_out = NULL."""
     tok = B * T * H
-    n = tok * (2 * dk + 2 * dv) * es + tok * es             # q, k, v, dO, beta
-    n += tok * (2 * dk + dv) * 4 + tok * 4                  # dq, dk, dv, dbeta
+    kdn = variant in ("diag_kdn", "iso_kdn")
+    n = tok * (2 * dk + 2 * dv) * es                        # q, k, v, dO
+    n += tok * (2 * dk + dv) * 4                            # dq, dk, dv
+    if not kdn:
+        n += tok * es + tok * 4                             # beta, dbeta
     if variant == "gated_deltanet":
-        n += tok * es + tok * 4
-    elif variant == "kda":
+        n += tok * es + tok * 4                             # alpha, dlog_alpha
+    elif variant != "deltanet":
         n += tok * dk * es + tok * dk * 4
+    if kdn:
+        n += tok * dk * es + tok * es + tok * dk * 4 + tok * 4   # xi, r, dxi, dr
+        n += 2 * B * H * (dk if variant == "diag_kdn" else 1) * 4  # p0, dp0
     n += B * H * dk * dv * 4                                # dS0
     return n
 
@@ -196,11 +203,14 @@ def bench_backward(name, steps, warmup, torch, kdn, synth):
     d_o = torch.randn((B, T, H, dv), generator=g, device="cuda").to(inp["q"].dtype)
     f = torch.float32
     new = lambda *shape: torch.empty(shape, dtype=f, device="cuda")
+    kdn_var = variant in ("diag_kdn", "iso_kdn")
     out = dict(dq=new(B, T, H, dk), dk=new(B, T, H, dk), dv=new(B, T, H, dv),
                dlog_alpha=None if variant == "deltanet" else (
                    new(B, T, H) if variant == "gated_deltanet" else new(B, T, H, dk)),
-               dbeta=new(B, T, H), dS0=new(B, H, dk, dv), dproc_noise=None,
-               dobs_noise=None, dp0=None)
+               dbeta=None if kdn_var else new(B, T, H), dS0=new(B, H, dk, dv),
+               dproc_noise=new(B, T, H, dk) if kdn_var else None,
+               dobs_noise=new(B, T, H) if kdn_var else None,
+               dp0=torch.empty_like(inp["p0"]) if kdn_var else None)
     dt = 1 if c["dtype"] == "bf16" else 0
     C = kdn.kdn_chunk_prefill_chunk_size(dt, dk, dv, 0)
     n = kdn.kdn_chunk_prefill_backward_workspace_size(kdn.VARIANTS[variant], dt, B, T, H,
@@ -209,8 +219,9 @@ def bench_backward(name, steps, warmup, torch, kdn, synth):
 
     def step():
         kdn.prefill_backward(variant, inp["q"], inp["k"], inp["v"], d_o,
-                             alpha=inp.get("alpha"), beta=inp.get("beta"), out=out,
-                             workspace=ws)
+                             alpha=inp.get("alpha"), beta=inp.get("beta"),
+                             proc_noise=inp.get("xi"), obs_noise=inp.get("r"),
+                             p0=inp.get("p0"), out=out, workspace=ws)
 
     wall, gpu = time_launches(step, steps, warmup, torch)
     es = 2 if c["dtype"] == "bf16" else 4
@@ -421,8 +432,9 @@ def main():
             w[f"{name}_prefill"] = bench_prefill(name, max(3, args.steps // 2),
                                                  args.warmup, torch, kdn, synth,
                                                  args.schedule)
-        w["gated_deltanet_backward"] = bench_backward("gated_deltanet", max(3, args.steps // 2),
-                                                      args.warmup, torch, kdn, synth)
+        for name in ("gated_deltanet", "kda", "diag_kdn", "iso_kdn"):
+            w[f"{name}_backward"] = bench_backward(name, max(3, args.steps // 2),
+                                                   args.warmup, torch, kdn, synth)
         w["decode_diag_kdn"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
         w["verify16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth)
         out["workloads"] = w

@@ -68,6 +68,30 @@ struct RecUnits {
                 *reinterpret_cast<uint4 *>(dst + row * pitch + g * 32 + (l >> 4) * 8) = u[n];
                 continue;
             }
+            if (TRANS && sizeof(E) == 2) {
+                // Lanes l and l^1 hold rows r and r+1 (r even) of the same 8
+                // columns: they swap halves (one DPP quad permute per dword),
+                // then each writes 4 dwords, rows (r, r+1) of one column each
+                // (the even lane columns 0-3, the odd lane columns 4-7).
+                const bool odd = l & 1;
+                const uint32_t flip = sgn < 0.f ? 0x80008000u : 0u;   // exact bf16 negation
+                const uint32_t w0 = u[n].x ^ flip, w1 = u[n].y ^ flip;
+                const uint32_t w2 = u[n].z ^ flip, w3 = u[n].w ^ flip;
+                const uint32_t m0 = odd ? w2 : w0, m1 = odd ? w3 : w1;   // kept
+                const uint32_t s0 = odd ? w0 : w2, s1 = odd ? w1 : w3;   // sent
+                const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0xB1, 0xf, 0xf, false);
+                const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0xB1, 0xf, 0xf, false);
+                const uint32_t lo0 = odd ? r0 : m0, lo1 = odd ? r1 : m1;   // row r
+                const uint32_t hi0 = odd ? m0 : r0, hi1 = odd ? m1 : r1;   // row r + 1
+                const int col = g * 32 + (l >> 4) * 8 + (odd ? 4 : 0);
+                uint32_t *d = reinterpret_cast<uint32_t *>(dst + col * pitch + (row & ~1));
+                const int pw = pitch / 2;                                  // dwords per row
+                d[0] = (lo0 & 0xffffu) | (hi0 << 16);
+                d[pw] = (lo0 >> 16) | (hi0 & 0xffff0000u);
+                d[2 * pw] = (lo1 & 0xffffu) | (hi1 << 16);
+                d[3 * pw] = (lo1 >> 16) | (hi1 & 0xffff0000u);
+                continue;
+            }
             const uint4 v = u[n];
             const E *e = reinterpret_cast<const E *>(&v);
 #pragma unroll
@@ -187,14 +211,15 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
         X.tm.load(rec + LW.off_tm, tid);
         X.qd.load(rec + LW.off_qd, tid);
         X.kd.load(rec + LW.off_kd, tid);
-        X.gc = (DECAY && tid < DK) ? reinterpret_cast<const float *>(rec + LW.off_gc)[tid] : 1.f;
+        // every load unconditional (rows clamped into the sequence, zeroed
+        // where used), so all of them are in flight together
+        X.gc = DECAY ? reinterpret_cast<const float *>(rec + LW.off_gc)[tid % DK] : 1.f;
         const int L = min(C, T - c * C);
 #pragma unroll
         for (int n = 0; n < NDO; ++n) {
-            const int x = tid + NT * n, t = x / NV, j = x % NV;
+            const int x = tid + NT * n, t = min(x / NV, L - 1), j = x % NV;
             const long row = ((long)b * T + c * C + t) * H + h;
-            X.dov[n] = ((C * NV) % NT == 0 || x < C * NV) && t < L ? gdo[row * DV + v0 + j]
-                                                                  : from_f32<E>(0.f);
+            X.dov[n] = gdo[row * DV + v0 + j];
         }
     };
     Rec X;
@@ -220,11 +245,12 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
         X.kd.template store<true>(KT, PC, -1.f, tid);
         if (DECAY && tid < DK)
             GC[tid] = X.gc;
+        const int L = min(C, T - c * C);
 #pragma unroll
         for (int n = 0; n < NDO; ++n) {                // dO^T (rows past the end are 0)
             const int x = tid + NT * n;
             if ((C * NV) % NT == 0 || x < C * NV)
-                DOT[(x % NV) * PC + x / NV] = X.dov[n];
+                DOT[(x % NV) * PC + x / NV] = x / NV < L ? X.dov[n] : from_f32<E>(0.f);
         }
         if (c > 0)
             load(X, c - 1);                            // in flight during this chunk
@@ -1363,8 +1389,9 @@ static hipError_t launch_bwd_vc(const BackwardParams &P, hipStream_t st) {
     const long heads = (long)P.B * P.H;
     const long nc = (P.T + C - 1) / C;
     constexpr bool DECAY = VAR != DELTANET;
-    // reverse state pass: value blocks of 32 (bf16) or 16 columns
-    if (sizeof(E) == 2 && P.dv % 32 == 0) {
+    // reverse state pass: value blocks of 32 columns (bf16) when that gives a
+    // workgroup per compute unit, else of 16 (twice the sequential chains)
+    if (sizeof(E) == 2 && P.dv % 32 == 0 && heads * (P.dv / 32) >= P.cus) {
         const dim3 grid((unsigned)(heads * (P.dv / 32))), block(512);
         hipLaunchKernelGGL((backward_state_kernel<E, DECAY, DK, 32, C>), grid, block, 0, st, P);
     } else {
