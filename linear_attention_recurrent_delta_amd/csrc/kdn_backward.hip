@@ -184,7 +184,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 #pragma unroll
     for (int k = 0; k < NSS; ++k) {
         const int tau = wv + NW * k;
-        if (tau >= NTI * NTJ) continue;
+        if (NSS * NW != NTI * NTJ && tau >= NTI * NTJ) continue;
         const int i0 = (tau / NTJ) * 16 + (lane >> 4) * 4, j = (tau % NTJ) * 16 + (lane & 15);
         float s4[4];
 #pragma unroll
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSS; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NTI * NTJ) continue;
+            if (NSS * NW != NTI * NTJ && tau >= NTI * NTJ) continue;
             const int i0 = (tau / NTJ) * 16 + (lane >> 4) * 4, j = (tau % NTJ) * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSE; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NTC * NTJ) continue;
+            if (NSE * NW != NTC * NTJ && tau >= NTC * NTJ) continue;
             const int ms = tau / NTJ, nj = tau % NTJ;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_tile_k<E, C>(acc, AQT + ms * 16 * PC, PC, DOT + nj * 16 * PC, PC, lane);
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSE; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NTC * NTJ) continue;
+            if (NSE * NW != NTC * NTJ && tau >= NTC * NTJ) continue;
             const int mt = tau / NTJ, nj = tau % NTJ;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_tile_k<E, C>(acc, TT + mt * 16 * PC, PC, DET + nj * 16 * PC, PC, lane);
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSS; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NTI * NTJ) continue;
+            if (NSS * NW != NTI * NTJ && tau >= NTI * NTJ) continue;
             const int mi = tau / NTJ, nj = tau % NTJ;
             const int i0 = mi * 16 + (lane >> 4) * 4, j = nj * 16 + (lane & 15);
             if (DECAY) {
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSS; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NTI * NTJ) continue;
+            if (NSS * NW != NTI * NTJ && tau >= NTI * NTJ) continue;
             const int i0 = (tau / NTJ) * 16 + (lane >> 4) * 4, j = (tau % NTJ) * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -466,12 +466,13 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     float sv[NS4][4], dsv[NS4][4];
     Raw4<E> dov[NO4];
     E vv[NSH][4];
+    // Issued in the order of first use (S and dO, then V, then dS'), since a
+    // wave's loads complete in order.
     auto load_half = [&](int jh) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
             const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
             gload4(Sg + (long)i * DV + jh + j4, sv[n]);
-            gload4(dSg + (long)i * DV + jh + j4, dsv[n]);
         }
 #pragma unroll
         for (int n = 0; n < NO4; ++n) {
@@ -486,6 +487,11 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 vv[k][r] = gv[row(min(t0 + r, L - 1)) * DV + jh + j];
+        }
+#pragma unroll
+        for (int n = 0; n < NS4; ++n) {
+            const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
+            gload4(dSg + (long)i * DV + jh + j4, dsv[n]);
         }
     };
     // S^T (or dS'^T) of the half into SB1 as [j][i]
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSH; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTH) continue;
+            if (NSH * NW != NB * NTH && tau >= NB * NTH) continue;
             const int mt = tau / NTH, nj = tau % NTH;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_tile_k<E, DK>(acc, KR + mt * 16 * PK, PK, SB1 + nj * 16 * PK, PK, lane);
@@ -552,7 +558,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSH; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTH) continue;
+            if (NSH * NW != NB * NTH && tau >= NB * NTH) continue;
             const int mt = tau / NTH, nj = tau % NTH;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_tile_k<E, C>(acc, TR + mt * 16 * PC, PC, UE + nj * 16 * PC, PC, lane);
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSH; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTH) continue;
+            if (NSH * NW != NB * NTH && tau >= NB * NTH) continue;
             const int ms = tau / NTH, nj = tau % NTH;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_tile_k<E, C>(acc, AQT + ms * 16 * PC, PC, DOT + nj * 16 * PC, PC, lane);
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NSH; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTH) continue;
+            if (NSH * NW != NB * NTH && tau >= NB * NTH) continue;
             const int mt = tau / NTH, nj = tau % NTH;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_tile_k<E, C>(acc, TT + mt * 16 * PC, PC, UE + nj * 16 * PC, PC, lane);
@@ -624,7 +630,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NS3; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTI) continue;
+            if (NS3 * NW != NB * NTI && tau >= NB * NTI) continue;
             const int mt = tau / NTI, ni = tau % NTI;
             mma_tile_k<E, DVH>(dq3[k], DOH + mt * 16 * PH, PH, SB1 + ni * 16 * PH, PH, lane);
             mma_tile_k<E, DVH>(dk3[k], DUH + mt * 16 * PH, PH, SB1 + ni * 16 * PH, PH, lane);
@@ -721,7 +727,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NS3; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTI) continue;
+            if (NS3 * NW != NB * NTI && tau >= NB * NTI) continue;
             const int mt = tau / NTI, ni = tau % NTI;
             const int i = ni * 16 + (lane & 15), t0 = mt * 16 + (lane >> 4) * 4;
             float acc = 0.f;
@@ -782,7 +788,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NS3; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTI) continue;
+            if (NS3 * NW != NB * NTI && tau >= NB * NTI) continue;
             const int mt = tau / NTI, ni = tau % NTI;
             const int i0 = ni * 16 + (lane & 15);
 #pragma unroll
@@ -812,7 +818,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int k = 0; k < NS3; ++k) {
             const int tau = wv + NW * k;
-            if (tau >= NB * NTI) continue;
+            if (NS3 * NW != NB * NTI && tau >= NB * NTI) continue;
             const int mt = tau / NTI, ni = tau % NTI;
             const int i = ni * 16 + (lane & 15);
 #pragma unroll
@@ -854,7 +860,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
     for (int k = 0; k < NS3; ++k) {
         const int tau = wv + NW * k;
-        if (tau >= NB * NTI) continue;
+        if (NS3 * NW != NB * NTI && tau >= NB * NTI) continue;
         const int mt = tau / NTI, ni = tau % NTI;
         const int i = ni * 16 + (lane & 15);
 #pragma unroll
