@@ -272,12 +272,13 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype,
 /*
  * Bytes of workspace kdn_chunk_prefill_backward needs (0 when there are no
  * tokens), or 0 with *status set when the combination is invalid or
- * unsupported.  It is the forward pass's workspace plus two float32 states
- * (S at each chunk start, dS at each chunk end) per (sequence, head, chunk):
- * 66,048 + 131,072 bytes per (sequence, head, chunk) for bf16, d = 128, C = 64,
- * each section rounded up to 256 bytes; isotropic KDN adds 8 bytes per token
- * and 12 per chunk, diagonal KDN 12 d_k + 8 bytes per token and 12 d_k per
- * chunk.
+ * unsupported.  It is the forward pass's workspace plus two states (S at
+ * each chunk start, dS at each chunk end) per (sequence, head, chunk), kept
+ * in the call's dtype (the precision in which the gradient products read
+ * them): 66,048 + 65,536 bytes per (sequence, head, chunk) for bf16, d = 128,
+ * C = 64, each section rounded up to 256 bytes; isotropic KDN adds 8 bytes
+ * per token and 12 per chunk, diagonal KDN 12 d_k + 8 bytes per token and
+ * 12 d_k per chunk.
  */
 unsigned long long kdn_chunk_prefill_backward_workspace_size(kdn_variant variant,
                                                              kdn_dtype dtype, int B, int T,

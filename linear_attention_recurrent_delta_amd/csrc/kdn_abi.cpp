@@ -409,8 +409,9 @@ BwdWs backward_ws(int variant, int bf16, long long B, long long T, long long H, 
     const bool iso = variant == KDN_ISO_KDN, diag = variant == KDN_DIAG_KDN;
     long long o = up256(kdn::prefill_workspace_bytes(variant, bf16, B, T, H, d_k, C));
     w.fwd = 0;
-    w.states = o;  o += up256(bh * nc * d_k * d_v * 4);
-    w.dstates = o; o += up256(bh * nc * d_k * d_v * 4);
+    const long long es = bf16 ? 2 : 4;                 // saved states: the call dtype
+    w.states = o;  o += up256(bh * nc * d_k * d_v * es);
+    w.dstates = o; o += up256(bh * nc * d_k * d_v * es);
     if (iso) {
         w.beta = o;  o += up256(tok * 4);
         w.dbeta = o; o += up256(tok * 4);
@@ -546,7 +547,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     F.cus = device_cus();
     if (W.total > 0) {
         F.ws = base;
-        F.states = reinterpret_cast<float *>(base + W.states);
+        F.states = base + W.states;
         if (iso) {
             char *vb = base + kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
             const long long n_mob = kdn::WsLayout::mobius_bytes(bh, nc, 1);
@@ -605,7 +606,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     G.dp_out = dp_out; G.dxi = dproc_noise; G.dr = dobs_noise; G.dp0 = dp0;
     G.ws = F.ws;
     G.states = F.states;
-    G.dstates = W.total > 0 ? reinterpret_cast<float *>(base + W.dstates) : nullptr;
+    G.dstates = W.total > 0 ? static_cast<void *>(base + W.dstates) : nullptr;
     G.ws_stat = F.ws_stat; G.ws_p0 = F.ws_p0;
     G.chain_map = kdn && W.total > 0 ? reinterpret_cast<float *>(base + W.cmap) : nullptr;
     G.chain_dp = kdn && W.total > 0 ? reinterpret_cast<float *>(base + W.cdp) : nullptr;

@@ -114,6 +114,7 @@ template <typename E> struct Raw4;
 template <> struct Raw4<float> {
     float4 v;
     __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const float4 *>(p); }
+    __device__ __forceinline__ void store(float *p) const { *reinterpret_cast<float4 *>(p) = v; }
     __device__ __forceinline__ float operator[](int e) const {
         return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
     }
@@ -121,6 +122,7 @@ template <> struct Raw4<float> {
 template <> struct Raw4<bf16> {
     uint2 v;
     __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ void store(bf16 *p) const { *reinterpret_cast<uint2 *>(p) = v; }
     __device__ __forceinline__ float operator[](int e) const {
         const uint32_t w = e < 2 ? v.x : v.y;
         return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 
     for (int c = NC - 1; c >= 0; --c) {
         // dS leaving this chunk, for the local-gradient kernel
-        float *sv = P.dstates + ((long)bh * NC + c) * DK * DV;
+        E *sv = static_cast<E *>(P.dstates) + ((long)bh * NC + c) * DK * DV;
 #pragma unroll
         for (int k = 0; k < NSS; ++k) {
             const int tau = wv + NW * k;
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
             const int i0 = (tau / NTJ) * 16 + (lane >> 4) * 4, j = (tau % NTJ) * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sv[(long)(i0 + r) * DV + v0 + j] = dacc[k][r];
+                sv[(long)(i0 + r) * DV + v0 + j] = from_f32<E>(dacc[k][r]);
         }
         X.aq.template store<true>(AQT, PC, 1.f, tid);
         X.wt.template store<true>(WR, PK, 1.f, tid);
@@ -412,8 +414,8 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     const long tok0 = ((long)b * T + c0) * H + h;      // row of (b, c0, h)
     const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
     const char *rec = static_cast<const char *>(P.ws) + ((long)bh * NC + c) * LW.rec;
-    const float *Sg = P.states + ((long)bh * NC + c) * DK * DV;
-    const float *dSg = P.dstates + ((long)bh * NC + c) * DK * DV;
+    const E *Sg = static_cast<const E *>(P.states) + ((long)bh * NC + c) * DK * DV;
+    const E *dSg = static_cast<const E *>(P.dstates) + ((long)bh * NC + c) * DK * DV;
     const E *gq = static_cast<const E *>(P.q);
     const E *gk = static_cast<const E *>(P.k);
     const E *gv = static_cast<const E *>(P.v);
@@ -463,8 +465,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
     // its columns, dO, and V in the U-tile layout.  Rows past the sequence
     // end read the last row (every load unconditional, so they are all in
     // flight together) and are zeroed where used.
-    float sv[NS4][4], dsv[NS4][4];
-    Raw4<E> dov[NO4];
+    Raw4<E> sv[NS4], dsv[NS4], dov[NO4];
     E vv[NSH][4];
     // Issued in the order of first use (S and dO, then V, then dS'), since a
     // wave's loads complete in order.
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
             const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
-            gload4(Sg + (long)i * DV + jh + j4, sv[n]);
+            sv[n].load(Sg + (long)i * DV + jh + j4);
         }
 #pragma unroll
         for (int n = 0; n < NO4; ++n) {
@@ -491,11 +492,11 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
             const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
-            gload4(dSg + (long)i * DV + jh + j4, dsv[n]);
+            dsv[n].load(dSg + (long)i * DV + jh + j4);
         }
     };
     // S^T (or dS'^T) of the half into SB1 as [j][i]
-    auto stage_t = [&](const float (&v)[NS4][4]) {
+    auto stage_t = [&](const Raw4<E> (&v)[NS4]) {
 #pragma unroll
         for (int n = 0; n < NS4; ++n) {
             const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
@@ -603,8 +604,8 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 #pragma unroll
             for (int n = 0; n < NS4; ++n) {
                 const int x = tid + NT * n, i = x / G4, j4 = (x % G4) * 4;
-                lds_stn<4>(SB1 + i * PH + j4, sv[n]);
-                lds_stn<4>(SB2 + i * PH + j4, dsv[n]);
+                sv[n].store(SB1 + i * PH + j4);
+                dsv[n].store(SB2 + i * PH + j4);
                 if (DECAY) {
                     // sum over the G4 lanes of key channel i, then one atomic
                     float p = sv[n][0] * dsv[n][0] + sv[n][1] * dsv[n][1] +

@@ -41,8 +41,9 @@ struct PrefillParams {
     float *ws_p0;
     float *ws_stat;
     // Gradient computation: S at every chunk start is saved here by the state
-    // pass ([batch*head][chunk][dk][dv] float32; null otherwise).
-    float *states;
+    // pass ([batch*head][chunk][dk][dv] in the call's element type, the
+    // precision the gradient products read it in; null otherwise).
+    void *states;
     // Isotropic KDN, gradient computation: the derived write strengths
     // [B, T, H] (float32) are saved here by the prep kernel (null otherwise).
     float *beta_out;
@@ -80,8 +81,8 @@ struct BackwardParams {
     const float *dp_out;                    // isotropic KDN: dL/dp_final [B, H], may be null
     float *dxi, *dr, *dp0;                  // isotropic KDN gradients
     void *ws;                               // forward records (kdn_workspace.h)
-    float *states;                          // S at every chunk start
-    float *dstates;                         // dS leaving every chunk
+    void *states;                           // S at every chunk start (call dtype)
+    void *dstates;                          // dS leaving every chunk (call dtype)
     // isotropic KDN: the forward variance pass's per-token sums (mean a^2,
     // mean xi, |k|^2, r) and chunk-start variances; the chain's chunk maps
     // and the variance gradient at every chunk end

@@ -282,7 +282,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
 
     auto compute = [&](const Chunk &X, int c) {
         if constexpr (SAVE) {
-            float *sv = P.states + ((long)bh * NC + c) * DK * DV;
+            E *sv = static_cast<E *>(P.states) + ((long)bh * NC + c) * DK * DV;
 #pragma unroll
             for (int k = 0; k < NSW; ++k) {
                 const int tau = wv + 8 * k;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillParams P) {
                 const int j = (tau / NIBT) * 16 + (lane & 15);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sv[(long)(i0 + r) * DV + v0 + j] = sacc[k][r];
+                    sv[(long)(i0 + r) * DV + v0 + j] = from_f32<E>(sacc[k][r]);
             }
         }
         // phase 1: chain waves U = V - K~ S; output waves finish chunk c-1

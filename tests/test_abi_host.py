@@ -351,7 +351,7 @@ def test_backward_workspace_size(lib):
     f = lib.kdn_chunk_prefill_backward_workspace_size
     rec = 66048
     n = f(1, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
-    assert st.value == OK and n == 2 * 4 * 2 * (rec + 2 * 128 * 128 * 4)
+    assert st.value == OK and n == 2 * 4 * 2 * (rec + 2 * 128 * 128 * 2)
     n_diag = f(3, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
     assert st.value == OK and n_diag > n
     n_iso = f(4, 1, 2, 100, 4, 128, 128, 0, ctypes.byref(st))
