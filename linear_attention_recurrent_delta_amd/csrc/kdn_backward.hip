@@ -909,14 +909,20 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
         }
     }
     if (VAR == GATED_DELTANET) {
-        // one decay per token: sum the channels first (a wave per row), then a
+        // one decay per token: 8 lanes per token sum its channels (a row of 8
+        // lanes reads 32 consecutive floats), a DPP sum over the 8; then a
         // suffix sum over the tokens across the lanes of wave 0
-        for (int t = wv; t < C; t += NW) {
+        static_assert(DK % 32 == 0 && C * 8 <= NT, "row sums");
+        if (tid < C * 8) {
+            const int t = tid >> 3, part = tid & 7;
             float x = 0.f;
-            for (int i = lane; i < DK; i += WAVE)
-                x += DG[t * PF + i];
-            x = wave_sum(x);
-            if (lane == 0)
+#pragma unroll
+            for (int q = 0; q < DK / 32; ++q) {
+                const float4 v = *reinterpret_cast<const float4 *>(DG + t * PF + part * 4 + 32 * q);
+                x += (v.x + v.y) + (v.z + v.w);
+            }
+            x = row8_sum_last(x);
+            if (part == 7)
                 s_dla[t] = x;
         }
         __syncthreads();

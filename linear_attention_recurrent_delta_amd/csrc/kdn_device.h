@@ -61,6 +61,15 @@ __device__ __forceinline__ float row16_sum_last(float x) {
     return x;
 }
 
+// Sum over each group of 8 lanes by DPP row shifts; lane 7 of the group
+// holds the total.
+__device__ __forceinline__ float row8_sum_last(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+    return x;
+}
+
 // Sum over the 64 lanes of a wave; every lane gets the total.  Fixed
 // butterfly order, so results are deterministic.
 __device__ __forceinline__ float wave_sum(float x) {
