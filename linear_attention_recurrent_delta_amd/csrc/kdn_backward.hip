@@ -1,5 +1,7 @@
-// kdn_backward.hip -- gradients of the chunkwise prefill (gfx950), for the
-// write-strength variants (DeltaNet, Gated DeltaNet, KDA).
+// kdn_backward.hip -- gradients of the chunkwise prefill (gfx950): the
+// memory part of every variant (DeltaNet, Gated DeltaNet, KDA; the KDN
+// variants through KDA's with their derived write vectors) and the adjoints
+// of the KDN variance chains.
 //
 // The forward chunk algebra (page "معماری KDA: حذف تداخل حافظه با قانون دلتا در
 // توالی‌های بلند", section "حل مشکل وابستگی علی"), per chunk entering with state S:
@@ -17,11 +19,13 @@
 //   d log gamma_t = k (gamma dK~) + q dq - w dw  (+ the gamma_C terms at the
 //   chunk end), and d log a_r = sum over t >= r of d log gamma_t.
 //
-// Three launches after the forward pass (which saves S at every chunk start):
+// Two launches after the forward pass (which saves S at every chunk start):
 //   backward_state_kernel: one workgroup per (batch*head, value block) walks
 //     the chunks in reverse, dS in registers, and saves dS' of every chunk;
 //   backward_chunk_kernel: one workgroup per (batch*head, chunk) forms the
 //     chunk's local gradients from S, dS', the tiles and the forward record.
+// For KDN three more reverse the variance chain (map, scan over chunks,
+// per-token gradients).
 #include "kdn_device.h"
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
