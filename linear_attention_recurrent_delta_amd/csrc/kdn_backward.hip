@@ -885,12 +885,10 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
                 if (gw)
                     P.dw_out[row(t) * DK + i] = dw;
             }
-            float db = (gw ? wv : kk) * dw;           // diagonal KDN: sum w dw
-            db += __shfl_xor(db, 1, WAVE);
-            db += __shfl_xor(db, 2, WAVE);
-            db += __shfl_xor(db, 4, WAVE);
-            db += __shfl_xor(db, 8, WAVE);
-            if ((lane & 15) == 0)
+            // dbeta (diagonal KDN: sum w dw) over the 16 channels of the row:
+            // a DPP row sum, then one atomic per row
+            const float db = row16_sum_last((gw ? wv : kk) * dw);
+            if ((lane & 15) == 15)
                 atomicAdd(&s_db[t], db);
             if (DECAY)
                 DG[t * PF + i] = kk * dkd + qq * dq - wv * dw;
