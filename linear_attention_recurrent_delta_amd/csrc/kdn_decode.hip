@@ -88,7 +88,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
     const int row0 = rg * RPT;
 
     __shared__ float sk[DK], sq[DK], sa[DK], sg[DK];
-    __shared__ f32x4 red[RG][CG];
+    // partial column sums of the read (red) and of the output (ored): two
+    // buffers, so no barrier separates reading one from writing the other
+    __shared__ f32x4 red[RG][CG], ored[RG][CG];
     __shared__ float part[3][NT / WAVE];
 
     // The first token's vectors are requested first and the state after
@@ -201,7 +203,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
             ev[2] = in.v[2] - x0.z;
             ev[3] = in.v[3] - x0.w;
         }
-        __syncthreads();   // red is reused below
 
         // Write S = S- + w e^T, partial output over this thread's rows.
         const bool last = t + 1 == T;
@@ -218,13 +219,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeParams P) {
                 __builtin_nontemporal_store(
                     s[m], reinterpret_cast<f32x4 *>(S + (long)(row0 + m) * DV) + cg);
         }
-        red[rg][cg] = op;
+        ored[rg][cg] = op;
         __syncthreads();
         if (tid < CG) {
-            f32x4 x0 = red[0][tid];
+            f32x4 x0 = ored[0][tid];
 #pragma unroll
             for (int g = 1; g < RG; ++g) {
-                const f32x4 x = red[g][tid];
+                const f32x4 x = ored[g][tid];
                 x0.x += x.x; x0.y += x.y; x0.z += x.z; x0.w += x.w;
             }
             TIn *o = static_cast<TIn *>(P.o) + row_of(t) * DV + 4 * tid;
