@@ -252,3 +252,29 @@ def test_backward_kdn_long_sampled(variant):
     log(f"backward {variant} B2 H16 T2048: sampled heads")
     inp = _kdn_inputs(variant, 2, 2048, 16, 128, 128, "bf16", seed=synth.seed_of(variant))
     _kdn_compare(variant, inp, TOL["bf16"], heads=[(0, 0), (1, 9)])
+
+
+# ---------------------------------------------------------------------------
+# The gradient workloads bench.py times (KDA B2 H32 T8192; diagonal and
+# isotropic KDN B2 H16 T16384; d = 128, bf16, default chunk and workspace),
+# with exactly its inputs and dO: every head on the GPU, two sampled heads
+# against the oracle at full length.
+BENCH_BWD = ("kda", "diag_kdn", "iso_kdn")
+
+
+@pytest.mark.parametrize("name", BENCH_BWD)
+def test_backward_bench_workload_sampled(name):
+    c = synth.CONFIGS[name]
+    B, T, H, dv = c["B"], c["T"], c["H"], c["dv"]
+    log(f"backward workload {name} B{B} H{H} T{T}: sampled heads")
+    inp = synth.gen_config(name, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.seed_of(name) + 7)
+    inp["dO"] = torch.randn((B, T, H, dv), generator=g, device="cuda").to(inp["q"].dtype)
+    inp["dS"] = None
+    heads = [(0, 0), (B - 1, H - 1)]
+    if name == "kda":
+        _compare(name, inp, TOL["bf16"], heads=heads)
+    else:
+        inp["dp"] = None
+        _kdn_compare(name, inp, TOL["bf16"], heads=heads)
