@@ -658,7 +658,7 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
         for (int r = 0; r < 4; ++r)
             dk3[k][r] = -dk3[k][r];
 
-    // ---- decays gamma_t per channel; W'^T = (beta k / gamma)^T, Q~^T, K~^T;
+    // ---- decays gamma_t per channel; W'^T = (w / gamma)^T, Q~^T, K~^T;
     //      the dA matrices (masked) and their transposes; sum_s W~ dW~
     // decays into GAM (a_t per channel; 1 past the sequence end)
     constexpr int GK4 = DK / 4, NK4 = C * GK4 / NT;
