@@ -330,6 +330,41 @@ def bench_verify(T, reps, torch, kdn, synth):
     return res
 
 
+def measure_achievable(torch, copy_mib=2048, gemm_n=8192, reps=10):
+    """What this machine reaches on plain work, reported beside the published
+    peaks (the roofline fractions stay against the published ones): a plain
+    streaming kernel out = 1.0 * in over 2 GiB of float32 (read + write bytes
+    / time) and a dense bf16 GEMM through the vendor library (2 n^3 flop /
+    time).  Context for the fractions, not part of the path."""
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+    n = copy_mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: torch.mul(src, 1.0, out=dst))
+    del src, dst
+    a = torch.randn(gemm_n, gemm_n, device="cuda").to(torch.bfloat16).contiguous()
+    b = torch.randn(gemm_n, gemm_n, device="cuda").to(torch.bfloat16).contiguous()
+    c = torch.empty(gemm_n, gemm_n, dtype=torch.bfloat16, device="cuda")
+    t_gemm = timed(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": 2 * n * 4 / t_copy / 1e9,
+            "bf16_gemm_TFLOPs": 2 * gemm_n ** 3 / t_gemm / 1e12,
+            "method": f"out = 1.0 * in over {copy_mib} MiB float32; {gemm_n}^3 bf16 "
+                      f"matmul (vendor library); mean of {reps} after 3 warm-ups"}
+
+
 def cpu_baseline(name, synth, budget_s=20.0):
     """The fp64 oracle, as it stands, on a bounded sample of the workload:
     whole-length (batch, head) streams, as many as fit the time budget."""
@@ -438,6 +473,15 @@ def main():
         w["decode_diag_kdn"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
         w["verify16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth)
         out["workloads"] = w
+    ach = measure_achievable(torch)
+    out["achievable"] = ach
+    # the same achieved rates against what this machine reaches on plain work
+    for r in [out] + list(out.get("workloads", {}).values()):
+        rl = r["roofline"]
+        base = ach["hbm_copy_GBs"] if rl["bound"] == "hbm" else None
+        rl["frac_of_measured_copy"] = rl["achieved"] / base if base else None
+        if r.get("mfma"):
+            r["mfma"]["frac_of_measured_gemm"] = r["mfma"]["achieved"] / ach["bf16_gemm_TFLOPs"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline("gated_deltanet", synth)
     out["kernel_hash"] = kernel_hash()
