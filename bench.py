@@ -409,8 +409,17 @@ def cpu_baseline(name, synth, budget_s=20.0):
                           nthreads=threads)
         el += time.perf_counter() - t0
         reps += 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh
+                          if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": reps * nheads * T / H / el, "unit": "tokens/s", "cores": used,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
+            "one_thread_value": T / H / one,
+            "one_thread_sample": f"1 (batch, head) stream at T={T}, {one:.2f} s on 1 thread",
             "sample": f"{nheads} of {B * H} (batch, head) streams at full length "
                       f"T={T} ({nheads * T} head-tokens) x {reps} passes, fp64, "
                       f"{el:.1f} s on {used} threads; tokens/s counts all {H} heads "
