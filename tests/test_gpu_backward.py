@@ -278,3 +278,12 @@ def test_backward_bench_workload_sampled(name):
     else:
         inp["dp"] = None
         _kdn_compare(name, inp, TOL["bf16"], heads=heads)
+
+
+@pytest.mark.parametrize("variant", KDNS)
+def test_backward_kdn_chunk32(variant):
+    """The KDN chain kernels at a chunk of 32 (bf16, d = 128), over several
+    chunks and a ragged tail."""
+    log(f"backward {variant} chunk 32 B2 T200 H2")
+    _kdn_compare(variant, _kdn_inputs(variant, 2, 200, 2, 128, 128, "bf16", seed=131),
+                 TOL["bf16"], chunk=32)
