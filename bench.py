@@ -441,7 +441,7 @@ def main():
                          "hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the recurrence shards "
+        print("bench.py: runs on one GPU only; the recurrence shards "
               "over (batch, head) with no communication, so N GPUs = N "
               "independent copies of this run.", file=sys.stderr)
         sys.exit(2)
