@@ -3,15 +3,17 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--workloads all|headline]
 
-One step is one chunkwise prefill call over the Gated DeltaNet workload
-(B=4, H=16, T=4096, d_k=d_v=128, bf16 inputs, fp32 state, C=64) with inputs
-resident in HBM.  Rank 0 prints ONE JSON line with the headline value
-(prefill tokens/s), the roofline of the prefill kernel (HBM-bound by its
-algorithmic bytes; the MFMA fraction of its algorithmic flops is reported
-next to it), the fp64 oracle timed on the host cores, and the other
-workloads (KDA, diagonal-KDN and isotropic-KDN prefill, the gradient calls of
-Gated DeltaNet, KDA and both KDN variants, diagonal-KDN decode, 16-token
-multi-token decode) each with its own roofline.
+One step is one chunkwise prefill call over the diagonal-KDN workload
+(B=2, H=16, T=16384, d_k=d_v=128, bf16 inputs, fp32 state and variance,
+C=64) -- the largest prefill workload -- with inputs resident in HBM.  Rank 0
+prints ONE JSON line with the headline value (prefill tokens/s), the roofline
+of the prefill call (HBM-bound by its algorithmic bytes; the MFMA fraction of
+its algorithmic flops is reported next to it), the diagonal-KDN decode
+workload beside it (256 sequences x 32 heads, 1024 steps: steps/s and its
+HBM roofline), the fp64 oracle timed on the host cores on the headline
+workload, and the other workloads (Gated DeltaNet, KDA and isotropic-KDN
+prefill, the gradient calls of Gated DeltaNet, KDA and both KDN variants,
+16-token multi-token decode) each with its own roofline.
 """
 from __future__ import annotations
 
@@ -29,6 +31,8 @@ METRIC = "prefill tokens/s + decode steps/s per head-state; % MFMA / % HBM roofl
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
+# the largest prefill workload: diagonal KDN, B2 H16 T16384, d_k = d_v = 128, bf16
+HEADLINE = "diag_kdn"
 KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_variance.hip", "kdn_backward.hip",
                   "kdn_decode.hip", "kdn_device.h", "kdn_launch.h", "kdn_workspace.h"]
 
@@ -433,6 +437,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", choices=["all", "headline"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run one workload and print its JSON object only (for "
+                         "profiling): <name>_prefill, <name>_backward, "
+                         "decode_diag_kdn or verify16_diag_kdn")
     ap.add_argument("--schedule", choices=["two_pass", "single_pass"], default="two_pass",
                     help="prefill schedule: with a workspace (two-pass) or without")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -459,7 +467,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head = bench_prefill("gated_deltanet", args.steps, args.warmup, torch, kdn, synth,
+    if args.only:
+        w = args.only
+        if w.endswith("_prefill"):
+            r = bench_prefill(w[:-len("_prefill")], args.steps, args.warmup, torch, kdn,
+                              synth, args.schedule)
+        elif w.endswith("_backward"):
+            r = bench_backward(w[:-len("_backward")], args.steps, args.warmup, torch, kdn,
+                               synth)
+        elif w == "decode_diag_kdn":
+            r = bench_decode(w, max(1, args.steps // 1024), torch, kdn, synth)
+        elif w.startswith("verify") and w.endswith("_diag_kdn"):
+            r = bench_verify(int(w[len("verify"):-len("_diag_kdn")]), args.steps, torch,
+                             kdn, synth)
+        else:
+            raise SystemExit(f"bench.py: unknown workload {w!r}")
+        r["kernel_hash"] = kernel_hash()
+        print(json.dumps(r), flush=True)
+        return
+
+    head = bench_prefill(HEADLINE, args.steps, args.warmup, torch, kdn, synth,
                          args.schedule)
     out = {
         "metric": METRIC, "value": head["value"], "unit": "tokens/s",
@@ -470,29 +497,30 @@ def main():
         "config": dict(head["config"], parallelism="single GPU"),
         "roofline": head["roofline"], "mfma": head["mfma"],
     }
+    # decode beside prefill: the metric's second half
+    out["decode"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
     if args.workloads == "all":
         w = {}
-        for name in ("kda", "diag_kdn", "iso_kdn"):
+        for name in ("gated_deltanet", "kda", "iso_kdn"):
             w[f"{name}_prefill"] = bench_prefill(name, max(3, args.steps // 2),
                                                  args.warmup, torch, kdn, synth,
                                                  args.schedule)
         for name in ("gated_deltanet", "kda", "diag_kdn", "iso_kdn"):
             w[f"{name}_backward"] = bench_backward(name, max(3, args.steps // 2),
                                                    args.warmup, torch, kdn, synth)
-        w["decode_diag_kdn"] = bench_decode("decode_diag_kdn", 2, torch, kdn, synth)
         w["verify16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth)
         out["workloads"] = w
     ach = measure_achievable(torch)
     out["achievable"] = ach
     # the same achieved rates against what this machine reaches on plain work
-    for r in [out] + list(out.get("workloads", {}).values()):
+    for r in [out, out["decode"]] + list(out.get("workloads", {}).values()):
         rl = r["roofline"]
         base = ach["hbm_copy_GBs"] if rl["bound"] == "hbm" else None
         rl["frac_of_measured_copy"] = rl["achieved"] / base if base else None
         if r.get("mfma"):
             r["mfma"]["frac_of_measured_gemm"] = r["mfma"]["achieved"] / ach["bf16_gemm_TFLOPs"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline("gated_deltanet", synth)
+        out["cpu_baseline"] = cpu_baseline(HEADLINE, synth)
     out["kernel_hash"] = kernel_hash()
     print(json.dumps(out), flush=True)
 

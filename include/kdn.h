@@ -114,8 +114,10 @@ typedef enum kdn_status {
  *   o           [B, T, H, d_v] dtype (output, o_t = S_t^T q_t)
  *   S_out       [B, H, d_k, d_v] float32 (output); may be exactly S0, must not
  *               overlap it otherwise
- *   p_out       shaped as p0, float32 (output, KDN only, else NULL); must
- *               not overlap p0
+ *   p_out       shaped as p0, float32 (output, KDN only, else NULL); may be
+ *               exactly p0 when a workspace is passed (or T = 0), must not
+ *               overlap it otherwise (the single-pass schedule reads p0 from
+ *               several workgroups of a head while one of them writes p_out)
  *   mu          information scaling of the variance update (KDN only; 1 =
  *               unscaled)
  *   chunk       chunk length C; 0 picks the library default (64 for bf16,

@@ -180,14 +180,21 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     const long long n_b = kdn ? 0 : tok * es;
     const long long n_x = kdn ? tok * d_k * es : 0, n_r = kdn ? tok * es : 0;
     const long long n_S = bh * d_k * d_v * 4, n_p = bh * p_per_head(variant, d_k) * 4;
-    // o overlaps no input; S_out may be S0 exactly; p_out must not touch p0.
+    // o overlaps no input; S_out may be S0 exactly (every workgroup reads its
+    // slice of S0 before it writes the same slice).  p_out may be p0 exactly
+    // with a workspace (the variance scan reads each entry of p0 in the thread
+    // that later writes it) or without tokens; the single-pass kernel reads p0
+    // in every value-block workgroup of a head and writes p_out from one of
+    // them, so there it must lie elsewhere.
+    const bool p_in_place = kdn && p0 && p_out == p0 && (tok == 0 || workspace);
     struct R { const void *p; long long n; } ins[] = {
         {q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, n_b},
         {proc_noise, n_x}, {obs_noise, n_r}, {S0, n_S}, {p0, n_p}};
     for (const R &x : ins) {
         if (overlap(o, tok * d_v * es, x.p, x.n)) return KDN_ERR_ALIAS;
         if (x.p != S0 && overlap(S_out, n_S, x.p, x.n)) return KDN_ERR_ALIAS;
-        if (kdn && overlap(p_out, n_p, x.p, x.n)) return KDN_ERR_ALIAS;
+        if (kdn && !(p_in_place && x.p == p0) && overlap(p_out, n_p, x.p, x.n))
+            return KDN_ERR_ALIAS;
     }
     if (S0 && S0 != S_out && overlap(S_out, n_S, S0, n_S)) return KDN_ERR_ALIAS;
     if (overlap(o, tok * d_v * es, S_out, n_S)) return KDN_ERR_ALIAS;

@@ -20,12 +20,18 @@
 // head; inside a chunk its token maps (Mobius form) are scanned across the
 // lanes of one wave.
 //
-// Work split: one workgroup (4 waves) owns one (batch, head, d_v block of NV
-// columns) and walks all chunks in order; the d_k x NV slice of S stays in
-// MFMA accumulator registers in float32 for the whole sequence.  Sibling
-// workgroups of a head (different d_v blocks) repeat the S-independent work
-// (decay prep, gains, A matrices, triangular inverse) so that the grid fills
-// the 256 CUs; they are placed on one XCD so that q/k/gate reads hit its L2.
+// Two kernels are instantiated from prefill_kernel:
+//  - PREP = true, the chunk-parallel prep kernel of the two-pass schedule:
+//    persistent 8-wave workgroups, one per CU, each walking every gridDim-th
+//    (batch*head, chunk) unit and writing steps 1-4 of the unit to its
+//    workspace record (kdn_workspace.h);
+//  - PREP = false, the single-pass kernel: one 8-wave workgroup owns one
+//    (batch, head, d_v block of NV columns) and walks all chunks in order, the
+//    d_k x NV slice of S in MFMA accumulator registers in float32 for the whole
+//    sequence.  Sibling workgroups of a head (different d_v blocks) repeat the
+//    S-independent work (decay prep, gains, A matrices, triangular inverse) so
+//    that the grid fills the CUs; they are placed on one XCD so that q/k/gate
+//    reads hit its L2.
 //
 // Per chunk:
 //   1  commit the raw q, k, alpha, xi tiles and the v block (loaded one chunk
@@ -36,9 +42,13 @@
 //      Q~, W' = w / gamma and W~^T with 16 B LDS accesses;
 //   3  A_kk, A_qk on MFMA from K~ W'^T and Q~ W'^T (exact elementwise
 //      fallback when a channel decays below 2^-90 inside the chunk);
-//   4  T = (I + A_kk)^-1: 16x16 diagonal blocks by forward substitution (one
-//      wave per block), off-diagonal blocks by MFMA block doubling:
-//      T[b,a] = -T[b,b] A[b,a] T[a,a] on 16- then 32-row blocks;
+//   4  T = (I + A_kk)^-1: each 16x16 diagonal block by one wave (two 8x8
+//      forward substitutions and one 8x8 product); the blocks below the
+//      diagonal on (near) fp32 MFMA -- in the prep kernel from the
+//      factorisation I + A = (I + N D) D^-1 (D the inverted diagonal blocks,
+//      N the blocks below the diagonal) in three levels of independent block
+//      products, in the single-pass kernel one chain per block column,
+//      T[I,J] = -T[I,I] sum_K A[I,K] T[K,J];
 //   5  U = V - K~ S on MFMA (overlaps 4's diagonal blocks);
 //   6  E = T U on MFMA;
 //   7  O = Q~ S + A_qk E (stored), S = gamma_C S + W~^T E on MFMA;
@@ -1359,13 +1369,13 @@ hipError_t KDN_CAT(launch_prefill_prep_v, KDN_PREFILL_VARIANT)(const PrefillPara
 
 #ifdef KDN_PREFILL_DISPATCH
 int prefill_value_block(const PrefillParams &P) {
-    // Enough workgroups to cover the 256 CUs, value blocks of 16 or 32
+    // Enough workgroups to cover the device's CUs, value blocks of 16 or 32
     // columns (float32 operands: 16, for the LDS budget).
     if (!P.bf16)
         return 16;
     const long heads = (long)P.B * P.H;
     int nv = 32;
-    while (nv > 16 && heads * (P.dv / nv) < 256)
+    while (nv > 16 && heads * (P.dv / nv) < P.cus)
         nv >>= 1;
     return nv;
 }

@@ -92,7 +92,42 @@ def _ptr(x):
         return x
     if not x.is_contiguous():
         raise ValueError("kdn: tensor arguments must be contiguous")
+    if x.device.type != "cuda":
+        raise ValueError(f"kdn: tensor arguments must be in GPU memory, not on {x.device}")
     return x.data_ptr()
+
+
+def _expect(args, device):
+    """Check (name, tensor or None, shape, dtype) tuples before a call: the
+    shape, then the dtype, then contiguity, then that every tensor lives on
+    ``device`` (a GPU).  The C library checks sizes and pointers only; a host
+    tensor, a tensor on another GPU or a wrongly shaped one would otherwise
+    reach the kernels."""
+    for name, x, shape, dtype in args:
+        if x is None:
+            continue
+        if not isinstance(x, torch.Tensor):
+            raise TypeError(f"kdn: {name} must be a tensor or None")
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError(f"kdn: {name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+        if x.dtype != dtype:
+            raise ValueError(f"kdn: {name} has dtype {x.dtype}, expected {dtype}")
+        if not x.is_contiguous():
+            raise ValueError(f"kdn: {name} must be contiguous")
+    if device.type != "cuda":
+        raise ValueError(f"kdn: tensors must be in GPU memory, not on {device}")
+    for name, x, _, _ in args:
+        if x is not None and x.device != device:
+            raise ValueError(f"kdn: {name} is on {x.device}, the other tensors on {device}")
+
+
+def _gate_specs(vid, lead, dk, dt, alpha, beta, proc_noise, obs_noise):
+    """Expected (name, tensor, shape, dtype) of the gates for leading dims
+    ``lead`` ([B,T,H] or [N,H])."""
+    lead = tuple(lead)
+    a_shape = lead if vid == 1 else lead + (dk,)
+    return [("alpha", alpha, a_shape, dt), ("beta", beta, lead, dt),
+            ("proc_noise", proc_noise, lead + (dk,), dt), ("obs_noise", obs_noise, lead, dt)]
 
 
 def _stream(stream):
@@ -239,6 +274,13 @@ def prefill(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
         p = _new_p(vid, B, H, dk, q.device)
     else:
         o, S, p = out
+    f32, pshape = torch.float32, _p_shape(vid, B, H, dk)
+    _expect([("q", q, (B, T, H, dk), q.dtype), ("k", k, (B, T, H, dk), q.dtype),
+             ("v", v, (B, T, H, dv), q.dtype)]
+            + _gate_specs(vid, (B, T, H), dk, q.dtype, alpha, beta, proc_noise, obs_noise)
+            + [("S0", S0, (B, H, dk, dv), f32), ("p0", p0, pshape, f32),
+               ("o", o, (B, T, H, dv), q.dtype), ("S_out", S, (B, H, dk, dv), f32),
+               ("p_out", p, pshape, f32)], q.device)
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError(f"kdn: workspace must be 'auto', None or a tensor, not {workspace!r}")
@@ -257,6 +299,12 @@ def decode(variant, q, k, v, S, p=None, alpha=None, beta=None, proc_noise=None,
     dv = v.shape[-1]
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    f32 = torch.float32
+    _expect([("q", q, (N, H, dk), q.dtype), ("k", k, (N, H, dk), q.dtype),
+             ("v", v, (N, H, dv), q.dtype)]
+            + _gate_specs(vid, (N, H), dk, q.dtype, alpha, beta, proc_noise, obs_noise)
+            + [("S", S, (N, H, dk, dv), f32), ("p", p, _p_shape(vid, N, H, dk), f32),
+               ("o", o, (N, H, dv), q.dtype)], q.device)
     kdn_recurrent_decode(vid, DTYPES[q.dtype], N, H, dk, dv, mu, q, k, v, alpha,
                          beta, proc_noise, obs_noise, S, p, o, stream)
     return o
@@ -278,6 +326,13 @@ def decode_multi(variant, q, k, v, alpha=None, beta=None, proc_noise=None,
         p = _new_p(vid, N, H, dk, q.device)
     else:
         o, S, p = out
+    f32, pshape = torch.float32, _p_shape(vid, N, H, dk)
+    _expect([("q", q, (N, T, H, dk), q.dtype), ("k", k, (N, T, H, dk), q.dtype),
+             ("v", v, (N, T, H, dv), q.dtype)]
+            + _gate_specs(vid, (N, T, H), dk, q.dtype, alpha, beta, proc_noise, obs_noise)
+            + [("S0", S0, (N, H, dk, dv), f32), ("p0", p0, pshape, f32),
+               ("o", o, (N, T, H, dv), q.dtype), ("S_out", S, (N, H, dk, dv), f32),
+               ("p_out", p, pshape, f32)], q.device)
     kdn_recurrent_decode_multi(vid, DTYPES[q.dtype], N, T, H, dk, dv, mu, q, k, v,
                                alpha, beta, proc_noise, obs_noise, S0, p0, o, S, p,
                                stream)
@@ -310,6 +365,21 @@ def prefill_backward(variant, q, k, v, d_o, alpha=None, beta=None, proc_noise=No
                    dproc_noise=new(B, T, H, dk) if iso else None,
                    dobs_noise=new(B, T, H) if iso else None,
                    dp0=(new(B, H, dk) if vid == 3 else new(B, H)) if iso else None)
+    f32, pshape = torch.float32, _p_shape(vid, B, H, dk)
+    la_shape = (B, T, H) if vid == 1 else (B, T, H, dk)
+    _expect([("q", q, (B, T, H, dk), q.dtype), ("k", k, (B, T, H, dk), q.dtype),
+             ("v", v, (B, T, H, dv), q.dtype), ("d_o", d_o, (B, T, H, dv), q.dtype)]
+            + _gate_specs(vid, (B, T, H), dk, q.dtype, alpha, beta, proc_noise, obs_noise)
+            + [("S0", S0, (B, H, dk, dv), f32), ("p0", p0, pshape, f32),
+               ("dS_out", dS_out, (B, H, dk, dv), f32), ("dp_out", dp_out, pshape, f32),
+               ("dq", out["dq"], (B, T, H, dk), f32), ("dk", out["dk"], (B, T, H, dk), f32),
+               ("dv", out["dv"], (B, T, H, dv), f32),
+               ("dlog_alpha", out["dlog_alpha"], la_shape, f32),
+               ("dbeta", out["dbeta"], (B, T, H), f32),
+               ("dproc_noise", out["dproc_noise"], (B, T, H, dk), f32),
+               ("dobs_noise", out["dobs_noise"], (B, T, H), f32),
+               ("dS0", out["dS0"], (B, H, dk, dv), f32), ("dp0", out["dp0"], pshape, f32)],
+            q.device)
     if workspace is None:
         n = kdn_chunk_prefill_backward_workspace_size(vid, dt, B, T, H, dk, dv, chunk)
         workspace = torch.empty(n, dtype=torch.uint8, device=dev) if n else None

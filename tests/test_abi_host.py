@@ -136,6 +136,15 @@ def test_workspace_validation(lib):
     assert call(ws=A + 2 * MB, ws_bytes=n) == EALIAS           # overlaps v
     nk = _ws_ok(lib, variant=3)
     assert lib.kdn_chunk_prefill(*_prefill_args(variant=3, ws=W, ws_bytes=nk - 1)) == EWS
+    # p_out == p0 (in-place variance) passes the alias checks with a workspace:
+    # the call then fails only on the workspace size, which is checked after
+    for v in (3, 4):
+        nv = _ws_ok(lib, variant=v)
+        assert lib.kdn_chunk_prefill(*_prefill_args(variant=v, p_out=A + 8 * MB, ws=W,
+                                                    ws_bytes=nv - 1)) == EWS
+        # a partial overlap is still refused
+        assert lib.kdn_chunk_prefill(*_prefill_args(variant=v, p_out=A + 8 * MB + 16, ws=W,
+                                                    ws_bytes=nv)) == EALIAS
     # validation of the other arguments still comes first
     assert call(q=None, ws=W, ws_bytes=0) == ENULL
 
@@ -184,7 +193,8 @@ PREFILL_CASES = [
     ("S_out overlaps q", dict(S_out=A + 64), EALIAS),
     ("S_out partially overlaps S0", dict(S_out=A + 7 * MB + 1024), EALIAS),
     ("o overlaps S_out", dict(o=A + 10 * MB + 16), EALIAS),
-    ("KDN p_out equals p0", dict(variant=3, p_out=A + 8 * MB), EALIAS),
+    ("KDN p_out equals p0 without workspace", dict(variant=3, p_out=A + 8 * MB), EALIAS),
+    ("iso KDN p_out equals p0 without workspace", dict(variant=4, p_out=A + 8 * MB), EALIAS),
     ("iso KDN with beta", dict(variant=4, beta=A + 4 * MB), ENULL),
     ("iso KDN without proc noise", dict(variant=4, xi=None), ENULL),
     ("iso KDN without p0", dict(variant=4, p0=None), ENULL),

@@ -3,9 +3,10 @@
 Every case generates seeded inputs, runs the library on the GPU, runs the
 oracle on exactly the same rounded values, and compares each output tensor
 (o, S, p) by max|gpu - ref| / max|ref| against 1e-4 (float32 inputs) or 2e-2
-(bfloat16 inputs, float32 state).  The full-size workloads are compared on
-sampled (batch, head) streams, which the oracle computes one by one at full
-length in the same launch configuration the benchmark times.
+(bfloat16 inputs, float32 state).  The full-size prefill workloads are
+compared on every (batch, head) stream, in the launch configuration the
+benchmark times; the full decode workload on 256 streams spread over all
+sequences and heads.
 """
 import numpy as np
 import pytest
@@ -145,7 +146,7 @@ def test_prefill_kdn_degenerate_values(variant):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_prefill_state_in_place(variant):
+def test_prefill_state_in_place(variant, schedule):
     log(f"prefill S_out is S0 {variant}")
     inp = _inputs(variant, 2, 100, 2, 128, 128, "bf16", seed=18)
     ref = oracle_prefill(variant, inp)
@@ -157,6 +158,22 @@ def test_prefill_state_in_place(variant):
     gpu_prefill(variant, inp2, out=(o, S, p))
     check("o", np64(o), ref[0], TOL["bf16"])
     check("S (in place)", np64(S), ref[1], TOL["bf16"])
+    if variant not in KDNS:
+        return
+    # p_out == p0 as well: allowed with a workspace (two-pass schedule),
+    # refused by the single-pass schedule
+    S = inp["S0"].clone()
+    p = inp["p0"].clone()
+    inp3 = dict(inp, S0=S, p0=p)
+    if schedule == "single_pass":
+        with pytest.raises(kdn.KdnError) as ei:
+            gpu_prefill(variant, inp3, out=(o, S, p))
+        assert ei.value.status == 5          # KDN_ERR_ALIAS
+        return
+    gpu_prefill(variant, inp3, out=(o, S, p))
+    check("o (S and p in place)", np64(o), ref[0], TOL["bf16"])
+    check("S (S and p in place)", np64(S), ref[1], TOL["bf16"])
+    check("p (in place)", np64(p), ref[2], TOL["bf16"])
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -243,22 +260,56 @@ def test_workload_deltanet_fp32_full():
     compare_prefill("deltanet", inp, got, TOL["f32"])
 
 
-@pytest.mark.parametrize("name,heads", [
-    ("gated_deltanet", [(0, 0), (3, 15), (2, 7)]),
-    ("kda", [(0, 0), (1, 31)]),
-    ("diag_kdn", [(0, 0), (1, 15)]),
-    ("iso_kdn", [(0, 0), (1, 9)]),
-])
-def test_workload_full_size_sampled(name, heads):
+# Oracle results of the full-size workloads, shared by the two schedules.
+_FULL_REF = {}
+
+
+def _full_ref(name, inp, variant):
+    if name not in _FULL_REF:
+        import time
+        t0 = time.time()
+        _FULL_REF[name] = oracle_prefill(variant, inp)
+        log(f"  {name} oracle over every stream {time.time() - t0:.1f}s")
+    return _FULL_REF[name]
+
+
+def _check_every_stream(label, got, ref, tol):
+    """Per (batch, head) stream: max|gpu - ref| / max|ref| of that stream.
+    The first two axes of ``got``/``ref`` are (b, t) for o and (b, h) for S
+    and p; ``head_axis`` picks the head axis."""
+    worst, where = 0.0, None
+    g = np.asarray(got, np.float64)
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[label[1]]):
+            sl = (b, slice(None), h) if label[1] == 2 else (b, h)
+            e = gpu_util.rel_err(g[sl], ref[sl])
+            if e > worst:
+                worst, where = e, (b, h)
+    log(f"    {label[0]}: worst stream rel err {worst:.3e} at (b, h) = {where} "
+        f"(tol {tol:.0e})")
+    assert worst <= tol, f"{label[0]}: stream {where} relative error {worst:.3e} > {tol:.0e}"
+
+
+@pytest.mark.parametrize("name", ["gated_deltanet", "kda", "diag_kdn", "iso_kdn"])
+def test_workload_full_size_every_stream(name):
+    """The workload at full size in the launch configuration the benchmark
+    times; every (batch, head) stream compared with the oracle."""
     c = synth.CONFIGS[name]
-    log(f"workload {name} B{c['B']} H{c['H']} T{c['T']}: sampled heads {heads}")
+    log(f"workload {name} B{c['B']} H{c['H']} T{c['T']}: every stream")
     inp = synth.gen_config(name, device="cuda")
     o, S, p = gpu_prefill(c["variant"], inp)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
     if p is not None:
         assert torch.isfinite(p).all() and (p >= 0).all()
-    compare_prefill(c["variant"], inp, (o, S, p), TOL[c["dtype"]], heads=heads,
-                    label=name)
+    ro, rS, rp = _full_ref(name, inp, c["variant"])
+    tol = TOL[c["dtype"]]
+    check("o (whole tensor)", np64(o), ro, tol)
+    check("S (whole tensor)", np64(S), rS, tol)
+    _check_every_stream(("o", 2), np64(o), ro, tol)
+    _check_every_stream(("S", 1), np64(S), rS, tol)
+    if rp is not None:
+        check("p (whole tensor)", np64(p), rp, tol)
+        _check_every_stream(("p", 1), np64(p), rp, tol)
 
 
 def test_workload_decode_reduced_all_heads():
@@ -273,17 +324,24 @@ def test_workload_decode_reduced_all_heads():
 
 
 def test_workload_decode_full_size_sampled():
+    """The decode workload at full size (256 sequences x 32 heads, 1024
+    steps): 256 (sequence, head) streams, one per sequence with the heads
+    spread over all 32, so every workgroup slot position is covered."""
     c = synth.CONFIGS["decode_diag_kdn"]
-    log(f"workload decode diag_kdn N{c['N']} H{c['H']} {c['steps']} steps: sampled")
+    log(f"workload decode diag_kdn N{c['N']} H{c['H']} {c['steps']} steps: 256 streams")
     d = synth.gen_decode(c["N"], c["H"], c["steps"], c["dk"], c["dv"], c["dtype"],
                          seed=synth.seed_of("decode_diag_kdn"), device="cuda")
     os_, S, p = gpu_decode_run("diag_kdn", d)
     assert torch.isfinite(S).all() and torch.isfinite(p).all()
-    for (n, h) in [(0, 0), (255, 31), (97, 12)]:
-        sub = {k: (v[:, n:n + 1, h:h + 1] if k not in ("S0", "p0")
-                   else v[n:n + 1, h:h + 1]) for k, v in d.items()}
-        ro, rS, rp = oracle_prefill("diag_kdn", decode_inputs_as_prefill(sub))
-        check(f"o[n={n},h={h}]", np64(os_[:, n:n + 1, h:h + 1].transpose(0, 1)), ro,
-              TOL["bf16"])
-        check(f"S[n={n},h={h}]", np64(S[n:n + 1, h:h + 1]), rS, TOL["bf16"])
-        check(f"p[n={n},h={h}]", np64(p[n:n + 1, h:h + 1]), rp, TOL["bf16"])
+    ns = torch.arange(c["N"], device="cuda")
+    hs = (ns * 13 + 5) % c["H"]
+    # [steps, 256, 1, ...]: sequence n with its head hs[n] as a one-head batch
+    sub = {k: (v[:, ns, hs].unsqueeze(2) if k not in ("S0", "p0")
+               else v[ns, hs].unsqueeze(1)) for k, v in d.items()}
+    ro, rS, rp = oracle_prefill("diag_kdn", decode_inputs_as_prefill(sub))
+    go = os_[:, ns, hs].unsqueeze(2).transpose(0, 1)
+    check("o (256 streams)", np64(go), ro, TOL["bf16"])
+    check("S (256 streams)", np64(S[ns, hs].unsqueeze(1)), rS, TOL["bf16"])
+    check("p (256 streams)", np64(p[ns, hs].unsqueeze(1)), rp, TOL["bf16"])
+    _check_every_stream(("o", 2), np64(go), ro, TOL["bf16"])
+    _check_every_stream(("S", 1), np64(S[ns, hs].unsqueeze(1)), rS, TOL["bf16"])
