@@ -33,8 +33,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 # the largest prefill workload: diagonal KDN, B2 H16 T16384, d_k = d_v = 128, bf16
 HEADLINE = "diag_kdn"
-KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_variance.hip", "kdn_backward.hip",
-                  "kdn_decode.hip", "kdn_device.h", "kdn_launch.h", "kdn_workspace.h"]
+KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_prefill_chain.hip",
+                  "kdn_variance.hip", "kdn_backward.hip", "kdn_decode.hip", "kdn_device.h",
+                  "kdn_launch.h", "kdn_workspace.h"]
 
 
 def kernel_hash(names=KERNEL_SOURCES):

@@ -34,6 +34,9 @@ UNITS += [("kdn_prefill.hip", [f"-DKDN_PREFILL_VARIANT={v}"], f"kdn_prefill_{v}.
           for v in range(5)]
 UNITS += [("kdn_prefill.hip", ["-DKDN_PREFILL_DISPATCH"], "kdn_prefill_dispatch.o"),
           ("kdn_prefill_state.hip", [], "kdn_prefill_state.o"),
+          # MFMA accumulators in VGPRs: the chain applies VALU work (decay,
+          # subtraction, bf16 rounding) to every accumulator it produces
+          ("kdn_prefill_chain.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"], "kdn_prefill_chain.o"),
           ("kdn_variance.hip", [], "kdn_variance.o"),
           ("kdn_backward.hip", [], "kdn_backward.o")]
 

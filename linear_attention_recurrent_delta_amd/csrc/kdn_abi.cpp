@@ -133,14 +133,17 @@ unsigned long long kdn_chunk_prefill_workspace_size(kdn_variant variant, kdn_dty
                                                             H, d_k, C);
 }
 
-kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
-                             int H, int d_k, int d_v, int chunk, float mu,
-                             const void *q, const void *k, const void *v,
-                             const void *alpha, const void *beta,
-                             const void *proc_noise, const void *obs_noise,
-                             const float *S0, const float *p0, void *o,
-                             float *S_out, float *p_out, void *workspace,
-                             unsigned long long workspace_bytes, void *stream) {
+}  // extern "C"
+
+// Every argument check of kdn_chunk_prefill except the workspace's own (size,
+// alignment, overlap); `workspace` says whether the call has one (the
+// in-place variance rule depends on it).  No HIP call.
+kdn_status kdn::prefill_check(int variant, int dtype, int B, int T, int H, int d_k, int d_v,
+                              int chunk, const void *q, const void *k, const void *v,
+                              const void *alpha, const void *beta, const void *proc_noise,
+                              const void *obs_noise, const float *S0, const float *p0,
+                              const void *o, const float *S_out, const float *p_out,
+                              bool workspace, int *C_out) {
     int C = 0;
     if (kdn_status st = prefill_shape(variant, dtype, B, T, H, d_k, d_v, chunk, &C))
         return st;
@@ -200,6 +203,38 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     if (overlap(o, tok * d_v * es, S_out, n_S)) return KDN_ERR_ALIAS;
     if (kdn && (overlap(o, tok * d_v * es, p_out, n_p) || overlap(S_out, n_S, p_out, n_p)))
         return KDN_ERR_ALIAS;
+    *C_out = C;
+    return KDN_OK;
+}
+
+extern "C" {
+
+kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
+                             int H, int d_k, int d_v, int chunk, float mu,
+                             const void *q, const void *k, const void *v,
+                             const void *alpha, const void *beta,
+                             const void *proc_noise, const void *obs_noise,
+                             const float *S0, const float *p0, void *o,
+                             float *S_out, float *p_out, void *workspace,
+                             unsigned long long workspace_bytes, void *stream) {
+    int C = 0;
+    if (kdn_status st = kdn::prefill_check(variant, dtype, B, T, H, d_k, d_v, chunk, q, k, v,
+                                           alpha, beta, proc_noise, obs_noise, S0, p0, o,
+                                           S_out, p_out, workspace != nullptr, &C))
+        return st;
+    const long long bh = (long long)B * H;
+    const long long tok = bh * T;
+    const bool kdn = is_kdn(variant);
+    const long long es = dtype == KDN_BF16 ? 2 : 4;
+    const long long n_qk = tok * d_k * es, n_v = tok * d_v * es;
+    const long long n_a = variant == KDN_GATED_DELTANET ? tok * es
+                        : (variant == KDN_DELTANET ? 0 : tok * d_k * es);
+    const long long n_b = kdn ? 0 : tok * es;
+    const long long n_x = kdn ? tok * d_k * es : 0, n_r = kdn ? tok * es : 0;
+    const long long n_S = bh * d_k * d_v * 4, n_p = bh * p_per_head(variant, d_k) * 4;
+    struct R { const void *p; long long n; } ins[] = {
+        {q, n_qk}, {k, n_qk}, {v, n_v}, {alpha, n_a}, {beta, n_b},
+        {proc_noise, n_x}, {obs_noise, n_r}, {S0, n_S}, {p0, n_p}};
     // Workspace of the two-pass schedule: none when there is nothing to do.
     long long n_ws = 0;
     if (workspace && tok > 0) {
@@ -224,6 +259,8 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.xi = proc_noise; P.r = obs_noise;
     P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
     P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr; P.ws_stat = nullptr;
+    // bf16 two-pass: permuted records for the chain kernel
+    P.rec_perm = (n_ws > 0 && dtype == KDN_BF16) ? 1 : 0;
     P.states = nullptr;
     P.beta_out = nullptr;
     P.w_out = nullptr;
@@ -550,6 +587,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     F.xi = proc_noise; F.r = obs_noise;
     F.S0 = S0; F.p0 = p0; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
     F.ws = nullptr; F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
+    F.rec_perm = 0;                 // the gradient kernels read the plain order
     F.states = nullptr; F.beta_out = nullptr; F.w_out = nullptr; F.invs_out = nullptr;
     F.cus = device_cus();
     if (W.total > 0) {

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "kdn.h"
+
 namespace kdn {
 
 struct DecodeParams {
@@ -40,6 +42,10 @@ struct PrefillParams {
     float *ws_mob;
     float *ws_p0;
     float *ws_stat;
+    // Record matrices with the contraction index of each 32-group permuted
+    // (kdn_workspace.h), the layout the bf16 chain kernel reads; 0: plain
+    // fragment order (the state kernel and the gradient kernels).
+    int rec_perm;
     // Gradient computation: S at every chunk start is saved here by the state
     // pass ([batch*head][chunk][dk][dv] in the call's element type, the
     // precision the gradient products read it in; null otherwise).
@@ -114,6 +120,18 @@ hipError_t launch_prefill_prep_v3(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_prefill_prep_v4(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_variance_scan(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_prefill_state(const PrefillParams &P, hipStream_t stream);
+// bf16 state pass on permuted records, one wave per 16-column block
+hipError_t launch_prefill_chain(const PrefillParams &P, hipStream_t stream);
+
+// Every argument check of kdn_chunk_prefill except the workspace's own;
+// `workspace` tells whether the call has one.  The chunk length in use goes
+// to *C_out.  Host only, no HIP call (kdn_abi.cpp).
+kdn_status prefill_check(int variant, int dtype, int B, int T, int H, int d_k, int d_v,
+                         int chunk, const void *q, const void *k, const void *v,
+                         const void *alpha, const void *beta, const void *proc_noise,
+                         const void *obs_noise, const float *S0, const float *p0,
+                         const void *o, const float *S_out, const float *p_out,
+                         bool workspace, int *C_out);
 
 // Bytes of workspace the two-pass schedule needs (0 when there is no chunk).
 long long prefill_workspace_bytes(int variant, int bf16, long long B, long long T,

@@ -235,9 +235,11 @@ __device__ __forceinline__ void mma16_f32(f32x4 &acc, const float *A, int lda,
 }
 
 // A-operand fragment order of the workspace (kdn_workspace.h): copy the
-// R x K matrix at src (LDS, pitch in elements) to dst, 16 bytes per unit.
+// R x K matrix at src (LDS, pitch in elements) to dst, 16 bytes per unit;
+// with perm (bf16), the columns of each 32-group in the permuted order.
 template <typename E, int R, int K, int NT>
-__device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, int tid) {
+__device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, int tid,
+                                           bool perm) {
     constexpr int EPU = 16 / (int)sizeof(E);
     constexpr int KG = sizeof(E) == 2 ? 32 : 16;
     constexpr int NU = R * K / EPU;
@@ -252,7 +254,14 @@ __device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, i
             const int row = m * 16 + (l & 15);
             uint4 val;
             if constexpr (sizeof(E) == 2) {
-                val = *reinterpret_cast<const uint4 *>(src + row * pitch + g * 32 + (l >> 4) * 8);
+                if (perm) {
+                    const E *sp = src + row * pitch + g * 32 + (l >> 4) * 4;
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(sp);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(sp + 16);
+                    val = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                } else {
+                    val = *reinterpret_cast<const uint4 *>(src + row * pitch + g * 32 + (l >> 4) * 8);
+                }
             } else {
                 const float *sp = reinterpret_cast<const float *>(src) + row * pitch + g * 16 + (l >> 4);
                 val = __builtin_bit_cast(uint4, make_float4(sp[0], sp[4], sp[8], sp[12]));
@@ -264,7 +273,7 @@ __device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, i
 
 // As store_frag, each element computed by f(row, k) (a float).
 template <typename E, int R, int K, int NT, typename F>
-__device__ __forceinline__ void store_frag_fn(char *dst, int tid, F f) {
+__device__ __forceinline__ void store_frag_fn(char *dst, int tid, bool perm, F f) {
     constexpr int EPU = 16 / (int)sizeof(E);
     constexpr int KG = sizeof(E) == 2 ? 32 : 16;
     constexpr int NU = R * K / EPU;
@@ -279,7 +288,9 @@ __device__ __forceinline__ void store_frag_fn(char *dst, int tid, F f) {
             E v[EPU];
 #pragma unroll
             for (int e = 0; e < EPU; ++e) {
-                const int k = sizeof(E) == 2 ? g * 32 + (l >> 4) * 8 + e : g * 16 + e * 4 + (l >> 4);
+                const int k = sizeof(E) == 2
+                                  ? (perm ? perm_col(g, l >> 4, e) : g * 32 + (l >> 4) * 8 + e)
+                                  : g * 16 + e * 4 + (l >> 4);
                 v[e] = from_f32<E>(f(row, k));
             }
             d[u] = *reinterpret_cast<const uint4 *>(v);
@@ -344,6 +355,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    // records in the permuted column order (bf16 chain kernel)
+    const bool perm = sizeof(E) == 2 && P.rec_perm != 0;
 
     // Workgroup -> (batch*head, value block).  Dispatch is round-robin over
     // the 8 XCDs; place the value blocks of one head on one XCD.
@@ -394,6 +407,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             ST[j * PK + i] = from_f32<E>(sacc[u][r]);
         }
     }
+    // Prep kernel, diagonal KDN: the variance chain of a chunk runs on every
+    // thread, NT / DK segments of tokens per channel (2v below), when the
+    // segment maps fit the W' region.
+    constexpr bool KSEG = KDN && PREP && NT % DK == 0 && C % (4 * (NT / DK)) == 0 &&
+                          LY::SZ_CK >= NT * 16;
     float p_reg = 0.f;                 // KDN variance of channel tid (isotropic:
                                        // of the head, in wave 0)
     float p_nxt = 0.f;                 // PREP: variance at the next unit's start
@@ -413,8 +431,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     auto fetch = [&](int bs, int cs) {
         const int Ls = min(C, T - cs);
         const long tk = ((long)(bs / H) * T + cs) * H + bs % H;
-        if (PREP && KDN && tid < DK)
-            p_nxt = P.ws_p0[((long)bs * NC + cs / C) * DK + tid];
+        if (PREP && KDN && (KSEG || tid < DK))
+            p_nxt = P.ws_p0[((long)bs * NC + cs / C) * DK + tid % DK];
         if (PREP && ISO && tid < WAVE)
             p_nxt = P.ws_p0[(long)bs * NC + cs / C];
         rk.fetch(gk + tk * DK, sk_, Ls, tid);
@@ -522,7 +540,72 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         }
 
         // ---------------- 2. decays and write vectors ----------------
+        if constexpr (KSEG) {
+            // 2v. Variance chain of the chunk, per channel i, on every thread:
+            // thread (seg, i) owns tokens [seg SL, seg SL + SL).  Each token's
+            // step p -> p- r / (r + mu p- k^2), p- = a^2 p + xi, is a Mobius
+            // map [[a^2, xi], [c a^2, c xi + 1]] (c = mu k^2 / r; for r = 0 the
+            // limits of the update), so (1) each thread composes its
+            // segment's maps, (2) applies the earlier segments' maps to the
+            // chunk-start variance, (3) runs its tokens in order from there
+            // ("给记忆装一个信任度探测器 ...", section "各向同性近似：把整个头压缩成
+            // 一个数", last paragraph: the variance recursion composes as 2 x 2
+            // matrix products).  Padded tokens (a = 1, xi = 0, k = 0, r = 1)
+            // are the identity.
+            constexpr int NSEG = NT / DK, SL = C / NSEG;
+            const int i = tid % DK, seg = tid / DK, tb0 = seg * SL;
+            const float mu = P.mu;
+            float4 *SM = reinterpret_cast<float4 *>(Wp);   // dead until 2c
+            // token tb0 + s2 of channel i: a^2, xi, k, r and mu k^2
+            auto tok = [&](int s2, float &a2, float &xx, float &kk, float &rr, float &m2) {
+                const int t = tb0 + s2;
+                kk = ld(Kt + t * PK + i);
+                const float a = ld(ALP + t * PK + i);
+                a2 = a * a;
+                xx = ld(XR + t * PK + i);
+                rr = s_r[t];
+                m2 = mu * kk * kk;
+            };
+            float ma = 1.f, mb = 0.f, mc = 0.f, md = 1.f;
+#pragma unroll 4
+            for (int s2 = 0; s2 < SL; ++s2) {
+                float a2, xx, kk, rr, m2;
+                tok(s2, a2, xx, kk, rr, m2);
+                const bool rp = rr > 0.f;
+                const bool kill = !rp && m2 != 0.f;         // r = 0: p -> 0
+                const float c = rp ? m2 * fast_rcp(rr) : 0.f;
+                const float ya = kill ? 0.f : a2, yb = kill ? 0.f : xx;
+                const float na = fmaf(ya, ma, yb * mc), nb = fmaf(ya, mb, yb * md);
+                mc = fmaf(c, na, mc);
+                md = fmaf(c, nb, md);
+                ma = na;
+                mb = nb;
+                if ((s2 & 3) == 3) {          // SL is a multiple of 4
+                    const float sc = fast_rcp(fmaxf(fmaxf(ma, mb), fmaxf(mc, md)));
+                    ma *= sc; mb *= sc; mc *= sc; md *= sc;
+                }
+            }
+            SM[seg * DK + i] = make_float4(ma, mb, mc, md);
+            __syncthreads();
+            float pc = p_reg;
+            for (int s2 = 0; s2 < seg; ++s2) {
+                const float4 y = SM[s2 * DK + i];
+                pc = fmaf(y.x, pc, y.y) / fmaf(y.z, pc, y.w);
+            }
+#pragma unroll 4
+            for (int s2 = 0; s2 < SL; ++s2) {
+                float a2, xx, kk, rr, m2;
+                tok(s2, a2, xx, kk, rr, m2);
+                const float pm = fmaf(a2, pc, xx);
+                U32[(tb0 + s2) * PP + i] = pm * kk;
+                const float den = fmaf(m2, pm, rr);
+                pc = (den != 0.f) ? pm * rr * fast_rcp(den) : pm;
+            }
+            if (ts >= 0)
+                group_products();          // decays, independent of the variance
+        }
         if constexpr (KDN) {
+          if constexpr (!KSEG) {
             // Variance chain, one thread per key channel (sequential in t):
             //   p- = a^2 p + xi,  u = p- k,  p = p- r / (r + mu p- k^2).
             // Inputs are read a few tokens ahead into registers so the LDS
@@ -568,6 +651,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                 }
                 p_reg = pc;
             }
+          }
             __syncthreads();
             // innovation variances s_t = r_t + sum_i u_ti k_ti
             constexpr int TPR = LY::TPR;           // threads per token row
@@ -964,19 +1048,19 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
             if constexpr (SPREP) {
-                store_frag_fn<E, C, DK, 256>(rec + LW.off_kd, tid, [&](int t, int i) {
+                store_frag_fn<E, C, DK, 256>(rec + LW.off_kd, tid, perm, [&](int t, int i) {
                     return ld(Kt + t * PK + i) * s_gt[t]; });
-                store_frag_fn<E, C, DK, 256>(rec + LW.off_qd, tid, [&](int t, int i) {
+                store_frag_fn<E, C, DK, 256>(rec + LW.off_qd, tid, perm, [&](int t, int i) {
                     return ld(Qt + t * PK + i) * s_gt[t]; });
                 // W~^T (strided reads of K): half here, half on waves 4-7 below
-                store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, [&](int i, int t) {
+                store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, perm, [&](int i, int t) {
                     return ld(Kt + t * PK + i) * s_wsc[t]; });
             } else {
-                store_frag<E, C, DK, 256>(rec + LW.off_kd, Kt, PK, tid);
-                store_frag<E, C, DK, 256>(rec + LW.off_qd, Qt, PK, tid);
-                store_frag<E, DK, C, 256>(rec + LW.off_wdt, WtT, PC, tid);
+                store_frag<E, C, DK, 256>(rec + LW.off_kd, Kt, PK, tid, perm);
+                store_frag<E, C, DK, 256>(rec + LW.off_qd, Qt, PK, tid, perm);
+                store_frag<E, DK, C, 256>(rec + LW.off_wdt, WtT, PC, tid, perm);
             }
-            store_frag<E, C, C, 256>(rec + LW.off_aqk, AQ, PC, tid);
+            store_frag<E, C, C, 256>(rec + LW.off_aqk, AQ, PC, tid, perm);
         } else if (!PREP && wv < 4) {
             for (int x = wv; x < NTU; x += 4) {
                 const int mi = x / NTJ, nj = x % NTJ;
@@ -1072,7 +1156,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             // the other half of its units, after this wave's diagonal block
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
-            store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, [&](int i, int t) {
+            store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, perm, [&](int i, int t) {
                 return ld(Kt + t * PK + i) * s_wsc[t]; });
         }
         __syncthreads();
@@ -1206,7 +1290,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             // ---------------- record of this chunk ----------------
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
-            store_frag<E, C, C, NT>(rec + LW.off_tm, Tm, PC, tid);
+            store_frag<E, C, C, NT>(rec + LW.off_tm, Tm, PC, tid, perm);
             if (DECAY && tid < DK)
                 reinterpret_cast<float *>(rec + LW.off_gc)[tid] = s_gc[tid];
             __syncthreads();            // LDS reads done before the next commit
@@ -1409,7 +1493,7 @@ static hipError_t launch_two_pass(const PrefillParams &P, hipStream_t st) {
         if (e != hipSuccess)
             return e;
     }
-    return launch_prefill_state(P, st);
+    return P.rec_perm ? launch_prefill_chain(P, st) : launch_prefill_state(P, st);
 }
 
 hipError_t launch_prefill(const PrefillParams &P, hipStream_t st) {

@@ -21,6 +21,16 @@
 //     float: X[m*16 + (l & 15)][g*16 + s*4 + (l >> 4)],       s = 0..3
 //   i.e. exactly the A operand of v_mfma_f32_16x16x32_bf16 (one step) or of
 //   four v_mfma_f32_16x16x4_f32 steps.
+// Permuted order (bf16 only; the forward prefill's records): element e of
+// lane l in group g holds column
+//     g*32 + (e < 4 ? 4 (l >> 4) + e : 16 + 4 (l >> 4) + e - 4)
+//   instead of g*32 + (l >> 4)*8 + e: the k-slots of lane l then line up
+//   with the rows 4 (l >> 4) .. + 3 that lane l holds of two adjacent 16-row
+//   accumulator tiles, so a product's B operand can be taken from the lane's
+//   own accumulators (kdn_prefill_chain.hip).
+__host__ __device__ inline int perm_col(int g, int q, int e) {
+    return g * 32 + (e & 4 ? 16 : 0) + 4 * q + (e & 3);
+}
 //
 // For diagonal KDN the workspace also holds, after the records:
 //   Mob  [bh][chunk][DK][4] float32  per-chunk composition of the variance
