@@ -82,7 +82,10 @@ typedef enum kdn_status {
     KDN_ERR_ALIGN = 4,        /* a pointer is not aligned as required      */
     KDN_ERR_ALIAS = 5,        /* an output overlaps an input it may not    */
     KDN_ERR_HIP = 6,          /* the HIP runtime refused the launch        */
-    KDN_ERR_WORKSPACE = 7     /* workspace smaller than the size query     */
+    KDN_ERR_WORKSPACE = 7,    /* workspace smaller than the size query     */
+    KDN_ERR_SCRATCH = 8       /* kdn_chunk_prefill_noalloc: one chunk of
+                                 every head of a sequence exceeds the
+                                 library's static scratch                  */
 } kdn_status;
 
 /*
@@ -144,6 +147,43 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype,
                              void *o, float *S_out, float *p_out,
                              void *workspace, unsigned long long workspace_bytes,
                              void *stream);
+
+/*
+ * kdn_chunk_prefill without a caller-provided workspace and without any
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and checks as kdn_chunk_prefill with a workspace
+ * (the two-pass schedule; p_out may be exactly p0), but the workspace is the
+ * library's own static device array of KDN_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ * When the call's workspace would not fit in it, the call runs each sequence
+ * in segments of whole chunks, one after another on `stream`, each segment
+ * continuing from the previous one's S_out / p_out (the recurrence over
+ * T1 + T2 tokens is the recurrence over T2 tokens from the state after T1);
+ * results then differ from one kdn_chunk_prefill call by floating-point
+ * rounding only.  KDN_ERR_SCRATCH if the workspace of a single chunk of all
+ * H heads of one sequence exceeds the scratch (bf16, d_k = d_v = 128, C = 64:
+ * H > 1016 for the write-strength variants, H > 978 for diagonal KDN).
+ * Every argument is checked before the first launch.  Calls on one GPU share
+ * its scratch: calls that overlap in time on one GPU race (serialise them,
+ * e.g. on one stream).  Nothing is allocated or freed, on the host or the
+ * device, by this call.
+ */
+#define KDN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+kdn_status kdn_chunk_prefill_noalloc(kdn_variant variant, kdn_dtype dtype,
+                                     int B, int T, int H, int d_k, int d_v, int chunk,
+                                     float mu,
+                                     const void *q, const void *k, const void *v,
+                                     const void *alpha, const void *beta,
+                                     const void *proc_noise, const void *obs_noise,
+                                     const float *S0, const float *p0,
+                                     void *o, float *S_out, float *p_out,
+                                     void *stream);
+
+/* Size in bytes of the static scratch kdn_chunk_prefill_noalloc uses. */
+unsigned long long kdn_noalloc_scratch_bytes(void);
 
 /*
  * Bytes of workspace kdn_chunk_prefill's two-pass schedule needs for these
@@ -297,7 +337,7 @@ int kdn_chunk_prefill_chunk_size(kdn_dtype dtype, int d_k, int d_v, int chunk);
 /* ABI version of this header (incremented on any incompatible change). */
 int kdn_abi_version(void);
 
-#define KDN_ABI_VERSION 4
+#define KDN_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

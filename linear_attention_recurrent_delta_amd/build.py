@@ -38,6 +38,7 @@ UNITS += [("kdn_prefill.hip", ["-DKDN_PREFILL_DISPATCH"], "kdn_prefill_dispatch.
           # subtraction, bf16 rounding) to every accumulator it produces
           ("kdn_prefill_chain.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"], "kdn_prefill_chain.o"),
           ("kdn_variance.hip", [], "kdn_variance.o"),
+          ("kdn_noalloc.hip", [], "kdn_noalloc.o"),
           ("kdn_backward.hip", [], "kdn_backward.o")]
 
 

@@ -83,6 +83,7 @@ const char *kdn_status_string(kdn_status s) {
     case KDN_ERR_ALIAS: return "an output overlaps an input it may not overlap";
     case KDN_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     case KDN_ERR_WORKSPACE: return "the workspace is smaller than kdn_chunk_prefill_workspace_size";
+    case KDN_ERR_SCRATCH: return "one chunk of every head of a sequence needs more than the library's static scratch";
     }
     return "unknown status";
 }

@@ -32,7 +32,7 @@ def _new_p(vid, N, H, dk, device):
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "KDN_OK", 1: "KDN_ERR_NULL", 2: "KDN_ERR_SHAPE",
           3: "KDN_ERR_UNSUPPORTED", 4: "KDN_ERR_ALIGN", 5: "KDN_ERR_ALIAS",
-          6: "KDN_ERR_HIP", 7: "KDN_ERR_WORKSPACE"}
+          6: "KDN_ERR_HIP", 7: "KDN_ERR_WORKSPACE", 8: "KDN_ERR_SCRATCH"}
 
 _lib = None
 
@@ -56,6 +56,10 @@ def load(path: str = LIB_PATH):
     lib.kdn_chunk_prefill.restype = i
     u64 = ctypes.c_ulonglong
     lib.kdn_chunk_prefill.argtypes = [i, i, i, i, i, i, i, i, f] + [vp] * 12 + [vp, u64, vp]
+    lib.kdn_chunk_prefill_noalloc.restype = i
+    lib.kdn_chunk_prefill_noalloc.argtypes = [i, i, i, i, i, i, i, i, f] + [vp] * 12 + [vp]
+    lib.kdn_noalloc_scratch_bytes.restype = u64
+    lib.kdn_noalloc_scratch_bytes.argtypes = []
     lib.kdn_chunk_prefill_workspace_size.restype = u64
     lib.kdn_chunk_prefill_workspace_size.argtypes = [i] * 8 + [ctypes.POINTER(i)]
     lib.kdn_recurrent_decode.restype = i
@@ -171,6 +175,24 @@ def kdn_chunk_prefill(variant, dtype, B, T, H, d_k, d_v, chunk, mu, q, k, v,
         _ptr(o), _ptr(S_out), _ptr(p_out), _ptr(workspace), int(workspace_bytes),
         _stream(stream))
     _check(lib, st)
+
+
+def kdn_chunk_prefill_noalloc(variant, dtype, B, T, H, d_k, d_v, chunk, mu, q, k, v,
+                              alpha, beta, proc_noise, obs_noise, S0, p0, o, S_out,
+                              p_out, stream=None):
+    """Raw entry point: same arguments as the C function (the two-pass
+    prefill on the library's static scratch; allocates nothing)."""
+    lib = load()
+    st = lib.kdn_chunk_prefill_noalloc(
+        int(variant), int(dtype), int(B), int(T), int(H), int(d_k), int(d_v),
+        int(chunk), float(mu), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+        _ptr(beta), _ptr(proc_noise), _ptr(obs_noise), _ptr(S0), _ptr(p0),
+        _ptr(o), _ptr(S_out), _ptr(p_out), _stream(stream))
+    _check(lib, st)
+
+
+def kdn_noalloc_scratch_bytes() -> int:
+    return int(load().kdn_noalloc_scratch_bytes())
 
 
 def kdn_chunk_prefill_workspace_size(variant, dtype, B, T, H, d_k, d_v, chunk):

@@ -16,7 +16,7 @@ from linear_attention_recurrent_delta_amd import kdn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kdn.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EHIP, EWS = range(8)
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EALIAS, EHIP, EWS, ESCRATCH = range(9)
 A = 1 << 32          # fake, 16-byte aligned device addresses spaced far apart
 MB = 1 << 26
 
@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
               "kdn_recurrent_decode_multi", "kdn_chunk_prefill_backward",
               "kdn_chunk_prefill_backward_workspace_size",
               "kdn_chunk_prefill_chunk_size", "kdn_abi_version",
-              "kdn_chunk_prefill_workspace_size"):
+              "kdn_chunk_prefill_workspace_size", "kdn_chunk_prefill_noalloc",
+              "kdn_noalloc_scratch_bytes"):
         assert n in names
 
 
@@ -49,12 +50,12 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.kdn_abi_version() == 4
+    assert lib.kdn_abi_version() == 5
 
 
 def test_status_strings(lib):
     seen = set()
-    for s in range(8):
+    for s in range(9):
         msg = lib.kdn_status_string(s).decode()
         assert msg and msg not in seen
         seen.add(msg)
@@ -383,3 +384,24 @@ def test_binding_raises_with_status(lib):
 def test_binding_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         kdn.load(str(tmp_path / "libkdn.so"))
+
+
+def test_noalloc_validation(lib):
+    """kdn_chunk_prefill_noalloc checks every argument of the full call, and
+    the static scratch's limit, before any HIP call."""
+    f = lib.kdn_chunk_prefill_noalloc
+    assert lib.kdn_noalloc_scratch_bytes() == 64 << 20
+
+    def call(**over):
+        a = list(_prefill_args(**over))
+        return f(*(a[:21] + [None]))          # no workspace arguments
+    for name, over, status in PREFILL_CASES:
+        if "without workspace" in name:
+            continue                          # in-place p is allowed here
+        assert call(**over) == status, name
+    # one chunk of all heads of a sequence exceeds the 64 MiB scratch
+    # (d = 64: 41,216 bytes per head and chunk; the fake tensors stay apart)
+    big = dict(B=1, T=10, H=1700, dk=64, dv=64)
+    assert call(**big) == ESCRATCH
+    assert call(variant=3, **big) == ESCRATCH
+    assert call(q=None, **big) == ENULL         # argument errors come first
