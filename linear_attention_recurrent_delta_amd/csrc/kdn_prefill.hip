@@ -407,11 +407,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             ST[j * PK + i] = from_f32<E>(sacc[u][r]);
         }
     }
-    // Prep kernel, diagonal KDN: the variance chain of a chunk runs on every
-    // thread, NT / DK segments of tokens per channel (2v below), when the
-    // segment maps fit the W' region.
-    constexpr bool KSEG = KDN && PREP && NT % DK == 0 && C % (4 * (NT / DK)) == 0 &&
-                          LY::SZ_CK >= NT * 16;
     float p_reg = 0.f;                 // KDN variance of channel tid (isotropic:
                                        // of the head, in wave 0)
     float p_nxt = 0.f;                 // PREP: variance at the next unit's start
@@ -431,8 +426,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     auto fetch = [&](int bs, int cs) {
         const int Ls = min(C, T - cs);
         const long tk = ((long)(bs / H) * T + cs) * H + bs % H;
-        if (PREP && KDN && (KSEG || tid < DK))
-            p_nxt = P.ws_p0[((long)bs * NC + cs / C) * DK + tid % DK];
+        if (PREP && KDN && tid < DK)
+            p_nxt = P.ws_p0[((long)bs * NC + cs / C) * DK + tid];
         if (PREP && ISO && tid < WAVE)
             p_nxt = P.ws_p0[(long)bs * NC + cs / C];
         rk.fetch(gk + tk * DK, sk_, Ls, tid);
@@ -540,72 +535,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         }
 
         // ---------------- 2. decays and write vectors ----------------
-        if constexpr (KSEG) {
-            // 2v. Variance chain of the chunk, per channel i, on every thread:
-            // thread (seg, i) owns tokens [seg SL, seg SL + SL).  Each token's
-            // step p -> p- r / (r + mu p- k^2), p- = a^2 p + xi, is a Mobius
-            // map [[a^2, xi], [c a^2, c xi + 1]] (c = mu k^2 / r; for r = 0 the
-            // limits of the update), so (1) each thread composes its
-            // segment's maps, (2) applies the earlier segments' maps to the
-            // chunk-start variance, (3) runs its tokens in order from there
-            // ("给记忆装一个信任度探测器 ...", section "各向同性近似：把整个头压缩成
-            // 一个数", last paragraph: the variance recursion composes as 2 x 2
-            // matrix products).  Padded tokens (a = 1, xi = 0, k = 0, r = 1)
-            // are the identity.
-            constexpr int NSEG = NT / DK, SL = C / NSEG;
-            const int i = tid % DK, seg = tid / DK, tb0 = seg * SL;
-            const float mu = P.mu;
-            float4 *SM = reinterpret_cast<float4 *>(Wp);   // dead until 2c
-            // token tb0 + s2 of channel i: a^2, xi, k, r and mu k^2
-            auto tok = [&](int s2, float &a2, float &xx, float &kk, float &rr, float &m2) {
-                const int t = tb0 + s2;
-                kk = ld(Kt + t * PK + i);
-                const float a = ld(ALP + t * PK + i);
-                a2 = a * a;
-                xx = ld(XR + t * PK + i);
-                rr = s_r[t];
-                m2 = mu * kk * kk;
-            };
-            float ma = 1.f, mb = 0.f, mc = 0.f, md = 1.f;
-#pragma unroll 4
-            for (int s2 = 0; s2 < SL; ++s2) {
-                float a2, xx, kk, rr, m2;
-                tok(s2, a2, xx, kk, rr, m2);
-                const bool rp = rr > 0.f;
-                const bool kill = !rp && m2 != 0.f;         // r = 0: p -> 0
-                const float c = rp ? m2 * fast_rcp(rr) : 0.f;
-                const float ya = kill ? 0.f : a2, yb = kill ? 0.f : xx;
-                const float na = fmaf(ya, ma, yb * mc), nb = fmaf(ya, mb, yb * md);
-                mc = fmaf(c, na, mc);
-                md = fmaf(c, nb, md);
-                ma = na;
-                mb = nb;
-                if ((s2 & 3) == 3) {          // SL is a multiple of 4
-                    const float sc = fast_rcp(fmaxf(fmaxf(ma, mb), fmaxf(mc, md)));
-                    ma *= sc; mb *= sc; mc *= sc; md *= sc;
-                }
-            }
-            SM[seg * DK + i] = make_float4(ma, mb, mc, md);
-            __syncthreads();
-            float pc = p_reg;
-            for (int s2 = 0; s2 < seg; ++s2) {
-                const float4 y = SM[s2 * DK + i];
-                pc = fmaf(y.x, pc, y.y) / fmaf(y.z, pc, y.w);
-            }
-#pragma unroll 4
-            for (int s2 = 0; s2 < SL; ++s2) {
-                float a2, xx, kk, rr, m2;
-                tok(s2, a2, xx, kk, rr, m2);
-                const float pm = fmaf(a2, pc, xx);
-                U32[(tb0 + s2) * PP + i] = pm * kk;
-                const float den = fmaf(m2, pm, rr);
-                pc = (den != 0.f) ? pm * rr * fast_rcp(den) : pm;
-            }
-            if (ts >= 0)
-                group_products();          // decays, independent of the variance
-        }
         if constexpr (KDN) {
-          if constexpr (!KSEG) {
             // Variance chain, one thread per key channel (sequential in t):
             //   p- = a^2 p + xi,  u = p- k,  p = p- r / (r + mu p- k^2).
             // Inputs are read a few tokens ahead into registers so the LDS
@@ -651,7 +581,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                 }
                 p_reg = pc;
             }
-          }
             __syncthreads();
             // innovation variances s_t = r_t + sum_i u_ti k_ti
             constexpr int TPR = LY::TPR;           // threads per token row

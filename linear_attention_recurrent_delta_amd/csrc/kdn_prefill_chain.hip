@@ -81,6 +81,16 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
     constexpr int NSF = GK * NTJ;       // S fragments handed to the output wave
     constexpr int NEF = GC * NTJ;       // E fragments
     __shared__ bf16x8 slot[2][(NSF + NEF) * 64];
+    // v and o tiles move between global memory and the accumulator layout
+    // through LDS: 16-byte row accesses in global memory (LPR lanes per row,
+    // RPI rows per instruction, NVI instructions per chunk), 2- and 8-byte
+    // LDS accesses in the MFMA layout.
+    constexpr int LPR = NV / 8, RPI = 64 / LPR, NVI = C / RPI;
+    constexpr int PVT = C + 4;            // v^T [column][token], pitch (bf16)
+    constexpr int POB = NV + 8;           // o [token][column], pitch (bf16)
+    static_assert(RPI * NVI == C && (PVT * 2) % 8 == 0 && (POB * 2) % 16 == 0, "v/o tiles");
+    __shared__ __attribute__((aligned(16))) bf16 VT[NV * PVT];
+    __shared__ __attribute__((aligned(16))) bf16 OB[C * POB];
 
     const int lane = threadIdx.x & 63;
     const bool chain = threadIdx.x < 64;
@@ -107,8 +117,10 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
     const unsigned lane16 = (unsigned)lane * 16u;
     // v / o element (t = 16 m + 4 q + r, column 16 j + n) of a chunk: the lane
     // part in a register, the (m, r, j) part as a uniform offset
-    const unsigned vlane = (unsigned)((4 * q * hdv + n) * 2);
-    auto vsoff = [&](int m, int r, int j) { return (int)(((16 * m + r) * hdv + 16 * j) * 2); };
+    // row access of the v / o tiles: lane -> (token row, 8 columns)
+    const int rrow = lane / LPR, rcol = (lane % LPR) * 8;
+    const unsigned rlane = (unsigned)((rrow * hdv + rcol) * 2);
+    auto rsoff = [&](int h) { return (int)(h * RPI * hdv * 2); };
     auto rec = [&](int c) { return rsrc(ws + (long)c * LW.rec, (unsigned)LW.rec); };
     // rows [c C, c C + L) of v or o in range; the rest read 0 / are dropped
     auto rows = [&](const bf16 *base, int c) {
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                                          : 0.f;
         bf16x8 kf[NB][GK], tf[NB][GC], wf[NIB][GC];
         f32x4 gm[NIB];
-        unsigned short vr[NB][4][NTJ];  // raw bits; widened only where used
+        u32x4 vraw[NVI];                // next chunk's v rows, 8 bf16 per lane
         auto load_k = [&](int c) {
             const auto rr = rec(c);
 #pragma unroll
@@ -142,13 +154,19 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
         auto load_v = [&](int c) {
             const auto vrr = rows(gv, c);
 #pragma unroll
-            for (int m = 0; m < NB; ++m)
+            for (int h = 0; h < NVI; ++h)
+                vraw[h] = __builtin_amdgcn_raw_buffer_load_b128(vrr, (int)rlane, rsoff(h), 0);
+        };
+        // the loaded rows into v^T (this wave alone reads VT, after its own
+        // writes, so no barrier is involved)
+        auto commit_v = [&]() {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+            for (int h = 0; h < NVI; ++h) {
+                const bf16x8 x = __builtin_bit_cast(bf16x8, vraw[h]);
 #pragma unroll
-                    for (int j = 0; j < NTJ; ++j)
-                        vr[m][r][j] = __builtin_amdgcn_raw_buffer_load_b16(
-                            vrr, (int)vlane, vsoff(m, r, j), 0);
+                for (int e = 0; e < 8; ++e)
+                    VT[(rcol + e) * PVT + h * RPI + rrow] = x[e];
+            }
         };
         auto load_t = [&](int c) {
             const auto rr = rec(c);
@@ -184,6 +202,7 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
             load_v(0);
             load_t(0);
             load_w(0);
+            commit_v();
         }
         for (int c = 0; c < NC; ++c) {
             const int cn = min(c + 1, NC - 1);   // the last chunk reloads itself
@@ -227,11 +246,16 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
 #pragma unroll
             for (int m = 0; m < NB; ++m)
 #pragma unroll
-                for (int j = 0; j < NTJ; ++j)
+                for (int j = 0; j < NTJ; ++j) {
+                    // v[16 m + 4 q + r][16 j + n], r = 0..3: one 8-byte read
+                    const uint2 vv = *reinterpret_cast<const uint2 *>(
+                        VT + (16 * j + n) * PVT + 16 * m + 4 * q);
+                    const unsigned w4[4] = {vv.x << 16, vv.x & 0xffff0000u, vv.y << 16,
+                                            vv.y & 0xffff0000u};
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        ua[m][j][r] = __builtin_bit_cast(float, (unsigned)vr[m][r][j] << 16) -
-                                      ua[m][j][r];
+                        ua[m][j][r] = __builtin_bit_cast(float, w4[r]) - ua[m][j][r];
+                }
             load_v(cn);
             bf16x8 ub[GC][NTJ];
 #pragma unroll
@@ -270,6 +294,7 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                     for (int j = 0; j < NTJ; ++j)
                         sacc[i][j] = mfma(wf[i][g], eb[g][j], sacc[i][j]);
             load_w(cn);
+            commit_v();                 // v of chunk cn, loaded during this chunk
         }
 #pragma unroll
         for (int i = 0; i < NIB; ++i)
@@ -361,16 +386,23 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                 asm volatile("" ::"v"(pf[k]));
             load_qa(cn);
             touch(c + 2);
-            const auto orr = rows(go, c);
+            // o through LDS into rows: 2-byte writes in the MFMA layout, then
+            // 16-byte reads and stores of whole row segments (rows past the
+            // sequence end fall outside the descriptor and are dropped)
 #pragma unroll
             for (int m = 0; m < NB; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int j = 0; j < NTJ; ++j)
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            __builtin_bit_cast(unsigned short, static_cast<bf16>(oa[m][j][r])),
-                            orr, (int)vlane, vsoff(m, r, j), 0);
+                        OB[(16 * m + 4 * q + r) * POB + 16 * j + n] =
+                            static_cast<bf16>(oa[m][j][r]);
+            const auto orr = rows(go, c);
+#pragma unroll
+            for (int h = 0; h < NVI; ++h) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(OB + (h * RPI + rrow) * POB + rcol);
+                __builtin_amdgcn_raw_buffer_store_b128(x, orr, (int)rlane, rsoff(h), 0);
+            }
         }
         if (NC > 0) {
 #pragma unroll
