@@ -538,41 +538,44 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
         if constexpr (KDN) {
             // Variance chain, one thread per key channel (sequential in t):
             //   p- = a^2 p + xi,  u = p- k,  p = p- r / (r + mu p- k^2).
-            // Inputs are read a few tokens ahead into registers so the LDS
-            // latency stays off the dependent chain.  Tokens past the end of
-            // the sequence were staged as a = 1, xi = 0, k = 0, r = 1, which
-            // leaves p unchanged bit for bit.
+            // The inputs of a block of CB tokens are read into registers one
+            // block ahead; the scheduling barrier keeps those LDS reads at the
+            // top of the block, so the dependent chain never waits on LDS.
+            // Tokens past the end of the sequence were staged as a = 1,
+            // xi = 0, k = 0, r = 1, which leaves p unchanged bit for bit.
             if (ts >= 0)
                 group_products();          // decays, independent of the variance
             if (tid < DK) {
                 const int i = tid;
                 const float mu = P.mu;
                 float pc = p_reg;
-                constexpr int PF = 4;              // tokens read ahead
-                float kk[PF], aa[PF], xx[PF], rr[PF];
-                auto loadpf = [&](int tb) {
+                constexpr int CB = 8;              // tokens per block
+                static_assert(C % CB == 0, "variance blocks");
+                float kk[CB], aa[CB], xx[CB], rr[CB];
+                auto loadb = [&](int tb) {
 #pragma unroll
-                    for (int j = 0; j < PF; ++j) {
+                    for (int j = 0; j < CB; ++j) {
                         kk[j] = ld(Kt + (tb + j) * PK + i);
                         aa[j] = ld(ALP + (tb + j) * PK + i);
                         xx[j] = ld(XR + (tb + j) * PK + i);
                         rr[j] = s_r[tb + j];
                     }
                 };
-                loadpf(0);
+                loadb(0);
+#pragma unroll 1
+                for (int tb = 0; tb < C; tb += CB) {
+                    float a2[CB], x8[CB], m8[CB], k8[CB], r8[CB];
 #pragma unroll
-                for (int tb = 0; tb < C; tb += PF) {
-                    float a2[PF], x8[PF], m8[PF], k8[PF], r8[PF];
-#pragma unroll
-                    for (int j = 0; j < PF; ++j) {
+                    for (int j = 0; j < CB; ++j) {
                         a2[j] = aa[j] * aa[j];
                         m8[j] = mu * kk[j] * kk[j];
                         x8[j] = xx[j]; k8[j] = kk[j]; r8[j] = rr[j];
                     }
-                    if (tb + PF < C)
-                        loadpf(tb + PF);
+                    // next block (the last block re-reads itself, unused)
+                    loadb(min(tb + CB, C - CB));
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int j = 0; j < PF; ++j) {
+                    for (int j = 0; j < CB; ++j) {
                         const float pm = fmaf(a2[j], pc, x8[j]);
                         U32[(tb + j) * PP + i] = pm * k8[j];
                         const float den = fmaf(m8[j], pm, r8[j]);
