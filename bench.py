@@ -34,7 +34,7 @@ FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 # the largest prefill workload: diagonal KDN, B2 H16 T16384, d_k = d_v = 128, bf16
 HEADLINE = "diag_kdn"
 KERNEL_SOURCES = ["kdn_prefill.hip", "kdn_prefill_state.hip", "kdn_prefill_chain.hip",
-                  "kdn_variance.hip", "kdn_backward.hip", "kdn_decode.hip", "kdn_device.h",
+                  "kdn_prefill_short.hip", "kdn_variance.hip", "kdn_backward.hip", "kdn_decode.hip", "kdn_device.h",
                   "kdn_launch.h", "kdn_workspace.h"]
 
 
@@ -292,9 +292,12 @@ def bench_decode(name, reps, torch, kdn, synth):
     return res
 
 
-def bench_verify(T, reps, torch, kdn, synth):
-    """T draft tokens per sequence checked against the resident state in one
-    multi-token decode call, at the decode workload's size."""
+def bench_verify(T, reps, torch, kdn, synth, path="chunk"):
+    """T draft tokens per sequence checked against the resident state at the
+    decode workload's size (diagonal KDN): path "chunk" is one
+    kdn_chunk_prefill call (the short-sequence kernel: chunk form on MFMA),
+    path "token" one kdn_recurrent_decode_multi call (token by token, the
+    bits of T decode steps)."""
     name = "decode_diag_kdn"
     c = synth.CONFIGS[name]
     N, H, dk, dv = c["N"], c["H"], c["dk"], c["dv"]
@@ -306,30 +309,46 @@ def bench_verify(T, reps, torch, kdn, synth):
     p = torch.empty_like(inp["p0"])
 
     def step():
-        kdn.decode_multi("diag_kdn", inp["q"], inp["k"], inp["v"], alpha=inp["alpha"],
-                         proc_noise=inp["xi"], obs_noise=inp["r"], S0=inp["S0"],
-                         p0=inp["p0"], out=(o, S, p))
+        if path == "chunk":
+            kdn.prefill("diag_kdn", inp["q"], inp["k"], inp["v"], alpha=inp["alpha"],
+                        proc_noise=inp["xi"], obs_noise=inp["r"], S0=inp["S0"],
+                        p0=inp["p0"], out=(o, S, p), workspace=None)
+        else:
+            kdn.decode_multi("diag_kdn", inp["q"], inp["k"], inp["v"], alpha=inp["alpha"],
+                             proc_noise=inp["xi"], obs_noise=inp["r"], S0=inp["S0"],
+                             p0=inp["p0"], out=(o, S, p))
 
     wall, gpu = time_launches(step, reps, 3, torch)
     es = 2 if c["dtype"] == "bf16" else 4
     nbytes = verify_bytes(N, T, H, dk, dv, es)
-    flops = decode_flops_per_head_token(dk, dv) * N * H * T
     launch_s = gpu / reps
+    workload = f"verify{T}_diag_kdn" if path == "chunk" else f"multi{T}_diag_kdn"
     res = {
         "value": N * T * reps / wall, "unit": "tokens/s",
         "head_tokens_per_s": N * H * T * reps / wall,
         "ms_per_step": wall / reps * 1e3,
-        "config": {"workload": f"verify{T}_diag_kdn", "variant": "diag_kdn", "N": N,
-                   "T": T, "H": H, "d_k": dk, "d_v": dv, "dtype": c["dtype"]},
+        "config": {"workload": workload, "variant": "diag_kdn", "N": N, "T": T, "H": H,
+                   "d_k": dk, "d_v": dv, "dtype": c["dtype"],
+                   "path": "kdn_chunk_prefill (short-sequence kernel)" if path == "chunk"
+                           else "kdn_recurrent_decode_multi (token by token)"},
         "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
-                     "traffic": load_traffic(f"verify{T}_diag_kdn"),
+                     "traffic": load_traffic(workload),
                      "algorithmic_bytes": nbytes, "kernel_ms": launch_s * 1e3},
-        "alu": {"achieved": flops / launch_s / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": flops / launch_s / 1e12 / FP32_VALU_PEAK_TFLOPS,
-                "algorithmic_flops": flops},
     }
+    if path == "chunk":
+        flops = prefill_flops_per_head_token(16, dk, dv) * N * H * T
+        res["mfma"] = {"achieved": flops / launch_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s",
+                       "frac": flops / launch_s / 1e12 / BF16_PEAK_TFLOPS,
+                       "algorithmic_flops": flops}
+    else:
+        flops = decode_flops_per_head_token(dk, dv) * N * H * T
+        res["alu"] = {"achieved": flops / launch_s / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                      "unit": "TFLOP/s",
+                      "frac": flops / launch_s / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                      "algorithmic_flops": flops}
     del inp, o, S, p
     torch.cuda.empty_cache()
     return res
@@ -441,7 +460,8 @@ def main():
     ap.add_argument("--only", default=None,
                     help="run one workload and print its JSON object only (for "
                          "profiling): <name>_prefill, <name>_backward, "
-                         "decode_diag_kdn or verify16_diag_kdn")
+                         "decode_diag_kdn, verify16_diag_kdn (chunk path) or "
+                         "multi16_diag_kdn (token by token)")
     ap.add_argument("--schedule", choices=["two_pass", "single_pass"], default="two_pass",
                     help="prefill schedule: with a workspace (two-pass) or without")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -480,7 +500,10 @@ def main():
             r = bench_decode(w, max(1, args.steps // 1024), torch, kdn, synth)
         elif w.startswith("verify") and w.endswith("_diag_kdn"):
             r = bench_verify(int(w[len("verify"):-len("_diag_kdn")]), args.steps, torch,
-                             kdn, synth)
+                             kdn, synth, "chunk")
+        elif w.startswith("multi") and w.endswith("_diag_kdn"):
+            r = bench_verify(int(w[len("multi"):-len("_diag_kdn")]), args.steps, torch,
+                             kdn, synth, "token")
         else:
             raise SystemExit(f"bench.py: unknown workload {w!r}")
         r["kernel_hash"] = kernel_hash()
@@ -509,7 +532,8 @@ def main():
         for name in ("gated_deltanet", "kda", "diag_kdn", "iso_kdn"):
             w[f"{name}_backward"] = bench_backward(name, max(3, args.steps // 2),
                                                    args.warmup, torch, kdn, synth)
-        w["verify16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth)
+        w["verify16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth, "chunk")
+        w["multi16_diag_kdn"] = bench_verify(16, 20, torch, kdn, synth, "token")
         out["workloads"] = w
     ach = measure_achievable(torch)
     out["achievable"] = ach

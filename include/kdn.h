@@ -103,6 +103,13 @@ typedef enum kdn_status {
  *     start, from a scan over per-chunk variance maps) to the workspace, then
  *     a sequential pass carries S through the chunks.  This is the fast path
  *     for long sequences.
+ * bf16 calls with 1 <= T <= 16 take neither: one kernel holds each head's
+ * state on chip and applies the chunk algebra to the T tokens at once (a
+ * chunk of 16), leaving any workspace untouched.  This is the fast way to
+ * check a run of draft tokens of speculative decoding against a resident
+ * state ("معماری KDA ...", section "گام بعدی شما"): S_out / p_out elsewhere
+ * keep S0 / p0 as they were (the rollback of a rejected draft), and
+ * S_out == S0, p_out == p0 update them in place.
  *
  *   q, k        [B, T, H, d_k]  dtype
  *   v           [B, T, H, d_v]  dtype
@@ -245,7 +252,9 @@ kdn_status kdn_recurrent_decode(kdn_variant variant, kdn_dtype dtype,
  * and p_out elsewhere the resident state is left as it was, which is the
  * rollback of a rejected draft.  T = 0 copies the state.  Token t of
  * sequence n gives the same bits as the t-th of T kdn_recurrent_decode calls
- * on row (n, t) of the same inputs.
+ * on row (n, t) of the same inputs.  The same T tokens through
+ * kdn_chunk_prefill (bf16, T <= 16: the chunk form on MFMA) are faster and
+ * equal these up to the chunk form's rounding.
  * Supported: d_k, d_v in {64, 128}; dtype KDN_F32 or KDN_BF16; N, T, H >= 0.
  * Errors and asynchrony as for kdn_chunk_prefill.
  */

@@ -37,6 +37,7 @@ UNITS += [("kdn_prefill.hip", ["-DKDN_PREFILL_DISPATCH"], "kdn_prefill_dispatch.
           # MFMA accumulators in VGPRs: the chain applies VALU work (decay,
           # subtraction, bf16 rounding) to every accumulator it produces
           ("kdn_prefill_chain.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"], "kdn_prefill_chain.o"),
+          ("kdn_prefill_short.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"], "kdn_prefill_short.o"),
           ("kdn_variance.hip", [], "kdn_variance.o"),
           ("kdn_noalloc.hip", [], "kdn_noalloc.o"),
           ("kdn_backward.hip", [], "kdn_backward.o")]

@@ -122,6 +122,10 @@ hipError_t launch_variance_scan(const PrefillParams &P, hipStream_t stream);
 hipError_t launch_prefill_state(const PrefillParams &P, hipStream_t stream);
 // bf16 state pass on permuted records, one wave per 16-column block
 hipError_t launch_prefill_chain(const PrefillParams &P, hipStream_t stream);
+// bf16 prefill of short sequences (T <= PREFILL_SHORT_T), one workgroup per
+// (batch, head), chunks of 16 tokens
+constexpr int PREFILL_SHORT_T = 16;
+hipError_t launch_prefill_short(const PrefillParams &P, hipStream_t stream);
 
 // Every argument check of kdn_chunk_prefill except the workspace's own;
 // `workspace` tells whether the call has one.  The chunk length in use goes

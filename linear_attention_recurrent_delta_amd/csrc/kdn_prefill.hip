@@ -1431,6 +1431,10 @@ static hipError_t launch_two_pass(const PrefillParams &P, hipStream_t st) {
 hipError_t launch_prefill(const PrefillParams &P, hipStream_t st) {
     if ((long)P.B * P.H == 0)
         return hipSuccess;
+    // a few tokens per sequence (e.g. draft tokens checked against a resident
+    // state): one workgroup per head, whatever the schedule asked for
+    if (P.bf16 && P.T > 0 && P.T <= PREFILL_SHORT_T)
+        return launch_prefill_short(P, st);
     if (P.ws)
         return launch_two_pass(P, st);
     const int nv = prefill_value_block(P);
