@@ -7,7 +7,7 @@
 // little work per sequence for the two-pass schedule, whose prep and state
 // passes are built for thousands of tokens.  Here one workgroup of four waves
 // owns the whole d_k x d_v state of a head in MFMA accumulators (fp32) and
-// takes the sequence 16 tokens at a time with the chunk algebra of
+// takes the T <= 16 tokens as one chunk with the chunk algebra of
 // kdn_prefill.hip ("حل مشکل وابستگی علی"):
 //   E = (I + A_kk)^-1 (V - K~ S),  O = Q~ S + A_qk E,  S <- diag(gamma) S + W~^T E.
 // At C = 16 every state product is a 16 x 16 MFMA tile: wave w owns columns
@@ -25,10 +25,11 @@
 //  - contractions over tokens take U and E as the B operand straight from
 //    the accumulators: at K = 16 lane (q, n) supplies k = 4q..4q+3, which are
 //    the rows it holds, so no permutation is needed.
-// The state is read once at the start and written once at the end; the
-// per-chunk work of one head is latency-bound, so several workgroups share a
-// CU (46 KB of LDS each at d_k = 128) and the state traffic of one overlaps
-// the chunk work of another.
+// The state is read once and written once; the chunk's inputs are requested
+// before it, so the S-independent work runs while the state streams in.  That
+// work is latency-bound, so three workgroups share a CU (45 KB of LDS and
+// under 170 VGPRs per lane each at d_k = 128) and the state traffic of one
+// overlaps the chunk work of another.
 #include "kdn_device.h"
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
@@ -106,8 +107,12 @@ __device__ __forceinline__ f32x4 mfma16(const s16x4 &a, const s16x4 &b, const f3
 
 }  // namespace
 
+#ifndef KDN_SHORT_WAVES_PER_SIMD
+#define KDN_SHORT_WAVES_PER_SIMD 3
+#endif
+
 template <int VAR, int DK, int DV>
-__global__ __launch_bounds__(NT) void prefill_short_kernel(PrefillParams P) {
+__global__ __launch_bounds__(NT, KDN_SHORT_WAVES_PER_SIMD) void prefill_short_kernel(PrefillParams P) {
     using LY = ShortLayout<DK>;
     constexpr int PK = LY::PK, PU = LY::PU, GK = LY::GK, NIB = LY::NIB;
     constexpr int NTJ = DV / 64;                 // 16-column tiles per wave
@@ -157,8 +162,45 @@ __global__ __launch_bounds__(NT) void prefill_short_kernel(PrefillParams P) {
     const bf16 *gr = static_cast<const bf16 *>(P.r);
     bf16 *go = static_cast<bf16 *>(P.o);
 
-    // S[16 i + 4 q + r][c0 + 16 j + n] in sacc[i][j][r]; requested first, so
-    // the state streams in while the first chunk's prep runs
+    // The chunk's raw tiles, per-token scalars and this wave's v values go
+    // to registers first (tokens past the end: k = q = 0, a = 1, xi = 0,
+    // r = 1, beta = 0, v = 0 -- no effect on S or p).
+    constexpr int TPR = DK / 8;                  // threads per raw row
+    const int st_t = tid / TPR, st_c = (tid % TPR) * 8;
+    const int L = T;                             // T <= 16: one chunk
+    uint4 rk = make_uint4(0u, 0u, 0u, 0u), rq = rk, rx = rk;
+    uint4 ra = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+    float rr = 1.f, rb = 0.f, rga = 1.f;
+    float rv[NTJ][4];
+    if (st_t < L) {
+        const long g = seqk + (long)st_t * hdk + st_c;
+        rk = *reinterpret_cast<const uint4 *>(gk + g);
+        rq = *reinterpret_cast<const uint4 *>(gq + g);
+        if (VDECAY)
+            ra = *reinterpret_cast<const uint4 *>(ga + g);
+        if (KDN || ISO)
+            rx = *reinterpret_cast<const uint4 *>(gx + g);
+    }
+    if (tid < L) {
+        const long g = seqs + (long)tid * H;
+        if (KDN || ISO)
+            rr = to_f32(gr[g]);
+        else
+            rb = to_f32(gb[g]);
+        if (VAR == GATED_DELTANET)
+            rga = to_f32(ga[g]);
+    }
+#pragma unroll
+    for (int j = 0; j < NTJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * q + r;
+            rv[j][r] = t < L ? to_f32(gv[seqv + (long)t * hdv + c0 + 16 * j + n]) : 0.f;
+        }
+
+    // S[16 i + 4 q + r][c0 + 16 j + n] in sacc[i][j][r]; requested after the
+    // chunk's inputs, so the state streams in while the S-independent part
+    // of the chunk is computed
     f32x4 sacc[NIB][NTJ];
     const float *S0 = P.S0 ? P.S0 + (long)bh * DK * DV : nullptr;
 #pragma unroll
@@ -174,46 +216,21 @@ __global__ __launch_bounds__(NT) void prefill_short_kernel(PrefillParams P) {
     if (ISO && tid == 0)
         p_reg = P.p0[bh];
 
-    for (int t0 = 0; t0 < T; t0 += TC) {
-        const int L = min(TC, T - t0);
-        // ---- 1. raw tiles of the chunk; tokens past the end: k = q = 0,
-        //      a = 1, xi = 0, r = 1, beta = 0 (no effect on S or p)
+    {
+        // ---- 1. the chunk's raw tiles into LDS
         {
-            constexpr int TPR = DK / 8;          // threads per row
-            const int t = tid / TPR, c = (tid % TPR) * 8;
-            if (t < TC) {
-                uint4 kv = make_uint4(0u, 0u, 0u, 0u), qv = kv, xv = kv;
-                uint4 av = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
-                if (t < L) {
-                    const long g = seqk + (long)(t0 + t) * hdk + c;
-                    kv = *reinterpret_cast<const uint4 *>(gk + g);
-                    qv = *reinterpret_cast<const uint4 *>(gq + g);
-                    if (VDECAY)
-                        av = *reinterpret_cast<const uint4 *>(ga + g);
-                    if (KDN || ISO)
-                        xv = *reinterpret_cast<const uint4 *>(gx + g);
-                }
-                *reinterpret_cast<uint4 *>(Kr + t * PK + c) = kv;
-                *reinterpret_cast<uint4 *>(Qr + t * PK + c) = qv;
+            if (st_t < TC) {
+                *reinterpret_cast<uint4 *>(Kr + st_t * PK + st_c) = rk;
+                *reinterpret_cast<uint4 *>(Qr + st_t * PK + st_c) = rq;
                 if (VDECAY)
-                    *reinterpret_cast<uint4 *>(Ar + t * PK + c) = av;
+                    *reinterpret_cast<uint4 *>(Ar + st_t * PK + st_c) = ra;
                 if (KDN || ISO)
-                    *reinterpret_cast<uint4 *>(Xr + t * PK + c) = xv;
+                    *reinterpret_cast<uint4 *>(Xr + st_t * PK + st_c) = rx;
             }
             if (tid < TC) {
-                float rv = 1.f, bv = 0.f, gav = 1.f;
-                if (tid < L) {
-                    const long g = seqs + (long)(t0 + tid) * H;
-                    if (KDN || ISO)
-                        rv = to_f32(gr[g]);
-                    else
-                        bv = to_f32(gb[g]);
-                    if (VAR == GATED_DELTANET)
-                        gav = to_f32(ga[g]);
-                }
-                s_r[tid] = rv;
-                s_b[tid] = bv;
-                s_a[tid] = gav;
+                s_r[tid] = rr;
+                s_b[tid] = rb;
+                s_a[tid] = rga;
             }
             if (tid == 0)
                 *s_flag = 0;
@@ -439,13 +456,8 @@ __global__ __launch_bounds__(NT) void prefill_short_kernel(PrefillParams P) {
             for (int j = 0; j < NTJ; ++j) {
                 // U = V - K~ S (rows past the sequence end read as 0)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * q + r;
-                    const float v = t < L ? to_f32(gv[seqv + (long)(t0 + t) * hdv + c0 +
-                                                       16 * j + n])
-                                          : 0.f;
-                    ua[j][r] = v - ua[j][r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    ua[j][r] = rv[j][r] - ua[j][r];
                 // E = T U
                 const f32x4 ea = mfma16(tf, pack4(ua[j]), f32x4{0.f, 0.f, 0.f, 0.f});
                 eb[j] = pack4(ea);
@@ -455,7 +467,7 @@ __global__ __launch_bounds__(NT) void prefill_short_kernel(PrefillParams P) {
                 for (int r = 0; r < 4; ++r) {
                     const int t = 4 * q + r;
                     if (t < L)
-                        go[seqv + (long)(t0 + t) * hdv + c0 + 16 * j + n] =
+                        go[seqv + (long)t * hdv + c0 + 16 * j + n] =
                             static_cast<bf16>(oa[j][r]);
                 }
             }
@@ -476,7 +488,6 @@ __global__ __launch_bounds__(NT) void prefill_short_kernel(PrefillParams P) {
                 }
             }
         }
-        __syncthreads();            // LDS reads done before the next chunk
     }
 
     float *So = P.S_out + (long)bh * DK * DV;
