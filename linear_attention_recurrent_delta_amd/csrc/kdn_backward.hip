@@ -175,8 +175,15 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Workgroup -> (batch*head, value block).  Dispatch is round-robin over
+    // the 8 XCDs; the value blocks of one head go to one XCD, so each chunk's
+    // record crosses HBM once and the other blocks read it from that L2.
     const int nvb = P.dv / NV;
-    const int bh = blockIdx.x / nvb, vb = blockIdx.x % nvb;
+    const int G = gridDim.x;
+    int lid = blockIdx.x;
+    if ((G & 7) == 0 && ((G >> 3) % nvb) == 0)
+        lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int bh = lid / nvb, vb = lid % nvb;
     const int b = bh / P.H, h = bh % P.H;
     const int v0 = vb * NV;
     const int T = P.T, H = P.H, DV = P.dv;
