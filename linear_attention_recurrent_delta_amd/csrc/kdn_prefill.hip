@@ -234,6 +234,14 @@ __device__ __forceinline__ void mma16_f32(f32x4 &acc, const float *A, int lda,
     }
 }
 
+// Records are written once and read once, by another kernel: their stores
+// are non-temporal, so that they do not push the prep kernel's own tiles out
+// of L2 (measured: every two-pass prefill about 4 % faster).
+__device__ __forceinline__ void store_rec16(uint4 *d, uint4 v) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(d));
+}
+
 // A-operand fragment order of the workspace (kdn_workspace.h): copy the
 // R x K matrix at src (LDS, pitch in elements) to dst, 16 bytes per unit;
 // with perm (bf16), the columns of each 32-group in the permuted order.
@@ -266,7 +274,7 @@ __device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, i
                 const float *sp = reinterpret_cast<const float *>(src) + row * pitch + g * 16 + (l >> 4);
                 val = __builtin_bit_cast(uint4, make_float4(sp[0], sp[4], sp[8], sp[12]));
             }
-            d[u] = val;
+            store_rec16(d + u, val);
         }
     }
 }
@@ -293,7 +301,7 @@ __device__ __forceinline__ void store_frag_fn(char *dst, int tid, bool perm, F f
                                   : g * 16 + e * 4 + (l >> 4);
                 v[e] = from_f32<E>(f(row, k));
             }
-            d[u] = *reinterpret_cast<const uint4 *>(v);
+            store_rec16(d + u, *reinterpret_cast<const uint4 *>(v));
         }
     }
 }
