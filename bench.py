@@ -254,8 +254,13 @@ def bench_backward(name, steps, warmup, torch, kdn, synth):
     return res
 
 
-def bench_decode(name, reps, torch, kdn, synth):
-    c = synth.CONFIGS[name]
+def bench_decode(name, reps, torch, kdn, synth, shape=None):
+    """Decode steps of the diagonal-KDN decode workload (or, with shape =
+    (N, H, d, steps), of another batch of sequences and head size)."""
+    c = dict(synth.CONFIGS[name])
+    if shape is not None:
+        c["N"], c["H"], c["dk"], c["steps"] = shape
+        c["dv"] = c["dk"]
     N, H, steps, dk, dv = c["N"], c["H"], c["steps"], c["dk"], c["dv"]
     d = synth.gen_decode(N, H, steps, dk, dv, c["dtype"], seed=synth.seed_of(name),
                          device="cuda")
@@ -279,13 +284,14 @@ def bench_decode(name, reps, torch, kdn, synth):
         "value": nsteps / wall, "unit": "steps/s",
         "head_state_steps_per_s": nsteps * N * H / wall,
         "ms_per_step": wall / nsteps * 1e3,
-        "config": {"workload": f"{name}", "variant": "diag_kdn", "N": N, "H": H,
+        "config": {"workload": name if shape is None else f"{name}_N{N}_H{H}_d{dk}",
+                   "variant": "diag_kdn", "N": N, "H": H,
                    "steps": steps, "d_k": dk, "d_v": dv, "dtype": c["dtype"]},
         "roofline": {"bound": "hbm", "achieved": nbytes / launch_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": nbytes / launch_s / 1e9 / HBM_PEAK_GBS,
-                     "traffic": load_traffic(name), "algorithmic_bytes": nbytes,
-                     "kernel_ms": launch_s * 1e3},
+                     "traffic": load_traffic(name) if shape is None else None,
+                     "algorithmic_bytes": nbytes, "kernel_ms": launch_s * 1e3},
     }
     del d, S, p, o, args
     torch.cuda.empty_cache()
@@ -462,6 +468,9 @@ def main():
                          "profiling): <name>_prefill, <name>_backward, "
                          "decode_diag_kdn, verify16_diag_kdn (chunk path) or "
                          "multi16_diag_kdn (token by token)")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="time diagonal-KDN decode steps over several batch sizes "
+                         "and head sizes (one JSON line each) instead of the bench")
     ap.add_argument("--schedule", choices=["two_pass", "single_pass"], default="two_pass",
                     help="prefill schedule: with a workspace (two-pass) or without")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -487,6 +496,17 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.decode_sweep:
+        # (sequences, heads, head size, steps): from a launch-bound batch to
+        # four times the decode workload, and head size 64
+        for shape in [(8, 32, 128, 256), (32, 32, 128, 256), (128, 32, 128, 128),
+                      (256, 32, 128, 64), (1024, 32, 128, 32), (256, 32, 64, 128),
+                      (1024, 32, 64, 64)]:
+            r = bench_decode("decode_diag_kdn", 4, torch, kdn, synth, shape)
+            r["kernel_hash"] = kernel_hash()
+            print(json.dumps(r), flush=True)
+        return
 
     if args.only:
         w = args.only
