@@ -588,7 +588,10 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     F.xi = proc_noise; F.r = obs_noise;
     F.S0 = S0; F.p0 = p0; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
     F.ws = nullptr; F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
-    F.rec_perm = 0;                 // the gradient kernels read the plain order
+    // bf16: records in the permuted order of the chain kernel, which re-runs
+    // the forward and saves S at every chunk start; the gradient kernels
+    // restore the order when they stage the records
+    F.rec_perm = dtype == KDN_BF16 ? 1 : 0;
     F.states = nullptr; F.beta_out = nullptr; F.w_out = nullptr; F.invs_out = nullptr;
     F.cus = device_cus();
     if (W.total > 0) {
@@ -625,7 +628,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
             }
         }
         if (e == hipSuccess)
-            e = kdn::launch_prefill_state(F, st);
+            e = F.rec_perm ? kdn::launch_prefill_chain(F, st) : kdn::launch_prefill_state(F, st);
         if (e != hipSuccess)
             return KDN_ERR_HIP;
     }
@@ -651,6 +654,7 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     G.dS0 = dS0;
     G.dp_out = dp_out; G.dxi = dproc_noise; G.dr = dobs_noise; G.dp0 = dp0;
     G.ws = F.ws;
+    G.rec_perm = F.rec_perm;
     G.states = F.states;
     G.dstates = W.total > 0 ? static_cast<void *>(base + W.dstates) : nullptr;
     G.ws_stat = F.ws_stat; G.ws_p0 = F.ws_p0;

@@ -59,8 +59,12 @@ struct RecUnits {
                 u[n] = s[x];
         }
     }
+    // perm (bf16): the record's contraction index is in the permuted order
+    // of the chain kernel's records (each 32-group: a lane's 8 elements are
+    // columns 4q..4q+3 and 16+4q..16+4q+3), restored here
     template <bool TRANS>
-    __device__ __forceinline__ void store(E *dst, int pitch, float sgn, int tid) const {
+    __device__ __forceinline__ void store(E *dst, int pitch, float sgn, int tid,
+                                          bool perm) const {
 #pragma unroll
         for (int n = 0; n < NPT; ++n) {
             const int x = tid + NT * n;
@@ -69,7 +73,13 @@ struct RecUnits {
             const int m = grp / (K / KG), g = grp % (K / KG);
             const int row = m * 16 + (l & 15);
             if (!TRANS && sizeof(E) == 2 && sgn == 1.f) {
-                *reinterpret_cast<uint4 *>(dst + row * pitch + g * 32 + (l >> 4) * 8) = u[n];
+                if (perm) {
+                    E *d = dst + row * pitch + g * 32 + (l >> 4) * 4;
+                    *reinterpret_cast<uint2 *>(d) = make_uint2(u[n].x, u[n].y);
+                    *reinterpret_cast<uint2 *>(d + 16) = make_uint2(u[n].z, u[n].w);
+                } else {
+                    *reinterpret_cast<uint4 *>(dst + row * pitch + g * 32 + (l >> 4) * 8) = u[n];
+                }
                 continue;
             }
             if (TRANS && sizeof(E) == 2) {
@@ -87,7 +97,8 @@ struct RecUnits {
                 const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0xB1, 0xf, 0xf, false);
                 const uint32_t lo0 = odd ? r0 : m0, lo1 = odd ? r1 : m1;   // row r
                 const uint32_t hi0 = odd ? m0 : r0, hi1 = odd ? m1 : r1;   // row r + 1
-                const int col = g * 32 + (l >> 4) * 8 + (odd ? 4 : 0);
+                const int col = perm ? g * 32 + (l >> 4) * 4 + (odd ? 16 : 0)
+                                     : g * 32 + (l >> 4) * 8 + (odd ? 4 : 0);
                 uint32_t *d = reinterpret_cast<uint32_t *>(dst + col * pitch + (row & ~1));
                 const int pw = pitch / 2;                                  // dwords per row
                 d[0] = (lo0 & 0xffffu) | (hi0 << 16);
@@ -100,8 +111,10 @@ struct RecUnits {
             const E *e = reinterpret_cast<const E *>(&v);
 #pragma unroll
             for (int xx = 0; xx < EPU; ++xx) {
-                const int col = sizeof(E) == 2 ? g * 32 + (l >> 4) * 8 + xx
-                                               : g * 16 + xx * 4 + (l >> 4);
+                const int col = sizeof(E) == 2
+                                    ? (perm ? g * 32 + (l >> 4) * 4 + (xx < 4 ? xx : 12 + xx)
+                                            : g * 32 + (l >> 4) * 8 + xx)
+                                    : g * 16 + xx * 4 + (l >> 4);
                 const E val = from_f32<E>(sgn * to_f32(e[xx]));
                 if (TRANS)
                     dst[col * pitch + row] = val;
@@ -175,6 +188,8 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // records in the chain kernel's permuted column order (bf16 calls)
+    const bool perm = sizeof(E) == 2 && P.rec_perm != 0;
     // Workgroup -> (batch*head, value block).  Dispatch is round-robin over
     // the 8 XCDs; the value blocks of one head go to one XCD, so each chunk's
     // record crosses HBM once and the other blocks read it from that L2.
@@ -251,11 +266,11 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
             for (int r = 0; r < 4; ++r)
                 sv[(long)(i0 + r) * DV + v0 + j] = from_f32<E>(dacc[k][r]);
         }
-        X.aq.template store<true>(AQT, PC, 1.f, tid);
-        X.wt.template store<true>(WR, PK, 1.f, tid);
-        X.tm.template store<true>(TT, PC, 1.f, tid);
-        X.qd.template store<true>(QT, PC, 1.f, tid);
-        X.kd.template store<true>(KT, PC, -1.f, tid);
+        X.aq.template store<true>(AQT, PC, 1.f, tid, perm);
+        X.wt.template store<true>(WR, PK, 1.f, tid, perm);
+        X.tm.template store<true>(TT, PC, 1.f, tid, perm);
+        X.qd.template store<true>(QT, PC, 1.f, tid, perm);
+        X.kd.template store<true>(KT, PC, -1.f, tid, perm);
         if (DECAY && tid < DK)
             GC[tid] = X.gc;
         const int L = min(C, T - c * C);
@@ -417,6 +432,8 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // records in the chain kernel's permuted column order (bf16 calls)
+    const bool perm = sizeof(E) == 2 && P.rec_perm != 0;
     const int T = P.T, H = P.H, DV = P.dv;
     const int NC = (T + C - 1) / C;
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
@@ -528,11 +545,11 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
         tm.load(rec + LW.off_tm, tid);
         aq.load(rec + LW.off_aqk, tid);
         load_half(0);
-        wt.template store<true>(WR, PK, 1.f, tid);     // W~     [s][i]
-        kd.template store<false>(KR, PK, 1.f, tid);    // K~     [t][i]
-        tm.template store<false>(TR, PC, 1.f, tid);    // T      [t][s]
-        tm.template store<true>(TT, PC, 1.f, tid);     // T^T    [t][s]
-        aq.template store<true>(AQT, PC, 1.f, tid);    // A_qk^T [s][t]
+        wt.template store<true>(WR, PK, 1.f, tid, perm);     // W~     [s][i]
+        kd.template store<false>(KR, PK, 1.f, tid, perm);    // K~     [t][i]
+        tm.template store<false>(TR, PC, 1.f, tid, perm);    // T      [t][s]
+        tm.template store<true>(TT, PC, 1.f, tid, perm);     // T^T    [t][s]
+        aq.template store<true>(AQT, PC, 1.f, tid, perm);    // A_qk^T [s][t]
     }
     for (int jh = 0; jh < DV; jh += DVH) {
         // ---- S^T of the half, dO^T and dO

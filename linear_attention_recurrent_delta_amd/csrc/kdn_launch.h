@@ -87,6 +87,7 @@ struct BackwardParams {
     const float *dp_out;                    // isotropic KDN: dL/dp_final [B, H], may be null
     float *dxi, *dr, *dp0;                  // isotropic KDN gradients
     void *ws;                               // forward records (kdn_workspace.h)
+    int rec_perm;                           // bf16 records in the permuted column order
     void *states;                           // S at every chunk start (call dtype)
     void *dstates;                          // dS leaving every chunk (call dtype)
     // isotropic KDN: the forward variance pass's per-token sums (mean a^2,

@@ -70,7 +70,11 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 
 }  // namespace
 
-template <bool DECAY, int DK, int C, int NTJ>
+// SAVE (the forward re-run of the gradient computation): the output wave
+// writes S at the start of every chunk to P.states ([batch*head][chunk][d_k]
+// [d_v], bf16, as rounded for the chunk's products) instead of computing o;
+// S_out is not written.
+template <bool DECAY, int DK, int C, int NTJ, bool SAVE>
 __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
     constexpr int NB = C / 16;          // 16-row token blocks of a chunk
     constexpr int NIB = DK / 16;        // 16-row key blocks of S
@@ -296,14 +300,77 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
             load_w(cn);
             commit_v();                 // v of chunk cn, loaded during this chunk
         }
+        if constexpr (!SAVE) {
 #pragma unroll
-        for (int i = 0; i < NIB; ++i)
+            for (int i = 0; i < NIB; ++i)
 #pragma unroll
-            for (int j = 0; j < NTJ; ++j)
+                for (int j = 0; j < NTJ; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    P.S_out[((long)bh * DK + 16 * i + 4 * q + r) * DV + v0 + 16 * j + n] =
-                        sacc[i][j][r];
+                    for (int r = 0; r < 4; ++r)
+                        P.S_out[((long)bh * DK + 16 * i + 4 * q + r) * DV + v0 + 16 * j + n] =
+                            sacc[i][j][r];
+        }
+    } else if constexpr (SAVE) {
+        // S of chunk c from the slot into rows of an LDS tile (lane (q, n) of
+        // fragment (g, j) holds rows 32 g + 4 q + e (e < 4) and 32 g + 16 +
+        // 4 q + e - 4 of column 16 j + n), then 16-byte row segments out
+        constexpr int PSB = NV + 8, SPR = NV / 8, NSU = DK * SPR / 64;
+        static_assert(NSU * 64 == DK * SPR, "state rows");
+        __shared__ __attribute__((aligned(16))) unsigned short SBT[DK * PSB];
+        bf16 *gs = static_cast<bf16 *>(P.states) + (long)bh * NC * DK * DV;
+        unsigned pf[5];
+        auto touch = [&](int cn) {      // as the output wave's L2 probes below
+            const bool in = cn < NC;
+            const int cc = in ? cn : 0;
+            const auto rr = rsrc(ws + (long)cc * LW.rec, in ? (unsigned)LW.rec : 0u);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                pf[k] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rr, (int)(((k * 64 + lane) * nvb + vb) * 128), 0, 0);
+            const int L = min(C, T - cc * C);
+            const auto vrr = rsrc(gv + seq0 + (long)cc * C * hdv,
+                                  in ? (unsigned)(((L - 1) * hdv + NV) * 2) : 0u);
+            pf[4] = __builtin_amdgcn_raw_buffer_load_b32(vrr, (int)(lane * hdv * 2), 0, 0);
+            asm volatile("" ::: "memory");
+        };
+        if (NC > 0)
+            touch(1);
+        for (int c = 0; c < NC; ++c) {
+            __syncthreads();
+            const bf16x8 *sl = slot[c & 1];
+#pragma unroll
+            for (int g = 0; g < GK; ++g)
+#pragma unroll
+                for (int j = 0; j < NTJ; ++j) {
+                    // (halves taken from the 32-bit words: a bf16 element
+                    // extracted from the vector for a 16-bit store compiled
+                    // to element 0 every time)
+                    const u32x4 x = __builtin_bit_cast(u32x4, sl[(g * NTJ + j) * 64 + lane]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int row = 32 * g + 4 * q + (e < 4 ? e : 12 + e);
+                        const unsigned w = x[e >> 1];
+                        SBT[row * PSB + 16 * j + n] =
+                            (unsigned short)((e & 1) ? w >> 16 : w & 0xffffu);
+                    }
+                }
+#pragma unroll
+            for (int k = 0; k < 5; ++k)
+                asm volatile("" ::"v"(pf[k]));
+            touch(c + 2);
+            const auto srr = rsrc(gs + (long)c * DK * DV, (unsigned)(DK * DV * 2));
+#pragma unroll
+            for (int u = 0; u < NSU; ++u) {
+                const int x = u * 64 + lane, r = x / SPR, hs = x % SPR;
+                const u32x4 val = *reinterpret_cast<const u32x4 *>(SBT + r * PSB + 8 * hs);
+                __builtin_amdgcn_raw_buffer_store_b128(val, srr, (r * DV + v0 + 8 * hs) * 2, 0, 0);
+            }
+        }
+        if (NC > 0) {
+#pragma unroll
+            for (int k = 0; k < 5; ++k)
+                asm volatile("" ::"v"(pf[k]));
+        }
     } else {
         bf16x8 qf[NB][GK], af[NB][GC];
         auto load_qa = [&](int c) {
@@ -416,7 +483,10 @@ template <bool DECAY, int DK, int C, int NTJ>
 static hipError_t launch_chain_one(const PrefillParams &P, hipStream_t st) {
     const long heads = (long)P.B * P.H;
     const dim3 grid((unsigned)(heads * (P.dv / (16 * NTJ)))), block(128);
-    hipLaunchKernelGGL((prefill_chain_kernel<DECAY, DK, C, NTJ>), grid, block, 0, st, P);
+    if (P.states)
+        hipLaunchKernelGGL((prefill_chain_kernel<DECAY, DK, C, NTJ, true>), grid, block, 0, st, P);
+    else
+        hipLaunchKernelGGL((prefill_chain_kernel<DECAY, DK, C, NTJ, false>), grid, block, 0, st, P);
     return hipGetLastError();
 }
 

@@ -19,9 +19,10 @@
 // LDS traffic is the S / U / E exchange between the MFMA output and operand
 // layouts.  Three barriers per chunk.
 //
-// SAVE (the forward pass of the gradient computation): S at the start of every
-// chunk is written to P.states ([batch*head][chunk][d_k][d_v], float32), and
-// neither o nor S_out is written.
+// SAVE (the forward pass of a float32 gradient computation; bf16 ones use the
+// chain kernel's SAVE mode): S at the start of every chunk is written to
+// P.states ([batch*head][chunk][d_k][d_v], float32), and neither o nor S_out
+// is written.
 #include "kdn_device.h"
 #include "kdn_launch.h"
 #include "kdn_workspace.h"
