@@ -197,7 +197,7 @@ unsigned long long kdn_noalloc_scratch_bytes(void);
  * sizes (0 when there are no tokens or heads), or 0 with *status set when the
  * combination is invalid or unsupported (status may be NULL).  For bf16,
  * d_k = d_v = 128, C = 64 this is 66,048 bytes per (sequence, head, chunk),
- * plus 2,560 for diagonal KDN or 1,044 for isotropic KDN.
+ * plus 8,704 for diagonal KDN or 1,044 for isotropic KDN.
  */
 unsigned long long kdn_chunk_prefill_workspace_size(kdn_variant variant, kdn_dtype dtype,
                                                     int B, int T, int H, int d_k,

@@ -259,7 +259,8 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
     P.q = q; P.k = k; P.v = v; P.alpha = alpha; P.beta = beta;
     P.xi = proc_noise; P.r = obs_noise;
     P.S0 = S0; P.p0 = p0; P.o = o; P.S_out = S_out; P.p_out = p_out;
-    P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr; P.ws_stat = nullptr;
+    P.ws = nullptr; P.ws_mob = nullptr; P.ws_p0 = nullptr; P.ws_pre = nullptr;
+    P.ws_stat = nullptr;
     // bf16 two-pass: permuted records for the chain kernel
     P.rec_perm = (n_ws > 0 && dtype == KDN_BF16) ? 1 : 0;
     P.states = nullptr;
@@ -273,8 +274,11 @@ kdn_status kdn_chunk_prefill(kdn_variant variant, kdn_dtype dtype, int B, int T,
         char *base = static_cast<char *>(workspace) +
                      kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
         if (variant == KDN_DIAG_KDN) {
+            const long long n_mob = kdn::WsLayout::mobius_bytes(bh, nc, d_k);
             P.ws_mob = reinterpret_cast<float *>(base);
-            P.ws_p0 = reinterpret_cast<float *>(base + kdn::WsLayout::mobius_bytes(bh, nc, d_k));
+            P.ws_p0 = reinterpret_cast<float *>(base + n_mob);
+            P.ws_pre = reinterpret_cast<float *>(base + n_mob +
+                                                 kdn::WsLayout::p0_bytes(bh, nc, d_k));
         } else if (variant == KDN_ISO_KDN) {
             const long long n_mob = kdn::WsLayout::mobius_bytes(bh, nc, 1);
             P.ws_mob = reinterpret_cast<float *>(base);
@@ -587,7 +591,8 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
     F.q = q; F.k = k; F.v = v; F.alpha = alpha; F.beta = iso ? nullptr : beta;
     F.xi = proc_noise; F.r = obs_noise;
     F.S0 = S0; F.p0 = p0; F.o = nullptr; F.S_out = nullptr; F.p_out = nullptr;
-    F.ws = nullptr; F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_stat = nullptr;
+    F.ws = nullptr; F.ws_mob = nullptr; F.ws_p0 = nullptr; F.ws_pre = nullptr;
+    F.ws_stat = nullptr;
     // bf16: records in the permuted order of the chain kernel, which re-runs
     // the forward and saves S at every chunk start; the gradient kernels
     // restore the order when they stage the records
@@ -607,8 +612,11 @@ kdn_status kdn_chunk_prefill_backward(kdn_variant variant, kdn_dtype dtype, int 
         }
         if (diag) {
             char *vb = base + kdn::WsLayout::make(dtype == KDN_BF16, C, d_k).records(bh, nc);
+            const long long n_mob = kdn::WsLayout::mobius_bytes(bh, nc, d_k);
             F.ws_mob = reinterpret_cast<float *>(vb);
-            F.ws_p0 = reinterpret_cast<float *>(vb + kdn::WsLayout::mobius_bytes(bh, nc, d_k));
+            F.ws_p0 = reinterpret_cast<float *>(vb + n_mob);
+            F.ws_pre = reinterpret_cast<float *>(vb + n_mob +
+                                                 kdn::WsLayout::p0_bytes(bh, nc, d_k));
             F.w_out = reinterpret_cast<float *>(base + W.w);
             F.invs_out = reinterpret_cast<float *>(base + W.invs);
         }

@@ -36,11 +36,13 @@ struct PrefillParams {
     float *S_out;
     float *p_out;      // diagonal KDN
     // Two-pass schedule (null: single pass).  ws holds the per-chunk records
-    // (kdn_workspace.h); ws_mob / ws_p0 the KDN variance scan; ws_stat the
-    // isotropic-KDN per-token sums (mean a^2, mean xi, |k|^2, r).
+    // (kdn_workspace.h); ws_mob / ws_p0 the KDN variance scan; ws_pre the
+    // diagonal-KDN maps from each chunk start to its token segments; ws_stat
+    // the isotropic-KDN per-token sums (mean a^2, mean xi, |k|^2, r).
     void *ws;
     float *ws_mob;
     float *ws_p0;
+    float *ws_pre;
     float *ws_stat;
     // Record matrices with the contraction index of each 32-group permuted
     // (kdn_workspace.h), the layout the bf16 chain kernel reads; 0: plain

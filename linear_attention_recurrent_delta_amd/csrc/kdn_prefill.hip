@@ -418,6 +418,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     float p_reg = 0.f;                 // KDN variance of channel tid (isotropic:
                                        // of the head, in wave 0)
     float p_nxt = 0.f;                 // PREP: variance at the next unit's start
+    // Diagonal-KDN prep: thread (s, i) = (tid / DK, tid % DK) runs the
+    // variance chain of key channel i over token segment s of the chunk
+    // (VLEN tokens), starting from the chunk-start variance pushed through
+    // the segment's prefix map (identity for s = 0).
+    constexpr int VNS = WsLayout::var_segments(DK);
+    constexpr int VLEN = PREP ? C / VNS : C;
+    static_assert(!(PREP && KDN) || (VNS * DK == NT && C % VNS == 0), "variance segments");
+    float4 q_nxt = make_float4(1.f, 0.f, 0.f, 1.f);
     if (KDN && tid < DK && !PREP)
         p_reg = P.p0[(long)bh * DK + tid];
     if (ISO && tid < WAVE && !PREP)
@@ -434,8 +442,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     auto fetch = [&](int bs, int cs) {
         const int Ls = min(C, T - cs);
         const long tk = ((long)(bs / H) * T + cs) * H + bs % H;
-        if (PREP && KDN && tid < DK)
-            p_nxt = P.ws_p0[((long)bs * NC + cs / C) * DK + tid];
+        if (PREP && KDN) {
+            const long u = (long)bs * NC + cs / C;
+            p_nxt = P.ws_p0[u * DK + tid % DK];
+            if (tid >= DK)
+                q_nxt = reinterpret_cast<const float4 *>(P.ws_pre)[
+                    (u * (VNS - 1) + tid / DK - 1) * DK + pre_pos(tid % DK, (int)(16 / sizeof(E)), DK)];
+        }
         if (PREP && ISO && tid < WAVE)
             p_nxt = P.ws_p0[(long)bs * NC + cs / C];
         rk.fetch(gk + tk * DK, sk_, Ls, tid);
@@ -464,11 +477,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
     constexpr int H2 = (NT / LY::NTS) < TPG ? (NT / LY::NTS) : TPG;
     constexpr int TPG2 = TPG / H2, NG2 = NG * H2, NTO = LY::NTS * H2;
     static_assert(TPG2 * H2 == TPG && NTO <= NT, "operand layout");
-    // Diagonal KDN runs the scan layout on the last NTS threads, alongside
-    // the variance chain on the first DK (phase 2).
-    static_assert(!KDN || LY::NTS <= NT - DK, "scan threads clear of the variance chain");
+    // The single-pass diagonal-KDN kernel runs the scan layout on the last
+    // NTS threads, alongside the variance chain on the first DK (phase 2).
+    // In the prep every thread runs a variance chain; the scan layout is on
+    // the first NTS threads, whose waves pass the next unit's loads first.
+    static_assert(!(KDN && !PREP) || LY::NTS <= NT - DK, "scan threads clear of the variance chain");
     static_assert(!ISO || LY::NTS <= NT - WAVE, "scan threads clear of wave 0");
-    const int ts = (KDN || ISO) ? tid - (NT - LY::NTS) : tid;   // scan-layout thread, if >= 0
+    const int ts = ((KDN && !PREP) || ISO) ? tid - (NT - LY::NTS) : tid;   // scan-layout thread, if >= 0
     const int grp = ts % NG, oc = (ts / NG) % NO;
     const int i0 = oc * 8, t0 = grp * TPG;
     const int gh = tid % NG2, oc2 = tid / NG2;
@@ -505,6 +520,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             b = bh / H;
             h = bh % H;
             p_reg = p_nxt;
+            if (KDN && tid >= DK)        // variance at the segment start
+                p_reg = fmaf(q_nxt.x, p_reg, q_nxt.y) / fmaf(q_nxt.z, p_reg, q_nxt.w);
         }
         const int L = min(C, T - c0);
         const long tok0 = ((long)b * T + c0) * H + h;   // (b, c0, h)
@@ -544,21 +561,24 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
 
         // ---------------- 2. decays and write vectors ----------------
         if constexpr (KDN) {
-            // Variance chain, one thread per key channel (sequential in t):
+            // Variance chain, sequential in t per key channel:
             //   p- = a^2 p + xi,  u = p- k,  p = p- r / (r + mu p- k^2).
+            // Single pass: one thread per channel over the whole chunk.  Prep:
+            // one thread per (token segment, channel), each from its segment's
+            // start variance, so the dependent chain is VLEN steps long.
             // The inputs of a block of CB tokens are read into registers one
             // block ahead; the scheduling barrier keeps those LDS reads at the
             // top of the block, so the dependent chain never waits on LDS.
             // Tokens past the end of the sequence were staged as a = 1,
             // xi = 0, k = 0, r = 1, which leaves p unchanged bit for bit.
-            if (ts >= 0)
+            if (ts >= 0 && ts < LY::NTS)
                 group_products();          // decays, independent of the variance
-            if (tid < DK) {
-                const int i = tid;
+            if (PREP || tid < DK) {
+                const int i = tid % DK, t0v = (tid / DK) * VLEN, t1v = t0v + VLEN;
                 const float mu = P.mu;
                 float pc = p_reg;
-                constexpr int CB = 8;              // tokens per block
-                static_assert(C % CB == 0, "variance blocks");
+                constexpr int CB = VLEN < 8 ? VLEN : 8;   // tokens per block
+                static_assert(VLEN % CB == 0, "variance blocks");
                 float kk[CB], aa[CB], xx[CB], rr[CB];
                 auto loadb = [&](int tb) {
 #pragma unroll
@@ -569,9 +589,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                         rr[j] = s_r[tb + j];
                     }
                 };
-                loadb(0);
+                loadb(t0v);
 #pragma unroll 1
-                for (int tb = 0; tb < C; tb += CB) {
+                for (int tb = t0v; tb < t1v; tb += CB) {
                     float a2[CB], x8[CB], m8[CB], k8[CB], r8[CB];
 #pragma unroll
                     for (int j = 0; j < CB; ++j) {
@@ -580,7 +600,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
                         x8[j] = xx[j]; k8[j] = kk[j]; r8[j] = rr[j];
                     }
                     // next block (the last block re-reads itself, unused)
-                    loadb(min(tb + CB, C - CB));
+                    loadb(min(tb + CB, t1v - CB));
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int j = 0; j < CB; ++j) {
@@ -1409,7 +1429,8 @@ long long prefill_workspace_bytes(int variant, int bf16, long long B, long long 
     const long long bh = B * H, nc = num_chunks(T, C);
     long long n = WsLayout::make(bf16, C, dk).records(bh, nc);
     if (variant == DIAG_KDN)
-        n += WsLayout::mobius_bytes(bh, nc, dk) + WsLayout::p0_bytes(bh, nc, dk);
+        n += WsLayout::mobius_bytes(bh, nc, dk) + WsLayout::p0_bytes(bh, nc, dk) +
+             WsLayout::pre_bytes(bh, nc, dk);
     if (variant == ISO_KDN)
         n += WsLayout::mobius_bytes(bh, nc, 1) + WsLayout::stat_bytes(bh, nc, C) +
              WsLayout::p0_bytes(bh, nc, 1);

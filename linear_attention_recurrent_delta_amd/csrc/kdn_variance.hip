@@ -12,7 +12,9 @@
 // at the start of every chunk without a sequential pass over all tokens:
 //   1. one wave per (batch*head, chunk) composes the chunk's maps, each lane
 //      a range of its tokens for a few channels, the ranges combined in a
-//      shuffle tree;
+//      shuffle scan; besides the chunk map it stores the map from the chunk
+//      start to the start of each token segment, so the prep kernel can run
+//      the per-token chain of all segments of a chunk at once;
 //   2. per (batch*head, channel) the chunk maps are composed per segment of
 //      chunks, the segment maps applied in order from p0, then each segment's
 //      chunk maps from its start: the variance at each chunk start, and p_out.
@@ -39,14 +41,21 @@ template <typename E> struct VarVec { static constexpr int N = 16 / (int)sizeof(
 
 // One wave per (batch*head, chunk): lane = sub * TPU + cg holds channels
 // [cg N, cg N + N) over the sub-th of SUBS equal token ranges of the chunk.
-// Each lane composes its range, then the ranges are combined in a shuffle
-// tree (later ranges on the left) and lanes of range 0 write the chunk map.
+// Each lane composes its range (one or two token segments of C / NS tokens,
+// NS = WsLayout::var_segments(DK)); an inclusive scan over the ranges (a
+// shuffle per level, earlier ranges applied first) gives each lane the map
+// from the chunk start to its range end.  The last range's lanes write the
+// chunk map; every segment s >= 1 gets the map from the chunk start to its
+// first token, from which the prep kernel starts that segment's chain.
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void variance_chunk_kernel(PrefillParams P) {
     constexpr int N = VarVec<E>::N;                    // channels per lane
     constexpr int TPU = DK / N;                        // lanes per token range
     constexpr int SUBS = WAVE / TPU;                   // token ranges per chunk
     static_assert(TPU * SUBS == WAVE && (SUBS & (SUBS - 1)) == 0, "variance lanes");
+    constexpr int NS = WsLayout::var_segments(DK);     // token segments per chunk
+    constexpr int Q = NS / SUBS;                       // segments per range
+    static_assert(Q * SUBS == NS && (Q == 1 || Q == 2), "variance segments");
     const int C = P.chunk, T = P.T, H = P.H;
     const int NC = (T + C - 1) / C;
     const long unit = (long)blockIdx.x * (256 / WAVE) + threadIdx.x / WAVE;
@@ -60,8 +69,8 @@ __global__ __launch_bounds__(256) void variance_chunk_kernel(PrefillParams P) {
     const int bh = (int)(unit % BH), c = (int)(unit / BH);
     const int b = bh / H, h = bh % H;
     const int c0 = c * C, L = min(C, T - c0);
-    const int LS = C / SUBS;                           // tokens per range
-    const int tb = sub * LS, te = min(tb + LS, L);
+    const int LG = C / NS;                             // tokens per segment
+    const int tb = sub * Q * LG;
     const E *gk = static_cast<const E *>(P.k);
     const E *ga = static_cast<const E *>(P.alpha);
     const E *gx = static_cast<const E *>(P.xi);
@@ -69,56 +78,94 @@ __global__ __launch_bounds__(256) void variance_chunk_kernel(PrefillParams P) {
     const float mu = P.mu;
 
     Map2 m[N];                                         // maps p(range start) -> p
+    Map2 h1[N];                                        // Q = 2: over the first segment
 #pragma unroll
     for (int e = 0; e < N; ++e)
         m[e] = Map2{1.f, 0.f, 0.f, 1.f};
     const long row0 = ((long)b * T + c0) * H + h;
-#pragma unroll 2
-    for (int t = tb; t < te; ++t) {
-        const long row = row0 + (long)t * H;
-        float k[N], a[N], x[N];
-        load16(gk + row * DK + i0, k);
-        load16(ga + row * DK + i0, a);
-        load16(gx + row * DK + i0, x);
-        const float r = to_f32(gr[row]);
-        const float rinv = r > 0.f ? 1.f / r : 0.f;
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-            const float a2 = a[e] * a[e], mk2 = mu * k[e] * k[e];
-            float n00 = a2, n01 = x[e], n10 = 0.f, n11 = 1.f;
-            if (r > 0.f) {
-                const float cc = mk2 * rinv;
-                n10 = cc * a2;
-                n11 = fmaf(cc, x[e], 1.f);
-            } else if (mk2 != 0.f) {
-                n00 = 0.f;
-                n01 = 0.f;
+    for (int j = 0; j < Q; ++j) {
+        const int te = min(tb + (j + 1) * LG, L);
+#pragma unroll 2
+        for (int t = tb + j * LG; t < te; ++t) {
+            const long row = row0 + (long)t * H;
+            float k[N], a[N], x[N];
+            load16(gk + row * DK + i0, k);
+            load16(ga + row * DK + i0, a);
+            load16(gx + row * DK + i0, x);
+            const float r = to_f32(gr[row]);
+            const float rinv = r > 0.f ? 1.f / r : 0.f;
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                const float a2 = a[e] * a[e], mk2 = mu * k[e] * k[e];
+                float n00 = a2, n01 = x[e], n10 = 0.f, n11 = 1.f;
+                if (r > 0.f) {
+                    const float cc = mk2 * rinv;
+                    n10 = cc * a2;
+                    n11 = fmaf(cc, x[e], 1.f);
+                } else if (mk2 != 0.f) {
+                    n00 = 0.f;
+                    n01 = 0.f;
+                }
+                m[e].after(n00, n01, n10, n11);
+                if (((t - tb) & 3) == 3)
+                    m[e].rescale();
             }
-            m[e].after(n00, n01, n10, n11);
-            if (((t - tb) & 3) == 3)
-                m[e].rescale();
+        }
+        if (Q == 2 && j == 0) {
+#pragma unroll
+            for (int e = 0; e < N; ++e)
+                h1[e] = m[e];
         }
     }
+    // inclusive scan over the ranges: m <- m o (map of the ranges before)
 #pragma unroll
     for (int off = 1; off < SUBS; off <<= 1) {
-        const bool take = (sub & (2 * off - 1)) == 0;  // then sub + off < SUBS
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            const float ya = __shfl_down(m[e].a, off * TPU, WAVE);
-            const float yb = __shfl_down(m[e].b, off * TPU, WAVE);
-            const float yc = __shfl_down(m[e].c, off * TPU, WAVE);
-            const float yd = __shfl_down(m[e].d, off * TPU, WAVE);
-            if (take) {
-                m[e].after(ya, yb, yc, yd);
+            const float ya = __shfl_up(m[e].a, off * TPU, WAVE);
+            const float yb = __shfl_up(m[e].b, off * TPU, WAVE);
+            const float yc = __shfl_up(m[e].c, off * TPU, WAVE);
+            const float yd = __shfl_up(m[e].d, off * TPU, WAVE);
+            if (sub >= off) {
+                m[e].before(ya, yb, yc, yd);
                 m[e].rescale();
             }
         }
     }
-    if (sub == 0) {
-        float4 *dst = reinterpret_cast<float4 *>(P.ws_mob) + ((long)bh * NC + c) * DK + i0;
+    const long u = (long)bh * NC + c;
+    if (sub == SUBS - 1) {
+        float4 *dst = reinterpret_cast<float4 *>(P.ws_mob) + u * DK + i0;
 #pragma unroll
         for (int e = 0; e < N; ++e)
             dst[e] = make_float4(m[e].a, m[e].b, m[e].c, m[e].d);
+    }
+    // segment starts: segment g >= 1 starts from the map over segments
+    // 0 .. g-1.  Q = 1: that is the inclusive map of range g - 1, stored by
+    // its own lanes.  Q = 2: segment 2 sub starts from the inclusive map of
+    // range sub - 1, segment 2 sub + 1 from that map followed by this range's
+    // first segment.  Channel i0 + e goes to position e * TPU + i0 / N
+    // (pre_pos), so a store instruction writes contiguous entries.
+    float4 *pre = reinterpret_cast<float4 *>(P.ws_pre) + u * (NS - 1) * DK + i0 / N;
+    if constexpr (Q == 1) {
+        if (sub < SUBS - 1) {
+#pragma unroll
+            for (int e = 0; e < N; ++e)
+                pre[(long)sub * DK + e * TPU] = make_float4(m[e].a, m[e].b, m[e].c, m[e].d);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            Map2 x{__shfl_up(m[e].a, TPU, WAVE), __shfl_up(m[e].b, TPU, WAVE),
+                   __shfl_up(m[e].c, TPU, WAVE), __shfl_up(m[e].d, TPU, WAVE)};
+            if (sub == 0)
+                x = Map2{1.f, 0.f, 0.f, 1.f};
+            if (sub > 0)
+                pre[(long)(2 * sub - 1) * DK + e * TPU] = make_float4(x.a, x.b, x.c, x.d);
+            x.after(h1[e].a, h1[e].b, h1[e].c, h1[e].d);
+            x.rescale();
+            pre[(long)(2 * sub) * DK + e * TPU] = make_float4(x.a, x.b, x.c, x.d);
+        }
     }
 }
 

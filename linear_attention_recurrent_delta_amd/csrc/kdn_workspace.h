@@ -36,6 +36,16 @@ __host__ __device__ inline int perm_col(int g, int q, int e) {
 //   Mob  [bh][chunk][DK][4] float32  per-chunk composition of the variance
 //                                    maps (Mobius form, kdn_variance.hip)
 //   P0   [bh][chunk][DK]    float32  variance at each chunk start
+//   Pre  [bh][chunk][NS-1][DK][4] float32  maps from the chunk start to the
+//                                    start of token segment s = 1 .. NS-1
+//                                    (NS = var_segments(DK) segments of C / NS
+//                                    tokens), so that the prep kernel runs
+//                                    the per-token variance chain of every
+//                                    segment at once; within a [DK] block
+//                                    channel i sits at pre_pos(i, n, DK),
+//                                    n = 16 / element size (the channels one
+//                                    lane of the writing kernel holds), so
+//                                    that its lanes store contiguous entries
 // and for isotropic KDN (one variance per head):
 //   Mob  [bh][chunk][4]     float32
 //   Stat [bh][chunk][C][4]  float32  per token: mean a^2, mean xi, |k|^2, r
@@ -71,8 +81,18 @@ struct WsLayout {
     __host__ __device__ long records(long bh, long nc) const { return bh * nc * rec; }
     __host__ __device__ static long mobius_bytes(long bh, long nc, int DK) { return bh * nc * DK * 4 * 4; }
     __host__ __device__ static long p0_bytes(long bh, long nc, int DK) { return bh * nc * DK * 4; }
+    __host__ __device__ static long pre_bytes(long bh, long nc, int DK) {
+        return bh * nc * (var_segments(DK) - 1) * DK * 4 * 4;
+    }
+    // Token segments per chunk of the diagonal-KDN variance chain: one thread
+    // per (segment, key channel) in the prep kernel's 512 threads.
+    __host__ __device__ static constexpr int var_segments(int DK) { return 512 / DK; }
     __host__ __device__ static long stat_bytes(long bh, long nc, int C) { return bh * nc * C * 16; }
 };
+
+// Position of key channel i in a [DK] block of segment maps whose writer
+// holds n consecutive channels per lane (see Pre above).
+__host__ __device__ inline int pre_pos(int i, int n, int DK) { return (i % n) * (DK / n) + i / n; }
 
 // Number of chunks of a sequence of T tokens.
 __host__ __device__ inline long num_chunks(long T, int C) { return (T + C - 1) / C; }

@@ -103,7 +103,10 @@ def test_workspace_size_query(lib):
     rec = 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4
     assert rec == 66048
     assert _ws_size(lib) == (2 * 4 * 2 * rec, OK)                # T = 100: 2 chunks
-    kdn_extra = 128 * 4 * 4 + 128 * 4                            # variance maps, p0
+    # variance chunk maps, chunk-start variances, and the maps from each chunk
+    # start to its token segments 1..3 (four segments of 16 tokens at d_k = 128)
+    kdn_extra = 128 * 4 * 4 + 128 * 4 + 3 * 128 * 4 * 4
+    assert kdn_extra == 8704
     assert _ws_size(lib, variant=3) == (2 * 4 * 2 * (rec + kdn_extra), OK)
     iso_extra = 4 * 4 + 64 * 4 * 4 + 4                           # map, token sums, p0
     assert iso_extra == 1044

@@ -139,6 +139,8 @@ def test_prefill_kdn_degenerate_values(variant):
     e = dict(inp)
     r = inp["r"].clone()
     r[:, 5] = 0
+    r[:, 16] = 0          # first token of a 16-token segment of the prep's chain
+    r[:, 47:49] = 0       # last and first tokens on either side of a segment start
     r[:, 64:67] = 0
     r[:, 129] = 0
     e["r"] = r
