@@ -100,7 +100,9 @@ typedef enum kdn_status {
  *   - workspace != NULL: the two-pass schedule.  Chunk-parallel kernels write
  *     each chunk's S-independent products (decay-scaled operands, A_qk, the
  *     triangular inverse; for KDN also the variance at each chunk
- *     start, from a scan over per-chunk variance maps) to the workspace, then
+ *     start, from a scan over per-chunk variance maps, and for diagonal KDN
+ *     the maps from each chunk start to its token segments) to the
+ *     workspace, then
  *     a sequential pass carries S through the chunks.  This is the fast path
  *     for long sequences.
  * bf16 calls with 1 <= T <= 16 take neither: one kernel holds each head's
