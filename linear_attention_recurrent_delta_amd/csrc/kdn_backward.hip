@@ -266,8 +266,9 @@ __global__ __launch_bounds__(512) void backward_state_kernel(BackwardParams P) {
             for (int r = 0; r < 4; ++r)
                 sv[(long)(i0 + r) * DV + v0 + j] = from_f32<E>(dacc[k][r]);
         }
-        X.aq.template store<true>(AQT, PC, 1.f, tid, perm);
-        X.wt.template store<true>(WR, PK, 1.f, tid, perm);
+        // permuted (bf16 chain kernel) records hold -A_qk and -W~^T
+        X.aq.template store<true>(AQT, PC, perm ? -1.f : 1.f, tid, perm);
+        X.wt.template store<true>(WR, PK, perm ? -1.f : 1.f, tid, perm);
         X.tm.template store<true>(TT, PC, 1.f, tid, perm);
         X.qd.template store<true>(QT, PC, 1.f, tid, perm);
         X.kd.template store<true>(KT, PC, -1.f, tid, perm);
@@ -545,11 +546,12 @@ __global__ __launch_bounds__(512) void backward_chunk_kernel(BackwardParams P) {
         tm.load(rec + LW.off_tm, tid);
         aq.load(rec + LW.off_aqk, tid);
         load_half(0);
-        wt.template store<true>(WR, PK, 1.f, tid, perm);     // W~     [s][i]
+        // permuted (bf16 chain kernel) records hold -W~^T and -A_qk
+        wt.template store<true>(WR, PK, perm ? -1.f : 1.f, tid, perm);     // W~     [s][i]
         kd.template store<false>(KR, PK, 1.f, tid, perm);    // K~     [t][i]
         tm.template store<false>(TR, PC, 1.f, tid, perm);    // T      [t][s]
         tm.template store<true>(TT, PC, 1.f, tid, perm);     // T^T    [t][s]
-        aq.template store<true>(AQT, PC, 1.f, tid, perm);    // A_qk^T [s][t]
+        aq.template store<true>(AQT, PC, perm ? -1.f : 1.f, tid, perm);    // A_qk^T [s][t]
     }
     for (int jh = 0; jh < DV; jh += DVH) {
         // ---- S^T of the half, dO^T and dO

@@ -244,10 +244,11 @@ __device__ __forceinline__ void store_rec16(uint4 *d, uint4 v) {
 
 // A-operand fragment order of the workspace (kdn_workspace.h): copy the
 // R x K matrix at src (LDS, pitch in elements) to dst, 16 bytes per unit;
-// with perm (bf16), the columns of each 32-group in the permuted order.
+// with perm (bf16), the columns of each 32-group in the permuted order, and
+// with neg (bf16) every element negated (sign bit flipped, exact).
 template <typename E, int R, int K, int NT>
 __device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, int tid,
-                                           bool perm) {
+                                           bool perm, bool neg = false) {
     constexpr int EPU = 16 / (int)sizeof(E);
     constexpr int KG = sizeof(E) == 2 ? 32 : 16;
     constexpr int NU = R * K / EPU;
@@ -270,6 +271,8 @@ __device__ __forceinline__ void store_frag(char *dst, const E *src, int pitch, i
                 } else {
                     val = *reinterpret_cast<const uint4 *>(src + row * pitch + g * 32 + (l >> 4) * 8);
                 }
+                const unsigned flip = neg ? 0x80008000u : 0u;
+                val = make_uint4(val.x ^ flip, val.y ^ flip, val.z ^ flip, val.w ^ flip);
             } else {
                 const float *sp = reinterpret_cast<const float *>(src) + row * pitch + g * 16 + (l >> 4);
                 val = __builtin_bit_cast(uint4, make_float4(sp[0], sp[4], sp[8], sp[12]));
@@ -1007,20 +1010,22 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             // waves 4.. invert the diagonal blocks
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
+            // permuted (chain kernel) records hold -W~^T and -A_qk
             if constexpr (SPREP) {
+                const float sg = perm ? -1.f : 1.f;
                 store_frag_fn<E, C, DK, 256>(rec + LW.off_kd, tid, perm, [&](int t, int i) {
                     return ld(Kt + t * PK + i) * s_gt[t]; });
                 store_frag_fn<E, C, DK, 256>(rec + LW.off_qd, tid, perm, [&](int t, int i) {
                     return ld(Qt + t * PK + i) * s_gt[t]; });
                 // W~^T (strided reads of K): half here, half on waves 4-7 below
                 store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, perm, [&](int i, int t) {
-                    return ld(Kt + t * PK + i) * s_wsc[t]; });
+                    return ld(Kt + t * PK + i) * (sg * s_wsc[t]); });
             } else {
                 store_frag<E, C, DK, 256>(rec + LW.off_kd, Kt, PK, tid, perm);
                 store_frag<E, C, DK, 256>(rec + LW.off_qd, Qt, PK, tid, perm);
-                store_frag<E, DK, C, 256>(rec + LW.off_wdt, WtT, PC, tid, perm);
+                store_frag<E, DK, C, 256>(rec + LW.off_wdt, WtT, PC, tid, perm, perm);
             }
-            store_frag<E, C, C, 256>(rec + LW.off_aqk, AQ, PC, tid, perm);
+            store_frag<E, C, C, 256>(rec + LW.off_aqk, AQ, PC, tid, perm, perm);
         } else if (!PREP && wv < 4) {
             for (int x = wv; x < NTU; x += 4) {
                 const int mi = x / NTJ, nj = x % NTJ;
@@ -1116,8 +1121,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(PrefillParams P) {
             // the other half of its units, after this wave's diagonal block
             const WsLayout LW = WsLayout::make(sizeof(E) == 2, C, DK);
             char *rec = static_cast<char *>(P.ws) + ((long)bh * NC + c0 / C) * LW.rec;
+            const float sg = perm ? -1.f : 1.f;     // -W~^T in permuted records
             store_frag_fn<E, DK, C, 512>(rec + LW.off_wdt, tid, perm, [&](int i, int t) {
-                return ld(Kt + t * PK + i) * s_wsc[t]; });
+                return ld(Kt + t * PK + i) * (sg * s_wsc[t]); });
         }
         __syncthreads();
         // ---------------- 4b. off-diagonal blocks of T ----------------

@@ -20,6 +20,12 @@
 // adjacent 16-row tiles, rounded to bf16.  The whole chain runs inside one
 // wave: no LDS exchange and no barrier between its three products.
 //
+// v enters without a transposition: its token rows are loaded as A-operand
+// fragments (16-byte row segments) and multiplied by -I, which puts -V in the
+// accumulator layout of U exactly; K~ S then accumulates onto it, so the
+// chain carries -U and -E, and the permuted records hold -W~^T and -A_qk
+// (kdn_workspace.h), which turn them back into the S update and the output.
+//
 // Workgroup = two waves for one (batch*head, 16*NTJ columns of S):
 //   wave 0 (chain): S in registers for the whole sequence; per chunk U, E and
 //     the S update, then hands S (as it was at the chunk start) and E to
@@ -85,15 +91,12 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
     constexpr int NSF = GK * NTJ;       // S fragments handed to the output wave
     constexpr int NEF = GC * NTJ;       // E fragments
     __shared__ bf16x8 slot[2][(NSF + NEF) * 64];
-    // v and o tiles move between global memory and the accumulator layout
-    // through LDS: 16-byte row accesses in global memory (LPR lanes per row,
-    // RPI rows per instruction, NVI instructions per chunk), 2- and 8-byte
-    // LDS accesses in the MFMA layout.
+    // o moves from the accumulator layout to global memory through LDS:
+    // 2-byte LDS writes in the MFMA layout, then 16-byte row accesses (LPR
+    // lanes per row, RPI rows per instruction, NVI instructions per chunk).
     constexpr int LPR = NV / 8, RPI = 64 / LPR, NVI = C / RPI;
-    constexpr int PVT = C + 4;            // v^T [column][token], pitch (bf16)
     constexpr int POB = NV + 8;           // o [token][column], pitch (bf16)
-    static_assert(RPI * NVI == C && (PVT * 2) % 8 == 0 && (POB * 2) % 16 == 0, "v/o tiles");
-    __shared__ __attribute__((aligned(16))) bf16 VT[NV * PVT];
+    static_assert(RPI * NVI == C && (POB * 2) % 16 == 0, "o tiles");
     __shared__ __attribute__((aligned(16))) bf16 OB[C * POB];
 
     const int lane = threadIdx.x & 63;
@@ -146,7 +149,23 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                                          : 0.f;
         bf16x8 kf[NB][GK], tf[NB][GC], wf[NIB][GC];
         f32x4 gm[NIB];
-        u32x4 vraw[NVI];                // next chunk's v rows, 8 bf16 per lane
+        // v of the chunk as A-operand fragments: vf[m] holds token row
+        // 16 m + n, columns 8 q .. 8 q + 7 of the block (zero for q >= NV / 8),
+        // so that -V comes out of one MFMA per tile against -I (below) in the
+        // accumulator layout of U, with no transposition
+        bf16x8 vf[NB];
+        unsigned voff[NB];
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+            voff[m] = 8 * q < NV ? (unsigned)(((16 * m + n) * hdv + 8 * q) * 2) : 0x70000000u;
+        // B operand -I for column tile j: k-slot 8 q + e (column 8 q + e of
+        // the block) against column 16 j + n
+        bf16x8 nid[NTJ];
+#pragma unroll
+        for (int j = 0; j < NTJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                nid[j][e] = static_cast<bf16>(8 * q + e == 16 * j + n ? -1.f : 0.f);
         auto load_k = [&](int c) {
             const auto rr = rec(c);
 #pragma unroll
@@ -155,22 +174,12 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                 for (int g = 0; g < GK; ++g)
                     kf[m][g] = frag(rr, lane16, (int)LW.off_kd + (m * GK + g) * 1024);
         };
+        // rows past the sequence end and columns past the block read 0
         auto load_v = [&](int c) {
             const auto vrr = rows(gv, c);
 #pragma unroll
-            for (int h = 0; h < NVI; ++h)
-                vraw[h] = __builtin_amdgcn_raw_buffer_load_b128(vrr, (int)rlane, rsoff(h), 0);
-        };
-        // the loaded rows into v^T (this wave alone reads VT, after its own
-        // writes, so no barrier is involved)
-        auto commit_v = [&]() {
-#pragma unroll
-            for (int h = 0; h < NVI; ++h) {
-                const bf16x8 x = __builtin_bit_cast(bf16x8, vraw[h]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    VT[(rcol + e) * PVT + h * RPI + rrow] = x[e];
-            }
+            for (int m = 0; m < NB; ++m)
+                vf[m] = frag(vrr, voff[m], 0);
         };
         auto load_t = [&](int c) {
             const auto rr = rec(c);
@@ -206,7 +215,6 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
             load_v(0);
             load_t(0);
             load_w(0);
-            commit_v();
         }
         for (int c = 0; c < NC; ++c) {
             const int cn = min(c + 1, NC - 1);   // the last chunk reloads itself
@@ -232,13 +240,15 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                             sacc[i][j][r] *= gm[i][r];
                 load_g(cn);
             }
-            // U = V - K~ S
+            // -U = K~ S - V: the accumulators start at -V (V times -I, exact)
+            // and K~ S accumulates onto them
             f32x4 ua[NB][NTJ];
 #pragma unroll
             for (int m = 0; m < NB; ++m)
 #pragma unroll
                 for (int j = 0; j < NTJ; ++j)
-                    ua[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    ua[m][j] = mfma(vf[m], nid[j], f32x4{0.f, 0.f, 0.f, 0.f});
+            load_v(cn);
 #pragma unroll
             for (int g = 0; g < GK; ++g)
 #pragma unroll
@@ -247,27 +257,13 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                     for (int j = 0; j < NTJ; ++j)
                         ua[m][j] = mfma(kf[m][g], sb[g][j], ua[m][j]);
             load_k(cn);
-#pragma unroll
-            for (int m = 0; m < NB; ++m)
-#pragma unroll
-                for (int j = 0; j < NTJ; ++j) {
-                    // v[16 m + 4 q + r][16 j + n], r = 0..3: one 8-byte read
-                    const uint2 vv = *reinterpret_cast<const uint2 *>(
-                        VT + (16 * j + n) * PVT + 16 * m + 4 * q);
-                    const unsigned w4[4] = {vv.x << 16, vv.x & 0xffff0000u, vv.y << 16,
-                                            vv.y & 0xffff0000u};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        ua[m][j][r] = __builtin_bit_cast(float, w4[r]) - ua[m][j][r];
-                }
-            load_v(cn);
             bf16x8 ub[GC][NTJ];
 #pragma unroll
             for (int g = 0; g < GC; ++g)
 #pragma unroll
                 for (int j = 0; j < NTJ; ++j)
                     ub[g][j] = pack8(ua[2 * g][j], ua[2 * g + 1][j]);
-            // E = T U (T lower triangular: groups at or left of the diagonal)
+            // -E = T (-U) (T lower triangular: groups at or left of the diagonal)
             f32x4 ea[NB][NTJ];
 #pragma unroll
             for (int m = 0; m < NB; ++m)
@@ -289,7 +285,7 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                     sl[(NSF + g * NTJ + j) * 64 + lane] = eb[g][j];
                 }
             __syncthreads();
-            // S <- diag(gamma_C) S + W~^T E
+            // S <- diag(gamma_C) S + W~^T E, as (-W~^T) (-E) from the record
 #pragma unroll
             for (int g = 0; g < GC; ++g)
 #pragma unroll
@@ -298,7 +294,6 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
                     for (int j = 0; j < NTJ; ++j)
                         sacc[i][j] = mfma(wf[i][g], eb[g][j], sacc[i][j]);
             load_w(cn);
-            commit_v();                 // v of chunk cn, loaded during this chunk
         }
         if constexpr (!SAVE) {
 #pragma unroll

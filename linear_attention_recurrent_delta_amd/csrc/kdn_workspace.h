@@ -27,7 +27,8 @@
 //   instead of g*32 + (l >> 4)*8 + e: the k-slots of lane l then line up
 //   with the rows 4 (l >> 4) .. + 3 that lane l holds of two adjacent 16-row
 //   accumulator tiles, so a product's B operand can be taken from the lane's
-//   own accumulators (kdn_prefill_chain.hip).
+//   own accumulators (kdn_prefill_chain.hip).  Permuted records also hold
+//   WdT and Aqk negated (-W~^T, -A_qk): the chain kernel carries -U and -E.
 __host__ __device__ inline int perm_col(int g, int q, int e) {
     return g * 32 + (e & 4 ? 16 : 0) + 4 * q + (e & 3);
 }
