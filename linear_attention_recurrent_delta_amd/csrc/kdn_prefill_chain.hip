@@ -155,9 +155,12 @@ __global__ __launch_bounds__(128) void prefill_chain_kernel(PrefillParams P) {
         // accumulator layout of U, with no transposition
         bf16x8 vf[NB];
         unsigned voff[NB];
+        // lanes past the block's columns: an offset at the range of a whole
+        // chunk, which no chunk's descriptor reaches
+        const unsigned vdead = (unsigned)(((C - 1) * hdv + NV) * 2);
 #pragma unroll
         for (int m = 0; m < NB; ++m)
-            voff[m] = 8 * q < NV ? (unsigned)(((16 * m + n) * hdv + 8 * q) * 2) : 0x70000000u;
+            voff[m] = 8 * q < NV ? (unsigned)(((16 * m + n) * hdv + 8 * q) * 2) : vdead;
         // B operand -I for column tile j: k-slot 8 q + e (column 8 q + e of
         // the block) against column 16 j + n
         bf16x8 nid[NTJ];
